@@ -1,0 +1,205 @@
+"""CPU oracle for the Gated DeltaNet hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the bench's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding) never
+loads it.  The arithmetic lives in ``gdn_oracle.c`` (plain C, double precision);
+this module compiles it with gcc and marshals numpy arrays through ctypes.
+
+Parity status of every function: pinned (see tests/test_oracle_pins.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, F16, BF16 = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile gdn_oracle.c -> liboracle.so (gcc -O2, strict IEEE: no fast-math,
+    no FMA contraction, so every product and sum is rounded as written)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+                               "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i64, vp, dbl, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_int
+        lib.oracle_decode_value.restype = dbl
+        lib.oracle_decode_value.argtypes = [vp, i32, i64]
+        lib.oracle_softplus.restype = None
+        lib.oracle_softplus.argtypes = [vp, vp, i64]
+        lib.oracle_gate.restype = i32
+        lib.oracle_gate.argtypes = [i64, i64, vp, i32, i64, vp, vp, vp]
+        lib.oracle_l2norm.restype = None
+        lib.oracle_l2norm.argtypes = [vp, vp, i64, i64, dbl]
+        lib.oracle_decode.restype = i32
+        lib.oracle_decode.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, i32, i64, i64, i64,
+                                      vp, vp, i64, vp, i64, vp, dbl, dbl, i32, vp, vp, vp]
+        lib.oracle_prefill_varlen.restype = i32
+        lib.oracle_prefill_varlen.argtypes = [i64, vp, i64, i64, i64, i64, vp, vp, vp, i32,
+                                              i64, i64, i64, vp, vp, i64, vp, i64, vp, vp,
+                                              dbl, dbl, i32, vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _need(a: np.ndarray, dtype) -> np.ndarray:
+    assert a.dtype == dtype and a.flags.c_contiguous, (a.dtype, dtype)
+    return a
+
+
+def decode_value(buf: np.ndarray, dt: int, off: int) -> float:
+    return _load().oracle_decode_value(_p(buf), dt, off)
+
+
+def softplus(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    _load().oracle_softplus(_p(x), _p(y), x.size)
+    return y
+
+
+def l2norm(x, eps: float) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    y = np.empty_like(x)
+    _load().oracle_l2norm(_p(x), _p(y), x.size // d, d, float(eps))
+    return y
+
+
+def gate(alpha: np.ndarray, alpha_dt: int, dt_bias: np.ndarray, ssm_a: np.ndarray,
+         alpha_row_stride: Optional[int] = None) -> np.ndarray:
+    """g [rows, hv] f64 from alpha [rows, hv] (storage array, 2-D)."""
+    rows = alpha.shape[0]
+    hv = dt_bias.shape[0]
+    rs = alpha.shape[1] if alpha_row_stride is None else alpha_row_stride
+    g = np.empty((rows, hv), dtype=np.float64)
+    rc = _load().oracle_gate(rows, hv, _p(np.ascontiguousarray(alpha)), alpha_dt, rs,
+                             _p(_need(dt_bias, np.float32)), _p(_need(ssm_a, np.float32)),
+                             _p(g))
+    if rc:
+        raise OracleError(f"oracle_gate: error {rc}")
+    return g
+
+
+def decode(*, batch, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs, v, v_off, v_rs, in_dt,
+           g, beta, pool, idx, scale, l2_eps=1e-6, l2norm=True, head_mask=None,
+           state_out=None):
+    """One decode step.  q/k/v are storage buffers addressed as
+    buf.flat[off + row*rs + head*D + d].  Returns (out [B,hv,dv] f64,
+    state_out [B,hv,dv,dk] f64 = updated states of the live rows)."""
+    lib = _load()
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    beta = _need(beta, np.float32)
+    pool = _need(pool, np.float32)
+    idx = _need(np.asarray(idx, dtype=np.int32), np.int32)
+    out = np.zeros((batch, hv, dv), dtype=np.float64)
+    if state_out is None:
+        state_out = np.zeros((batch, hv, dv, dk), dtype=np.float64)
+    hm = None if head_mask is None else np.ascontiguousarray(head_mask, dtype=np.uint8)
+    es = q.itemsize
+    rc = lib.oracle_decode(batch, hk, hv, dk, dv,
+                           q.ctypes.data + q_off * es, k.ctypes.data + k_off * es,
+                           v.ctypes.data + v_off * es, in_dt, q_rs, k_rs, v_rs,
+                           _p(g), _p(beta), beta.shape[1], _p(pool), pool.shape[0], _p(idx),
+                           float(scale), float(l2_eps), int(bool(l2norm)), _p(hm),
+                           _p(out), _p(state_out))
+    if rc:
+        raise OracleError(f"oracle_decode: error {rc}")
+    return out, state_out
+
+
+def prefill_varlen(*, cu_seqlens, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs, v, v_off,
+                   v_rs, in_dt, g, beta, pool, idx, has_init, scale, l2_eps=1e-6,
+                   l2norm=True, head_mask=None):
+    """Varlen prefill.  Returns (out [T,hv,dv] f64, final states [N,hv,dv,dk] f64)."""
+    lib = _load()
+    cu = _need(np.asarray(cu_seqlens, dtype=np.int32), np.int32)
+    n = cu.shape[0] - 1
+    t = int(cu[-1])
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    beta = _need(beta, np.float32)
+    pool = _need(pool, np.float32)
+    idx_a = None if idx is None else _need(np.asarray(idx, dtype=np.int32), np.int32)
+    hi = None if has_init is None else _need(np.asarray(has_init, dtype=np.int8), np.int8)
+    hm = None if head_mask is None else np.ascontiguousarray(head_mask, dtype=np.uint8)
+    out = np.zeros((t, hv, dv), dtype=np.float64)
+    st = np.zeros((n, hv, dv, dk), dtype=np.float64)
+    es = q.itemsize
+    rc = lib.oracle_prefill_varlen(n, _p(cu), hk, hv, dk, dv,
+                                   q.ctypes.data + q_off * es, k.ctypes.data + k_off * es,
+                                   v.ctypes.data + v_off * es, in_dt, q_rs, k_rs, v_rs,
+                                   _p(g), _p(beta), beta.shape[1], _p(pool), pool.shape[0],
+                                   _p(idx_a), _p(hi), float(scale), float(l2_eps),
+                                   int(bool(l2norm)), _p(hm), _p(out), _p(st))
+    if rc:
+        raise OracleError(f"oracle_prefill_varlen: error {rc}")
+    return out, st
+
+
+# ---- convenience wrappers over the seeded workload cases ------------------
+def decode_case(case, head_mask=None, rows=None):
+    """Oracle for a workloads.DecodeCase: gate then one recurrence step.
+    `rows` (optional index array) restricts the batch to those rows."""
+    qv, kv, vv = case.q, case.k, case.v
+    alpha, beta, idx = case.alpha, case.beta, case.idx
+    qbuf, kbuf, vbuf = qv.buf, kv.buf, vv.buf
+    if rows is not None:
+        rows = np.asarray(rows)
+        qbuf = np.ascontiguousarray(qbuf.reshape(case.batch, -1)[rows])
+        kbuf = qbuf if kv.buf is qv.buf else np.ascontiguousarray(
+            kbuf.reshape(case.batch, -1)[rows])
+        vbuf = qbuf if vv.buf is qv.buf else np.ascontiguousarray(
+            vbuf.reshape(case.batch, -1)[rows])
+        alpha = np.ascontiguousarray(alpha[rows])
+        beta = np.ascontiguousarray(beta[rows])
+        idx = np.ascontiguousarray(idx[rows])
+    batch = alpha.shape[0]
+    g = gate(alpha, F32, case.dt_bias, case.ssm_a)
+    return decode(batch=batch, hk=case.hk, hv=case.hv, dk=case.dk, dv=case.dv,
+                  q=qbuf, q_off=qv.offset, q_rs=qv.row_stride,
+                  k=kbuf, k_off=kv.offset, k_rs=kv.row_stride,
+                  v=vbuf, v_off=vv.offset, v_rs=vv.row_stride, in_dt=case.in_dtype,
+                  g=g, beta=beta, pool=case.pool, idx=idx, scale=case.scale,
+                  l2_eps=case.l2_eps, l2norm=case.l2norm, head_mask=head_mask)
+
+
+def prefill_case(case, head_mask=None):
+    """Oracle for a workloads.PrefillCase: gate then the varlen recurrence."""
+    g = gate(case.alpha, F32, case.dt_bias, case.ssm_a)
+    return prefill_varlen(cu_seqlens=case.cu_seqlens, hk=case.hk, hv=case.hv, dk=case.dk,
+                          dv=case.dv, q=case.q.buf, q_off=case.q.offset, q_rs=case.q.row_stride,
+                          k=case.k.buf, k_off=case.k.offset, k_rs=case.k.row_stride,
+                          v=case.v.buf, v_off=case.v.offset, v_rs=case.v.row_stride,
+                          in_dt=case.in_dtype, g=g, beta=case.beta, pool=case.pool,
+                          idx=case.idx, has_init=case.has_init, scale=case.scale,
+                          l2_eps=case.l2_eps, l2norm=case.l2norm, head_mask=head_mask)

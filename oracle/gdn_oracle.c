@@ -1,0 +1,308 @@
+/*
+ * gdn_oracle.c -- plain, slow CPU reference for the Gated DeltaNet hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the GPU library and neither one includes the other.
+ *
+ * Everything is computed in double precision from the exact input bytes the GPU
+ * reads (f32, IEEE-754 binary16 or bfloat16, decoded here by this file's own
+ * routines), token by token, with no blocking, fusion or reassociation beyond
+ * what the definitions below state.  Results are returned unrounded in f64.
+ *
+ * Sources (the web pages this method is defined on):
+ *  - Winery-Strata, src/kernels/elementwise_parity.cpp, "1. gdn_gate" block:
+ *    the gate g = softplus(alpha + dt_bias) * ssm_a, softplus returning x when
+ *    x > 20 and log1p(exp(x)) otherwise, computed in double.
+ *  - vllm.cpp, tests/vt/test_ops_gdn.cpp:
+ *      "gdn decode: hand-computed single step" (the per-token recurrence:
+ *       decay, S@k, v', rank-1 update, output from the updated state; state
+ *       rows index v, columns index k);
+ *      "gdn prefill: hand-computed 3-token recurrence table" and the varlen
+ *       test (cu_seqlens segments, per-sequence state read then overwritten);
+ *      "gdn decode + conv update: indexed in-place == compact reference"
+ *       (state addressed through per-sequence slot indices);
+ *      PackedDecodeReference (q/k L2-norm with eps inside the square root,
+ *       q scaled after normalising, GQA head hk = hv / (Hv/Hk), slot < 0 gives
+ *       a zero output row and leaves the state alone, duplicate or
+ *       out-of-range live slots are errors);
+ *      "l2norm: plain sum of squares over the last dim".
+ *
+ * Parity pins live in tests/test_oracle_pins.py (the pages' worked values and
+ * the invariants listed there).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_F16 1
+#define OR_BF16 2
+
+#define OR_OK 0
+#define OR_ERR_ARG -1
+#define OR_ERR_SHAPE -3
+#define OR_ERR_SLOT -4
+
+/* ------------------------------------------------------------------------
+ * Storage decoders, from the format definitions.
+ *  binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits;
+ *            exponent 0 = subnormal (fraction * 2^-24), 31 = inf/NaN.
+ *  bfloat16: the top 16 bits of an IEEE-754 binary32.
+ * ------------------------------------------------------------------------ */
+static double half_to_double(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int e = (h >> 10) & 0x1f;
+  const int f = h & 0x3ff;
+  double mag;
+  if (e == 0) {
+    mag = ldexp((double)f, -24);
+  } else if (e == 31) {
+    mag = f ? NAN : INFINITY;
+  } else {
+    mag = ldexp((double)(1024 + f), e - 25);
+  }
+  return sign ? -mag : mag;
+}
+
+static double bf16_to_double(uint16_t b) {
+  uint32_t bits = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+static double load_elem(const void* base, int dt, int64_t off) {
+  switch (dt) {
+    case OR_F32: return (double)((const float*)base)[off];
+    case OR_F16: return half_to_double(((const uint16_t*)base)[off]);
+    case OR_BF16: return bf16_to_double(((const uint16_t*)base)[off]);
+    default: return NAN;
+  }
+}
+
+/* exported so the tests can pin the decoders against the format definitions */
+double oracle_decode_value(const void* base, int dt, int64_t off) {
+  return load_elem(base, dt, off);
+}
+
+/* ------------------------------------------------------------------------
+ * Gate (Winery-Strata elementwise_parity.cpp, gdn_gate fixture):
+ *   x  = alpha + dt_bias[h]
+ *   sp = x > 20 ? x : log1p(exp(x))
+ *   g  = sp * ssm_a[h]           (ssm_a = -exp(A_log) < 0 is given)
+ * alpha is [rows, hv] with a row stride in elements.  g is [rows, hv] f64.
+ * ------------------------------------------------------------------------ */
+static double softplus_branch(double x) { return x > 20.0 ? x : log1p(exp(x)); }
+
+void oracle_softplus(const double* x, double* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = softplus_branch(x[i]);
+}
+
+int oracle_gate(int64_t rows, int64_t hv, const void* alpha, int alpha_dt,
+                int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
+                double* g) {
+  if (rows < 0 || hv <= 0 || alpha_row_stride < hv) return OR_ERR_SHAPE;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t h = 0; h < hv; ++h) {
+      const double x = load_elem(alpha, alpha_dt, r * alpha_row_stride + h) + (double)dt_bias[h];
+      g[r * hv + h] = softplus_branch(x) * (double)ssm_a[h];
+    }
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * L2 norm over the last dim (vllm.cpp "l2norm: plain sum of squares"):
+ *   y = x / sqrt(sum_d x_d^2 + eps)
+ * ------------------------------------------------------------------------ */
+static void l2_normalize(double* x, int64_t d, double eps) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < d; ++i) ss += x[i] * x[i];
+  const double inv = 1.0 / sqrt(ss + eps);
+  for (int64_t i = 0; i < d; ++i) x[i] *= inv;
+}
+
+void oracle_l2norm(const double* x, double* y, int64_t rows, int64_t d, double eps) {
+  for (int64_t r = 0; r < rows; ++r) {
+    memcpy(y + r * d, x + r * d, (size_t)d * sizeof(double));
+    l2_normalize(y + r * d, d, eps);
+  }
+}
+
+/* ------------------------------------------------------------------------
+ * One token of the gated delta rule on one head (vllm.cpp, "gdn decode:
+ * hand-computed single step").  S is [dv][dk], rows index v, columns index k.
+ *   S  *= exp(g)
+ *   sk  = S @ k
+ *   v'  = beta * (v - sk)
+ *   S  += v' (outer) k
+ *   o   = S @ q            (q already normalised and scaled; updated S)
+ * ------------------------------------------------------------------------ */
+static void recurrence_step(double* S, int64_t dv, int64_t dk, const double* k,
+                            const double* q, const double* v, double g, double beta,
+                            double* o, double* work /* [dv] */) {
+  const double decay = exp(g);
+  for (int64_t i = 0; i < dv * dk; ++i) S[i] *= decay;
+  for (int64_t i = 0; i < dv; ++i) {
+    double sk = 0.0;
+    for (int64_t j = 0; j < dk; ++j) sk += S[i * dk + j] * k[j];
+    work[i] = beta * (v[i] - sk);
+  }
+  for (int64_t i = 0; i < dv; ++i)
+    for (int64_t j = 0; j < dk; ++j) S[i * dk + j] += work[i] * k[j];
+  for (int64_t i = 0; i < dv; ++i) {
+    double acc = 0.0;
+    for (int64_t j = 0; j < dk; ++j) acc += S[i * dk + j] * q[j];
+    o[i] = acc;
+  }
+}
+
+/* Load token `row`'s q and k head `hk` and v head `hv`, normalise and scale. */
+static void load_qkv(const void* q, const void* k, const void* v, int in_dt, int64_t q_rs,
+                     int64_t k_rs, int64_t v_rs, int64_t row, int64_t hk, int64_t hv,
+                     int64_t dk, int64_t dv, int l2norm, double l2_eps, double scale,
+                     double* qd, double* kd, double* vd) {
+  for (int64_t j = 0; j < dk; ++j) {
+    qd[j] = load_elem(q, in_dt, row * q_rs + hk * dk + j);
+    kd[j] = load_elem(k, in_dt, row * k_rs + hk * dk + j);
+  }
+  for (int64_t i = 0; i < dv; ++i) vd[i] = load_elem(v, in_dt, row * v_rs + hv * dv + i);
+  if (l2norm) {
+    l2_normalize(qd, dk, l2_eps);
+    l2_normalize(kd, dk, l2_eps);
+  }
+  for (int64_t j = 0; j < dk; ++j) qd[j] *= scale;
+}
+
+static int check_common(int64_t hk, int64_t hv, int64_t dk, int64_t dv, double scale) {
+  if (hk <= 0 || hv <= 0 || dk <= 0 || dv <= 0) return OR_ERR_SHAPE;
+  if (hv % hk != 0) return OR_ERR_SHAPE;
+  if (!(scale > 0.0) || !isfinite(scale)) return OR_ERR_ARG;
+  return OR_OK;
+}
+
+/* live slots must be in range and distinct (PackedDecodeReference's caller
+   rejects duplicate and out-of-range live slots) */
+static int check_slots(const int32_t* idx, int64_t n, int64_t num_slots, int allow_null) {
+  char* seen = (char*)calloc((size_t)(num_slots > 0 ? num_slots : 1), 1);
+  if (!seen) return OR_ERR_ARG;
+  int rc = OR_OK;
+  for (int64_t b = 0; b < n; ++b) {
+    const int32_t s = idx[b];
+    if (s < 0) {
+      if (!allow_null) { rc = OR_ERR_SLOT; break; }
+      continue;
+    }
+    if (s >= num_slots || seen[s]) { rc = OR_ERR_SLOT; break; }
+    seen[s] = 1;
+  }
+  free(seen);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------
+ * Decode: one token for each of `batch` sequences.  Sequence b's state is
+ * pool[idx[b]] ([hv][dv][dk] f32, read only here); idx[b] < 0 marks a padded
+ * row whose output is zero and whose state is not touched.
+ * g is [batch, hv] (from oracle_gate), beta is [batch, hv] f32 with a row stride.
+ * Outputs: out [batch, hv, dv] f64; state_out [batch, hv, dv, dk] f64 holding
+ * the updated state of each live row (rows with idx < 0 are left as given).
+ * head_mask [hv] (NULL = all heads) restricts the work to the marked v-heads;
+ * entries of other heads are left as given.
+ * ------------------------------------------------------------------------ */
+int oracle_decode(int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
+                  const void* q, const void* k, const void* v, int in_dt, int64_t q_rs,
+                  int64_t k_rs, int64_t v_rs, const double* g, const float* beta,
+                  int64_t beta_rs, const float* pool, int64_t num_slots, const int32_t* idx,
+                  double scale, double l2_eps, int l2norm, const uint8_t* head_mask,
+                  double* out, double* state_out) {
+  int rc = check_common(hk, hv, dk, dv, scale);
+  if (rc) return rc;
+  rc = check_slots(idx, batch, num_slots, 1);
+  if (rc) return rc;
+  const int64_t ratio = hv / hk;
+  double* qd = (double*)malloc((size_t)dk * sizeof(double));
+  double* kd = (double*)malloc((size_t)dk * sizeof(double));
+  double* vd = (double*)malloc((size_t)dv * sizeof(double));
+  double* work = (double*)malloc((size_t)dv * sizeof(double));
+  if (!qd || !kd || !vd || !work) { free(qd); free(kd); free(vd); free(work); return OR_ERR_ARG; }
+  const int64_t head_elems = dv * dk;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int32_t slot = idx[b];
+    for (int64_t h = 0; h < hv; ++h) {
+      if (head_mask && !head_mask[h]) continue;
+      double* o = out + (b * hv + h) * dv;
+      if (slot < 0) {
+        for (int64_t i = 0; i < dv; ++i) o[i] = 0.0;
+        continue;
+      }
+      const int64_t hkh = h / ratio;
+      load_qkv(q, k, v, in_dt, q_rs, k_rs, v_rs, b, hkh, h, dk, dv, l2norm, l2_eps, scale, qd,
+               kd, vd);
+      double* S = state_out + (b * hv + h) * head_elems;
+      const float* S0 = pool + ((int64_t)slot * hv + h) * head_elems;
+      for (int64_t e = 0; e < head_elems; ++e) S[e] = (double)S0[e];
+      recurrence_step(S, dv, dk, kd, qd, vd, g[b * hv + h], (double)beta[b * beta_rs + h], o,
+                      work);
+    }
+  }
+  free(qd); free(kd); free(vd); free(work);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Varlen prefill.  Sequence s covers tokens [cu[s], cu[s+1]).  Its state starts
+ * as pool[idx[s]] when has_init[s] != 0 (has_init == NULL: all 1), else as
+ * zeros (the slot is then never read); idx == NULL means slot s.  The
+ * recurrence runs over the sequence's tokens in order and the final state of
+ * each sequence is returned in state_out [num_seqs, hv, dv, dk] f64.
+ * g, beta: [T, hv] (g f64 from oracle_gate; beta f32 with a row stride).
+ * out: [T, hv, dv] f64.  head_mask as for oracle_decode.
+ * ------------------------------------------------------------------------ */
+int oracle_prefill_varlen(int64_t num_seqs, const int32_t* cu, int64_t hk, int64_t hv,
+                          int64_t dk, int64_t dv, const void* q, const void* k, const void* v,
+                          int in_dt, int64_t q_rs, int64_t k_rs, int64_t v_rs,
+                          const double* g, const float* beta, int64_t beta_rs,
+                          const float* pool, int64_t num_slots, const int32_t* idx,
+                          const int8_t* has_init, double scale, double l2_eps, int l2norm,
+                          const uint8_t* head_mask, double* out, double* state_out) {
+  int rc = check_common(hk, hv, dk, dv, scale);
+  if (rc) return rc;
+  if (num_seqs < 0 || cu[0] != 0) return OR_ERR_SHAPE;
+  for (int64_t s = 0; s < num_seqs; ++s)
+    if (cu[s + 1] < cu[s]) return OR_ERR_SHAPE;
+  if (idx) {
+    rc = check_slots(idx, num_seqs, num_slots, 0);
+    if (rc) return rc;
+  } else if (num_seqs > num_slots) {
+    return OR_ERR_SLOT;
+  }
+  const int64_t ratio = hv / hk;
+  double* qd = (double*)malloc((size_t)dk * sizeof(double));
+  double* kd = (double*)malloc((size_t)dk * sizeof(double));
+  double* vd = (double*)malloc((size_t)dv * sizeof(double));
+  double* work = (double*)malloc((size_t)dv * sizeof(double));
+  if (!qd || !kd || !vd || !work) { free(qd); free(kd); free(vd); free(work); return OR_ERR_ARG; }
+  const int64_t head_elems = dv * dk;
+  for (int64_t s = 0; s < num_seqs; ++s) {
+    const int64_t slot = idx ? idx[s] : s;
+    const int init = has_init ? has_init[s] != 0 : 1;
+    for (int64_t h = 0; h < hv; ++h) {
+      if (head_mask && !head_mask[h]) continue;
+      double* S = state_out + (s * hv + h) * head_elems;
+      const float* S0 = pool + (slot * hv + h) * head_elems;
+      for (int64_t e = 0; e < head_elems; ++e) S[e] = init ? (double)S0[e] : 0.0;
+      const int64_t hkh = h / ratio;
+      for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+        load_qkv(q, k, v, in_dt, q_rs, k_rs, v_rs, t, hkh, h, dk, dv, l2norm, l2_eps, scale,
+                 qd, kd, vd);
+        recurrence_step(S, dv, dk, kd, qd, vd, g[t * hv + h], (double)beta[t * beta_rs + h],
+                        out + (t * hv + h) * dv, work);
+      }
+    }
+  }
+  free(qd); free(kd); free(vd); free(work);
+  return OR_OK;
+}
