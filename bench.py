@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet hot path on one MI355X.
+
+Headline (the decode leg): one step = one gdn_decode launch over B=256
+single-token sequences (Hk=16, Hv=32, Dk=Dv=128, bf16 q/k/v/out, gate and
+q/k L2-norm fused) updating fp32 states in place in a 1024-slot pool.  Launches
+rotate over four disjoint 256-slot subsets of the pool, so every launch reads
+and writes 512 MiB of state that the previous three launches did not touch.
+value = algorithmic bytes per step / time per step, in GB/s.
+
+Second leg (same JSON line, "prefill"): gdn_gate + gdn_prefill_varlen over 8
+sequences with lengths U(1,8192) summing to 32768 tokens (Hk=8, Hv=24, D=128,
+fp16, initial states from a 64-slot pool), reported in tokens/s.
+
+Inputs are seeded synthetic tensors already resident in HBM when timing
+starts.  The CPU oracle is timed on a bounded sample on the host as a
+baseline (not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+METRIC = "GDN decode state GB/s (% HBM peak) @B=256; varlen prefill tokens/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(B, hk, hv, dk, dv, in_bytes, out_bytes, alpha_bytes=4):
+    """Algorithmic HBM bytes of one decode step: the state is read and written
+    once per live (row, v-head); q/k once per (row, q/k head); v and out once;
+    alpha, beta per (row, v-head); dt_bias, ssm_a per v-head; the slot index."""
+    state = 2 * B * hv * dv * dk * 4
+    qk = 2 * B * hk * dk * in_bytes
+    vo = B * hv * dv * (in_bytes + out_bytes)
+    gate = B * hv * (alpha_bytes + 4) + 2 * hv * 4 + B * 4
+    return state + qk + vo + gate
+
+
+def prefill_bytes(T, N, hk, hv, dk, dv, in_bytes, out_bytes):
+    """Algorithmic HBM bytes of gate + varlen prefill: q/k/v read once, out
+    written once, alpha read and g written by the gate, g and beta read by the
+    recurrence, each sequence's state read and written once."""
+    qkv = T * (2 * hk * dk + hv * dv) * in_bytes
+    out = T * hv * dv * out_bytes
+    gate = T * hv * 4 * 2          # alpha read, g written
+    gb = T * hv * 4 * 2            # g and beta read
+    state = 2 * N * hv * dv * dk * 4
+    return qkv + out + gate + gb + state
+
+
+def prefill_flops(T, hv, dk, dv, C=64):
+    """Flops of the chunked form per (token, v-head) at chunk size C:
+    2 [C (3 Dk + 2 Dv) + 3 Dk Dv + C^2 / 6]."""
+    return 2.0 * T * hv * (C * (3 * dk + 2 * dv) + 3 * dk * dv + C * C / 6.0)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=12)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of each CPU-oracle baseline leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        sys.exit("bench.py: this build measures one GPU only (the decode and prefill kernels "
+                 "shard by sequence with no exchange); run with --gpus 1")
+
+    import torch
+    import workloads as W
+    import linear_attention_recurrence_gdn_amd as gdn
+
+    dev = torch.device("cuda:0")
+    t_setup = time.time()
+
+    # ---------------- decode leg ----------------
+    case = W.decode_b256()
+    B, hk, hv, dk, dv = case.batch, case.hk, case.hv, case.dk, case.dv
+    to_dev = lambda a: torch.from_numpy(a).to(dev)
+    qb = to_dev(case.q.buf.view(np.int16)).view(torch.bfloat16).view(B, hk, dk)
+    kb = to_dev(case.k.buf.view(np.int16)).view(torch.bfloat16).view(B, hk, dk)
+    vb = to_dev(case.v.buf.view(np.int16)).view(torch.bfloat16).view(B, hv, dv)
+    alpha, dt_bias, ssm_a, beta = (to_dev(case.alpha), to_dev(case.dt_bias),
+                                   to_dev(case.ssm_a), to_dev(case.beta))
+    pool = to_dev(case.pool)
+    perm = np.random.default_rng([202, 0xB]).permutation(case.num_slots).astype(np.int32)
+    subsets = [to_dev(np.ascontiguousarray(perm[i * B:(i + 1) * B])) for i in range(4)]
+    out = torch.empty((B, hv, dv), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"decode setup {time.time() - t_setup:.1f}s")
+
+    def decode_step(i):
+        gdn.decode(qb, kb, vb, alpha, dt_bias, ssm_a, beta, pool, subsets[i % 4],
+                   scale=case.scale, out=out, stream=stream)
+
+    for i in range(args.warmup):
+        decode_step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        decode_step(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    step_bytes = decode_bytes(B, hk, hv, dk, dv, 2, 2)
+    ms_per_step = wall * 1e3 / args.steps
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kavg = float(kernel_ms.mean())
+    k_gbs = step_bytes / (kavg * 1e-3) / 1e9
+    log(f"decode: {ms_per_step * 1e3:.1f} us/step wall, kernel avg {kavg * 1e3:.1f} us "
+        f"(min {kernel_ms.min() * 1e3:.1f}, median {np.median(kernel_ms) * 1e3:.1f}) "
+        f"-> {k_gbs:.0f} GB/s = {k_gbs / HBM_PEAK_GBS * 100:.1f}% of peak")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode B=256 x 1 token, Hk=16, Hv=32, Dk=Dv=128, bf16 q/k/v/out, "
+                        "fp32 state pool of 1024 slots (4 rotating 256-slot subsets), gate and "
+                        "q/k L2-norm fused",
+            "global_batch": B, "seq_len": 1, "parallelism": "none (1 GPU)",
+            "algorithmic_bytes_per_step": step_bytes,
+            "pct_hbm_peak": round(gbs / HBM_PEAK_GBS * 100, 2),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "decode_kernel<128,16>", "kernel_avg_us": round(kavg * 1e3, 2),
+        },
+    }
+
+    # ---------------- prefill leg ----------------
+    if not args.no_prefill:
+        pre = W.prefill_varlen_gqa3()
+        T, N = pre.total_tokens, pre.num_seqs
+        qp = to_dev(pre.q.buf).view(T, pre.hk, pre.dk)
+        kp = to_dev(pre.k.buf).view(T, pre.hk, pre.dk)
+        vp = to_dev(pre.v.buf).view(T, pre.hv, pre.dv)
+        pa, pdt, pssm, pbeta = (to_dev(pre.alpha), to_dev(pre.dt_bias), to_dev(pre.ssm_a),
+                                to_dev(pre.beta))
+        ppool = to_dev(pre.pool)
+        pcu, pidx, phi = to_dev(pre.cu_seqlens), to_dev(pre.idx), to_dev(pre.has_init)
+        pout = torch.empty((T, pre.hv, pre.dv), dtype=torch.float16, device=dev)
+        g = torch.empty((T, pre.hv), dtype=torch.float32, device=dev)
+        ws_n = gdn.prefill_workspace_size(T, N, pre.hk, pre.hv, pre.dk, pre.dv, torch.float16)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+        def prefill_step():
+            gdn.gate(pa, pdt, pssm, out=g, stream=stream)
+            gdn.prefill_varlen(qp, kp, vp, g, pbeta, ppool, pcu, scale=pre.scale,
+                               state_idx=pidx, has_initial_state=phi, out=pout,
+                               workspace=ws, stream=stream)
+
+        for _ in range(2):
+            prefill_step()
+        torch.cuda.synchronize()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.prefill_steps)]
+        t0 = time.perf_counter()
+        for i in range(args.prefill_steps):
+            pev[i][0].record(stream)
+            prefill_step()
+            pev[i][1].record(stream)
+        torch.cuda.synchronize()
+        pwall = time.perf_counter() - t0
+        pms = np.array([a.elapsed_time(b) for a, b in pev])
+        p_ms_step = pwall * 1e3 / args.prefill_steps
+        pbytes = prefill_bytes(T, N, pre.hk, pre.hv, pre.dk, pre.dv, 2, 2)
+        pflops = prefill_flops(T, pre.hv, pre.dk, pre.dv)
+        pavg = float(pms.mean())
+        result["prefill"] = {
+            "workload": "varlen prefill, 8 sequences, lengths U(1,8192) summing to 32768, "
+                        "Hk=8, Hv=24 (GQA 3), D=128, fp16 q/k/v/out, fp32 states from a "
+                        "64-slot pool; gate + recurrence",
+            "lengths": pre.meta["lengths"],
+            "tokens_per_s": round(T / (p_ms_step * 1e-3), 1),
+            "ms_per_step": round(p_ms_step, 4),
+            "kernel_avg_ms": round(pavg, 4),
+            "achieved_GBs": round(pbytes / (pavg * 1e-3) / 1e9, 1),
+            "hbm_frac": round(pbytes / (pavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "chunked_flops_per_step": pflops,
+            "mfma_frac_if_chunked": round(pflops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "path": "chunked" if ws_n > 0 else "token-sequential",
+        }
+        log(f"prefill: {p_ms_step:.3f} ms/step -> {T / (p_ms_step * 1e-3) / 1e6:.2f} M tokens/s")
+
+    # ---------------- CPU oracle baseline ----------------
+    if not args.no_cpu:
+        import oracle
+        ncores = 1
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.decode_case(case)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        cpu_t = time.perf_counter() - t0
+        cpu_gbs = step_bytes * reps / cpu_t / 1e9
+        result["cpu_baseline"] = {
+            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": ncores, "kind": "oracle",
+            "sample": f"{reps} full decode step(s) of the B=256 workload (gate + step in f64, "
+                      f"single thread) in {cpu_t:.1f} s",
+        }
+        log(f"cpu oracle decode: {cpu_gbs:.3f} GB/s over {reps} step(s)")
+        if not args.no_prefill:
+            # the first 2048 tokens of the longest sequence, one v-head
+            s = int(np.argmax(pre.meta["lengths"]))
+            a0, a1 = int(pre.cu_seqlens[s]), int(pre.cu_seqlens[s]) + 2048
+            mask = np.zeros(pre.hv, np.uint8)
+            mask[0] = 1
+            sub = W.PrefillCase(
+                name="cpu-sample", total_tokens=a1 - a0, num_seqs=1, hk=pre.hk, hv=pre.hv,
+                dk=pre.dk, dv=pre.dv, in_dtype=pre.in_dtype, out_dtype=pre.out_dtype,
+                q=W.View(np.ascontiguousarray(pre.q.buf[a0:a1]), 0, pre.q.row_stride, W.F16),
+                k=W.View(np.ascontiguousarray(pre.k.buf[a0:a1]), 0, pre.k.row_stride, W.F16),
+                v=W.View(np.ascontiguousarray(pre.v.buf[a0:a1]), 0, pre.v.row_stride, W.F16),
+                alpha=np.ascontiguousarray(pre.alpha[a0:a1]), dt_bias=pre.dt_bias,
+                ssm_a=pre.ssm_a, beta=np.ascontiguousarray(pre.beta[a0:a1]),
+                cu_seqlens=np.array([0, a1 - a0], np.int32), pool=pre.pool,
+                idx=pre.idx[s:s + 1].copy(), has_init=np.ones(1, np.int8), scale=pre.scale)
+            t0 = time.perf_counter()
+            oracle.prefill_case(sub, head_mask=mask)
+            pt = time.perf_counter() - t0
+            # one v-head of 2048 tokens = 2048/Hv token-equivalents of the whole layer
+            result["prefill"]["cpu_baseline"] = {
+                "value": round((a1 - a0) / pre.hv / pt, 2), "unit": "tokens/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"1 of {pre.hv} v-heads over {a1 - a0} tokens of sequence {s} "
+                          f"({pt:.1f} s), scaled to all heads",
+            }
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet (GDN) hot path for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (sources are web pages; each entry point names the passage that
+ * defines it):
+ *   gate        g = softplus(alpha + dt_bias) * ssm_a, softplus(x) = x when
+ *               x > 20 and log1p(exp(x)) otherwise; ssm_a = -exp(A_log) < 0
+ *               (Winery-Strata, src/kernels/elementwise_parity.cpp, the
+ *               gdn_gate block and its softplus-branch / negative-ssm_a notes).
+ *   recurrence  per v-head, state S[Dv][Dk] in fp32 (rows index v, columns k):
+ *               S *= exp(g); v' = beta * (v - S k); S += v' (outer) k;
+ *               o = S (q * scale), the output read from the updated state
+ *               (vllm.cpp, tests/vt/test_ops_gdn.cpp, "gdn decode:
+ *               hand-computed single step" and the 3-token prefill table).
+ *   q/k norm    x / sqrt(sum_d x_d^2 + eps), per (token, q/k head), q scaled
+ *               after normalising (same file, the l2norm cases and
+ *               PackedDecodeReference).
+ *   GQA         v-head hv reads q/k head hv / (Hv / Hk) (same file, "GQA
+ *               ratio 3 broadcast").
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *     the return value of gdn_last_error().  The library allocates nothing,
+ *     frees nothing and never synchronises: each call enqueues its kernels on
+ *     `stream` and returns; results are visible after the stream completes.
+ *     No call reads device data on the host, so calls can be captured into a
+ *     HIP graph.
+ *   - Sizes and strides are in ELEMENTS of the named dtype.  A "row" is one
+ *     token (prefill) or one sequence (decode).  Within a row, head h of a
+ *     [rows, H, D] operand starts at element h*D and is contiguous.
+ *   - Input buffers are never written.  The state pool is updated in place.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     violation the call returns a negative code, enqueues nothing, and
+ *     gdn_last_error() describes the problem (thread-local, prefixed with the
+ *     entry point's name).  GDN_ERR_HIP means a launch failed.
+ *   - Supported head sizes: Dk in {16, 32, 64, 128, 256}; any Dv >= 1.
+ *     Pointers must be aligned to their element size and the state pool to
+ *     16 bytes.  q/k are read with vector loads when every head start is
+ *     aligned to 4 elements, with scalar loads otherwise.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GDN_F32 = 0, GDN_F16 = 1, GDN_BF16 = 2 } gdn_dtype;
+
+enum {
+  GDN_OK = 0,
+  GDN_ERR_ARG = -1,    /* bad scalar argument, null pointer or misalignment */
+  GDN_ERR_DTYPE = -2,  /* unsupported dtype or dtype combination */
+  GDN_ERR_SHAPE = -3,  /* Hv not a multiple of Hk, unsupported Dk, stride < width */
+  GDN_ERR_SLOT = -4,   /* reserved for slot validation done by the caller */
+  GDN_ERR_HIP = -5     /* a kernel launch failed */
+};
+
+enum {
+  GDN_L2NORM_QK = 1u << 0,          /* L2-normalise q and k per head, eps = l2_eps */
+  GDN_PREFILL_SEQUENTIAL = 1u << 2  /* prefill: force the token-sequential kernel */
+};
+
+/*
+ * gdn_gate -- g[r, h] = softplus(alpha[r, h] + dt_bias[h]) * ssm_a[h].
+ * Winery-Strata elementwise_parity.cpp, gdn_gate block.
+ *   g        [rows, hv] f32 output, row stride g_row_stride (>= hv).
+ *   alpha    [rows, hv] in alpha_dt (f32, f16 or bf16), row stride
+ *            alpha_row_stride (>= hv).
+ *   dt_bias  [hv] f32.   ssm_a [hv] f32 (= -exp(A_log); negative).
+ * Computed in f32 with the x > 20 branch, so it is finite for any finite x.
+ * rows == 0 enqueues nothing and returns GDN_OK.
+ */
+int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_dt,
+             int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
+             int64_t rows, int64_t hv, hipStream_t stream);
+
+/*
+ * gdn_decode -- one token for each of `batch` sequences, gate fused, states
+ * updated in place in a slot-indexed pool.
+ * vllm.cpp test_ops_gdn.cpp: "gdn decode: hand-computed single step" (the
+ * step), "indexed in-place == compact reference" (slot addressing),
+ * PackedDecodeReference (row-strided packed q|k|v, fused gate, q/k norm,
+ * slot < 0 gives a zero output row).
+ *   out        [batch, hv, dv] contiguous, out_dt (f32, or the input dtype).
+ *   q, k       [batch, hk, dk] in in_dt with row strides q_row_stride,
+ *              k_row_stride (>= hk*dk).  v: [batch, hv, dv], v_row_stride
+ *              (>= hv*dv).  A packed q|k|v row is passed as three pointers
+ *              into the same buffer with the same row stride.
+ *   alpha      [batch, hv] in alpha_dt, row stride alpha_row_stride.
+ *   dt_bias, ssm_a  [hv] f32.   beta [batch, hv] f32 (post-sigmoid),
+ *              row stride beta_row_stride.
+ *   state_pool [num_slots, hv, dv, dk] f32, read and written in place.
+ *   state_idx  [batch] int32: row b uses slot state_idx[b].  A negative
+ *              index marks a padded row: its output row is written as zeros
+ *              and no state is touched.  An index >= num_slots is a caller
+ *              error; such a row's output is written as NaN and no state is
+ *              touched.  Two rows naming the same slot race (undefined).
+ *   scale      > 0 and finite (usually 1/sqrt(dk)).
+ *   flags      GDN_L2NORM_QK to normalise q and k with l2_eps.
+ * batch == 0 enqueues nothing and returns GDN_OK.
+ */
+int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
+               gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+               int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
+               int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
+               const float* beta, int64_t beta_row_stride, float* state_pool,
+               int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
+               int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
+               uint32_t flags, hipStream_t stream);
+
+/*
+ * gdn_prefill_varlen_workspace_size -- bytes of device workspace that
+ * gdn_prefill_varlen needs for these sizes and flags (0 if none).
+ */
+size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs, int64_t hk,
+                                         int64_t hv, int64_t dk, int64_t dv, gdn_dtype in_dt,
+                                         uint32_t flags);
+
+/*
+ * gdn_prefill_varlen -- the recurrence over many sequences packed back to back.
+ * vllm.cpp test_ops_gdn.cpp: the 3-token prefill table, "multi-sequence
+ * varlen equals independent runs" (cu_seqlens = query_start_loc), "T=1
+ * equals decode", and the state gather/scatter cases (initial state read from
+ * a cache slot, fresh sequences start from zeros, final state written back).
+ *   out          [total_tokens, hv, dv] contiguous, out_dt.
+ *   q, k, v      as for gdn_decode with one row per token.
+ *   g            [total_tokens, hv] f32 (from gdn_gate), row stride g_row_stride.
+ *   beta         [total_tokens, hv] f32, row stride beta_row_stride.
+ *   state_pool   [num_slots, hv, dv, dk] f32.  Sequence s starts from
+ *                pool[slot] (slot = state_idx[s], or s when state_idx is
+ *                NULL) when has_initial_state[s] != 0 (NULL: all nonzero),
+ *                else from zeros without reading the slot, and its final
+ *                state is written to pool[slot].  Slots must be distinct and
+ *                in range (caller's responsibility; not checked on device).
+ *   cu_seqlens   [num_seqs + 1] int32, cu_seqlens[0] = 0, non-decreasing,
+ *                cu_seqlens[num_seqs] = total_tokens.  Read on the device.
+ *                A zero-length sequence passes its state through unchanged.
+ *   workspace    device buffer of at least
+ *                gdn_prefill_varlen_workspace_size(...) bytes (may be NULL
+ *                when that size is 0).
+ *   flags        GDN_L2NORM_QK; GDN_PREFILL_SEQUENTIAL forces the
+ *                token-sequential kernel instead of the chunked one.
+ * num_seqs == 0 enqueues nothing and returns GDN_OK.
+ */
+int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                       const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                       int64_t k_row_stride, int64_t v_row_stride, const float* g,
+                       int64_t g_row_stride, const float* beta, int64_t beta_row_stride,
+                       float* state_pool, int64_t num_slots, const int32_t* state_idx,
+                       const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                       int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                       int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Message for the last error returned on this thread ("" if none). */
+const char* gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,209 @@
+// gdn_api.hip -- the C ABI declared in include/gdn.h: host-side argument
+// validation and dispatch to the kernel launchers.  Nothing here allocates,
+// synchronises or reads device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return GDN_OK;
+}
+
+bool valid_dt(int dt) { return dt == GDN_F32 || dt == GDN_F16 || dt == GDN_BF16; }
+int elem_bytes(int dt) { return dt == GDN_F32 ? 4 : 2; }
+bool supported_dk(int64_t dk) {
+  return dk == 16 || dk == 32 || dk == 64 || dk == 128 || dk == 256;
+}
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// q/k are read 4 elements at a time from every head start: vector loads when
+// every head start is aligned to 4 elements, scalar loads otherwise.
+bool qk_vector_ok(const void* q, const void* k, int in_dt, int64_t q_rs, int64_t k_rs) {
+  const size_t vec = 4 * (size_t)elem_bytes(in_dt);
+  return aligned(q, vec) && aligned(k, vec) && q_rs % 4 == 0 && k_rs % 4 == 0;
+}
+
+int check_qk(const char* op, const void* q, const void* k, int in_dt, int64_t q_rs,
+             int64_t k_rs, int64_t hk, int64_t dk) {
+  const size_t eb = (size_t)elem_bytes(in_dt);
+  if (!aligned(q, eb) || !aligned(k, eb))
+    return fail(GDN_ERR_ARG, "%s: q/k pointers must be aligned to their element size", op);
+  if (q_rs < hk * dk || k_rs < hk * dk)
+    return fail(GDN_ERR_SHAPE, "%s: q/k row stride (%lld, %lld) below hk*dk = %lld", op,
+                (long long)q_rs, (long long)k_rs, (long long)(hk * dk));
+  return GDN_OK;
+}
+
+int check_heads(const char* op, int64_t hk, int64_t hv, int64_t dk, int64_t dv) {
+  if (hk <= 0 || hv <= 0 || dk <= 0 || dv <= 0)
+    return fail(GDN_ERR_SHAPE, "%s: head counts and sizes must be positive", op);
+  if (hv % hk != 0)
+    return fail(GDN_ERR_SHAPE, "%s: Hv (%lld) must be a multiple of Hk (%lld)", op,
+                (long long)hv, (long long)hk);
+  if (!supported_dk(dk))
+    return fail(GDN_ERR_SHAPE, "%s: Dk = %lld not supported (16, 32, 64, 128, 256)", op,
+                (long long)dk);
+  if (hv > (1 << 20) || dv > (1 << 20))
+    return fail(GDN_ERR_SHAPE, "%s: Hv/Dv too large", op);
+  return GDN_OK;
+}
+
+int check_scale(const char* op, float scale, float eps) {
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(GDN_ERR_ARG, "%s: scale must be set (finite and > 0), got %g", op,
+                (double)scale);
+  if (!(eps >= 0.0f) || !isfinite(eps))
+    return fail(GDN_ERR_ARG, "%s: l2_eps must be finite and >= 0", op);
+  return GDN_OK;
+}
+
+int hip_status(const char* op, hipError_t e) {
+  if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", op, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_last_error(void) { return g_err; }
+
+int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_dt,
+             int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a, int64_t rows,
+             int64_t hv, hipStream_t stream) {
+  const char* op = "gdn_gate";
+  if (rows < 0 || hv <= 0) return fail(GDN_ERR_SHAPE, "%s: rows >= 0 and hv > 0 required", op);
+  if (!valid_dt(alpha_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown alpha dtype %d", op, alpha_dt);
+  if (g_row_stride < hv || alpha_row_stride < hv)
+    return fail(GDN_ERR_SHAPE, "%s: row strides must be >= hv", op);
+  if (rows == 0) return ok();
+  if (!g || !alpha || !dt_bias || !ssm_a) return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  gdn::GateArgs a{g, g_row_stride, alpha, alpha_dt, alpha_row_stride, dt_bias, ssm_a, rows, hv};
+  return hip_status(op, gdn::launch_gate(a, stream));
+}
+
+int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
+               gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+               int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
+               int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
+               const float* beta, int64_t beta_row_stride, float* state_pool,
+               int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
+               int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+               hipStream_t stream) {
+  const char* op = "gdn_decode";
+  int rc;
+  if (batch < 0 || num_slots < 0) return fail(GDN_ERR_SHAPE, "%s: negative batch/num_slots", op);
+  if ((rc = check_heads(op, hk, hv, dk, dv))) return rc;
+  if ((rc = check_scale(op, scale, l2_eps))) return rc;
+  if (!valid_dt(in_dt) || !valid_dt(alpha_dt) || !valid_dt(out_dt))
+    return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
+  if (out_dt != GDN_F32 && out_dt != in_dt)
+    return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
+  if (flags & ~(uint32_t)GDN_L2NORM_QK) return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (batch == 0) return ok();
+  if (!out || !q || !k || !v || !alpha || !dt_bias || !ssm_a || !beta || !state_pool ||
+      !state_idx)
+    return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  if ((rc = check_qk(op, q, k, in_dt, q_row_stride, k_row_stride, hk, dk))) return rc;
+  if (v_row_stride < hv * dv || alpha_row_stride < hv || beta_row_stride < hv)
+    return fail(GDN_ERR_SHAPE, "%s: v/alpha/beta row stride below its row width", op);
+  if (!aligned(state_pool, 16)) return fail(GDN_ERR_ARG, "%s: state pool must be 16-byte aligned", op);
+  if (batch * hv > ((int64_t)1 << 40)) return fail(GDN_ERR_SHAPE, "%s: batch*hv too large", op);
+  gdn::DecodeArgs a{};
+  a.out = out; a.out_dt = out_dt; a.q = q; a.k = k; a.v = v; a.in_dt = in_dt;
+  a.q_rs = q_row_stride; a.k_rs = k_row_stride; a.v_rs = v_row_stride;
+  a.qk_vec = qk_vector_ok(q, k, in_dt, q_row_stride, k_row_stride) ? 1 : 0;
+  a.alpha = alpha; a.alpha_dt = alpha_dt; a.alpha_rs = alpha_row_stride;
+  a.dt_bias = dt_bias; a.ssm_a = ssm_a; a.beta = beta; a.beta_rs = beta_row_stride;
+  a.pool = state_pool; a.num_slots = num_slots; a.idx = state_idx; a.batch = batch;
+  a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
+  a.scale = scale; a.l2_eps = l2_eps; a.l2norm = (flags & GDN_L2NORM_QK) ? 1 : 0;
+  return hip_status(op, gdn::launch_decode(a, stream));
+}
+
+static bool use_chunked(int64_t hk, int64_t hv, int64_t dk, int64_t dv, int in_dt, int out_dt,
+                        uint32_t flags) {
+  (void)hk; (void)hv;
+  return !(flags & GDN_PREFILL_SEQUENTIAL) && gdn::chunked_supported(in_dt, out_dt, (int)dk, (int)dv);
+}
+
+size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs, int64_t hk,
+                                         int64_t hv, int64_t dk, int64_t dv, gdn_dtype in_dt,
+                                         uint32_t flags) {
+  if (total_tokens <= 0 || num_seqs <= 0 || hk <= 0 || hv <= 0 || dk <= 0 || dv <= 0) return 0;
+  if (!use_chunked(hk, hv, dk, dv, in_dt, in_dt, flags)) return 0;
+  return gdn::chunked_workspace_bytes(total_tokens, num_seqs, (int)hv, (int)dk, (int)dv);
+}
+
+int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
+                       gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+                       int64_t v_row_stride, const float* g, int64_t g_row_stride,
+                       const float* beta, int64_t beta_row_stride, float* state_pool,
+                       int64_t num_slots, const int32_t* state_idx,
+                       const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                       int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                       int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* op = "gdn_prefill_varlen";
+  int rc;
+  if (num_seqs < 0 || total_tokens < 0 || num_slots < 0)
+    return fail(GDN_ERR_SHAPE, "%s: negative size", op);
+  if ((rc = check_heads(op, hk, hv, dk, dv))) return rc;
+  if ((rc = check_scale(op, scale, l2_eps))) return rc;
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
+  if (out_dt != GDN_F32 && out_dt != in_dt)
+    return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
+  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_PREFILL_SEQUENTIAL))
+    return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (num_seqs == 0) return ok();
+  if (!state_pool || !cu_seqlens) return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  if (!state_idx && num_seqs > num_slots)
+    return fail(GDN_ERR_SLOT, "%s: %lld sequences but %lld slots", op, (long long)num_seqs,
+                (long long)num_slots);
+  if (!aligned(state_pool, 16)) return fail(GDN_ERR_ARG, "%s: state pool must be 16-byte aligned", op);
+  if (total_tokens > 0) {
+    if (!out || !q || !k || !v || !g || !beta) return fail(GDN_ERR_ARG, "%s: null pointer", op);
+    if ((rc = check_qk(op, q, k, in_dt, q_row_stride, k_row_stride, hk, dk))) return rc;
+    if (v_row_stride < hv * dv || g_row_stride < hv || beta_row_stride < hv)
+      return fail(GDN_ERR_SHAPE, "%s: v/g/beta row stride below its row width", op);
+  }
+  gdn::PrefillArgs a{};
+  a.out = out; a.out_dt = out_dt; a.q = q; a.k = k; a.v = v; a.in_dt = in_dt;
+  a.q_rs = q_row_stride; a.k_rs = k_row_stride; a.v_rs = v_row_stride;
+  a.qk_vec = qk_vector_ok(q, k, in_dt, q_row_stride, k_row_stride) ? 1 : 0;
+  a.g = g; a.g_rs = g_row_stride; a.beta = beta; a.beta_rs = beta_row_stride;
+  a.pool = state_pool; a.num_slots = num_slots; a.idx = state_idx;
+  a.has_init = has_initial_state; a.cu = cu_seqlens; a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
+  a.scale = scale; a.l2_eps = l2_eps; a.l2norm = (flags & GDN_L2NORM_QK) ? 1 : 0;
+  if (use_chunked(hk, hv, dk, dv, in_dt, out_dt, flags) && total_tokens > 0) {
+    const size_t need = gdn::chunked_workspace_bytes(total_tokens, num_seqs, (int)hv, (int)dk,
+                                                     (int)dv);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(GDN_ERR_ARG, "%s: workspace of %zu bytes required, got %zu", op, need,
+                  workspace_bytes);
+    if (need > 0 && !aligned(workspace, 256))
+      return fail(GDN_ERR_ARG, "%s: workspace must be 256-byte aligned", op);
+    return hip_status(op, gdn::launch_prefill_chunked(a, workspace, workspace_bytes, stream));
+  }
+  return hip_status(op, gdn::launch_prefill_sequential(a, stream));
+}
+
+}  // extern "C"

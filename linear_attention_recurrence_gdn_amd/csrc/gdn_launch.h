@@ -1,0 +1,83 @@
+// gdn_launch.h -- internal interface between the C ABI (gdn_api.hip) and the
+// kernel launchers.  Arguments are validated before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct GateArgs {
+  float* g;
+  int64_t g_rs;
+  const void* alpha;
+  int alpha_dt;
+  int64_t alpha_rs;
+  const float* dt_bias;
+  const float* ssm_a;
+  int64_t rows;
+  int64_t hv;
+};
+
+struct DecodeArgs {
+  void* out;
+  int out_dt;
+  const void* q;
+  const void* k;
+  const void* v;
+  int in_dt;
+  int64_t q_rs, k_rs, v_rs;
+  int qk_vec;  // q/k head starts are 4-element aligned: vector loads
+  const void* alpha;
+  int alpha_dt;
+  int64_t alpha_rs;
+  const float* dt_bias;
+  const float* ssm_a;
+  const float* beta;
+  int64_t beta_rs;
+  float* pool;
+  int64_t num_slots;
+  const int32_t* idx;
+  int64_t batch;
+  int hk, hv, dk, dv;
+  float scale, l2_eps;
+  int l2norm;
+};
+
+struct PrefillArgs {
+  void* out;
+  int out_dt;
+  const void* q;
+  const void* k;
+  const void* v;
+  int in_dt;
+  int64_t q_rs, k_rs, v_rs;
+  int qk_vec;
+  const float* g;
+  int64_t g_rs;
+  const float* beta;
+  int64_t beta_rs;
+  float* pool;
+  int64_t num_slots;
+  const int32_t* idx;       // may be null: slot s
+  const int8_t* has_init;   // may be null: all 1
+  const int32_t* cu;
+  int64_t num_seqs;
+  int64_t total_tokens;
+  int hk, hv, dk, dv;
+  float scale, l2_eps;
+  int l2norm;
+};
+
+hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill_sequential(const PrefillArgs& a, hipStream_t stream);
+
+// Chunked prefill (MFMA).  Returns hipErrorNotSupported when the shape or
+// dtype has no chunked kernel (the caller then uses the sequential one).
+bool chunked_supported(int in_dt, int out_dt, int dk, int dv);
+size_t chunked_workspace_bytes(int64_t total_tokens, int64_t num_seqs, int hv, int dk, int dv);
+hipError_t launch_prefill_chunked(const PrefillArgs& a, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,288 @@
+// gdn_recurrent.hip -- gate, single-token decode and token-sequential prefill
+// kernels for gfx950.
+//
+// Method (vllm.cpp tests/vt/test_ops_gdn.cpp, "gdn decode: hand-computed
+// single step"; Winery-Strata elementwise_parity.cpp, gdn_gate block):
+//   g = softplus(alpha + dt_bias) * ssm_a  (softplus(x) = x when x > 20)
+//   S *= exp(g);  v' = beta (v - S k);  S += v' k^T;  o = S (scale q)
+// with q, k optionally L2-normalised (eps inside the square root) and v-head
+// hv reading q/k head hv / (Hv / Hk).
+//
+// Decode is bound by HBM bandwidth: each (sequence, v-head) state is Dv x Dk
+// fp32 (64 KiB at 128 x 128) that must be read and written once, against ~1
+// flop per byte.  The layout of the work:
+//   - one wavefront owns a tile of BV = NL * RPI state rows of one head; lane
+//     l covers columns [4 (l % LPR), +4) of row r0 + i*RPI + l/LPR for
+//     i < NL, with LPR = Dk/4 lanes per row and RPI = 64/LPR rows per load
+//     instruction; every state access is a 16-byte load/store and each
+//     instruction moves 1 KiB of contiguous state;
+//   - all NL loads are issued before any arithmetic, so a wave keeps
+//     16*NL bytes per lane in flight;
+//   - S k and S q are reduced together from the OLD state with one
+//     transposed butterfly, and the output uses
+//       o = S_new q = decay (S_old q) + v' (k . q),
+//     which is the same quantity, so the state is streamed exactly once;
+//   - waves are independent: no LDS and no barriers.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+// ---------------------------------------------------------------------------
+// gate
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
+  const int64_t n = a.rows * a.hv;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / a.hv;
+    const int64_t h = i - r * a.hv;
+    const float x = load1(a.alpha, a.alpha_dt, r * a.alpha_rs + h) + a.dt_bias[h];
+    a.g[r * a.g_rs + h] = gate_value(x, a.ssm_a[h]);
+  }
+}
+
+hipError_t launch_gate(const GateArgs& a, hipStream_t stream) {
+  const int64_t n = a.rows * a.hv;
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(gate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// shared per-token step on a wave's register tile
+// ---------------------------------------------------------------------------
+template <int DK, int NL>
+struct Tile {
+  static constexpr int LPR = DK / 4;    // lanes per state row
+  static constexpr int RPI = 64 / LPR;  // rows per load instruction
+  static constexpr int BV = NL * RPI;   // rows per wave
+  static_assert(NL <= LPR, "tile needs NL <= lanes per row");
+  static constexpr int OWN = LPR / NL;  // lanes holding each reduced row
+};
+
+// q, k: this lane's 4 columns; returns normalised k in k4, scale*normalised q
+// in q4 and (k . q) summed over the row.
+template <int LPR>
+__device__ __forceinline__ float prepare_qk(float4& q4, float4& k4, bool l2norm, float eps,
+                                            float scale) {
+  float qn = scale, kn = 1.0f;
+  if (l2norm) {
+    const float qq = group_sum<LPR>(dot4(q4, q4));
+    const float kk = group_sum<LPR>(dot4(k4, k4));
+    qn = scale / sqrtf(qq + eps);
+    kn = 1.0f / sqrtf(kk + eps);
+  }
+  q4 = scale4(qn, q4);
+  k4 = scale4(kn, k4);
+  return group_sum<LPR>(dot4(k4, q4));
+}
+
+// One recurrence step on the wave's tile.  s[i] holds row r0 + i*RPI + sub.
+// Returns, in every lane, the output of row `myrow` (see the caller).
+template <int DK, int NL>
+__device__ __forceinline__ float tile_step(float4 (&s)[NL], float4 q4, float4 k4, float kq,
+                                           float decay, float beta, float vv, int lane,
+                                           int sub) {
+  using T = Tile<DK, NL>;
+  float pk[NL], pq[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    pk[i] = dot4(s[i], k4);
+    pq[i] = dot4(s[i], q4);
+  }
+  transpose_reduce<NL, T::LPR>(pk, lane);
+  transpose_reduce<NL, T::LPR>(pq, lane);
+  const float vp = beta * (vv - decay * pk[0]);
+  const float o = decay * pq[0] + vp * kq;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const float vpi = __shfl(vp, sub * T::LPR + i * T::OWN, 64);
+    s[i] = axpby4(decay, s[i], vpi, k4);
+  }
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------
+template <int DK, int NL>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total_waves,
+                                                     int tiles_per_head) {
+  using T = Tile<DK, NL>;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (wave >= total_waves) return;
+  const int tile = (int)(wave % tiles_per_head);
+  const int64_t bh = wave / tiles_per_head;
+  const int h = (int)(bh % a.hv);
+  const int64_t b = bh / a.hv;
+  const int r0 = tile * T::BV;
+  const int sub = lane / T::LPR;
+  const int col = (lane % T::LPR) * 4;
+  const int j = (lane % T::LPR) / T::OWN;
+  const int myrow = r0 + j * T::RPI + sub;
+  const bool writer = (lane % T::OWN) == 0 && myrow < a.dv;
+  const int64_t out_off = (b * a.hv + h) * a.dv + myrow;
+
+  const int32_t slot = a.idx[b];
+  if (slot < 0 || slot >= a.num_slots) {
+    // padded row: zeros; out-of-range slot (caller error): NaN.  No state access.
+    if (writer) store1(a.out, a.out_dt, out_off, slot < 0 ? 0.0f : __builtin_nanf(""));
+    return;
+  }
+
+  float* S = a.pool + (((int64_t)slot * a.hv + h) * a.dv) * DK + col;
+  float4 s[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int row = r0 + i * T::RPI + sub;
+    s[i] = row < a.dv ? *reinterpret_cast<const float4*>(S + (int64_t)row * DK)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+
+  const int hk = h / (a.hv / a.hk);
+  float4 q4 = load4u(a.q, a.in_dt, b * a.q_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
+  float4 k4 = load4u(a.k, a.in_dt, b * a.k_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
+  const float vv = myrow < a.dv ? load1(a.v, a.in_dt, b * a.v_rs + (int64_t)h * a.dv + myrow)
+                                : 0.0f;
+  const float x = load1(a.alpha, a.alpha_dt, b * a.alpha_rs + h) + a.dt_bias[h];
+  const float decay = expf(gate_value(x, a.ssm_a[h]));
+  const float beta = a.beta[b * a.beta_rs + h];
+
+  const float kq = prepare_qk<T::LPR>(q4, k4, a.l2norm != 0, a.l2_eps, a.scale);
+  const float o = tile_step<DK, NL>(s, q4, k4, kq, decay, beta, vv, lane, sub);
+  if (writer) store1(a.out, a.out_dt, out_off, o);
+
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int row = r0 + i * T::RPI + sub;
+    if (row < a.dv) *reinterpret_cast<float4*>(S + (int64_t)row * DK) = s[i];
+  }
+}
+
+template <int DK, int NL>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  using T = Tile<DK, NL>;
+  const int tiles = (a.dv + T::BV - 1) / T::BV;
+  const int64_t waves = a.batch * a.hv * tiles;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((decode_kernel<DK, NL>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
+                     waves, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.dk) {
+    case 16: return launch_decode_t<16, 4>(a, stream);
+    case 32: return launch_decode_t<32, 8>(a, stream);
+    case 64: return launch_decode_t<64, 16>(a, stream);
+    case 128: return launch_decode_t<128, 16>(a, stream);
+    case 256: return launch_decode_t<256, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// token-sequential prefill: one wave per (sequence, v-head, row tile) walks
+// the sequence's tokens with its state tile in registers; the next token's
+// inputs are loaded while the current one is processed.
+// ---------------------------------------------------------------------------
+struct TokenIn {
+  float4 q4, k4;
+  float vv, g, beta;
+};
+
+template <int DK>
+__device__ __forceinline__ TokenIn load_token(const PrefillArgs& a, int64_t t, int hk, int h,
+                                              int col, int myrow) {
+  TokenIn in;
+  in.q4 = load4u(a.q, a.in_dt, t * a.q_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
+  in.k4 = load4u(a.k, a.in_dt, t * a.k_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
+  in.vv = myrow < a.dv ? load1(a.v, a.in_dt, t * a.v_rs + (int64_t)h * a.dv + myrow) : 0.0f;
+  in.g = a.g[t * a.g_rs + h];
+  in.beta = a.beta[t * a.beta_rs + h];
+  return in;
+}
+
+template <int DK, int NL>
+__global__ __launch_bounds__(256) void prefill_seq_kernel(PrefillArgs a, int64_t total_waves,
+                                                          int tiles_per_head) {
+  using T = Tile<DK, NL>;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (wave >= total_waves) return;
+  const int tile = (int)(wave % tiles_per_head);
+  const int64_t sh = wave / tiles_per_head;
+  const int h = (int)(sh % a.hv);
+  const int64_t sq = sh / a.hv;
+  const int r0 = tile * T::BV;
+  const int sub = lane / T::LPR;
+  const int col = (lane % T::LPR) * 4;
+  const int j = (lane % T::LPR) / T::OWN;
+  const int myrow = r0 + j * T::RPI + sub;
+  const bool writer = (lane % T::OWN) == 0 && myrow < a.dv;
+
+  // cu_seqlens is device data: clamp so a malformed table cannot index past
+  // the token arrays.
+  const int64_t t1 = min((int64_t)a.cu[sq + 1], a.total_tokens);
+  const int64_t t0 = max((int64_t)0, min((int64_t)a.cu[sq], t1));
+  const int64_t slot = a.idx ? (int64_t)a.idx[sq] : sq;
+  if (slot < 0 || slot >= a.num_slots) {
+    if (writer)
+      for (int64_t t = t0; t < t1; ++t)
+        store1(a.out, a.out_dt, (t * a.hv + h) * a.dv + myrow, __builtin_nanf(""));
+    return;
+  }
+  const bool init = a.has_init ? a.has_init[sq] != 0 : true;
+  float* S = a.pool + ((slot * a.hv + h) * a.dv) * DK + col;
+  float4 s[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int row = r0 + i * T::RPI + sub;
+    s[i] = (init && row < a.dv) ? *reinterpret_cast<const float4*>(S + (int64_t)row * DK)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int hk = h / (a.hv / a.hk);
+  TokenIn nxt;
+  if (t0 < t1) nxt = load_token<DK>(a, t0, hk, h, col, myrow);
+  for (int64_t t = t0; t < t1; ++t) {
+    TokenIn cur = nxt;
+    if (t + 1 < t1) nxt = load_token<DK>(a, t + 1, hk, h, col, myrow);
+    const float kq = prepare_qk<T::LPR>(cur.q4, cur.k4, a.l2norm != 0, a.l2_eps, a.scale);
+    const float o = tile_step<DK, NL>(s, cur.q4, cur.k4, kq, expf(cur.g), cur.beta, cur.vv,
+                                      lane, sub);
+    if (writer) store1(a.out, a.out_dt, (t * a.hv + h) * a.dv + myrow, o);
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int row = r0 + i * T::RPI + sub;
+    if (row < a.dv) *reinterpret_cast<float4*>(S + (int64_t)row * DK) = s[i];
+  }
+}
+
+template <int DK, int NL>
+static hipError_t launch_prefill_seq_t(const PrefillArgs& a, hipStream_t stream) {
+  using T = Tile<DK, NL>;
+  const int tiles = (a.dv + T::BV - 1) / T::BV;
+  const int64_t waves = a.num_seqs * a.hv * tiles;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((prefill_seq_kernel<DK, NL>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     a, waves, tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_sequential(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.dk) {
+    case 16: return launch_prefill_seq_t<16, 1>(a, stream);
+    case 32: return launch_prefill_seq_t<32, 2>(a, stream);
+    case 64: return launch_prefill_seq_t<64, 4>(a, stream);
+    case 128: return launch_prefill_seq_t<128, 4>(a, stream);
+    case 256: return launch_prefill_seq_t<256, 4>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gdn

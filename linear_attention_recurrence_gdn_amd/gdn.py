@@ -1,0 +1,218 @@
+"""ctypes binding of libgdn (include/gdn.h): argument marshalling only.
+
+Every step of the path runs in the HIP kernels of libgdn.so; this module turns
+torch tensors into device pointers, element strides and dtype codes, passes
+torch's current HIP stream, and raises ``GdnError`` on a non-zero return code.
+There is no fallback: if the library is missing or fails to load, every entry
+point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
+GDN_L2NORM_QK = 1 << 0
+GDN_PREFILL_SEQUENTIAL = 1 << 2
+
+_TORCH_DT = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
+
+EXPORTS = ("gdn_gate", "gdn_decode", "gdn_prefill_varlen_workspace_size",
+           "gdn_prefill_varlen", "gdn_last_error")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgdn.so and declare the C signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libgdn.so not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i64, f32, u32, i32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+                                  ctypes.c_uint32, ctypes.c_int, ctypes.c_size_t)
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_gate.restype = i32
+    lib.gdn_gate.argtypes = [vp, i64, vp, i32, i64, vp, vp, i64, i64, vp]
+    lib.gdn_decode.restype = i32
+    lib.gdn_decode.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i32, i64, vp, vp,
+                               vp, i64, vp, i64, vp, i64, i64, i64, i64, i64, f32, f32, u32, vp]
+    lib.gdn_prefill_varlen_workspace_size.restype = sz
+    lib.gdn_prefill_varlen_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32, u32]
+    lib.gdn_prefill_varlen.restype = i32
+    lib.gdn_prefill_varlen.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp,
+                                       i64, vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                       f32, f32, u32, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise GdnError(rc, _lib.gdn_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _TORCH_DT[t.dtype]
+    except KeyError:
+        raise GdnError(-2, f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise GdnError(-1, f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise GdnError(-2, f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str, heads: int, dim: int) -> int:
+    """Row stride (elements) of a [rows, heads, dim] (or [rows, heads*dim])
+    operand whose rows are contiguous."""
+    if t.dim() == 3:
+        if t.shape[1] != heads or t.shape[2] != dim or t.stride(2) != 1 or t.stride(1) != dim:
+            raise GdnError(-3, f"{name}: need [rows, {heads}, {dim}] with contiguous rows")
+    elif t.dim() == 2:
+        if t.shape[1] != heads * dim or t.stride(1) != 1:
+            raise GdnError(-3, f"{name}: need [rows, {heads * dim}] with contiguous rows")
+    else:
+        raise GdnError(-3, f"{name}: rank {t.dim()} not supported")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), heads * dim)
+
+
+def _rows2(t: torch.Tensor, name: str, width: int) -> int:
+    if t.dim() != 2 or t.shape[1] != width or t.stride(1) != 1:
+        raise GdnError(-3, f"{name}: need [rows, {width}] with contiguous rows")
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), width)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def gate(alpha: torch.Tensor, dt_bias: torch.Tensor, ssm_a: torch.Tensor,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """g[r, h] = softplus(alpha[r, h] + dt_bias[h]) * ssm_a[h]  ->  [rows, hv] f32."""
+    lib = load_library()
+    rows, hv = alpha.shape[0], dt_bias.shape[0]
+    a_rs = _rows2(alpha, "alpha", hv)
+    if out is None:
+        out = torch.empty((rows, hv), dtype=torch.float32, device=alpha.device)
+    g_rs = _rows2(out, "g", hv)
+    _check(lib.gdn_gate(_dev(out, "g", torch.float32), g_rs, _dev(alpha, "alpha"), _dt(alpha),
+                        a_rs, _dev(dt_bias, "dt_bias", torch.float32),
+                        _dev(ssm_a, "ssm_a", torch.float32), rows, hv, _stream(stream)))
+    return out
+
+
+def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale: float,
+           l2norm: bool = True, l2_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
+           out_dtype=None, stream=None) -> torch.Tensor:
+    """One decode step, gate fused, pool updated in place.
+
+    q, k: [B, Hk, Dk]; v: [B, Hv, Dv] (rows may be strided, e.g. views into one
+    packed q|k|v buffer); alpha [B, Hv]; dt_bias, ssm_a [Hv] f32; beta [B, Hv] f32;
+    state_pool [slots, Hv, Dv, Dk] f32 contiguous; state_idx [B] int32."""
+    lib = load_library()
+    if state_pool.dim() != 4 or not state_pool.is_contiguous():
+        raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
+    slots, hv, dv, dk = state_pool.shape
+    B = state_idx.shape[0]
+    hk = q.shape[1] if q.dim() == 3 else q.shape[1] // dk
+    q_rs = _rows(q, "q", hk, dk)
+    k_rs = _rows(k, "k", hk, dk)
+    v_rs = _rows(v, "v", hv, dv)
+    a_rs = _rows2(alpha, "alpha", hv)
+    b_rs = _rows2(beta, "beta", hv)
+    for name, t in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("beta", beta)):
+        if t.shape[0] != B:
+            raise GdnError(-3, f"{name}: {t.shape[0]} rows, state_idx has {B}")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise GdnError(-2, "q, k, v must share a dtype")
+    if out is None:
+        out = torch.empty((B, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
+    if not out.is_contiguous() or tuple(out.shape) != (B, hv, dv):
+        raise GdnError(-3, "out: need contiguous [B, Hv, Dv]")
+    flags = GDN_L2NORM_QK if l2norm else 0
+    _check(lib.gdn_decode(
+        _dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
+        q_rs, k_rs, v_rs, _dev(alpha, "alpha"), _dt(alpha), a_rs,
+        _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
+        _dev(beta, "beta", torch.float32), b_rs, _dev(state_pool, "state_pool", torch.float32),
+        slots, _dev(state_idx, "state_idx", torch.int32), B, hk, hv, dk, dv, float(scale),
+        float(l2_eps), flags, _stream(stream)))
+    return out
+
+
+def prefill_workspace_size(total_tokens, num_seqs, hk, hv, dk, dv, in_dtype,
+                           sequential=False, l2norm=True) -> int:
+    lib = load_library()
+    flags = (GDN_L2NORM_QK if l2norm else 0) | (GDN_PREFILL_SEQUENTIAL if sequential else 0)
+    return lib.gdn_prefill_varlen_workspace_size(total_tokens, num_seqs, hk, hv, dk, dv,
+                                                 _TORCH_DT[in_dtype], flags)
+
+
+def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
+                   state_idx: Optional[torch.Tensor] = None,
+                   has_initial_state: Optional[torch.Tensor] = None, l2norm: bool = True,
+                   l2_eps: float = 1e-6, out: Optional[torch.Tensor] = None, out_dtype=None,
+                   sequential: bool = False, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Varlen prefill over sequences packed back to back (cu_seqlens [N+1] int32).
+
+    q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; g, beta: [T, Hv] f32; state_pool
+    [slots, Hv, Dv, Dk] f32 (initial states read, final states written)."""
+    lib = load_library()
+    if state_pool.dim() != 4 or not state_pool.is_contiguous():
+        raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
+    slots, hv, dv, dk = state_pool.shape
+    T = q.shape[0]
+    N = cu_seqlens.shape[0] - 1
+    hk = q.shape[1] if q.dim() == 3 else q.shape[1] // dk
+    q_rs = _rows(q, "q", hk, dk)
+    k_rs = _rows(k, "k", hk, dk)
+    v_rs = _rows(v, "v", hv, dv)
+    g_rs = _rows2(g, "g", hv)
+    b_rs = _rows2(beta, "beta", hv)
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise GdnError(-2, "q, k, v must share a dtype")
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
+    if not out.is_contiguous() or tuple(out.shape) != (T, hv, dv):
+        raise GdnError(-3, "out: need contiguous [T, Hv, Dv]")
+    flags = (GDN_L2NORM_QK if l2norm else 0) | (GDN_PREFILL_SEQUENTIAL if sequential else 0)
+    ws_need = lib.gdn_prefill_varlen_workspace_size(T, N, hk, hv, dk, dv, _dt(q), flags)
+    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if ws_need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_need else 0
+    _check(lib.gdn_prefill_varlen(
+        _dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
+        q_rs, k_rs, v_rs, _dev(g, "g", torch.float32), g_rs, _dev(beta, "beta", torch.float32),
+        b_rs, _dev(state_pool, "state_pool", torch.float32), slots,
+        _dev(state_idx, "state_idx", torch.int32),
+        _dev(has_initial_state, "has_initial_state", torch.int8),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32), N, T, hk, hv, dk, dv, float(scale),
+        float(l2_eps), flags, ws_ptr, ws_bytes, _stream(stream)))
+    return out

@@ -1,0 +1,181 @@
+"""Helpers that run the seeded workload cases through the HIP library and
+compare them with the oracle's f64 results.  Used by the GPU tests, smoke()
+and bench.py's parity spot check."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+import workloads as W
+import linear_attention_recurrence_gdn_amd as gdn
+
+TORCH_OF = {W.F32: torch.float32, W.F16: torch.float16, W.BF16: torch.bfloat16}
+
+# tolerances (relative L1 = sum|got - want| / sum|want|, accumulated in f64)
+OUT_TOL_F32 = 1e-5       # outputs when inputs are f32
+OUT_TOL_HALF = 2e-2      # outputs stored as bf16 / fp16
+STATE_TOL = 1e-4         # fp32 states
+
+
+def rel_l1(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    d = np.abs(got - want).sum()
+    m = np.abs(want).sum()
+    return float(d / max(m, 1e-30))
+
+
+def out_tol(case) -> float:
+    return OUT_TOL_F32 if (case.in_dtype == W.F32 and case.out_dtype == W.F32) else OUT_TOL_HALF
+
+
+def to_dev(buf: np.ndarray, dtype: int, dev) -> torch.Tensor:
+    """Storage array -> device tensor of the storage dtype (same bytes)."""
+    if dtype == W.BF16:
+        t = torch.from_numpy(np.ascontiguousarray(buf).view(np.int16)).to(dev)
+        return t.view(torch.bfloat16)
+    if dtype == W.F16:
+        return torch.from_numpy(np.ascontiguousarray(buf).view(np.float16)).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(buf, dtype=np.float32)).to(dev)
+
+
+def view_of(dbufs: dict, v: W.View, rows: int, heads: int, dim: int) -> torch.Tensor:
+    t = dbufs[id(v.buf)]
+    flat = t.reshape(-1)
+    return flat.as_strided((rows, heads, dim), (v.row_stride, dim, 1), v.offset)
+
+
+def upload_views(case, dev, rows):
+    dbufs = {}
+    for v in (case.q, case.k, case.v):
+        if id(v.buf) not in dbufs:
+            dbufs[id(v.buf)] = to_dev(v.buf, v.dtype, dev)
+    q = view_of(dbufs, case.q, rows, case.hk, case.dk)
+    k = view_of(dbufs, case.k, rows, case.hk, case.dk)
+    v = view_of(dbufs, case.v, rows, case.hv, case.dv)
+    return dbufs, q, k, v
+
+
+def bytes_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """Byte-wise equality (NaN canaries compare equal to themselves)."""
+    return torch.equal(a.contiguous().view(-1).view(torch.uint8),
+                       b.contiguous().view(-1).view(torch.uint8))
+
+
+def out_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+@dataclass
+class DecodeResult:
+    out: np.ndarray            # [B, hv, dv] f64 (values the GPU stored)
+    pool: torch.Tensor         # device pool after the call
+    pool0: Optional[torch.Tensor]  # device copy of the pool before the call
+    inputs_unchanged: bool
+
+
+def run_decode(case: W.DecodeCase, dev, *, keep_pool0: bool = True, pool=None,
+               out_dtype=None) -> DecodeResult:
+    dbufs, q, k, v = upload_views(case, dev, case.batch)
+    snap = [t.clone() for t in dbufs.values()]
+    alpha = torch.from_numpy(case.alpha).to(dev)
+    dt_bias = torch.from_numpy(case.dt_bias).to(dev)
+    ssm_a = torch.from_numpy(case.ssm_a).to(dev)
+    beta = torch.from_numpy(case.beta).to(dev)
+    idx = torch.from_numpy(case.idx).to(dev)
+    if pool is None:
+        pool = torch.from_numpy(case.pool).to(dev)
+    pool0 = pool.clone() if keep_pool0 else None
+    out = gdn.decode(q, k, v, alpha, dt_bias, ssm_a, beta, pool, idx, scale=case.scale,
+                     l2norm=case.l2norm, l2_eps=case.l2_eps,
+                     out_dtype=out_dtype or TORCH_OF[case.out_dtype])
+    torch.cuda.synchronize()
+    same = all(bytes_equal(a, b) for a, b in zip(snap, dbufs.values()))
+    return DecodeResult(out_to_f64(out), pool, pool0, same)
+
+
+def check_decode(case, res: DecodeResult, want_out, want_state, rows=None, out_tolerance=None):
+    """Compare a GPU decode with the oracle.  `rows` (sampled batch rows) when
+    the oracle ran on a subset."""
+    idx = case.idx if rows is None else case.idx[np.asarray(rows)]
+    got_out = res.out if rows is None else res.out[np.asarray(rows)]
+    live = idx >= 0
+    tol = out_tolerance or out_tol(case)
+    r_out = rel_l1(got_out[live], want_out[live])
+    assert np.all(got_out[~live] == 0.0), "padded rows must be exact zeros"
+    assert r_out <= tol, f"{case.name}: output rel-L1 {r_out:.3e} > {tol:g}"
+    got_state = res.pool[torch.from_numpy(idx[live].astype(np.int64)).to(res.pool.device)]
+    r_st = rel_l1(got_state.cpu().numpy(), want_state[live])
+    assert r_st <= STATE_TOL, f"{case.name}: state rel-L1 {r_st:.3e} > {STATE_TOL:g}"
+    assert np.isfinite(got_out[live]).all()
+    if res.pool0 is not None:
+        touched = np.zeros(case.num_slots, dtype=bool)
+        touched[case.idx[case.idx >= 0]] = True
+        untouched = torch.from_numpy(np.nonzero(~touched)[0]).to(res.pool.device)
+        if untouched.numel():
+            assert torch.equal(res.pool[untouched].view(torch.int32),
+                               res.pool0[untouched].view(torch.int32)), \
+                f"{case.name}: an untouched slot changed"
+    assert res.inputs_unchanged, f"{case.name}: an input buffer was written"
+    return r_out, r_st
+
+
+@dataclass
+class PrefillResult:
+    out: np.ndarray
+    pool: torch.Tensor
+    pool0: Optional[torch.Tensor]
+    inputs_unchanged: bool
+
+
+def run_prefill(case: W.PrefillCase, dev, *, sequential: bool = False, keep_pool0=True,
+                pool=None) -> PrefillResult:
+    dbufs, q, k, v = upload_views(case, dev, case.total_tokens)
+    snap = [t.clone() for t in dbufs.values()]
+    alpha = torch.from_numpy(case.alpha).to(dev)
+    dt_bias = torch.from_numpy(case.dt_bias).to(dev)
+    ssm_a = torch.from_numpy(case.ssm_a).to(dev)
+    beta = torch.from_numpy(case.beta).to(dev)
+    cu = torch.from_numpy(case.cu_seqlens).to(dev)
+    idx = torch.from_numpy(case.idx).to(dev)
+    has_init = torch.from_numpy(case.has_init).to(dev)
+    if pool is None:
+        pool = torch.from_numpy(case.pool).to(dev)
+    pool0 = pool.clone() if keep_pool0 else None
+    g = gdn.gate(alpha, dt_bias, ssm_a)
+    out = gdn.prefill_varlen(q, k, v, g, beta, pool, cu, scale=case.scale, state_idx=idx,
+                             has_initial_state=has_init, l2norm=case.l2norm,
+                             l2_eps=case.l2_eps, out_dtype=TORCH_OF[case.out_dtype],
+                             sequential=sequential)
+    torch.cuda.synchronize()
+    same = all(bytes_equal(a, b) for a, b in zip(snap, dbufs.values()))
+    return PrefillResult(out_to_f64(out), pool, pool0, same)
+
+
+def check_prefill(case, res: PrefillResult, want_out, want_state, heads=None,
+                  out_tolerance=None, state_tolerance=None):
+    """Compare a GPU prefill with the oracle (optionally on a subset of v-heads)."""
+    hsel = np.arange(case.hv) if heads is None else np.asarray(heads)
+    tol = out_tolerance or out_tol(case)
+    st_tol = state_tolerance or STATE_TOL
+    got = res.out[:, hsel]
+    r_out = rel_l1(got, want_out[:, hsel])
+    assert np.isfinite(got).all(), f"{case.name}: non-finite output"
+    assert r_out <= tol, f"{case.name}: output rel-L1 {r_out:.3e} > {tol:g}"
+    idx = torch.from_numpy(case.idx.astype(np.int64)).to(res.pool.device)
+    got_state = res.pool[idx][:, torch.from_numpy(hsel).to(res.pool.device)].cpu().numpy()
+    r_st = rel_l1(got_state, want_state[:, hsel])
+    assert r_st <= st_tol, f"{case.name}: state rel-L1 {r_st:.3e} > {st_tol:g}"
+    if res.pool0 is not None:
+        touched = np.zeros(case.num_slots, dtype=bool)
+        touched[case.idx] = True
+        untouched = torch.from_numpy(np.nonzero(~touched)[0]).to(res.pool.device)
+        if untouched.numel():
+            assert torch.equal(res.pool[untouched].view(torch.int32),
+                               res.pool0[untouched].view(torch.int32)), \
+                f"{case.name}: an untouched slot changed"
+    assert res.inputs_unchanged, f"{case.name}: an input buffer was written"
+    return r_out, r_st

@@ -1,0 +1,123 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+entry point include/gdn.h declares, and rejects bad arguments before anything
+is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import linear_attention_recurrence_gdn_amd as pkg
+from linear_attention_recurrence_gdn_amd import gdn as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gdn_gate", "gdn_decode", "gdn_prefill_varlen",
+              "gdn_prefill_varlen_workspace_size", "gdn_last_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkg.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for n in declared_functions():
+        assert ctypes.cast(getattr(raw, n), ctypes.c_void_p).value
+
+
+def test_binding_names_match_header():
+    assert set(B.EXPORTS) == set(declared_functions())
+
+
+# Argument checks.  Every device pointer is NULL or the checks fail before the
+# null-pointer check, so nothing can be enqueued even on a machine with a GPU.
+def _decode(lib, **kw):
+    a = dict(out=None, out_dt=2, q=None, k=None, v=None, in_dt=2, q_rs=2048, k_rs=2048,
+             v_rs=4096, alpha=None, alpha_dt=0, alpha_rs=32, dt_bias=None, ssm_a=None,
+             beta=None, beta_rs=32, pool=None, slots=8, idx=None, batch=4, hk=16, hv=32,
+             dk=128, dv=128, scale=0.088, eps=1e-6, flags=1, stream=None)
+    a.update(kw)
+    return lib.gdn_decode(*a.values())
+
+
+def _err(lib):
+    return lib.gdn_last_error().decode()
+
+
+def test_decode_argument_errors():
+    lib = pkg.load_library()
+    assert _decode(lib, hv=33) == -3 and "multiple of Hk" in _err(lib)
+    assert _decode(lib, dk=96) == -3 and "Dk = 96" in _err(lib)
+    assert _decode(lib, scale=0.0) == -1 and "scale" in _err(lib)
+    assert _decode(lib, scale=float("nan")) == -1
+    assert _decode(lib, scale=float("inf")) == -1
+    assert _decode(lib, eps=-1.0) == -1
+    assert _decode(lib, in_dt=7) == -2
+    assert _decode(lib, out_dt=1, in_dt=2) == -2      # f16 out from bf16 in
+    assert _decode(lib, flags=1 << 9) == -1
+    assert _decode(lib, batch=-1) == -3
+    assert _decode(lib) == -1 and "null pointer" in _err(lib)
+    assert _err(lib).startswith("gdn_decode:")
+    # batch == 0 is a no-op
+    assert _decode(lib, batch=0) == 0 and _err(lib) == ""
+
+
+def _prefill(lib, **kw):
+    a = dict(out=None, out_dt=1, q=None, k=None, v=None, in_dt=1, q_rs=1024, k_rs=1024,
+             v_rs=3072, g=None, g_rs=24, beta=None, beta_rs=24, pool=None, slots=64,
+             idx=None, has_init=None, cu=None, n=8, t=32768, hk=8, hv=24, dk=128, dv=128,
+             scale=0.088, eps=1e-6, flags=1, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.gdn_prefill_varlen(*a.values())
+
+
+def test_prefill_argument_errors():
+    lib = pkg.load_library()
+    assert _prefill(lib, hv=25) == -3
+    assert _prefill(lib, scale=-1.0) == -1
+    assert _prefill(lib, out_dt=2) == -2
+    assert _prefill(lib, flags=1 << 5) == -1
+    assert _prefill(lib) == -1 and _err(lib).startswith("gdn_prefill_varlen:")
+    assert _prefill(lib, n=0) == 0
+
+
+def test_gate_argument_errors():
+    lib = pkg.load_library()
+    assert lib.gdn_gate(None, 32, None, 0, 32, None, None, 10, 0, None) == -3
+    assert lib.gdn_gate(None, 16, None, 0, 32, None, None, 10, 32, None) == -3
+    assert lib.gdn_gate(None, 32, None, 5, 32, None, None, 10, 32, None) == -2
+    assert lib.gdn_gate(None, 32, None, 0, 32, None, None, 10, 32, None) == -1
+    assert lib.gdn_gate(None, 32, None, 0, 32, None, None, 0, 32, None) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="fake device pointers only without a GPU")
+def test_alignment_and_stride_errors_without_gpu():
+    lib = pkg.load_library()
+    fake = 1 << 20   # never dereferenced: every call below fails validation
+    kw = dict(out=fake, q=fake, k=fake, v=fake, alpha=fake, dt_bias=fake, ssm_a=fake,
+              beta=fake, pool=fake, idx=fake)
+    assert _decode(lib, **{**kw, "q": fake + 1}) == -1 and "aligned" in _err(lib)
+    assert _decode(lib, **{**kw, "k_rs": 1024}) == -3
+    assert _decode(lib, **{**kw, "v_rs": 100}) == -3
+    assert _decode(lib, **{**kw, "pool": fake + 4}) == -1
+    pk = dict(out=fake, q=fake, k=fake, v=fake, g=fake, beta=fake, pool=fake, cu=fake)
+    assert _prefill(lib, **{**pk, "g_rs": 3}) == -3
+    assert _prefill(lib, **pk, slots=4) == -4      # no state_idx and more seqs than slots
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros(4, 32)
+    with pytest.raises(B.GdnError):
+        pkg.gate(x, torch.zeros(32), torch.zeros(32))

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP library (through its C ABI) against the f64 oracle on the
+same seeded inputs.  Tolerances (relative L1, f64 accumulation): outputs 1e-5
+for f32 inputs, 2e-2 for bf16/fp16 outputs; fp32 states 1e-4; padded rows
+exact zeros; untouched slots and input buffers byte-identical."""
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import linear_attention_recurrence_gdn_amd as gdn
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------------------
+# gate
+# ---------------------------------------------------------------------------
+def test_gate_branch_fixture(dev):
+    announce("gate: page fixture + configured alphas")
+    n = 48
+    rng = np.random.default_rng(11)
+    alpha = np.where(np.arange(n) % 3 == 0, 22.0 + 6.0 * (np.arange(n) % 17),
+                     rng.normal(0, 3.0, n)).astype(np.float32)[None, :]
+    dt = rng.normal(0, 0.5, n).astype(np.float32)
+    a = (-(np.abs(rng.normal(0, 1, n)) + 0.1)).astype(np.float32)
+    want = oracle.gate(alpha, W.F32, dt, a)
+    got = gdn.gate(torch.from_numpy(alpha).to(dev), torch.from_numpy(dt).to(dev),
+                   torch.from_numpy(a).to(dev)).cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert H.rel_l1(got, want) <= 1e-6
+    assert np.all(np.exp(got.astype(np.float64)) < 1.0)
+
+
+@pytest.mark.parametrize("alpha_dt", [W.F32, W.BF16, W.F16])
+def test_gate_configured_inputs(dev, alpha_dt):
+    announce(f"gate: decode-B256 alphas, alpha dtype {alpha_dt}")
+    case = W.decode_b256()
+    alpha = W.encode(case.alpha, alpha_dt)
+    want = oracle.gate(alpha, alpha_dt, case.dt_bias, case.ssm_a)
+    # strided alpha: place the [B, hv] block inside wider rows
+    wide = np.zeros((case.batch, case.hv + 8), dtype=alpha.dtype)
+    wide[:, 3:3 + case.hv] = alpha
+    dwide = H.to_dev(wide, alpha_dt, dev)
+    got = gdn.gate(dwide[:, 3:3 + case.hv], torch.from_numpy(case.dt_bias).to(dev),
+                   torch.from_numpy(case.ssm_a).to(dev)).cpu().numpy()
+    assert H.rel_l1(got, want) <= 1e-6
+    assert np.all(np.isfinite(got)) and np.all(got < 0)
+
+
+# ---------------------------------------------------------------------------
+# decode: the pages' hand cases
+# ---------------------------------------------------------------------------
+def test_decode_hand_single_step(dev):
+    announce("decode: hand single step (page table)")
+    d = json.load(open(os.path.join(GOLD, "decode_single_step.json")))
+    # The gate is fused in decode: choose alpha, dt_bias, ssm_a so that
+    # g = softplus(25) * ssm_a = 25 * ssm_a = ln(0.5) (branch side: exact).
+    ssm_a = np.array([math.log(0.5) / 25.0], np.float32)
+    g = 25.0 * float(ssm_a[0])
+    for dt in (W.F32, W.BF16):
+        case = W.DecodeCase(
+            name="hand", batch=1, hk=1, hv=1, dk=16, dv=2, in_dtype=dt, out_dtype=dt,
+            q=W.View(W.encode(np.pad(np.array([d["q"]], float), ((0, 0), (0, 14))), dt), 0, 16, dt),
+            k=W.View(W.encode(np.pad(np.array([d["k"]], float), ((0, 0), (0, 14))), dt), 0, 16, dt),
+            v=W.View(W.encode(np.array([d["v"]], float), dt), 0, 2, dt),
+            alpha=np.array([[25.0]], np.float32), dt_bias=np.zeros(1, np.float32), ssm_a=ssm_a,
+            beta=np.array([[d["beta"]]], np.float32),
+            pool=np.pad(np.array(d["S0"], np.float32), ((0, 0), (0, 14)))[None, None].copy(),
+            idx=np.zeros(1, np.int32), scale=d["scale"], l2norm=False)
+        res = H.run_decode(case, dev)
+        tol = 1e-6 if dt == W.F32 else 0.01
+        # decay = exp(25 * ssm_a) differs from 0.5 by f32 rounding of ssm_a only
+        assert abs(math.exp(g) - 0.5) < 1e-7
+        np.testing.assert_allclose(res.out[0, 0], d["out"], rtol=tol)
+        st = res.pool[0, 0, :, :2].cpu().numpy()
+        np.testing.assert_allclose(st, d["S"], rtol=1e-6)
+        want_out, want_state = oracle.decode_case(case)
+        H.check_decode(case, res, want_out, want_state)
+
+
+# ---------------------------------------------------------------------------
+# decode: shape / dtype / layout matrix at small sizes
+# ---------------------------------------------------------------------------
+DECODE_CASES = [
+    # (batch, hk, hv, dk, dv, in, out, slots, packed_pad, null_rows)
+    (3, 1, 1, 16, 16, W.F32, W.F32, 4, None, ()),
+    (5, 2, 6, 16, 16, W.F32, W.F32, 8, None, (1,)),
+    (4, 2, 4, 32, 40, W.BF16, W.BF16, 6, None, ()),
+    (4, 1, 3, 64, 64, W.F16, W.F32, 5, None, (0, 3)),
+    (7, 2, 6, 128, 128, W.BF16, W.BF16, 11, None, (2,)),
+    (6, 2, 4, 128, 72, W.F16, W.F16, 9, 64, (5,)),
+    (5, 3, 9, 128, 130, W.BF16, W.F32, 7, 256, ()),
+    (3, 1, 2, 256, 128, W.BF16, W.BF16, 4, None, ()),
+    (9, 4, 8, 128, 128, W.F32, W.F32, 12, 32, (0,)),
+]
+
+
+@pytest.mark.parametrize("spec", DECODE_CASES, ids=lambda s: "B{}-hk{}-hv{}-dk{}-dv{}-{}-{}".format(
+    s[0], s[1], s[2], s[3], s[4], W.DTYPE_NAMES[s[5]], W.DTYPE_NAMES[s[6]]))
+def test_decode_matrix(dev, spec):
+    B, hk, hv, dk, dv, ind, outd, slots, pad, nulls = spec
+    announce(f"decode matrix {spec}")
+    case = W.make_decode_case("m", 1000 + B * dk + dv, batch=B, hk=hk, hv=hv, dk=dk, dv=dv,
+                              in_dtype=ind, out_dtype=outd, slots=slots, packed_pad=pad,
+                              null_rows=nulls, large_every_third=True)
+    res = H.run_decode(case, dev)
+    want_out, want_state = oracle.decode_case(case)
+    H.check_decode(case, res, want_out, want_state)
+
+
+def test_decode_without_l2norm(dev):
+    announce("decode without q/k norm")
+    case = W.make_decode_case("nonorm", 77, batch=4, hk=2, hv=4, dk=128, dv=128,
+                              in_dtype=W.F32, out_dtype=W.F32, slots=4)
+    # unnormalised keys make the step contractive only for small k: scale them down
+    case.k.buf[:] *= np.float32(0.05)
+    case.l2norm = False
+    res = H.run_decode(case, dev)
+    want_out, want_state = oracle.decode_case(case)
+    H.check_decode(case, res, want_out, want_state)
+
+
+def test_decode_beta0_g0_leaves_state_bit_exact(dev):
+    announce("decode: beta=0, g=0 invariant")
+    case = W.make_decode_case("inv", 5, batch=4, hk=2, hv=4, dk=128, dv=128, in_dtype=W.BF16,
+                              out_dtype=W.F32, slots=6)
+    case.beta[:] = 0.0
+    case.ssm_a[:] = -0.0   # g = softplus(.) * -0 = -0, decay = 1
+    res = H.run_decode(case, dev)
+    live = case.idx
+    assert torch.equal(res.pool[live].view(torch.int32), res.pool0[live].view(torch.int32))
+    want_out, want_state = oracle.decode_case(case)
+    H.check_decode(case, res, want_out, want_state, out_tolerance=1e-5)
+
+
+def test_decode_graph_replay(dev):
+    announce("decode: HIP graph capture and replay")
+    case = W.make_decode_case("graph", 21, batch=6, hk=2, hv=4, dk=128, dv=128,
+                              in_dtype=W.BF16, out_dtype=W.BF16, slots=8, null_rows=(4,))
+    dbufs, q, k, v = H.upload_views(case, dev, case.batch)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    alpha, dt_bias, ssm_a, beta, idx = (t(case.alpha), t(case.dt_bias), t(case.ssm_a),
+                                        t(case.beta), t(case.idx))
+    pool0 = t(case.pool)
+    # eager reference: two consecutive steps
+    pe = pool0.clone()
+    oe1 = gdn.decode(q, k, v, alpha, dt_bias, ssm_a, beta, pe, idx, scale=case.scale).clone()
+    oe2 = gdn.decode(q, k, v, alpha, dt_bias, ssm_a, beta, pe, idx, scale=case.scale).clone()
+    pg = pool0.clone()
+    out = torch.empty((case.batch, case.hv, case.dv), dtype=torch.bfloat16, device=dev)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        gdn.decode(q, k, v, alpha, dt_bias, ssm_a, beta, pg, idx, scale=case.scale, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(pg.view(torch.int32), pool0.view(torch.int32)), "capture must not run"
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), oe1.view(torch.int16))
+    o1 = out.clone()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), oe2.view(torch.int16))
+    assert torch.equal(pg.view(torch.int32), pe.view(torch.int32))
+    assert not torch.equal(o1, out)
+
+
+# ---------------------------------------------------------------------------
+# decode at the configured sizes
+# ---------------------------------------------------------------------------
+def test_decode_b256_full(dev):
+    announce("decode B=256 Hk16 Hv32 D128 bf16, 1024-slot pool: all rows vs oracle")
+    case = W.decode_b256()
+    res = H.run_decode(case, dev)
+    want_out, want_state = oracle.decode_case(case)
+    r_out, r_st = H.check_decode(case, res, want_out, want_state)
+    print(f"  out rel-L1 {r_out:.3e}  state rel-L1 {r_st:.3e}", flush=True)
+
+
+def test_decode_packed_b1024_sampled(dev):
+    announce("decode B=1024 packed fp16 stride+256, 4096-slot pool: sampled rows vs oracle")
+    case = W.decode_packed_b1024()
+    res = H.run_decode(case, dev)
+    rows = np.random.default_rng(1).choice(case.batch, 96, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, case.batch - 1]]))
+    rows = np.unique(rows)
+    want_out, want_state = oracle.decode_case(case, rows=rows)
+    r_out, r_st = H.check_decode(case, res, want_out, want_state, rows=rows)
+    # every row: finite, and the NaN padding columns were never read
+    assert np.isfinite(res.out).all()
+    print(f"  out rel-L1 {r_out:.3e}  state rel-L1 {r_st:.3e}", flush=True)
+
+
+def test_tiny_prefill_then_four_decode_steps(dev):
+    announce("tiny f32: T=64 prefill then 4 decode steps on the resulting state")
+    pre, steps = W.tiny_prefill_then_decode()
+    for sequential in (True, False):
+        res = H.run_prefill(pre, dev, sequential=sequential)
+        want_out, want_state = oracle.prefill_case(pre)
+        H.check_prefill(pre, res, want_out, want_state)
+        pool = res.pool
+        pool_np = want_state.astype(np.float32)  # oracle chain continues from its own state
+        for st in steps:
+            st.pool = pool_np
+            r = H.run_decode(st, dev, pool=pool)
+            o, s = oracle.decode_case(st)
+            # the GPU state entering this step differs from the oracle's by f32
+            # rounding only; compare against the oracle chain
+            H.check_decode(st, r, o, s)
+            pool = r.pool
+            pool_np = s.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+PREFILL_CASES = [
+    # (lengths, hk, hv, dk, dv, in, out, has_init)
+    ([64], 2, 2, 16, 16, W.F32, W.F32, [1]),
+    ([1, 0, 63, 64, 65, 130], 2, 6, 128, 128, W.BF16, W.BF16, [1, 1, 0, 1, 0, 1]),
+    ([200, 3], 1, 3, 128, 128, W.F16, W.F16, [1, 1]),
+    ([17, 140], 2, 4, 64, 48, W.F16, W.F32, [0, 1]),
+    ([33, 5, 96], 1, 2, 32, 32, W.BF16, W.BF16, [1, 0, 1]),
+    ([70], 1, 1, 256, 128, W.BF16, W.BF16, [1]),
+]
+
+
+@pytest.mark.parametrize("sequential", [True, False], ids=["sequential", "default"])
+@pytest.mark.parametrize("spec", PREFILL_CASES, ids=lambda s: "L{}-hk{}-hv{}-dk{}-dv{}-{}".format(
+    "_".join(map(str, s[0])), s[1], s[2], s[3], s[4], W.DTYPE_NAMES[s[5]]))
+def test_prefill_matrix(dev, spec, sequential):
+    lengths, hk, hv, dk, dv, ind, outd, hi = spec
+    announce(f"prefill matrix {spec} sequential={sequential}")
+    case = W.make_prefill_case("pm", 2000 + sum(lengths) + dk, lengths=lengths, hk=hk, hv=hv,
+                               dk=dk, dv=dv, in_dtype=ind, out_dtype=outd,
+                               slots=len(lengths) + 2, has_init=hi)
+    res = H.run_prefill(case, dev, sequential=sequential)
+    want_out, want_state = oracle.prefill_case(case)
+    H.check_prefill(case, res, want_out, want_state)
+
+
+def test_prefill_t1_equals_decode(dev):
+    announce("prefill T=1 equals decode")
+    dcase = W.make_decode_case("t1", 31, batch=1, hk=2, hv=4, dk=128, dv=128, in_dtype=W.F32,
+                               out_dtype=W.F32, slots=1)
+    r_dec = H.run_decode(dcase, dev)
+    pcase = W.PrefillCase(name="t1p", total_tokens=1, num_seqs=1, hk=2, hv=4, dk=128, dv=128,
+                          in_dtype=W.F32, out_dtype=W.F32, q=dcase.q, k=dcase.k, v=dcase.v,
+                          alpha=dcase.alpha, dt_bias=dcase.dt_bias, ssm_a=dcase.ssm_a,
+                          beta=dcase.beta, cu_seqlens=np.array([0, 1], np.int32),
+                          pool=dcase.pool, idx=dcase.idx, has_init=np.ones(1, np.int8),
+                          scale=dcase.scale)
+    r_pre = H.run_prefill(pcase, dev, sequential=True)
+    np.testing.assert_allclose(r_pre.out, r_dec.out, rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(r_pre.pool.cpu().numpy(), r_dec.pool.cpu().numpy(), rtol=2e-6,
+                               atol=1e-7)
+
+
+def test_prefill_t4096_sampled_heads(dev):
+    announce("prefill T=4096 Hk16 Hv32 D128 bf16, zero init (NaN slot): sampled heads")
+    case = W.prefill_t4096()
+    res = H.run_prefill(case, dev)
+    heads = [0, 1, 19]
+    mask = np.zeros(case.hv, np.uint8)
+    mask[heads] = 1
+    want_out, want_state = oracle.prefill_case(case, head_mask=mask)
+    r_out, r_st = H.check_prefill(case, res, want_out, want_state, heads=heads)
+    assert np.isfinite(res.out).all()
+    print(f"  out rel-L1 {r_out:.3e}  state rel-L1 {r_st:.3e}", flush=True)
+
+
+def test_prefill_varlen_gqa3_sampled_heads(dev):
+    announce("prefill varlen 8 seqs T=32768 Hk8 Hv24 GQA3 fp16: sampled heads")
+    case = W.prefill_varlen_gqa3()
+    res = H.run_prefill(case, dev)
+    heads = [0, 14]
+    mask = np.zeros(case.hv, np.uint8)
+    mask[heads] = 1
+    want_out, want_state = oracle.prefill_case(case, head_mask=mask)
+    r_out, r_st = H.check_prefill(case, res, want_out, want_state, heads=heads)
+    assert np.isfinite(res.out).all()
+    print(f"  lengths {case.meta['lengths']} out rel-L1 {r_out:.3e}  state rel-L1 {r_st:.3e}",
+          flush=True)
