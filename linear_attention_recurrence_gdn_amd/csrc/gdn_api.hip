@@ -193,7 +193,8 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
   a.total_tokens = total_tokens;
   a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
   a.scale = scale; a.l2_eps = l2_eps; a.l2norm = (flags & GDN_L2NORM_QK) ? 1 : 0;
-  if (use_chunked(hk, hv, dk, dv, in_dt, out_dt, flags) && total_tokens > 0) {
+  if (use_chunked(hk, hv, dk, dv, in_dt, out_dt, flags) && total_tokens > 0 &&
+      gdn::chunked_layout_ok(q, k, v, q_row_stride, k_row_stride, v_row_stride)) {
     const size_t need = gdn::chunked_workspace_bytes(total_tokens, num_seqs, (int)hv, (int)dk,
                                                      (int)dv);
     if (need > 0 && (!workspace || workspace_bytes < need))

@@ -62,6 +62,29 @@ __device__ __forceinline__ void store1(void* p, int dt, int64_t off, float x) {
   }
 }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte state access, optionally with the nontemporal (streaming) hint.
+template <bool NT>
+__device__ __forceinline__ float4 state_load(const float* p) {
+  if constexpr (NT) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void state_store(float* p, float4 x) {
+  if constexpr (NT) {
+    f32x4_t v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+  } else {
+    *reinterpret_cast<float4*>(p) = x;
+  }
+}
+
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
@@ -74,10 +97,32 @@ __device__ __forceinline__ float4 scale4(float a, float4 x) {
   return make_float4(a * x.x, a * x.y, a * x.z, a * x.w);
 }
 
-// Cross-lane exchange with lane ^ M inside the wavefront.
+// Butterfly partner exchange for bit M (a power of two <= 32): returns the
+// value of a lane whose bit M is flipped and whose bits above M are equal.
+// Bits below M may be flipped too (the mirrors below map lane l to l ^ (2M-1)),
+// which is all a butterfly reduction needs: at each step the partner sits on
+// the other side of bit M and holds partial sums over the same rows, and the
+// partners met over all steps still cover each lane exactly once.
+//   M = 1, 2: DPP quad_perm;  M = 4: DPP row_half_mirror (l ^ 7);
+//   M = 8: DPP row_mirror (l ^ 15);  M = 16: ds_swizzle xor within 32 lanes;
+//   M = 32: ds_bpermute.
 template <int M>
 __device__ __forceinline__ float xor_lane(float v) {
-  return __shfl_xor(v, M, 64);
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (M == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (M == 4) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
+  } else if constexpr (M == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
+  } else if constexpr (M == 16) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));
+  } else {
+    static_assert(M == 32, "xor_lane: M must be a power of two <= 32");
+    return __shfl_xor(v, 32, 64);
+  }
 }
 
 // Full sum over aligned groups of G lanes (G a power of two <= 64).
@@ -120,6 +165,65 @@ template <int N, int G>
 __device__ __forceinline__ void transpose_reduce(float* a, int lane) {
   static_assert(N <= G, "transpose_reduce needs N <= G");
   transpose_reduce_step<N, G / 2>(a, lane);
+}
+
+// Typed raw loads.  The raw bits are loaded first and converted later, so a
+// kernel can issue all of its loads back to back before waiting on any of
+// them (a conversion right after a load would force an early wait).
+template <int DT>
+struct Raw4 {
+  uint32_t w[DT == kF32 ? 4 : 2];
+};
+
+template <int DT>
+__device__ __forceinline__ Raw4<DT> load_raw4(const void* p, int64_t off, bool vec) {
+  Raw4<DT> r;
+  if constexpr (DT == kF32) {
+    const uint32_t* q = static_cast<const uint32_t*>(p) + off;
+    if (vec) {
+      const uint4 u = *reinterpret_cast<const uint4*>(q);
+      r.w[0] = u.x; r.w[1] = u.y; r.w[2] = u.z; r.w[3] = u.w;
+    } else {
+      r.w[0] = q[0]; r.w[1] = q[1]; r.w[2] = q[2]; r.w[3] = q[3];
+    }
+  } else {
+    const uint16_t* q = static_cast<const uint16_t*>(p) + off;
+    if (vec) {
+      const uint2 u = *reinterpret_cast<const uint2*>(q);
+      r.w[0] = u.x; r.w[1] = u.y;
+    } else {
+      r.w[0] = (uint32_t)q[0] | ((uint32_t)q[1] << 16);
+      r.w[1] = (uint32_t)q[2] | ((uint32_t)q[3] << 16);
+    }
+  }
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ float4 raw_to_f32(const Raw4<DT>& r) {
+  if constexpr (DT == kF32) {
+    return make_float4(__uint_as_float(r.w[0]), __uint_as_float(r.w[1]),
+                       __uint_as_float(r.w[2]), __uint_as_float(r.w[3]));
+  } else if constexpr (DT == kBF16) {
+    return make_float4(bf16_to_f32(r.w[0] & 0xffffu), bf16_to_f32(r.w[0] >> 16),
+                       bf16_to_f32(r.w[1] & 0xffffu), bf16_to_f32(r.w[1] >> 16));
+  } else {
+    return make_float4(f16_to_f32(r.w[0] & 0xffffu), f16_to_f32(r.w[0] >> 16),
+                       f16_to_f32(r.w[1] & 0xffffu), f16_to_f32(r.w[1] >> 16));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t load_raw1(const void* p, int64_t off) {
+  if constexpr (DT == kF32) return static_cast<const uint32_t*>(p)[off];
+  return static_cast<const uint16_t*>(p)[off];
+}
+
+template <int DT>
+__device__ __forceinline__ float raw1_to_f32(uint32_t u) {
+  if constexpr (DT == kF32) return __uint_as_float(u);
+  if constexpr (DT == kBF16) return bf16_to_f32(u);
+  return f16_to_f32(u);
 }
 
 // softplus with the large-x branch, then times ssm_a (negative): the gate g.

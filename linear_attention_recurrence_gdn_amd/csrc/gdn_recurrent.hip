@@ -17,7 +17,10 @@
 //     instruction; every state access is a 16-byte load/store and each
 //     instruction moves 1 KiB of contiguous state;
 //   - all NL loads are issued before any arithmetic, so a wave keeps
-//     16*NL bytes per lane in flight;
+//     16*NL bytes per lane in flight; NL = 8 (16 rows, 8 KiB of state per
+//     wave at Dk = 128) and nontemporal loads/stores measured fastest: the
+//     state is touched once per call, so it should not displace other lines
+//     in the caches;
 //   - S k and S q are reduced together from the OLD state with one
 //     transposed butterfly, and the output uses
 //       o = S_new q = decay (S_old q) + v' (k . q),
@@ -108,17 +111,22 @@ __device__ __forceinline__ float tile_step(float4 (&s)[NL], float4 q4, float4 k4
 // ---------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------
-template <int DK, int NL>
+// Wave -> (sequence b, v-head h, row tile) with the tile fastest, so the
+// waves of one head are neighbours.  All indices are wave-uniform (scalar
+// registers); the q/k/v/gate loads are issued before the slot index is
+// waited on, and the whole state tile is requested before any arithmetic.
+template <int DK, int NL, int TIN, int TAL, bool NT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total_waves,
                                                      int tiles_per_head) {
   using T = Tile<DK, NL>;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (wave >= total_waves) return;
-  const int tile = (int)(wave % tiles_per_head);
-  const int64_t bh = wave / tiles_per_head;
-  const int h = (int)(bh % a.hv);
-  const int64_t b = bh / a.hv;
+  // the host keeps the wave count below 2^31, so 32-bit index math suffices
+  const uint32_t wave = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= (uint32_t)total_waves) return;
+  const int tile = (int)(wave % (uint32_t)tiles_per_head);
+  const uint32_t bh = wave / (uint32_t)tiles_per_head;
+  const int h = (int)(bh % (uint32_t)a.hv);
+  const int64_t b = bh / (uint32_t)a.hv;
   const int r0 = tile * T::BV;
   const int sub = lane / T::LPR;
   const int col = (lane % T::LPR) * 4;
@@ -128,6 +136,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total
   const int64_t out_off = (b * a.hv + h) * a.dv + myrow;
 
   const int32_t slot = a.idx[b];
+  const int hk = h / (a.hv / a.hk);
+  const Raw4<TIN> qr = load_raw4<TIN>(a.q, b * a.q_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
+  const Raw4<TIN> kr = load_raw4<TIN>(a.k, b * a.k_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
+  const uint32_t vr = load_raw1<TIN>(a.v, b * a.v_rs + (int64_t)h * a.dv + min(myrow, a.dv - 1));
+  const uint32_t ar = load_raw1<TAL>(a.alpha, b * a.alpha_rs + h);
+  const float dtb = a.dt_bias[h];
+  const float ssa = a.ssm_a[h];
+  const float beta = a.beta[b * a.beta_rs + h];
+
   if (slot < 0 || slot >= a.num_slots) {
     // padded row: zeros; out-of-range slot (caller error): NaN.  No state access.
     if (writer) store1(a.out, a.out_dt, out_off, slot < 0 ? 0.0f : __builtin_nanf(""));
@@ -138,91 +155,104 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total
   float4 s[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int row = r0 + i * T::RPI + sub;
-    s[i] = row < a.dv ? *reinterpret_cast<const float4*>(S + (int64_t)row * DK)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int row = min(r0 + i * T::RPI + sub, a.dv - 1);
+    s[i] = state_load<NT>(S + (int64_t)row * DK);
   }
 
-  const int hk = h / (a.hv / a.hk);
-  float4 q4 = load4u(a.q, a.in_dt, b * a.q_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
-  float4 k4 = load4u(a.k, a.in_dt, b * a.k_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
-  const float vv = myrow < a.dv ? load1(a.v, a.in_dt, b * a.v_rs + (int64_t)h * a.dv + myrow)
-                                : 0.0f;
-  const float x = load1(a.alpha, a.alpha_dt, b * a.alpha_rs + h) + a.dt_bias[h];
-  const float decay = expf(gate_value(x, a.ssm_a[h]));
-  const float beta = a.beta[b * a.beta_rs + h];
-
+  float4 q4 = raw_to_f32<TIN>(qr);
+  float4 k4 = raw_to_f32<TIN>(kr);
+  const float vv = raw1_to_f32<TIN>(vr);
+  const float decay = expf(gate_value(raw1_to_f32<TAL>(ar) + dtb, ssa));
   const float kq = prepare_qk<T::LPR>(q4, k4, a.l2norm != 0, a.l2_eps, a.scale);
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    if (r0 + i * T::RPI + sub >= a.dv) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   const float o = tile_step<DK, NL>(s, q4, k4, kq, decay, beta, vv, lane, sub);
   if (writer) store1(a.out, a.out_dt, out_off, o);
 
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int row = r0 + i * T::RPI + sub;
-    if (row < a.dv) *reinterpret_cast<float4*>(S + (int64_t)row * DK) = s[i];
+    if (row < a.dv) state_store<NT>(S + (int64_t)row * DK, s[i]);
   }
 }
 
-template <int DK, int NL>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+template <int DK, int NL, int TIN, int TAL, bool NT>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   using T = Tile<DK, NL>;
   const int tiles = (a.dv + T::BV - 1) / T::BV;
   const int64_t waves = a.batch * a.hv * tiles;
+  if (waves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((decode_kernel<DK, NL>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
-                     waves, tiles);
+  hipLaunchKernelGGL((decode_kernel<DK, NL, TIN, TAL, NT>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, a, waves, tiles);
   return hipGetLastError();
+}
+
+template <int DK, int NL>
+static hipError_t launch_decode_dk(const DecodeArgs& a, hipStream_t stream) {
+#define GDN_DEC(TI, TA) \
+  if (a.in_dt == TI && a.alpha_dt == TA) return launch_decode_t<DK, NL, TI, TA, true>(a, stream);
+  GDN_DEC(kBF16, kF32) GDN_DEC(kF16, kF32) GDN_DEC(kF32, kF32)
+  GDN_DEC(kBF16, kBF16) GDN_DEC(kF16, kBF16) GDN_DEC(kF32, kBF16)
+  GDN_DEC(kBF16, kF16) GDN_DEC(kF16, kF16) GDN_DEC(kF32, kF16)
+#undef GDN_DEC
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   switch (a.dk) {
-    case 16: return launch_decode_t<16, 4>(a, stream);
-    case 32: return launch_decode_t<32, 8>(a, stream);
-    case 64: return launch_decode_t<64, 16>(a, stream);
-    case 128: return launch_decode_t<128, 16>(a, stream);
-    case 256: return launch_decode_t<256, 16>(a, stream);
+    case 16: return launch_decode_dk<16, 4>(a, stream);
+    case 32: return launch_decode_dk<32, 8>(a, stream);
+    case 64: return launch_decode_dk<64, 8>(a, stream);
+    case 128: return launch_decode_dk<128, 8>(a, stream);
+    case 256: return launch_decode_dk<256, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 // ---------------------------------------------------------------------------
 // token-sequential prefill: one wave per (sequence, v-head, row tile) walks
-// the sequence's tokens with its state tile in registers; the next token's
-// inputs are loaded while the current one is processed.
+// the sequence's tokens with its state tile in registers.  Token inputs are
+// fetched PF tokens at a time into a register ring one group ahead of use,
+// so each token's load latency is hidden behind the previous group's work.
 // ---------------------------------------------------------------------------
-struct TokenIn {
-  float4 q4, k4;
-  float vv, g, beta;
+template <int TIN>
+struct TokenRaw {
+  Raw4<TIN> q, k;
+  uint32_t v;
+  float g, beta;
 };
 
-template <int DK>
-__device__ __forceinline__ TokenIn load_token(const PrefillArgs& a, int64_t t, int hk, int h,
-                                              int col, int myrow) {
-  TokenIn in;
-  in.q4 = load4u(a.q, a.in_dt, t * a.q_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
-  in.k4 = load4u(a.k, a.in_dt, t * a.k_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
-  in.vv = myrow < a.dv ? load1(a.v, a.in_dt, t * a.v_rs + (int64_t)h * a.dv + myrow) : 0.0f;
+template <int DK, int TIN>
+__device__ __forceinline__ TokenRaw<TIN> load_token(const PrefillArgs& a, int64_t t, int hk,
+                                                    int h, int col, int vrow) {
+  TokenRaw<TIN> in;
+  in.q = load_raw4<TIN>(a.q, t * a.q_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
+  in.k = load_raw4<TIN>(a.k, t * a.k_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
+  in.v = load_raw1<TIN>(a.v, t * a.v_rs + (int64_t)h * a.dv + vrow);
   in.g = a.g[t * a.g_rs + h];
   in.beta = a.beta[t * a.beta_rs + h];
   return in;
 }
 
-template <int DK, int NL>
+template <int DK, int NL, int TIN, int PF>
 __global__ __launch_bounds__(256) void prefill_seq_kernel(PrefillArgs a, int64_t total_waves,
                                                           int tiles_per_head) {
   using T = Tile<DK, NL>;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (wave >= total_waves) return;
-  const int tile = (int)(wave % tiles_per_head);
-  const int64_t sh = wave / tiles_per_head;
-  const int h = (int)(sh % a.hv);
-  const int64_t sq = sh / a.hv;
+  const uint32_t wave = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave >= (uint32_t)total_waves) return;
+  const int tile = (int)(wave % (uint32_t)tiles_per_head);
+  const uint32_t sh = wave / (uint32_t)tiles_per_head;
+  const int h = (int)(sh % (uint32_t)a.hv);
+  const int64_t sq = sh / (uint32_t)a.hv;
   const int r0 = tile * T::BV;
   const int sub = lane / T::LPR;
   const int col = (lane % T::LPR) * 4;
   const int j = (lane % T::LPR) / T::OWN;
   const int myrow = r0 + j * T::RPI + sub;
+  const int vrow = min(myrow, a.dv - 1);
   const bool writer = (lane % T::OWN) == 0 && myrow < a.dv;
 
   // cu_seqlens is device data: clamp so a malformed table cannot index past
@@ -237,24 +267,44 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(PrefillArgs a, int64_t
     return;
   }
   const bool init = a.has_init ? a.has_init[sq] != 0 : true;
+  const int hk = h / (a.hv / a.hk);
+
+  TokenRaw<TIN> cur[PF], nxt[PF];
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    cur[u] = load_token<DK, TIN>(a, min(t0 + u, t1 - 1 < t0 ? t0 : t1 - 1), hk, h, col, vrow);
+
   float* S = a.pool + ((slot * a.hv + h) * a.dv) * DK + col;
   float4 s[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int row = r0 + i * T::RPI + sub;
-    s[i] = (init && row < a.dv) ? *reinterpret_cast<const float4*>(S + (int64_t)row * DK)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int row = min(r0 + i * T::RPI + sub, a.dv - 1);
+    s[i] = init ? *reinterpret_cast<const float4*>(S + (int64_t)row * DK)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const int hk = h / (a.hv / a.hk);
-  TokenIn nxt;
-  if (t0 < t1) nxt = load_token<DK>(a, t0, hk, h, col, myrow);
-  for (int64_t t = t0; t < t1; ++t) {
-    TokenIn cur = nxt;
-    if (t + 1 < t1) nxt = load_token<DK>(a, t + 1, hk, h, col, myrow);
-    const float kq = prepare_qk<T::LPR>(cur.q4, cur.k4, a.l2norm != 0, a.l2_eps, a.scale);
-    const float o = tile_step<DK, NL>(s, cur.q4, cur.k4, kq, expf(cur.g), cur.beta, cur.vv,
-                                      lane, sub);
-    if (writer) store1(a.out, a.out_dt, (t * a.hv + h) * a.dv + myrow, o);
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    if (r0 + i * T::RPI + sub >= a.dv) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  for (int64_t base = t0; base < t1; base += PF) {
+    // next group: clamped to the last token (a re-read, never out of range)
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      nxt[u] = load_token<DK, TIN>(a, min(base + PF + u, t1 - 1), hk, h, col, vrow);
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int64_t t = base + u;
+      if (t < t1) {
+        float4 q4 = raw_to_f32<TIN>(cur[u].q);
+        float4 k4 = raw_to_f32<TIN>(cur[u].k);
+        const float kq = prepare_qk<T::LPR>(q4, k4, a.l2norm != 0, a.l2_eps, a.scale);
+        const float o = tile_step<DK, NL>(s, q4, k4, kq, expf(cur[u].g), cur[u].beta,
+                                          raw1_to_f32<TIN>(cur[u].v), lane, sub);
+        if (writer) store1(a.out, a.out_dt, (t * a.hv + h) * a.dv + myrow, o);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u) cur[u] = nxt[u];
   }
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
@@ -263,24 +313,34 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(PrefillArgs a, int64_t
   }
 }
 
-template <int DK, int NL>
+template <int DK, int NL, int TIN>
 static hipError_t launch_prefill_seq_t(const PrefillArgs& a, hipStream_t stream) {
   using T = Tile<DK, NL>;
+  constexpr int PF = 8;
   const int tiles = (a.dv + T::BV - 1) / T::BV;
   const int64_t waves = a.num_seqs * a.hv * tiles;
+  if (waves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((prefill_seq_kernel<DK, NL>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                     a, waves, tiles);
+  hipLaunchKernelGGL((prefill_seq_kernel<DK, NL, TIN, PF>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, a, waves, tiles);
   return hipGetLastError();
+}
+
+template <int DK, int NL>
+static hipError_t launch_prefill_seq_dk(const PrefillArgs& a, hipStream_t stream) {
+  if (a.in_dt == kBF16) return launch_prefill_seq_t<DK, NL, kBF16>(a, stream);
+  if (a.in_dt == kF16) return launch_prefill_seq_t<DK, NL, kF16>(a, stream);
+  if (a.in_dt == kF32) return launch_prefill_seq_t<DK, NL, kF32>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_sequential(const PrefillArgs& a, hipStream_t stream) {
   switch (a.dk) {
-    case 16: return launch_prefill_seq_t<16, 1>(a, stream);
-    case 32: return launch_prefill_seq_t<32, 2>(a, stream);
-    case 64: return launch_prefill_seq_t<64, 4>(a, stream);
-    case 128: return launch_prefill_seq_t<128, 4>(a, stream);
-    case 256: return launch_prefill_seq_t<256, 4>(a, stream);
+    case 16: return launch_prefill_seq_dk<16, 1>(a, stream);
+    case 32: return launch_prefill_seq_dk<32, 2>(a, stream);
+    case 64: return launch_prefill_seq_dk<64, 4>(a, stream);
+    case 128: return launch_prefill_seq_dk<128, 4>(a, stream);
+    case 256: return launch_prefill_seq_dk<256, 4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

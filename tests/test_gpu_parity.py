@@ -244,6 +244,10 @@ PREFILL_CASES = [
     ([17, 140], 2, 4, 64, 48, W.F16, W.F32, [0, 1]),
     ([33, 5, 96], 1, 2, 32, 32, W.BF16, W.BF16, [1, 0, 1]),
     ([70], 1, 1, 256, 128, W.BF16, W.BF16, [1]),
+    # chunk-boundary lengths, GQA 3, two 32-row state tiles
+    ([1, 63, 64, 65, 127, 128, 129], 2, 6, 128, 64, W.BF16, W.BF16, [1, 0, 1, 1, 0, 1, 1]),
+    ([300, 17], 1, 2, 128, 96, W.F16, W.F16, [1, 0]),
+    ([190], 2, 4, 128, 128, W.BF16, W.F32, [1]),
 ]
 
 
@@ -303,3 +307,21 @@ def test_prefill_varlen_gqa3_sampled_heads(dev):
     assert np.isfinite(res.out).all()
     print(f"  lengths {case.meta['lengths']} out rel-L1 {r_out:.3e}  state rel-L1 {r_st:.3e}",
           flush=True)
+
+
+@pytest.mark.parametrize("ind", [W.BF16, W.F16], ids=["bf16", "f16"])
+def test_prefill_chunked_matches_sequential(dev, ind):
+    announce(f"prefill: chunked MFMA path vs token-sequential path ({W.DTYPE_NAMES[ind]})")
+    case = W.make_prefill_case("cvs", 4321, lengths=[257, 64, 1, 130], hk=2, hv=4, dk=128,
+                               dv=128, in_dtype=ind, out_dtype=ind, slots=6)
+    rs = H.run_prefill(case, dev, sequential=True)
+    rc = H.run_prefill(case, dev, sequential=False)
+    assert H.rel_l1(rc.out, rs.out) <= H.OUT_TOL_HALF
+    idx = torch.from_numpy(case.idx.astype(np.int64)).to(dev)
+    st_c, st_s = rc.pool[idx].cpu().numpy(), rs.pool[idx].cpu().numpy()
+    assert H.rel_l1(st_c, st_s) <= H.STATE_TOL
+    want_out, want_state = oracle.prefill_case(case)
+    H.check_prefill(case, rc, want_out, want_state)
+    H.check_prefill(case, rs, want_out, want_state)
+    print(f"  chunked vs sequential: out {H.rel_l1(rc.out, rs.out):.2e} "
+          f"state {H.rel_l1(st_c, st_s):.2e}", flush=True)
