@@ -50,6 +50,42 @@ def decode_bytes(B, hk, hv, dk, dv, in_bytes, out_bytes, alpha_bytes=4):
     return state + qk + vo + gate
 
 
+DECODE_SOURCES = ("linear_attention_recurrence_gdn_amd/csrc/gdn_recurrent.hip",
+                  "linear_attention_recurrence_gdn_amd/csrc/gdn_device.h")
+TRAFFIC_PROFILE = "profiles/decode_B256_hbm_traffic.md"
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed PMC summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy's counters), or None when the summary is
+    missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":", 1)[0].strip() in (
+                    "source_sha256", "traffic_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != decode_source_hash():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def prefill_bytes(T, N, hk, hv, dk, dv, in_bytes, out_bytes):
     """Algorithmic HBM bytes of gate + varlen prefill: q/k/v read once, out
     written once, alpha read and g written by the gate, g and beta read by the
@@ -78,6 +114,9 @@ def main():
                     help="wall-clock budget of each CPU-oracle baseline leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (scale factor for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.exit("bench.py: this build measures one GPU only (the decode and prefill kernels "
@@ -88,6 +127,17 @@ def main():
     import linear_attention_recurrence_gdn_amd as gdn
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 28
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n,
+                                               "launches": 5}}), flush=True)
+        return
     t_setup = time.time()
 
     # ---------------- decode leg ----------------
@@ -156,8 +206,11 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "decode_kernel<128,16>", "kernel_avg_us": round(kavg * 1e3, 2),
+            "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "copy-calibrated)",
+            "kernel": "gdn::decode_kernel (Dk=128, 8 state loads/lane, nontemporal)",
+            "kernel_avg_us": round(kavg * 1e3, 2),
         },
     }
 

@@ -20,7 +20,7 @@
 //                       strictly-lower A, T = (I + A)^{-1} by blocked forward
 //                       substitution (16x16 blocks), T_b = T diag(beta) to the
 //                       workspace -- all of it independent of the state;
-//   chunk_state_kernel  one workgroup per (sequence, v-head, 32-row tile of S)
+//   chunk_state_kernel  one workgroup per (sequence, v-head, 16-row tile of S)
 //                       walks the chunks in order with its S tile held in MFMA
 //                       accumulators:
 //                         X = K S^T,  Z = V - diag(e^G n_k) X,  U = T_b Z,
@@ -28,7 +28,7 @@
 //                         S = e^{G_C} S + (diag(e^{G_C - G} n_k) U)^T K.
 //                       Forming U as T_b (V - ...) never builds the 64 x 128
 //                       matrix T diag(beta e^G) K, so each tile does only work
-//                       proportional to its own 32 rows.
+//                       proportional to its own 16 rows.
 // Precision: the raw 16-bit q/k/v are exact MFMA operands; the L2 norms enter
 // as diagonal scalings; an f32 operand (S, T_b, Z, U) is split into a 16-bit
 // high part and a 16-bit remainder, and the products keep hi*hi + hi*lo +
@@ -44,10 +44,11 @@ namespace {
 
 constexpr int CK = 64;        // tokens per chunk
 constexpr int DKC = 128;      // key head size served here
-constexpr int BVT = 32;       // state rows per workgroup in the state walk
+constexpr int BVT = 16;       // state rows per workgroup in the state walk
 constexpr int LDQ = DKC + 8;  // padded LDS row (16-bit elements), token-major 128-wide tiles
 constexpr int LDT = CK + 8;   // padded LDS row (16-bit elements), 64-wide tiles
 constexpr int LDF = CK + 4;   // padded LDS row (f32), 64 x 64 matrices
+constexpr int kXcds = 8;      // accelerator complex dies (separate L2s) on MI355X
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -108,6 +109,16 @@ __device__ __forceinline__ void frag_split(const float* m, int ld, int r0, int k
   lo = __builtin_bit_cast(typename MT<TIN>::x8, l);
 }
 
+// Workgroup barrier ordering LDS only.  __syncthreads() also waits for every
+// outstanding global access, which would force the next chunk's prefetched
+// loads to land at the first barrier; all communication between the waves
+// here goes through LDS, so the global loads may stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void chunk_bounds(const PrefillArgs& a, int64_t s, int64_t& t0,
                                              int64_t& t1) {
   // cu_seqlens is device data: clamp so a malformed table cannot index past
@@ -117,9 +128,15 @@ __device__ __forceinline__ void chunk_bounds(const PrefillArgs& a, int64_t s, in
 }
 
 // ---------------------------------------------------------------------------
-// chunk offsets: cs[s] = number of chunks of sequences before s; cs[n] = total
+// chunk offsets: cs[s] = number of chunks of sequences before s; cs[n] = total.
+// order[k] = the sequence with the k-th most chunks (ties by index) when
+// n <= kOrderMax, else k: the state walk starts the longest sequences first,
+// since the longest one bounds the whole prefill.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, int32_t* cs) {
+constexpr int kOrderMax = 1024;
+
+__global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, int32_t* cs,
+                                                         int32_t* order) {
   __shared__ int32_t part[256];
   int32_t carry = 0;
   if (threadIdx.x == 0) cs[0] = 0;
@@ -143,6 +160,20 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, int32_t*
     carry += part[255];
     __syncthreads();
   }
+  __syncthreads();
+  const int n = (int)a.num_seqs;
+  for (int s = threadIdx.x; s < n; s += 256) {
+    int rank = s;
+    if (n <= kOrderMax) {
+      const int cnt = cs[s + 1] - cs[s];
+      rank = 0;
+      for (int t = 0; t < n; ++t) {
+        const int ct = cs[t + 1] - cs[t];
+        rank += (ct > cnt) || (ct == cnt && t < s);
+      }
+    }
+    order[rank] = s;
+  }
 }
 
 // inclusive prefix sum of 64 values held one per lane of a wave, in f64
@@ -156,18 +187,31 @@ __device__ __forceinline__ double wave_prefix64(double x, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// T_b = (I + A)^{-1} diag(beta) per (chunk, v-head)
+// Per (chunk, v-head) record written by the prep kernel and read by the state
+// walk (byte offsets):
+//   T_b = (I + A)^{-1} diag(beta), split into 16-bit high / low parts, [64][64] each
+//   P   = masked, scaled Q K^T:  P_ij = scale n_q,i n_k,j E_ij (q_i . k_j) for j <= i,
+//         16-bit (high part only; it multiplies U in the output term only)
+//   F   = f32 [4][64]: fz_i = e^{G_i} n_k,i,  fo_i = e^{G_i} scale n_q,i,
+//         fw_i = e^{G_last - G_i} n_k,i,  and F[3][0] = e^{G_last}
 // ---------------------------------------------------------------------------
+constexpr int REC_TH = 0;
+constexpr int REC_TL = CK * CK * 2;
+constexpr int REC_P = 2 * CK * CK * 2;
+constexpr int REC_F = 3 * CK * CK * 2;
+constexpr int REC_BYTES = REC_F + 4 * CK * 4;
+
 template <int TIN>
-__global__ __launch_bounds__(256) void chunk_t_kernel(PrefillArgs a, const int32_t* cs,
-                                                      float* tws) {
+__global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, const int32_t* cs,
+                                                         char* recs) {
+  __shared__ __align__(16) uint16_t Qs[CK * LDQ];
   __shared__ __align__(16) uint16_t Ks[CK * LDQ];
   __shared__ __align__(16) float Am[CK * LDF];
   __shared__ __align__(16) float Tm[CK * LDF];
   __shared__ float Rs[4][16 * 17];
   __shared__ double Gd[CK];
-  __shared__ float nk[CK];
-  __shared__ float bt[CK];
+  __shared__ float nq[CK], nk[CK], bt[CK];
+  using M = MT<TIN>;
 
   const int c = blockIdx.x;
   const int h = blockIdx.y;
@@ -187,17 +231,22 @@ __global__ __launch_bounds__(256) void chunk_t_kernel(PrefillArgs a, const int32
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
 
-  // stage K (zero rows past the sequence), g, beta
+  // stage Q and K (zero rows past the sequence), g, beta
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int idx = tid + 256 * u;
     const int row = idx >> 4, p = idx & 15;
-    uint4 val = {0, 0, 0, 0};
-    if (row < L)
-      val = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) +
-                                            (tb + row) * a.k_rs + (int64_t)hk * DKC + 8 * p);
-    *reinterpret_cast<uint4*>(Ks + row * LDQ + 8 * p) = val;
+    uint4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0};
+    if (row < L) {
+      qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
+                                           (tb + row) * a.q_rs + (int64_t)hk * DKC + 8 * p);
+      kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) +
+                                           (tb + row) * a.k_rs + (int64_t)hk * DKC + 8 * p);
+    }
+    *reinterpret_cast<uint4*>(Qs + row * LDQ + 8 * p) = qv;
+    *reinterpret_cast<uint4*>(Ks + row * LDQ + 8 * p) = kv;
   }
   if (w == 0) {
     const float gv = lane < L ? a.g[(tb + lane) * a.g_rs + h] : 0.0f;
@@ -206,48 +255,80 @@ __global__ __launch_bounds__(256) void chunk_t_kernel(PrefillArgs a, const int32
     bt[lane] = bv;
   }
   __syncthreads();
-  {  // row norms of K: 4 lanes per row
+  {  // row norms: 4 lanes per row, 32 elements each
     const int row = tid >> 2, qq = tid & 3;
-    float ss = 0.0f;
+    float sq = 0.0f, sk = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float x = MT<TIN>::dec(Ks[row * LDQ + 32 * qq + e]);
-      ss += x * x;
+    for (int u = 0; u < 4; ++u) {
+      const uint4 xq = *reinterpret_cast<const uint4*>(Qs + row * LDQ + 32 * qq + 8 * u);
+      const uint4 xk = *reinterpret_cast<const uint4*>(Ks + row * LDQ + 32 * qq + 8 * u);
+      const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w}, wk[4] = {xk.x, xk.y, xk.z, xk.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float q0 = M::dec(wq[e] & 0xffffu), q1 = M::dec(wq[e] >> 16);
+        const float k0 = M::dec(wk[e] & 0xffffu), k1 = M::dec(wk[e] >> 16);
+        sq += q0 * q0 + q1 * q1;
+        sk += k0 * k0 + k1 * k1;
+      }
     }
-    ss += xor_lane<1>(ss);
-    ss += xor_lane<2>(ss);
-    if (qq == 0) nk[row] = a.l2norm ? 1.0f / sqrtf(ss + a.l2_eps) : 1.0f;
+    sq += xor_lane<1>(sq);
+    sq += xor_lane<2>(sq);
+    sk += xor_lane<1>(sk);
+    sk += xor_lane<2>(sk);
+    if (qq == 0) {
+      nq[row] = a.l2norm ? 1.0f / sqrtf(sq + a.l2_eps) : 1.0f;
+      nk[row] = a.l2norm ? 1.0f / sqrtf(sk + a.l2_eps) : 1.0f;
+    }
   }
   __syncthreads();
+  if (w == 0) {  // per-token factors
+    float* F = reinterpret_cast<float*>(rec + REC_F);
+    const double gl = Gd[L - 1];
+    const float eg = expf((float)Gd[lane]);
+    F[lane] = eg * nk[lane];
+    F[CK + lane] = eg * a.scale * nq[lane];
+    F[2 * CK + lane] = expf((float)(gl - Gd[lane])) * nk[lane];
+    F[3 * CK + lane] = lane == 0 ? expf((float)gl) : 0.0f;
+  }
 
-  // A = strictly lower (beta_i E_ij nk_i nk_j (K K^T)_ij), lower tiles only
-  for (int t = w; t < 10; t += 4) {
+  // 20 tile products: K K^T (jobs 0..9) and Q K^T (jobs 10..19), lower tiles
+  uint16_t* P = reinterpret_cast<uint16_t*>(rec + REC_P);
+  for (int job = w; job < 20; job += 4) {
+    const bool is_p = job >= 10;
+    const int t = is_p ? job - 10 : job;
     const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
     const int tj = t - (ti * (ti + 1)) / 2;
+    const uint16_t* X = is_p ? Qs : Ks;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      acc = MT<TIN>::mma(frag<TIN>(Ks, LDQ, 16 * ti, 32 * kk, lane),
-                         frag<TIN>(Ks, LDQ, 16 * tj, 32 * kk, lane), acc);
+      acc = M::mma(frag<TIN>(X, LDQ, 16 * ti, 32 * kk, lane),
+                   frag<TIN>(Ks, LDQ, 16 * tj, 32 * kk, lane), acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * ti + 4 * (lane >> 4) + r;
       const int j = 16 * tj + (lane & 15);
-      float v = 0.0f;
-      if (j < i) v = bt[i] * expf((float)(Gd[i] - Gd[j])) * nk[i] * nk[j] * acc[r];
-      Am[i * LDF + j] = v;
+      const float e = expf((float)(Gd[i] - Gd[j]));
+      if (is_p) {
+        const float pv = j <= i ? acc[r] * a.scale * nq[i] * nk[j] * e : 0.0f;
+        P[i * CK + j] = M::enc(pv);
+      } else {
+        Am[i * LDF + j] = j < i ? bt[i] * e * nk[i] * nk[j] * acc[r] : 0.0f;
+      }
     }
   }
-  // zero the strictly-upper 16x16 blocks of T
+  // zero the strictly-upper 16x16 blocks of T and of P
   for (int idx = tid; idx < 6 * 256; idx += 256) {
     const int blk = idx >> 8, e = idx & 255;
     const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
     const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-    Tm[(16 * bi + (e >> 4)) * LDF + 16 * bj + (e & 15)] = 0.0f;
+    const int i = 16 * bi + (e >> 4), j = 16 * bj + (e & 15);
+    Tm[i * LDF + j] = 0.0f;
+    P[i * CK + j] = 0;
   }
   __syncthreads();
 
-  // diagonal blocks: forward substitution, one column per lane
+  // diagonal blocks of T = (I + A)^{-1}: forward substitution, one column per lane
   if (lane < 16) {
     const int b0 = 16 * w, col = lane;
     float x[16];
@@ -263,328 +344,433 @@ __global__ __launch_bounds__(256) void chunk_t_kernel(PrefillArgs a, const int32
   }
   __syncthreads();
 
-  // off-diagonal blocks by distance: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+  // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
+  // 16x16x16 products on the f32 MFMA (A: lane (m = l%16, k = l/16),
+  // B: lane (k = l/16, n = l%16), D: lane (m = 4 (l/16) + r, n = l%16))
   for (int d = 1; d < 4; ++d) {
     const int j = w, i = w + d;
     const bool active = i < 4;
-    const int cc = lane & 15, rb = 4 * (lane >> 4);
+    f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
     if (active) {
+      for (int k = j; k < i; ++k)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = rb + q;
-        float r = 0.0f;
-        for (int k = j; k < i; ++k)
+        for (int s4 = 0; s4 < 4; ++s4)
+          r4 = __builtin_amdgcn_mfma_f32_16x16x4f32(
+              Am[(16 * i + (lane & 15)) * LDF + 16 * k + 4 * s4 + (lane >> 4)],
+              Tm[(16 * k + 4 * s4 + (lane >> 4)) * LDF + 16 * j + (lane & 15)], r4, 0, 0, 0);
 #pragma unroll
-          for (int m = 0; m < 16; ++m)
-            r += Am[(16 * i + rr) * LDF + 16 * k + m] * Tm[(16 * k + m) * LDF + 16 * j + cc];
-        Rs[w][rr * 17 + cc] = r;
-      }
+      for (int r = 0; r < 4; ++r) Rs[w][(4 * (lane >> 4) + r) * 17 + (lane & 15)] = r4[r];
     }
     __syncthreads();
     if (active) {
+      f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = rb + q;
-        float t = 0.0f;
+      for (int s4 = 0; s4 < 4; ++s4)
+        t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(
+            Tm[(16 * i + (lane & 15)) * LDF + 16 * i + 4 * s4 + (lane >> 4)],
+            Rs[w][(4 * s4 + (lane >> 4)) * 17 + (lane & 15)], t4, 0, 0, 0);
 #pragma unroll
-        for (int m = 0; m < 16; ++m) t += Tm[(16 * i + rr) * LDF + 16 * i + m] * Rs[w][m * 17 + cc];
-        Tm[(16 * i + rr) * LDF + 16 * j + cc] = -t;
-      }
+      for (int r = 0; r < 4; ++r)
+        Tm[(16 * i + 4 * (lane >> 4) + r) * LDF + 16 * j + (lane & 15)] = -t4[r];
     }
     __syncthreads();
   }
 
-  float* out = tws + ((int64_t)c * a.hv + h) * (CK * CK);
+  // T_b = T diag(beta), split into high and low 16-bit parts
+  uint16_t* Th = reinterpret_cast<uint16_t*>(rec + REC_TH);
+  uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + REC_TL);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int idx = tid + 256 * u;
     const int i = idx >> 4, j4 = 4 * (idx & 15);
-    float4 t = *reinterpret_cast<const float4*>(Tm + i * LDF + j4);
-    t.x *= bt[j4]; t.y *= bt[j4 + 1]; t.z *= bt[j4 + 2]; t.w *= bt[j4 + 3];
-    *reinterpret_cast<float4*>(out + i * CK + j4) = t;
+    const float4 t = *reinterpret_cast<const float4*>(Tm + i * LDF + j4);
+    const float x[4] = {t.x * bt[j4], t.y * bt[j4 + 1], t.z * bt[j4 + 2], t.w * bt[j4 + 3]};
+    uint16_t hh[4], ll[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hh[e] = M::enc(x[e]);
+      ll[e] = M::enc(x[e] - M::dec(hh[e]));
+    }
+    *reinterpret_cast<uint2*>(Th + i * CK + j4) =
+        make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
+    *reinterpret_cast<uint2*>(Tl + i * CK + j4) =
+        make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
   }
 }
 
 // ---------------------------------------------------------------------------
 // the state walk
 // ---------------------------------------------------------------------------
-template <int TIN>
+// K^T is stored [dk][token] with the 8-token groups XOR-swizzled by dk, so the
+// transposed 2-byte writes of the four lane groups land in different banks and
+// an 8-token operand read stays one contiguous 16-byte access.
+__device__ __forceinline__ int kt_col(int dk, int token) { return token ^ (((dk >> 3) & 3) << 3); }
+
 struct WalkLds {
-  uint16_t Qs[CK * LDQ];
-  uint16_t Ks[CK * LDQ];
-  uint16_t Kt[DKC * LDT];
-  uint16_t Vs[CK * BVT];
-  float Ts[CK * LDF];
-  uint16_t Sh[BVT * LDQ], Sl[BVT * LDQ];
-  uint16_t Zh[BVT * LDT], Zl[BVT * LDT];
-  uint16_t Uh[BVT * LDT], Ul[BVT * LDT];
-  uint16_t Wh[BVT * LDT], Wl[BVT * LDT];
-  uint16_t Ph[CK * LDT];
-  double Gd[CK];
-  float nq[CK], nk[CK];
+  uint16_t Kt[DKC * LDT];                         // K^T of the chunk
+  uint16_t Sh[2][BVT * LDQ], Sl[2][BVT * LDQ];    // S tile [dv][dk], double-buffered
+  uint16_t Zh[BVT * LDT], Zl[BVT * LDT];          // Z^T  [dv][token]
+  uint16_t Uh[BVT * LDT], Ul[BVT * LDT];          // U^T
+  uint16_t Wh[BVT * LDT], Wl[BVT * LDT];          // (diag(fw) U)^T
 };
 
-template <int TIN>
-__global__ __launch_bounds__(256) void chunk_state_kernel(PrefillArgs a, const int32_t* cs,
-                                                          const float* tws, int ntiles,
-                                                          int max_chunks) {
-  __shared__ __align__(16) WalkLds<TIN> sm;
+// The chunk inputs a wave needs for its 16-row block: rows rb + lane % 16 for
+// the A operands, rows rb + 4 (lane/16) + r for the elementwise work.
+struct ChunkRegs {
+  uint4 q[4], k[4];    // Q, K rows, columns 32 kk + 8 (lane/16) .. +8
+  uint4 th[2], tl[2];  // T_b rows, columns 32 kt + 8 (lane/16) .. +8
+  uint4 p[2];          // P rows
+  uint32_t v[4];       // V[rb + 4 (lane/16) + r][dv0 + lane % 16]
+  float4 fz, fo, fw;   // factors of rows rb + 4 (lane/16) .. +3
+  float gc;
+};
+
+struct WalkCtx {
+  const PrefillArgs* a;
+  const char* recs;
+  int64_t t_begin, t_end;
+  int c0, h, hk, dv0, rb, nkt, lane;
+};
+
+__device__ __forceinline__ int chunk_len(const WalkCtx& c, int ch) {
+  return (int)min((int64_t)CK, c.t_end - (c.t_begin + (int64_t)ch * CK));
+}
+
+__device__ __forceinline__ const char* chunk_rec(const WalkCtx& c, int ch) {
+  return c.recs + ((int64_t)(c.c0 + ch) * c.a->hv + c.h) * REC_BYTES;
+}
+
+__device__ __forceinline__ void fetch_qk(ChunkRegs& R, const WalkCtx& c, int ch) {
+  const PrefillArgs& a = *c.a;
+  const int64_t tb = c.t_begin + (int64_t)ch * CK;
+  const int arow = min(c.rb + (c.lane & 15), chunk_len(c, ch) - 1);  // zeroed at use if >= L
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tb + arow) * a.q_rs +
+                       (int64_t)c.hk * DKC + 8 * (c.lane >> 4);
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tb + arow) * a.k_rs +
+                       (int64_t)c.hk * DKC + 8 * (c.lane >> 4);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    R.q[kk] = *reinterpret_cast<const uint4*>(qp + 32 * kk);
+    R.k[kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
+  }
+}
+
+__device__ __forceinline__ int rec_toff(const WalkCtx& c, int kt) {
+  return 2 * ((c.rb + (c.lane & 15)) * CK + 8 * (c.lane >> 4) + 32 * kt);
+}
+
+__device__ __forceinline__ void fetch_t(ChunkRegs& R, const WalkCtx& c, int ch) {
+  const char* rec = chunk_rec(c, ch);
+  // both k-steps are always loaded (for the first 32 rows the second one is
+  // the zero upper block), so every path issues the same memory operations
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    R.th[kt] = *reinterpret_cast<const uint4*>(rec + REC_TH + rec_toff(c, kt));
+    R.tl[kt] = *reinterpret_cast<const uint4*>(rec + REC_TL + rec_toff(c, kt));
+  }
+}
+
+__device__ __forceinline__ void fetch_p(ChunkRegs& R, const WalkCtx& c, int ch) {
+  const char* rec = chunk_rec(c, ch);
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+    R.p[kt] = *reinterpret_cast<const uint4*>(rec + REC_P + rec_toff(c, kt));
+}
+
+__device__ __forceinline__ void fetch_vf(ChunkRegs& R, const WalkCtx& c, int ch) {
+  const PrefillArgs& a = *c.a;
+  const int64_t tb = c.t_begin + (int64_t)ch * CK;
+  const int L = chunk_len(c, ch);
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (int64_t)c.h * a.dv + c.dv0 +
+                       (c.lane & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int vrow = min(c.rb + 4 * (c.lane >> 4) + r, L - 1);
+    R.v[r] = vp[(tb + vrow) * a.v_rs];
+  }
+  const float* F = reinterpret_cast<const float*>(chunk_rec(c, ch) + REC_F);
+  const int frow = c.rb + 4 * (c.lane >> 4);
+  R.fz = *reinterpret_cast<const float4*>(F + frow);
+  R.fo = *reinterpret_cast<const float4*>(F + CK + frow);
+  R.fw = *reinterpret_cast<const float4*>(F + 2 * CK + frow);
+  R.gc = F[3 * CK];
+}
+
+__device__ __forceinline__ float f4(const float4& v, int r) {
+  return r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
+}
+
+// four consecutive 16-bit elements (rows i0..i0+3 of a transposed tile) as
+// one 8-byte LDS store
+__device__ __forceinline__ void store4(uint16_t* p, const uint16_t (&e)[4]) {
+  *reinterpret_cast<uint2*>(p) =
+      make_uint2((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16));
+}
+
+// Output element type of the state walk.
+template <int TOUT>
+struct OutT {
+  typedef uint16_t type;
+  static __device__ __forceinline__ uint16_t cvt(float x) {
+    return TOUT == kBF16 ? f32_to_bf16(x) : f32_to_f16(x);
+  }
+};
+template <>
+struct OutT<kF32> {
+  typedef float type;
+  static __device__ __forceinline__ float cvt(float x) { return x; }
+};
+
+// `dump` holds one 64 x 16 tile per workgroup: outputs of rows past the end of
+// a sequence are written there instead of being skipped, so every chunk step
+// issues the same number of stores and the compiler's memory-counter waits
+// for the prefetched next chunk stay exact (a data-dependent store count
+// makes it wait for all outstanding loads).
+template <int TIN, int TOUT>
+__global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, const int32_t* cs,
+                                                             const int32_t* order,
+                                                             const char* recs, int ntiles,
+                                                             int max_chunks, float* dump) {
+  __shared__ __align__(16) WalkLds sm;
   using M = MT<TIN>;
   using x8 = typename M::x8;
 
-  const int tile = blockIdx.x % ntiles;
-  const int sh = blockIdx.x / ntiles;
-  const int h = sh % a.hv;
-  const int s = sh / a.hv;
+  // XCD-aware mapping.  Workgroups are dealt round-robin to the 8 XCDs, each
+  // with its own L2; the tiles of one v-head re-read the same per-chunk
+  // records, and the v-heads of one GQA group the same q/k rows, so a unit
+  // (sequence, q/k head) keeps all ratio * ntiles of its workgroups on one
+  // XCD: block b -> xcd = b % 8, unit = (b / 8) / per_unit * 8 + xcd.
+  const int ratio = a.hv / a.hk;
+  const int per_unit = ratio * ntiles;
+  const int xcd = blockIdx.x % kXcds;
+  const int rblk = blockIdx.x / kXcds;
+  const int unit = (rblk / per_unit) * kXcds + xcd;
+  if (unit >= a.num_seqs * a.hk) return;
+  const int j = rblk % per_unit;
+  const int tile = j % ntiles;
+  const int h = (unit % a.hk) * ratio + j / ntiles;
+  const int s_rank = unit / a.hk;
+  const int s = order[s_rank];
+  const int sh = s_rank * a.hv + h;  // workgroup slot used for the dump area
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dv0 = tile * BVT;
-  const int hk = h / (a.hv / a.hk);
-  int64_t t_begin, t_end;
-  chunk_bounds(a, s, t_begin, t_end);
-  const int c0 = cs[s];
+  WalkCtx c;
+  c.a = &a;
+  c.recs = recs;
+  chunk_bounds(a, s, c.t_begin, c.t_end);
+  c.c0 = cs[s];
+  c.h = h;
+  c.hk = h / (a.hv / a.hk);
+  c.dv0 = tile * BVT;
+  c.rb = 16 * w;
+  c.nkt = (c.rb + 15) / 32 + 1;  // k-steps over tokens j <= i
+  c.lane = lane;
   // a well-formed cu_seqlens gives c0 + nch <= max_chunks; a malformed one
   // (overlapping ranges) must still never index past the workspace
-  const int nch = max(0, min((int)((t_end - t_begin + CK - 1) / CK), max_chunks - c0));
+  const int nch =
+      max(0, min((int)((c.t_end - c.t_begin + CK - 1) / CK), max_chunks - c.c0));
   const int64_t slot = a.idx ? (int64_t)a.idx[s] : (int64_t)s;
   const int64_t out_rs = (int64_t)a.hv * a.dv;
 
   if (slot < 0 || slot >= a.num_slots) {
     // caller error: NaN outputs for this tile, no state access
-    for (int64_t t = t_begin + (tid >> 3); t < t_end; t += 32)
-      for (int e = (tid & 7); e < BVT; e += 8)
-        store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + dv0 + e, __builtin_nanf(""));
+    for (int64_t t = c.t_begin + (tid >> 4); t < c.t_end; t += 16)
+      store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + c.dv0 + (tid & 15),
+             __builtin_nanf(""));
     return;
   }
   const bool init = a.has_init ? a.has_init[s] != 0 : true;
-  float* Sg = a.pool + ((slot * a.hv + h) * a.dv + dv0) * DKC;
+  float* Sg = a.pool + ((slot * a.hv + h) * a.dv + c.dv0) * DKC;
+  const int rb = c.rb;
+  const int nkt = c.nkt;
+  using Ot = typename OutT<TOUT>::type;
+  Ot* out = static_cast<Ot*>(a.out) + (int64_t)h * a.dv + c.dv0;
+  float* dump_tile = dump + ((int64_t)sh * ntiles + tile) * (CK * BVT);
 
-  // S tile in MFMA accumulators: wave w holds (mt, nt) = (q / 2, 2w + q % 2);
-  // element r of tile q is S[16 mt + 4 (lane/16) + r][16 nt + lane % 16].
-  f32x4 accs[4];
+  // S tile (16 x 128) in MFMA accumulators: wave w holds column tiles
+  // nt = 2w + q; element r is S[4 (lane/16) + r][16 nt + lane % 16].
+  f32x4 accs[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int mt = q >> 1, nt = 2 * w + (q & 1);
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * w + q;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * mt + 4 * (lane >> 4) + r, col = 16 * nt + (lane & 15);
-      accs[q][r] = init ? Sg[row * DKC + col] : 0.0f;
-    }
+    for (int r = 0; r < 4; ++r)
+      accs[q][r] = init ? Sg[(4 * (lane >> 4) + r) * DKC + 16 * nt + (lane & 15)] : 0.0f;
   }
-  auto write_s_lds = [&]() {
+  auto write_s_lds = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int mt = q >> 1, nt = 2 * w + (q & 1);
+    for (int q = 0; q < 2; ++q) {
+      const int nt = 2 * w + q;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * (lane >> 4) + r, col = 16 * nt + (lane & 15);
+        const int off = (4 * (lane >> 4) + r) * LDQ + 16 * nt + (lane & 15);
         const uint16_t hb = M::enc(accs[q][r]);
-        sm.Sh[row * LDQ + col] = hb;
-        sm.Sl[row * LDQ + col] = M::enc(accs[q][r] - M::dec(hb));
+        sm.Sh[buf][off] = hb;
+        sm.Sl[buf][off] = M::enc(accs[q][r] - M::dec(hb));
       }
     }
   };
-  write_s_lds();
+  // Q, K, V and the factors are fetched one chunk ahead; T_b and P (needed
+  // only from the second phase on) at the start of their own chunk, which
+  // keeps the two register sets small enough to avoid register reuse stalls.
+  auto fetch_ahead = [&](ChunkRegs& R, int ch) {
+    fetch_qk(R, c, ch);
+    fetch_vf(R, c, ch);
+  };
 
-  for (int ch = 0; ch < nch; ++ch) {
-    const int64_t tb = t_begin + (int64_t)ch * CK;
-    const int L = (int)min((int64_t)CK, t_end - tb);
-    // ---- stage the chunk's inputs ----
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = tid + 256 * u;
-      const int row = idx >> 4, p = idx & 15;
-      uint4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0};
-      if (row < L) {
-        qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
-                                             (tb + row) * a.q_rs + (int64_t)hk * DKC + 8 * p);
-        kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) +
-                                             (tb + row) * a.k_rs + (int64_t)hk * DKC + 8 * p);
-      }
-      *reinterpret_cast<uint4*>(sm.Qs + row * LDQ + 8 * p) = qv;
-      *reinterpret_cast<uint4*>(sm.Ks + row * LDQ + 8 * p) = kv;
-      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm.Kt[(8 * p + 2 * e) * LDT + row] = (uint16_t)(kw[e] & 0xffffu);
-        sm.Kt[(8 * p + 2 * e + 1) * LDT + row] = (uint16_t)(kw[e] >> 16);
-      }
-    }
-    {
-      const int row = tid >> 2, p = tid & 3;
-      uint4 vv = {0, 0, 0, 0};
-      if (row < L)
-        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) +
-                                             (tb + row) * a.v_rs + (int64_t)h * a.dv + dv0 + 8 * p);
-      *reinterpret_cast<uint4*>(sm.Vs + row * BVT + 8 * p) = vv;
-    }
-    {
-      const float* tsrc = tws + ((int64_t)(c0 + ch) * a.hv + h) * (CK * CK);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int idx = tid + 256 * u;
-        const int i = idx >> 4, j4 = 4 * (idx & 15);
-        *reinterpret_cast<float4*>(sm.Ts + i * LDF + j4) =
-            *reinterpret_cast<const float4*>(tsrc + i * CK + j4);
-      }
-    }
-    if (w == 0) {
-      const float gv = lane < L ? a.g[(tb + lane) * a.g_rs + h] : 0.0f;
-      sm.Gd[lane] = wave_prefix64((double)gv, lane);
-    }
-    __syncthreads();
-    {  // row norms of q and k
-      const int row = tid >> 2, qq = tid & 3;
-      float sq = 0.0f, sk = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) {
-        const float x = M::dec(sm.Qs[row * LDQ + 32 * qq + e]);
-        const float y = M::dec(sm.Ks[row * LDQ + 32 * qq + e]);
-        sq += x * x;
-        sk += y * y;
-      }
-      sq += xor_lane<1>(sq);
-      sq += xor_lane<2>(sq);
-      sk += xor_lane<1>(sk);
-      sk += xor_lane<2>(sk);
-      if (qq == 0) {
-        sm.nq[row] = a.l2norm ? 1.0f / sqrtf(sq + a.l2_eps) : 1.0f;
-        sm.nk[row] = a.l2norm ? 1.0f / sqrtf(sk + a.l2_eps) : 1.0f;
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 1: P (row block w), X = K S^T and Q S^T (rows 16w.., both column tiles) ----
-    const int rb = 16 * w;
-    {
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (tj <= w) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            acc = M::mma(frag<TIN>(sm.Qs, LDQ, rb, 32 * kk, lane),
-                         frag<TIN>(sm.Ks, LDQ, 16 * tj, 32 * kk, lane), acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = rb + 4 * (lane >> 4) + r;
-          const int j = 16 * tj + (lane & 15);
-          float p = 0.0f;
-          if (j <= i)
-            p = acc[r] * a.scale * sm.nq[i] * sm.nk[j] * expf((float)(sm.Gd[i] - sm.Gd[j]));
-          sm.Ph[i * LDT + j] = M::enc(p);
-        }
-      }
-    }
-    f32x4 accq[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4 accx = {0.f, 0.f, 0.f, 0.f};
-      accq[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // One chunk with its inputs in `R`; the next chunk's Q, K, V and factors
+  // are requested into `N` first.  The loop below alternates the two register sets so that
+  // no loaded register is copied across iterations (a copy would wait for the
+  // whole prefetch).
+  auto step = [&](ChunkRegs& R, ChunkRegs& N, int ch) {
+    const int cb = ch & 1;
+    const int64_t tb = c.t_begin + (int64_t)ch * CK;
+    const int L = chunk_len(c, ch);
+    fetch_t(R, c, ch);
+    fetch_p(R, c, ch);
+    fetch_ahead(N, min(ch + 1, nch - 1));  // the last step re-fetches its own chunk
+    // rows of this wave past the end of the sequence: zero operands
+    if (rb + (lane & 15) >= L) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const x8 shi = frag<TIN>(sm.Sh, LDQ, 16 * nt, 32 * kk, lane);
-        const x8 slo = frag<TIN>(sm.Sl, LDQ, 16 * nt, 32 * kk, lane);
-        const x8 kf = frag<TIN>(sm.Ks, LDQ, rb, 32 * kk, lane);
-        const x8 qf = frag<TIN>(sm.Qs, LDQ, rb, 32 * kk, lane);
-        accx = M::mma(kf, shi, accx);
-        accx = M::mma(kf, slo, accx);
-        accq[nt] = M::mma(qf, shi, accq[nt]);
-        accq[nt] = M::mma(qf, slo, accq[nt]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = rb + 4 * (lane >> 4) + r;
-        const int dvl = 16 * nt + (lane & 15);
-        const float z = M::dec(sm.Vs[i * BVT + dvl]) -
-                        expf((float)sm.Gd[i]) * sm.nk[i] * accx[r];
-        const uint16_t zh = M::enc(z);
-        sm.Zh[dvl * LDT + i] = zh;
-        sm.Zl[dvl * LDT + i] = M::enc(z - M::dec(zh));
+        R.q[kk] = make_uint4(0, 0, 0, 0);
+        R.k[kk] = make_uint4(0, 0, 0, 0);
       }
     }
-    __syncthreads();
 
-    // ---- phase 2: U = T_b Z (row block w) ----
-    const int nkt = (rb + 15) / 32 + 1;  // k-steps over tokens j <= i
-    const float gl = (float)sm.Gd[L - 1];
+    // ---- X = K S^T and QS = Q S^T of the row block; K^T to LDS; Z ----
+    f32x4 accx = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4 accu = {0.f, 0.f, 0.f, 0.f};
-      for (int kt = 0; kt < nkt; ++kt) {
-        x8 th, tl;
-        frag_split<TIN>(sm.Ts, LDF, rb, 32 * kt, lane, th, tl);
-        const x8 zh = frag<TIN>(sm.Zh, LDT, 16 * nt, 32 * kt, lane);
-        const x8 zl = frag<TIN>(sm.Zl, LDT, 16 * nt, 32 * kt, lane);
-        accu = M::mma(th, zh, accu);
-        accu = M::mma(th, zl, accu);
-        accu = M::mma(tl, zh, accu);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = rb + 4 * (lane >> 4) + r;
-        const int dvl = 16 * nt + (lane & 15);
-        const float u = accu[r];
-        const uint16_t uh = M::enc(u);
-        sm.Uh[dvl * LDT + i] = uh;
-        sm.Ul[dvl * LDT + i] = M::enc(u - M::dec(uh));
-        const float up = u * expf(gl - (float)sm.Gd[i]) * sm.nk[i];
-        const uint16_t wh = M::enc(up);
-        sm.Wh[dvl * LDT + i] = wh;
-        sm.Wl[dvl * LDT + i] = M::enc(up - M::dec(wh));
-      }
+    for (int kk = 0; kk < 4; ++kk) {
+      const x8 shi = frag<TIN>(sm.Sh[cb], LDQ, 0, 32 * kk, lane);
+      const x8 slo = frag<TIN>(sm.Sl[cb], LDQ, 0, 32 * kk, lane);
+      const x8 kf = __builtin_bit_cast(x8, R.k[kk]);
+      const x8 qf = __builtin_bit_cast(x8, R.q[kk]);
+      accx = M::mma(kf, shi, accx);
+      accq = M::mma(qf, shi, accq);
+      accx = M::mma(kf, slo, accx);
+      accq = M::mma(qf, slo, accq);
     }
-    __syncthreads();
-
-    // ---- phase 3: outputs of row block w; state update of the wave's S tiles ----
+    {
+      const int tok = rb + (lane & 15);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4 acco = {0.f, 0.f, 0.f, 0.f};
-      for (int kt = 0; kt < nkt; ++kt) {
-        const x8 pf = frag<TIN>(sm.Ph, LDT, rb, 32 * kt, lane);
-        acco = M::mma(pf, frag<TIN>(sm.Uh, LDT, 16 * nt, 32 * kt, lane), acco);
-        acco = M::mma(pf, frag<TIN>(sm.Ul, LDT, 16 * nt, 32 * kt, lane), acco);
-      }
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t kw[4] = {R.k[kk].x, R.k[kk].y, R.k[kk].z, R.k[kk].w};
+        const int d0 = 32 * kk + 8 * (lane >> 4);
+        const int col = kt_col(d0, tok);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = rb + 4 * (lane >> 4) + r;
-        const int dvl = 16 * nt + (lane & 15);
-        if (i < L) {
-          const float o = expf((float)sm.Gd[i]) * a.scale * sm.nq[i] * accq[nt][r] + acco[r];
-          store1(a.out, a.out_dt, (tb + i) * out_rs + (int64_t)h * a.dv + dv0 + dvl, o);
+        for (int e = 0; e < 4; ++e) {
+          sm.Kt[(d0 + 2 * e) * LDT + col] = (uint16_t)(kw[e] & 0xffffu);
+          sm.Kt[(d0 + 2 * e + 1) * LDT + col] = (uint16_t)(kw[e] >> 16);
         }
       }
     }
-    const float gc = expf(gl);
+    {
+      uint16_t zh[4], zl[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int mt = q >> 1, nt = 2 * w + (q & 1);
-      f32x4 acc = accs[q];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= gc;
+      for (int r = 0; r < 4; ++r) {
+        const int i = rb + 4 * (lane >> 4) + r;
+        const float vv = i < L ? M::dec(R.v[r]) : 0.0f;
+        const float z = vv - f4(R.fz, r) * accx[r];
+        zh[r] = M::enc(z);
+        zl[r] = M::enc(z - M::dec(zh[r]));
+      }
+      const int off = (lane & 15) * LDT + rb + 4 * (lane >> 4);
+      store4(sm.Zh + off, zh);
+      store4(sm.Zl + off, zl);
+    }
+    lds_barrier();
+
+    // ---- U = T_b Z (row block); U^T and (diag(fw) U)^T to LDS ----
+    {
+      f32x4 accu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const x8 kf = frag<TIN>(sm.Kt, LDT, 16 * nt, 32 * kt, lane);
-        acc = M::mma(frag<TIN>(sm.Wh, LDT, 16 * mt, 32 * kt, lane), kf, acc);
-        acc = M::mma(frag<TIN>(sm.Wl, LDT, 16 * mt, 32 * kt, lane), kf, acc);
+        if (kt < nkt) {
+          const x8 th = __builtin_bit_cast(x8, R.th[kt]);
+          const x8 tl = __builtin_bit_cast(x8, R.tl[kt]);
+          const x8 zh = frag<TIN>(sm.Zh, LDT, 0, 32 * kt, lane);
+          const x8 zl = frag<TIN>(sm.Zl, LDT, 0, 32 * kt, lane);
+          accu = M::mma(th, zh, accu);
+          accu = M::mma(th, zl, accu);
+          accu = M::mma(tl, zh, accu);
+        }
+      }
+      uint16_t uh[4], ul[4], wh[4], wl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float u = accu[r];
+        uh[r] = M::enc(u);
+        ul[r] = M::enc(u - M::dec(uh[r]));
+        const float up = u * f4(R.fw, r);
+        wh[r] = M::enc(up);
+        wl[r] = M::enc(up - M::dec(wh[r]));
+      }
+      const int off = (lane & 15) * LDT + rb + 4 * (lane >> 4);
+      store4(sm.Uh + off, uh);
+      store4(sm.Ul + off, ul);
+      store4(sm.Wh + off, wh);
+      store4(sm.Wl + off, wl);
+    }
+    lds_barrier();
+
+    // ---- outputs of the row block; state update; S to the other buffer ----
+    {
+      f32x4 acco = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        if (kt < nkt) {
+          const x8 pf = __builtin_bit_cast(x8, R.p[kt]);
+          acco = M::mma(pf, frag<TIN>(sm.Uh, LDT, 0, 32 * kt, lane), acco);
+          acco = M::mma(pf, frag<TIN>(sm.Ul, LDT, 0, 32 * kt, lane), acco);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rb + 4 * (lane >> 4) + r;
+        const float o = f4(R.fo, r) * accq[r] + acco[r];
+        Ot* dst = i < L ? out + (tb + i) * out_rs + (lane & 15)
+                        : reinterpret_cast<Ot*>(dump_tile) + i * BVT + (lane & 15);
+        *dst = OutT<TOUT>::cvt(o);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int nt = 2 * w + q;
+      const int dk = 16 * nt + (lane & 15);
+      f32x4 acc = accs[q];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] *= R.gc;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const x8 kf = *reinterpret_cast<const x8*>(
+            sm.Kt + dk * LDT + kt_col(dk, 32 * kt + 8 * (lane >> 4)));
+        acc = M::mma(frag<TIN>(sm.Wh, LDT, 0, 32 * kt, lane), kf, acc);
+        acc = M::mma(frag<TIN>(sm.Wl, LDT, 0, 32 * kt, lane), kf, acc);
       }
       accs[q] = acc;
     }
-    __syncthreads();
-    write_s_lds();
+    write_s_lds(cb ^ 1);
+    lds_barrier();
+  };
+
+  write_s_lds(0);
+  ChunkRegs RA, RB;
+  if (nch > 0) fetch_ahead(RA, 0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ch += 2) {
+    step(RA, RB, ch);
+    if (ch + 1 < nch) step(RB, RA, ch + 1);
   }
 
   // final state
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int mt = q >> 1, nt = 2 * w + (q & 1);
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * w + q;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * mt + 4 * (lane >> 4) + r, col = 16 * nt + (lane & 15);
-      Sg[row * DKC + col] = accs[q][r];
-    }
+    for (int r = 0; r < 4; ++r)
+      Sg[(4 * (lane >> 4) + r) * DKC + 16 * nt + (lane & 15)] = accs[q][r];
   }
 }
 
@@ -592,20 +778,34 @@ int64_t max_chunks(int64_t total_tokens, int64_t num_seqs) {
   return (total_tokens + CK - 1) / CK + num_seqs;
 }
 
-size_t meta_bytes(int64_t num_seqs) { return (size_t)((num_seqs + 1) * 4 + 255) / 256 * 256; }
+size_t meta_bytes(int64_t num_seqs) { return (size_t)((2 * num_seqs + 1) * 4 + 255) / 256 * 256; }
+
+size_t dump_bytes(int64_t num_seqs, int hv, int dv) {
+  return (size_t)num_seqs * hv * (dv / BVT) * CK * BVT * sizeof(float);
+}
 
 template <int TIN>
 hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) {
   int32_t* cs = static_cast<int32_t*>(ws);
-  float* tws = reinterpret_cast<float*>(static_cast<char*>(ws) + meta_bytes(a.num_seqs));
+  int32_t* order = cs + a.num_seqs + 1;
+  char* recs = static_cast<char*>(ws) + meta_bytes(a.num_seqs);
   const int64_t mc = max_chunks(a.total_tokens, a.num_seqs);
-  hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, cs);
-  hipLaunchKernelGGL((chunk_t_kernel<TIN>), dim3((unsigned)mc, (unsigned)a.hv), dim3(256), 0,
-                     stream, a, (const int32_t*)cs, tws);
+  float* dump = reinterpret_cast<float*>(recs + (size_t)mc * a.hv * REC_BYTES);
+  hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, cs, order);
+  hipLaunchKernelGGL((chunk_prep_kernel<TIN>), dim3((unsigned)mc, (unsigned)a.hv), dim3(256), 0,
+                     stream, a, (const int32_t*)cs, recs);
   const int ntiles = a.dv / BVT;
-  const int64_t blocks = a.num_seqs * a.hv * ntiles;
-  hipLaunchKernelGGL((chunk_state_kernel<TIN>), dim3((unsigned)blocks), dim3(256), 0, stream, a,
-                     (const int32_t*)cs, (const float*)tws, ntiles, (int)mc);
+  const int64_t units = a.num_seqs * a.hk;
+  const int64_t blocks = (units + kXcds - 1) / kXcds * kXcds * (a.hv / a.hk) * ntiles;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (a.out_dt == kF32)
+    hipLaunchKernelGGL((chunk_state_kernel<TIN, kF32>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a, (const int32_t*)cs, (const int32_t*)order, (const char*)recs,
+                       ntiles, (int)mc, dump);
+  else
+    hipLaunchKernelGGL((chunk_state_kernel<TIN, TIN>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, a, (const int32_t*)cs, (const int32_t*)order, (const char*)recs,
+                       ntiles, (int)mc, dump);
   return hipGetLastError();
 }
 
@@ -624,8 +824,8 @@ bool chunked_layout_ok(const void* q, const void* k, const void* v, int64_t q_rs
 
 size_t chunked_workspace_bytes(int64_t total_tokens, int64_t num_seqs, int hv, int dk, int dv) {
   (void)dk; (void)dv;
-  return meta_bytes(num_seqs) +
-         (size_t)max_chunks(total_tokens, num_seqs) * (size_t)hv * CK * CK * sizeof(float);
+  return meta_bytes(num_seqs) + (size_t)max_chunks(total_tokens, num_seqs) * (size_t)hv * REC_BYTES +
+         dump_bytes(num_seqs, hv, dv);
 }
 
 hipError_t launch_prefill_chunked(const PrefillArgs& a, void* ws, size_t ws_bytes,
