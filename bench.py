@@ -264,7 +264,7 @@ def main():
             "achieved_GBs": round(pbytes / (pavg * 1e-3) / 1e9, 1),
             "hbm_frac": round(pbytes / (pavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "chunked_flops_per_step": pflops,
-            "mfma_frac_if_chunked": round(pflops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_algorithmic": round(pflops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "path": "chunked" if ws_n > 0 else "token-sequential",
         }
         log(f"prefill: {p_ms_step:.3f} ms/step -> {T / (p_ms_step * 1e-3) / 1e6:.2f} M tokens/s")
