@@ -77,7 +77,8 @@ def measured_traffic():
             if ":" in line and line.split(":", 1)[0].strip() in (
                     "source_sha256", "traffic_bytes_per_launch"):
                 k, v = line.split(":", 1)
-                fields[k.strip()] = v.strip().strip("`")
+                v = v.split()
+                fields[k.strip()] = v[0].strip("`") if v else ""
     if fields.get("source_sha256") != decode_source_hash():
         return None
     try:
