@@ -44,7 +44,11 @@ namespace {
 
 constexpr int CK = 64;        // tokens per chunk
 constexpr int DKC = 128;      // key head size served here
-constexpr int BVT = 16;       // state rows per workgroup in the state walk
+#ifndef GDN_WALK_NT
+#define GDN_WALK_NT 2
+#endif
+constexpr int WALK_NT = GDN_WALK_NT;   // 16-row state tiles per workgroup in the state walk
+constexpr int BVT = 16 * WALK_NT;     // state rows per workgroup
 constexpr int LDQ = DKC + 8;  // padded LDS row (16-bit elements), token-major 128-wide tiles
 constexpr int LDT = CK + 8;   // padded LDS row (16-bit elements), 64-wide tiles
 constexpr int LDF = CK + 4;   // padded LDS row (f32), 64 x 64 matrices
@@ -406,21 +410,24 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, const in
 // an 8-token operand read stays one contiguous 16-byte access.
 __device__ __forceinline__ int kt_col(int dk, int token) { return token ^ (((dk >> 3) & 3) << 3); }
 
+template <int NT>
 struct WalkLds {
-  uint16_t Kt[DKC * LDT];                         // K^T of the chunk
-  uint16_t Sh[2][BVT * LDQ], Sl[2][BVT * LDQ];    // S tile [dv][dk], double-buffered
-  uint16_t Zh[BVT * LDT], Zl[BVT * LDT];          // Z^T  [dv][token]
-  uint16_t Uh[BVT * LDT], Ul[BVT * LDT];          // U^T
-  uint16_t Wh[BVT * LDT], Wl[BVT * LDT];          // (diag(fw) U)^T
+  static constexpr int BV = 16 * NT;            // state rows of the workgroup
+  uint16_t Kt[DKC * LDT];                       // K^T of the chunk
+  uint16_t Sh[2][BV * LDQ], Sl[2][BV * LDQ];    // S tile [dv][dk], double-buffered
+  uint16_t Zh[BV * LDT], Zl[BV * LDT];          // Z^T  [dv][token]
+  uint16_t Uh[BV * LDT], Ul[BV * LDT];          // U^T
+  uint16_t Wh[BV * LDT], Wl[BV * LDT];          // (diag(fw) U)^T
 };
 
 // The chunk inputs a wave needs for its 16-row block: rows rb + lane % 16 for
 // the A operands, rows rb + 4 (lane/16) + r for the elementwise work.
+template <int NT>
 struct ChunkRegs {
   uint4 q[4], k[4];    // Q, K rows, columns 32 kk + 8 (lane/16) .. +8
   uint4 th[2], tl[2];  // T_b rows, columns 32 kt + 8 (lane/16) .. +8
   uint4 p[2];          // P rows
-  uint32_t v[4];       // V[rb + 4 (lane/16) + r][dv0 + lane % 16]
+  uint32_t v[NT][4];   // V[rb + 4 (lane/16) + r][dv0 + 16 nt + lane % 16]
   float4 fz, fo, fw;   // factors of rows rb + 4 (lane/16) .. +3
   float gc;
 };
@@ -440,7 +447,8 @@ __device__ __forceinline__ const char* chunk_rec(const WalkCtx& c, int ch) {
   return c.recs + ((int64_t)(c.c0 + ch) * c.a->hv + c.h) * REC_BYTES;
 }
 
-__device__ __forceinline__ void fetch_qk(ChunkRegs& R, const WalkCtx& c, int ch) {
+template <int NT>
+__device__ __forceinline__ void fetch_qk(ChunkRegs<NT>& R, const WalkCtx& c, int ch) {
   const PrefillArgs& a = *c.a;
   const int64_t tb = c.t_begin + (int64_t)ch * CK;
   const int arow = min(c.rb + (c.lane & 15), chunk_len(c, ch) - 1);  // zeroed at use if >= L
@@ -459,10 +467,11 @@ __device__ __forceinline__ int rec_toff(const WalkCtx& c, int kt) {
   return 2 * ((c.rb + (c.lane & 15)) * CK + 8 * (c.lane >> 4) + 32 * kt);
 }
 
-__device__ __forceinline__ void fetch_t(ChunkRegs& R, const WalkCtx& c, int ch) {
+// both k-steps are always loaded (for the first 32 rows the second one is the
+// zero upper block), so every path issues the same memory operations
+template <int NT>
+__device__ __forceinline__ void fetch_t(ChunkRegs<NT>& R, const WalkCtx& c, int ch) {
   const char* rec = chunk_rec(c, ch);
-  // both k-steps are always loaded (for the first 32 rows the second one is
-  // the zero upper block), so every path issues the same memory operations
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     R.th[kt] = *reinterpret_cast<const uint4*>(rec + REC_TH + rec_toff(c, kt));
@@ -470,14 +479,16 @@ __device__ __forceinline__ void fetch_t(ChunkRegs& R, const WalkCtx& c, int ch) 
   }
 }
 
-__device__ __forceinline__ void fetch_p(ChunkRegs& R, const WalkCtx& c, int ch) {
+template <int NT>
+__device__ __forceinline__ void fetch_p(ChunkRegs<NT>& R, const WalkCtx& c, int ch) {
   const char* rec = chunk_rec(c, ch);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
     R.p[kt] = *reinterpret_cast<const uint4*>(rec + REC_P + rec_toff(c, kt));
 }
 
-__device__ __forceinline__ void fetch_vf(ChunkRegs& R, const WalkCtx& c, int ch) {
+template <int NT>
+__device__ __forceinline__ void fetch_vf(ChunkRegs<NT>& R, const WalkCtx& c, int ch) {
   const PrefillArgs& a = *c.a;
   const int64_t tb = c.t_begin + (int64_t)ch * CK;
   const int L = chunk_len(c, ch);
@@ -486,7 +497,8 @@ __device__ __forceinline__ void fetch_vf(ChunkRegs& R, const WalkCtx& c, int ch)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int vrow = min(c.rb + 4 * (c.lane >> 4) + r, L - 1);
-    R.v[r] = vp[(tb + vrow) * a.v_rs];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) R.v[nt][r] = vp[(tb + vrow) * a.v_rs + 16 * nt];
   }
   const float* F = reinterpret_cast<const float*>(chunk_rec(c, ch) + REC_F);
   const int frow = c.rb + 4 * (c.lane >> 4);
@@ -521,17 +533,21 @@ struct OutT<kF32> {
   static __device__ __forceinline__ float cvt(float x) { return x; }
 };
 
-// `dump` holds one 64 x 16 tile per workgroup: outputs of rows past the end of
-// a sequence are written there instead of being skipped, so every chunk step
-// issues the same number of stores and the compiler's memory-counter waits
-// for the prefetched next chunk stay exact (a data-dependent store count
-// makes it wait for all outstanding loads).
-template <int TIN, int TOUT>
+// One workgroup walks one (sequence, v-head, 16 NT-row tile of S); wave w
+// owns rows [16w, 16w + 16) of the chunk for X, Z, U and O, and the S tiles
+// (mt, 2w + q) for mt < NT, q < 2.
+// `dump` holds one 64 x 16 NT tile per workgroup: outputs of rows past the end
+// of a sequence are written there instead of being skipped, so every chunk
+// step issues the same number of stores and the compiler's memory-counter
+// waits for the prefetched next chunk stay exact (a data-dependent store
+// count makes it wait for all outstanding loads).
+template <int TIN, int TOUT, int NT>
 __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, const int32_t* cs,
                                                              const int32_t* order,
                                                              const char* recs, int ntiles,
                                                              int max_chunks, float* dump) {
-  __shared__ __align__(16) WalkLds sm;
+  constexpr int BV = 16 * NT;
+  __shared__ __align__(16) WalkLds<NT> sm;
   using M = MT<TIN>;
   using x8 = typename M::x8;
 
@@ -561,8 +577,8 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
   chunk_bounds(a, s, c.t_begin, c.t_end);
   c.c0 = cs[s];
   c.h = h;
-  c.hk = h / (a.hv / a.hk);
-  c.dv0 = tile * BVT;
+  c.hk = h / ratio;
+  c.dv0 = tile * BV;
   c.rb = 16 * w;
   c.nkt = (c.rb + 15) / 32 + 1;  // k-steps over tokens j <= i
   c.lane = lane;
@@ -575,8 +591,8 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
 
   if (slot < 0 || slot >= a.num_slots) {
     // caller error: NaN outputs for this tile, no state access
-    for (int64_t t = c.t_begin + (tid >> 4); t < c.t_end; t += 16)
-      store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + c.dv0 + (tid & 15),
+    for (int64_t t = c.t_begin + tid / BV; t < c.t_end; t += 256 / BV)
+      store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + c.dv0 + tid % BV,
              __builtin_nanf(""));
     return;
   }
@@ -586,25 +602,26 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
   const int nkt = c.nkt;
   using Ot = typename OutT<TOUT>::type;
   Ot* out = static_cast<Ot*>(a.out) + (int64_t)h * a.dv + c.dv0;
-  float* dump_tile = dump + ((int64_t)sh * ntiles + tile) * (CK * BVT);
+  Ot* dump_tile = reinterpret_cast<Ot*>(dump + ((int64_t)sh * ntiles + tile) * (CK * BV));
 
-  // S tile (16 x 128) in MFMA accumulators: wave w holds column tiles
-  // nt = 2w + q; element r is S[4 (lane/16) + r][16 nt + lane % 16].
-  f32x4 accs[2];
+  // S tile (BV x 128) in MFMA accumulators: wave w holds tiles q = 2 mt + e
+  // at (row block mt, column block 2w + e); element r of tile q is
+  // S[16 mt + 4 (lane/16) + r][16 (2w + e) + lane % 16].
+  f32x4 accs[2 * NT];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int nt = 2 * w + q;
+  for (int q = 0; q < 2 * NT; ++q) {
+    const int mt = q >> 1, nt = 2 * w + (q & 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      accs[q][r] = init ? Sg[(4 * (lane >> 4) + r) * DKC + 16 * nt + (lane & 15)] : 0.0f;
+      accs[q][r] = init ? Sg[(16 * mt + 4 * (lane >> 4) + r) * DKC + 16 * nt + (lane & 15)] : 0.0f;
   }
   auto write_s_lds = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int nt = 2 * w + q;
+    for (int q = 0; q < 2 * NT; ++q) {
+      const int mt = q >> 1, nt = 2 * w + (q & 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int off = (4 * (lane >> 4) + r) * LDQ + 16 * nt + (lane & 15);
+        const int off = (16 * mt + 4 * (lane >> 4) + r) * LDQ + 16 * nt + (lane & 15);
         const uint16_t hb = M::enc(accs[q][r]);
         sm.Sh[buf][off] = hb;
         sm.Sl[buf][off] = M::enc(accs[q][r] - M::dec(hb));
@@ -612,18 +629,17 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
     }
   };
   // Q, K, V and the factors are fetched one chunk ahead; T_b and P (needed
-  // only from the second phase on) at the start of their own chunk, which
-  // keeps the two register sets small enough to avoid register reuse stalls.
-  auto fetch_ahead = [&](ChunkRegs& R, int ch) {
+  // only from the second phase on) at the start of their own chunk.
+  auto fetch_ahead = [&](ChunkRegs<NT>& R, int ch) {
     fetch_qk(R, c, ch);
     fetch_vf(R, c, ch);
   };
 
   // One chunk with its inputs in `R`; the next chunk's Q, K, V and factors
-  // are requested into `N` first.  The loop below alternates the two register sets so that
-  // no loaded register is copied across iterations (a copy would wait for the
-  // whole prefetch).
-  auto step = [&](ChunkRegs& R, ChunkRegs& N, int ch) {
+  // are requested into `N` first.  The loop below alternates the two register
+  // sets so that no loaded register is copied across iterations (a copy would
+  // wait for the whole prefetch).
+  auto step = [&](ChunkRegs<NT>& R, ChunkRegs<NT>& N, int ch) {
     const int cb = ch & 1;
     const int64_t tb = c.t_begin + (int64_t)ch * CK;
     const int L = chunk_len(c, ch);
@@ -640,17 +656,34 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
     }
 
     // ---- X = K S^T and QS = Q S^T of the row block; K^T to LDS; Z ----
-    f32x4 accx = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
+    f32x4 accq[NT];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const x8 shi = frag<TIN>(sm.Sh[cb], LDQ, 0, 32 * kk, lane);
-      const x8 slo = frag<TIN>(sm.Sl[cb], LDQ, 0, 32 * kk, lane);
-      const x8 kf = __builtin_bit_cast(x8, R.k[kk]);
-      const x8 qf = __builtin_bit_cast(x8, R.q[kk]);
-      accx = M::mma(kf, shi, accx);
-      accq = M::mma(qf, shi, accq);
-      accx = M::mma(kf, slo, accx);
-      accq = M::mma(qf, slo, accq);
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 accx = {0.f, 0.f, 0.f, 0.f};
+      accq[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const x8 shi = frag<TIN>(sm.Sh[cb], LDQ, 16 * nt, 32 * kk, lane);
+        const x8 slo = frag<TIN>(sm.Sl[cb], LDQ, 16 * nt, 32 * kk, lane);
+        const x8 kf = __builtin_bit_cast(x8, R.k[kk]);
+        const x8 qf = __builtin_bit_cast(x8, R.q[kk]);
+        accx = M::mma(kf, shi, accx);
+        accq[nt] = M::mma(qf, shi, accq[nt]);
+        accx = M::mma(kf, slo, accx);
+        accq[nt] = M::mma(qf, slo, accq[nt]);
+      }
+      uint16_t zh[4], zl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rb + 4 * (lane >> 4) + r;
+        const float vv = i < L ? M::dec(R.v[nt][r]) : 0.0f;
+        const float z = vv - f4(R.fz, r) * accx[r];
+        zh[r] = M::enc(z);
+        zl[r] = M::enc(z - M::dec(zh[r]));
+      }
+      const int off = (16 * nt + (lane & 15)) * LDT + rb + 4 * (lane >> 4);
+      store4(sm.Zh + off, zh);
+      store4(sm.Zl + off, zl);
     }
     {
       const int tok = rb + (lane & 15);
@@ -666,32 +699,19 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
         }
       }
     }
-    {
-      uint16_t zh[4], zl[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = rb + 4 * (lane >> 4) + r;
-        const float vv = i < L ? M::dec(R.v[r]) : 0.0f;
-        const float z = vv - f4(R.fz, r) * accx[r];
-        zh[r] = M::enc(z);
-        zl[r] = M::enc(z - M::dec(zh[r]));
-      }
-      const int off = (lane & 15) * LDT + rb + 4 * (lane >> 4);
-      store4(sm.Zh + off, zh);
-      store4(sm.Zl + off, zl);
-    }
     lds_barrier();
 
     // ---- U = T_b Z (row block); U^T and (diag(fw) U)^T to LDS ----
-    {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       f32x4 accu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         if (kt < nkt) {
           const x8 th = __builtin_bit_cast(x8, R.th[kt]);
           const x8 tl = __builtin_bit_cast(x8, R.tl[kt]);
-          const x8 zh = frag<TIN>(sm.Zh, LDT, 0, 32 * kt, lane);
-          const x8 zl = frag<TIN>(sm.Zl, LDT, 0, 32 * kt, lane);
+          const x8 zh = frag<TIN>(sm.Zh, LDT, 16 * nt, 32 * kt, lane);
+          const x8 zl = frag<TIN>(sm.Zl, LDT, 16 * nt, 32 * kt, lane);
           accu = M::mma(th, zh, accu);
           accu = M::mma(th, zl, accu);
           accu = M::mma(tl, zh, accu);
@@ -707,7 +727,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
         wh[r] = M::enc(up);
         wl[r] = M::enc(up - M::dec(wh[r]));
       }
-      const int off = (lane & 15) * LDT + rb + 4 * (lane >> 4);
+      const int off = (16 * nt + (lane & 15)) * LDT + rb + 4 * (lane >> 4);
       store4(sm.Uh + off, uh);
       store4(sm.Ul + off, ul);
       store4(sm.Wh + off, wh);
@@ -716,28 +736,29 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
     lds_barrier();
 
     // ---- outputs of the row block; state update; S to the other buffer ----
-    {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       f32x4 acco = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         if (kt < nkt) {
           const x8 pf = __builtin_bit_cast(x8, R.p[kt]);
-          acco = M::mma(pf, frag<TIN>(sm.Uh, LDT, 0, 32 * kt, lane), acco);
-          acco = M::mma(pf, frag<TIN>(sm.Ul, LDT, 0, 32 * kt, lane), acco);
+          acco = M::mma(pf, frag<TIN>(sm.Uh, LDT, 16 * nt, 32 * kt, lane), acco);
+          acco = M::mma(pf, frag<TIN>(sm.Ul, LDT, 16 * nt, 32 * kt, lane), acco);
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = rb + 4 * (lane >> 4) + r;
-        const float o = f4(R.fo, r) * accq[r] + acco[r];
-        Ot* dst = i < L ? out + (tb + i) * out_rs + (lane & 15)
-                        : reinterpret_cast<Ot*>(dump_tile) + i * BVT + (lane & 15);
+        const float o = f4(R.fo, r) * accq[nt][r] + acco[r];
+        Ot* dst = i < L ? out + (tb + i) * out_rs + 16 * nt + (lane & 15)
+                        : dump_tile + i * BV + 16 * nt + (lane & 15);
         *dst = OutT<TOUT>::cvt(o);
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int nt = 2 * w + q;
+    for (int q = 0; q < 2 * NT; ++q) {
+      const int mt = q >> 1, nt = 2 * w + (q & 1);
       const int dk = 16 * nt + (lane & 15);
       f32x4 acc = accs[q];
 #pragma unroll
@@ -746,8 +767,8 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
       for (int kt = 0; kt < 2; ++kt) {
         const x8 kf = *reinterpret_cast<const x8*>(
             sm.Kt + dk * LDT + kt_col(dk, 32 * kt + 8 * (lane >> 4)));
-        acc = M::mma(frag<TIN>(sm.Wh, LDT, 0, 32 * kt, lane), kf, acc);
-        acc = M::mma(frag<TIN>(sm.Wl, LDT, 0, 32 * kt, lane), kf, acc);
+        acc = M::mma(frag<TIN>(sm.Wh, LDT, 16 * mt, 32 * kt, lane), kf, acc);
+        acc = M::mma(frag<TIN>(sm.Wl, LDT, 16 * mt, 32 * kt, lane), kf, acc);
       }
       accs[q] = acc;
     }
@@ -756,7 +777,7 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
   };
 
   write_s_lds(0);
-  ChunkRegs RA, RB;
+  ChunkRegs<NT> RA, RB;
   if (nch > 0) fetch_ahead(RA, 0);
   __syncthreads();
   for (int ch = 0; ch < nch; ch += 2) {
@@ -766,11 +787,11 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
 
   // final state
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int nt = 2 * w + q;
+  for (int q = 0; q < 2 * NT; ++q) {
+    const int mt = q >> 1, nt = 2 * w + (q & 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      Sg[(4 * (lane >> 4) + r) * DKC + 16 * nt + (lane & 15)] = accs[q][r];
+      Sg[(16 * mt + 4 * (lane >> 4) + r) * DKC + 16 * nt + (lane & 15)] = accs[q][r];
   }
 }
 
@@ -799,11 +820,11 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   const int64_t blocks = (units + kXcds - 1) / kXcds * kXcds * (a.hv / a.hk) * ntiles;
   if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (a.out_dt == kF32)
-    hipLaunchKernelGGL((chunk_state_kernel<TIN, kF32>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((chunk_state_kernel<TIN, kF32, WALK_NT>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a, (const int32_t*)cs, (const int32_t*)order, (const char*)recs,
                        ntiles, (int)mc, dump);
   else
-    hipLaunchKernelGGL((chunk_state_kernel<TIN, TIN>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((chunk_state_kernel<TIN, TIN, WALK_NT>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a, (const int32_t*)cs, (const int32_t*)order, (const char*)recs,
                        ntiles, (int)mc, dump);
   return hipGetLastError();
