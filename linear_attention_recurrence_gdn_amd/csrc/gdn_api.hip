@@ -139,8 +139,8 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
 
 static bool use_chunked(int64_t hk, int64_t hv, int64_t dk, int64_t dv, int in_dt, int out_dt,
                         uint32_t flags) {
-  (void)hk; (void)hv;
-  return !(flags & GDN_PREFILL_SEQUENTIAL) && gdn::chunked_supported(in_dt, out_dt, (int)dk, (int)dv);
+  (void)hk;
+  return !(flags & GDN_PREFILL_SEQUENTIAL) && gdn::chunked_supported(in_dt, out_dt, hv, (int)dk, (int)dv);
 }
 
 size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs, int64_t hk,

@@ -44,13 +44,16 @@ namespace {
 
 constexpr int CK = 64;        // tokens per chunk
 constexpr int DKC = 128;      // key head size served here
-#ifndef GDN_WALK_NT
-#define GDN_WALK_NT 2
+#ifndef GDN_WALK_NW
+#define GDN_WALK_NW 4
 #endif
-constexpr int WALK_NT = GDN_WALK_NT;   // 16-row state tiles per workgroup in the state walk
-constexpr int BVT = 16 * WALK_NT;     // state rows per workgroup
+#ifndef GDN_WALK_MINB
+#define GDN_WALK_MINB 1
+#endif
+constexpr int WALK_NW = GDN_WALK_NW;      // waves per state-walk workgroup (16 state rows each)
+constexpr int WALK_MINB = GDN_WALK_MINB;  // state-walk workgroups per CU the registers allow
+constexpr int WALK_BV = 16 * WALK_NW;     // state rows per workgroup
 constexpr int LDQ = DKC + 8;  // padded LDS row (16-bit elements), token-major 128-wide tiles
-constexpr int LDT = CK + 8;   // padded LDS row (16-bit elements), 64-wide tiles
 constexpr int LDF = CK + 4;   // padded LDS row (f32), 64 x 64 matrices
 constexpr int kXcds = 8;      // accelerator complex dies (separate L2s) on MI355X
 
@@ -405,38 +408,59 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, const in
 // ---------------------------------------------------------------------------
 // the state walk
 // ---------------------------------------------------------------------------
-// K^T is stored [dk][token] with the 8-token groups XOR-swizzled by dk, so the
-// transposed 2-byte writes of the four lane groups land in different banks and
-// an 8-token operand read stays one contiguous 16-byte access.
-__device__ __forceinline__ int kt_col(int dk, int token) { return token ^ (((dk >> 3) & 3) << 3); }
+// One workgroup of NW waves walks one (sequence, v-head, block of 16 NW state
+// rows); wave w owns the 16 state rows dv = dv0 + 16 w .. +15 for all 128 keys
+// and keeps them transposed, St = S^T [dk][dv], in eight MFMA accumulator
+// tiles.  Every product of a chunk step takes its state operand straight from
+// those registers and every result's accumulator layout is the B-operand
+// layout of the product that consumes it, so the waves never exchange data:
+// they share only the chunk's inputs, staged once per workgroup in LDS.
+//
+// MFMA 16x16x32 layouts (lane l, g = l / 16, c = l % 16):
+//   A: A[c][8g + e] (e < 8),  B: B[8g + e][c],  D: D[4g + r][c] (r < 4).
+// Two D tiles stacked along k form one B operand when row m of tile 2j + h
+// stands for index 32j + 8 (m / 4) + 4h + m % 4: lane group g then holds the
+// 8 consecutive indices 32j + 8g .. +7, the standard B layout.  The token
+// blocks of a chunk and the key blocks of St are both numbered that way.
+__device__ __forceinline__ int blk_row(int b, int m) {
+  return 32 * (b >> 1) + 8 * (m >> 2) + 4 * (b & 1) + (m & 3);
+}
 
-template <int NT>
-struct WalkLds {
-  static constexpr int BV = 16 * NT;            // state rows of the workgroup
-  uint16_t Kt[DKC * LDT];                       // K^T of the chunk
-  uint16_t Sh[2][BV * LDQ], Sl[2][BV * LDQ];    // S tile [dv][dk], double-buffered
-  uint16_t Zh[BV * LDT], Zl[BV * LDT];          // Z^T  [dv][token]
-  uint16_t Uh[BV * LDT], Ul[BV * LDT];          // U^T
-  uint16_t Wh[BV * LDT], Wl[BV * LDT];          // (diag(fw) U)^T
-};
+// K and Q of the chunk in LDS, [token][key] 16-bit, 16-byte chunks XOR-swizzled
+// by row: the A-operand reads (the 16 rows of one token block, one chunk), the
+// transposing reads (4 rows x 4 chunks) and the row-major staging writes each
+// touch 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kq_off(int row, int ch) {
+  return row * DKC + 8 * (ch ^ (((row & 3) << 2) | ((row >> 3) & 3)));
+}
+// T_b (high, low) and P of the chunk, [token][token] 16-bit, 8 chunks per row
+__device__ __forceinline__ int tp_off(int row, int ch) {
+  return row * CK + 8 * (ch ^ (((row >> 1) & 1) | (((row >> 3) & 3) << 1)));
+}
 
-// The chunk inputs a wave needs for its 16-row block: rows rb + lane % 16 for
-// the A operands, rows rb + 4 (lane/16) + r for the elementwise work.
-template <int NT>
-struct ChunkRegs {
-  uint4 q[4], k[4];    // Q, K rows, columns 32 kk + 8 (lane/16) .. +8
-  uint4 th[2], tl[2];  // T_b rows, columns 32 kt + 8 (lane/16) .. +8
-  uint4 p[2];          // P rows
-  uint32_t v[NT][4];   // V[rb + 4 (lane/16) + r][dv0 + 16 nt + lane % 16]
-  float4 fz, fo, fw;   // factors of rows rb + 4 (lane/16) .. +3
-  float gc;
+constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer resource word 3 on gfx9
+
+// V of the chunk, [token][16 NW columns] 16-bit, 16-byte chunks XOR-swizzled so
+// the four rows 8 apart read by one D-layout access hit distinct banks
+__device__ __forceinline__ int v_swz(int row) { return ((row >> 3) & 3) << 1; }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One chunk's inputs in LDS.  The walk keeps two and fills one with direct
+// global-to-LDS loads while it computes on the other.
+template <int NW>
+struct WalkBuf {
+  uint16_t K[CK * DKC], Q[CK * DKC];
+  uint16_t Th[CK * CK], Tl[CK * CK], P[CK * CK];
+  uint16_t V[CK * 16 * NW];
+  float F[4 * CK];
 };
 
 struct WalkCtx {
   const PrefillArgs* a;
   const char* recs;
   int64_t t_begin, t_end;
-  int c0, h, hk, dv0, rb, nkt, lane;
+  int c0, h, hk, dv0;
 };
 
 __device__ __forceinline__ int chunk_len(const WalkCtx& c, int ch) {
@@ -447,107 +471,122 @@ __device__ __forceinline__ const char* chunk_rec(const WalkCtx& c, int ch) {
   return c.recs + ((int64_t)(c.c0 + ch) * c.a->hv + c.h) * REC_BYTES;
 }
 
-template <int NT>
-__device__ __forceinline__ void fetch_qk(ChunkRegs<NT>& R, const WalkCtx& c, int ch) {
-  const PrefillArgs& a = *c.a;
-  const int64_t tb = c.t_begin + (int64_t)ch * CK;
-  const int arow = min(c.rb + (c.lane & 15), chunk_len(c, ch) - 1);  // zeroed at use if >= L
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (tb + arow) * a.q_rs +
-                       (int64_t)c.hk * DKC + 8 * (c.lane >> 4);
-  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + (tb + arow) * a.k_rs +
-                       (int64_t)c.hk * DKC + 8 * (c.lane >> 4);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    R.q[kk] = *reinterpret_cast<const uint4*>(qp + 32 * kk);
-    R.k[kk] = *reinterpret_cast<const uint4*>(kp + 32 * kk);
-  }
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at dst + 16 l (dst is the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
-__device__ __forceinline__ int rec_toff(const WalkCtx& c, int kt) {
-  return 2 * ((c.rb + (c.lane & 15)) * CK + 8 * (c.lane >> 4) + 32 * kt);
+// 16 bytes per lane through a buffer resource straight into LDS: lane l's
+// bytes land at dst + 16 l; a lane whose offset lies past the resource's range
+// reads zeros.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, int off, void* dst) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
 }
 
-// both k-steps are always loaded (for the first 32 rows the second one is the
-// zero upper block), so every path issues the same memory operations
-template <int NT>
-__device__ __forceinline__ void fetch_t(ChunkRegs<NT>& R, const WalkCtx& c, int ch) {
-  const char* rec = chunk_rec(c, ch);
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    R.th[kt] = *reinterpret_cast<const uint4*>(rec + REC_TH + rec_toff(c, kt));
-    R.tl[kt] = *reinterpret_cast<const uint4*>(rec + REC_TL + rec_toff(c, kt));
-  }
-}
-
-template <int NT>
-__device__ __forceinline__ void fetch_p(ChunkRegs<NT>& R, const WalkCtx& c, int ch) {
-  const char* rec = chunk_rec(c, ch);
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-    R.p[kt] = *reinterpret_cast<const uint4*>(rec + REC_P + rec_toff(c, kt));
-}
-
-template <int NT>
-__device__ __forceinline__ void fetch_vf(ChunkRegs<NT>& R, const WalkCtx& c, int ch) {
+// Issues the loads of chunk `ch` into B; each 1 KB wave load covers 64
+// consecutive 16-byte units of a matrix, unit p holding the row's chunk that
+// the swizzle puts there.  The q/k/v rows go through buffer resources that end
+// at the chunk's last token, so rows past the end of the sequence arrive as
+// zeros.  `ko`, `qo` and `vo` are the lanes' byte offsets within a chunk.
+template <int NW>
+__device__ __forceinline__ void stage_dma(WalkBuf<NW>& B, const WalkCtx& c, int ch, int w,
+                                          int lane, const int (&ko)[16 / NW],
+                                          const int (&qo)[16 / NW], const int (&vo)[2]) {
   const PrefillArgs& a = *c.a;
   const int64_t tb = c.t_begin + (int64_t)ch * CK;
   const int L = chunk_len(c, ch);
-  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (int64_t)c.h * a.dv + c.dv0 +
-                       (c.lane & 15);
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + tb * a.k_rs + (int64_t)c.hk * DKC),
+      0, (int)(L * a.k_rs * 2), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.q) + tb * a.q_rs + (int64_t)c.hk * DKC),
+      0, (int)(L * a.q_rs * 2), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + tb * a.v_rs + (int64_t)c.h * a.dv),
+      0, (int)(L * a.v_rs * 2), kBufferFlags);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int vrow = min(c.rb + 4 * (c.lane >> 4) + r, L - 1);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) R.v[nt][r] = vp[(tb + vrow) * a.v_rs + 16 * nt];
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int u = NW * i + w;
+    dma16_buf(kr, ko[i], B.K + 512 * u);
+    dma16_buf(qr, qo[i], B.Q + 512 * u);
   }
-  const float* F = reinterpret_cast<const float*>(chunk_rec(c, ch) + REC_F);
-  const int frow = c.rb + 4 * (c.lane >> 4);
-  R.fz = *reinterpret_cast<const float4*>(F + frow);
-  R.fo = *reinterpret_cast<const float4*>(F + CK + frow);
-  R.fw = *reinterpret_cast<const float4*>(F + 2 * CK + frow);
-  R.gc = F[3 * CK];
+  const char* rec = chunk_rec(c, ch);
+#pragma unroll
+  for (int i = 0; i < 8 / NW; ++i) {
+    const int u = NW * i + w;
+    const int p = 64 * u + lane, row = p >> 3;
+    const int off = 2 * (row * CK + 8 * ((p & 7) ^ (((row >> 1) & 1) | (((row >> 3) & 3) << 1))));
+    dma16(rec + REC_TH + off, B.Th + 512 * u);
+    dma16(rec + REC_TL + off, B.Tl + 512 * u);
+    dma16(rec + REC_P + off, B.P + 512 * u);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) dma16_buf(vr, vo[i], B.V + 512 * (NW * i + w));
+  if (w == 0) dma16(rec + REC_F + 16 * lane, B.F);
 }
 
-__device__ __forceinline__ float f4(const float4& v, int r) {
-  return r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
+// Waits for this wave's outstanding global accesses (the chunk loads above)
+// and then for the whole workgroup: the loaded chunk is visible to every wave
+// and every wave is done with the buffer the next loads will overwrite.
+__device__ __forceinline__ void stage_sync() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
 }
 
-// four consecutive 16-bit elements (rows i0..i0+3 of a transposed tile) as
-// one 8-byte LDS store
-__device__ __forceinline__ void store4(uint16_t* p, const uint16_t (&e)[4]) {
-  *reinterpret_cast<uint2*>(p) =
-      make_uint2((uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16));
-}
-
-// Output element type of the state walk.
+// Output element type of the state walk, stored through a buffer resource
+// whose range ends at the last row of the current chunk: stores of rows past
+// the end of the sequence fall outside it and are dropped by the hardware, so
+// every chunk issues the same stores (the compiler's memory-counter waits for
+// the staged loads stay exact) without a branch per row.
 template <int TOUT>
 struct OutT {
   typedef uint16_t type;
-  static __device__ __forceinline__ uint16_t cvt(float x) {
-    return TOUT == kBF16 ? f32_to_bf16(x) : f32_to_f16(x);
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, float x) {
+    const uint16_t h = TOUT == kBF16 ? f32_to_bf16(x) : f32_to_f16(x);
+    __builtin_amdgcn_raw_buffer_store_b16(h, r, off, 0, 0);
   }
 };
 template <>
 struct OutT<kF32> {
   typedef float type;
-  static __device__ __forceinline__ float cvt(float x) { return x; }
+  static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+  }
 };
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
-// One workgroup walks one (sequence, v-head, 16 NT-row tile of S); wave w
-// owns rows [16w, 16w + 16) of the chunk for X, Z, U and O, and the S tiles
-// (mt, 2w + q) for mt < NT, q < 2.
-// `dump` holds one 64 x 16 NT tile per workgroup: outputs of rows past the end
-// of a sequence are written there instead of being skipped, so every chunk
-// step issues the same number of stores and the compiler's memory-counter
-// waits for the prefetched next chunk stay exact (a data-dependent store
-// count makes it wait for all outstanding loads).
-template <int TIN, int TOUT, int NT>
-__global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, const int32_t* cs,
-                                                             const int32_t* order,
-                                                             const char* recs, int ntiles,
-                                                             int max_chunks, float* dump) {
-  constexpr int BV = 16 * NT;
-  __shared__ __align__(16) WalkLds<NT> sm;
+// 8-byte transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, result lane i element e is element i % 4 of the 8 bytes addressed by
+// lane 4e + i / 4 of the group.
+__device__ __forceinline__ u16x4 lds_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) lds_h4 lds_ptr_t;
+  const lds_h4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_ptr_t*)(p));
+  return __builtin_bit_cast(u16x4, v);
+}
+
+// Packs two D tiles (tile 2j: slots 0-3, tile 2j + 1: slots 4-7) into a B
+// operand, split into 16-bit high and low parts (lo = x - hi, rounded).
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+template <int TIN>
+__device__ __forceinline__ void pack_split(const f32x4& t0, const f32x4& t1,
+                                           typename MT<TIN>::x8& hi, typename MT<TIN>::x8& lo) {
+  using x8 = typename MT<TIN>::x8;
+  const f32x8 x = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  hi = __builtin_convertvector(x, x8);
+  lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), x8);
+}
+
+template <int TIN, int TOUT, int NW, int MINB>
+__global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
+    PrefillArgs a, const int32_t* cs, const int32_t* order, const char* recs, int ntiles,
+    int max_chunks) {
+  constexpr int NTH = 64 * NW;
+  __shared__ __align__(16) WalkBuf<NW> sb[2];
   using M = MT<TIN>;
   using x8 = typename M::x8;
 
@@ -562,14 +601,14 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
   const int rblk = blockIdx.x / kXcds;
   const int unit = (rblk / per_unit) * kXcds + xcd;
   if (unit >= a.num_seqs * a.hk) return;
-  const int j = rblk % per_unit;
-  const int tile = j % ntiles;
-  const int h = (unit % a.hk) * ratio + j / ntiles;
+  const int j0 = rblk % per_unit;
+  const int tile = j0 % ntiles;
+  const int h = (unit % a.hk) * ratio + j0 / ntiles;
   const int s_rank = unit / a.hk;
   const int s = order[s_rank];
-  const int sh = s_rank * a.hv + h;  // workgroup slot used for the dump area
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int g = lane >> 4, cl = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   WalkCtx c;
   c.a = &a;
@@ -578,10 +617,9 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
   c.c0 = cs[s];
   c.h = h;
   c.hk = h / ratio;
-  c.dv0 = tile * BV;
-  c.rb = 16 * w;
-  c.nkt = (c.rb + 15) / 32 + 1;  // k-steps over tokens j <= i
-  c.lane = lane;
+  c.dv0 = tile * 16 * NW;
+  const int dvw = c.dv0 + 16 * w;  // this wave's first state row
+  const bool active = dvw < a.dv;
   // a well-formed cu_seqlens gives c0 + nch <= max_chunks; a malformed one
   // (overlapping ranges) must still never index past the workspace
   const int nch =
@@ -590,209 +628,219 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(PrefillArgs a, cons
   const int64_t out_rs = (int64_t)a.hv * a.dv;
 
   if (slot < 0 || slot >= a.num_slots) {
-    // caller error: NaN outputs for this tile, no state access
-    for (int64_t t = c.t_begin + tid / BV; t < c.t_end; t += 256 / BV)
-      store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + c.dv0 + tid % BV,
-             __builtin_nanf(""));
+    // caller error: NaN outputs for these rows, no state access
+    constexpr int BV = 16 * NW;
+    for (int64_t t = c.t_begin + tid / BV; t < c.t_end; t += NTH / BV) {
+      const int col = c.dv0 + tid % BV;
+      if (col < a.dv) store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + col,
+                             __builtin_nanf(""));
+    }
     return;
   }
-  const bool init = a.has_init ? a.has_init[s] != 0 : true;
-  float* Sg = a.pool + ((slot * a.hv + h) * a.dv + c.dv0) * DKC;
-  const int rb = c.rb;
-  const int nkt = c.nkt;
+  const bool init = (a.has_init ? a.has_init[s] != 0 : true) && active;
+  float* Sg = a.pool + ((slot * a.hv + h) * a.dv + dvw + cl) * DKC;
   using Ot = typename OutT<TOUT>::type;
-  Ot* out = static_cast<Ot*>(a.out) + (int64_t)h * a.dv + c.dv0;
-  Ot* dump_tile = reinterpret_cast<Ot*>(dump + ((int64_t)sh * ntiles + tile) * (CK * BV));
+  Ot* out = static_cast<Ot*>(a.out) + (int64_t)h * a.dv + dvw;  // this wave's column 0
 
-  // S tile (BV x 128) in MFMA accumulators: wave w holds tiles q = 2 mt + e
-  // at (row block mt, column block 2w + e); element r of tile q is
-  // S[16 mt + 4 (lane/16) + r][16 (2w + e) + lane % 16].
-  f32x4 accs[2 * NT];
+  // St tile kb, element r: S[dvw + cl][blk_row(kb, 4g + r)]
+  f32x4 St[8];
 #pragma unroll
-  for (int q = 0; q < 2 * NT; ++q) {
-    const int mt = q >> 1, nt = 2 * w + (q & 1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      accs[q][r] = init ? Sg[(16 * mt + 4 * (lane >> 4) + r) * DKC + 16 * nt + (lane & 15)] : 0.0f;
+  for (int kb = 0; kb < 8; ++kb) {
+    const float4 v = init ? *reinterpret_cast<const float4*>(Sg + blk_row(kb, 4 * g))
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    St[kb] = (f32x4){v.x, v.y, v.z, v.w};
   }
-  auto write_s_lds = [&](int buf) {
+
+  auto store_state = [&]() {
+    if (active) {
 #pragma unroll
-    for (int q = 0; q < 2 * NT; ++q) {
-      const int mt = q >> 1, nt = 2 * w + (q & 1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int off = (16 * mt + 4 * (lane >> 4) + r) * LDQ + 16 * nt + (lane & 15);
-        const uint16_t hb = M::enc(accs[q][r]);
-        sm.Sh[buf][off] = hb;
-        sm.Sl[buf][off] = M::enc(accs[q][r] - M::dec(hb));
-      }
+      for (int kb = 0; kb < 8; ++kb)
+        *reinterpret_cast<float4*>(Sg + blk_row(kb, 4 * g)) =
+            make_float4(St[kb][0], St[kb][1], St[kb][2], St[kb][3]);
     }
   };
-  // Q, K, V and the factors are fetched one chunk ahead; T_b and P (needed
-  // only from the second phase on) at the start of their own chunk.
-  auto fetch_ahead = [&](ChunkRegs<NT>& R, int ch) {
-    fetch_qk(R, c, ch);
-    fetch_vf(R, c, ch);
-  };
+  if (nch == 0) {  // empty sequence: the state passes through (or is zeroed)
+    store_state();
+    return;
+  }
 
-  // One chunk with its inputs in `R`; the next chunk's Q, K, V and factors
-  // are requested into `N` first.  The loop below alternates the two register
-  // sets so that no loaded register is copied across iterations (a copy would
-  // wait for the whole prefetch).
-  auto step = [&](ChunkRegs<NT>& R, ChunkRegs<NT>& N, int ch) {
-    const int cb = ch & 1;
+  // per-lane byte offsets of the q/k and v units this lane loads (see stage_dma)
+  int ko[16 / NW], qo[16 / NW], vo[2];
+#pragma unroll
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int p = 64 * (NW * i + w) + lane, row = p >> 4;
+    const int chg = (p & 15) ^ (((row & 3) << 2) | ((row >> 3) & 3));
+    ko[i] = (int)(row * a.k_rs * 2) + 16 * chg;
+    qo[i] = (int)(row * a.q_rs * 2) + 16 * chg;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = 64 * (NW * i + w) + lane, row = p / (2 * NW);
+    const int chg = (p % (2 * NW)) ^ v_swz(row);
+    // columns past dv (a partial last block) re-read the last 8 columns
+    vo[i] = (int)(row * a.v_rs * 2) + 2 * min(c.dv0 + 8 * chg, a.dv - 8);
+  }
+  // rows past the end of a sequence arrive as zeros; clearing both buffers
+  // first also keeps every row that the first chunk does not load finite
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&sb[0]);
+    constexpr int n16 = (int)(2 * sizeof(WalkBuf<NW>) / 16);
+    for (int i = tid; i < n16; i += NTH) z[i] = (u32x4){0u, 0u, 0u, 0u};
+  }
+  lds_barrier();
+  stage_dma<NW>(sb[0], c, 0, w, lane, ko, qo, vo);
+  stage_sync();
+
+  // Per-lane LDS offsets (elements).  Every operand row of token block b is
+  // blk_row(b, m) = 32 (b / 2) + 4 (b % 2) + rm with rm = 8 (m / 4) + m % 4, and
+  // the swizzles depend on rm only, so each read is a per-lane base (one per
+  // k-step) plus a compile-time offset for the block.
+  const int rmA = 8 * (cl >> 2) + (cl & 3);        // A-operand row within a block pair
+  const int sK = ((cl & 3) << 2) | ((cl >> 2) & 3);  // K/Q chunk swizzle of those rows
+  const int sT = ((cl >> 1) & 1) | (((cl >> 2) & 3) << 1);
+  int kqb[4], tpb[2], trb[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) kqb[jj] = rmA * DKC + 8 * ((4 * jj + g) ^ sK);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) tpb[j] = rmA * CK + 8 * ((4 * j + g) ^ sT);
+  {
+    // transposing reads: this lane supplies row 32 j + 8 g + 4 h + e, chunk
+    // 4 (kb / 2) + q (+ 4 elements when kb is odd); the row swizzle is 4 e + g
+    const int e = cl >> 2, q = lane & 3;
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) trb[kp] = (8 * g + e) * DKC + 8 * ((4 * kp + q) ^ (4 * e + g));
+  }
+  // V rows 8 g + ..., this wave's column 16 w + cl (row swizzle 2 g)
+  const int vb = 8 * g * 16 * NW + 8 * ((2 * w + (cl >> 3)) ^ (2 * g)) + (cl & 7);
+  const int fb = 8 * g;                      // factor rows 8 g + ...
+  // output element (row 8 g + i, column cl) of a chunk, in bytes
+  const int out_lane = (int)((8 * g * out_rs + cl) * (int64_t)sizeof(Ot));
+  const int out_row = (int)(out_rs * (int64_t)sizeof(Ot));
+
+  for (int ch = 0; ch < nch; ++ch) {
     const int64_t tb = c.t_begin + (int64_t)ch * CK;
     const int L = chunk_len(c, ch);
-    fetch_t(R, c, ch);
-    fetch_p(R, c, ch);
-    fetch_ahead(N, min(ch + 1, nch - 1));  // the last step re-fetches its own chunk
-    // rows of this wave past the end of the sequence: zero operands
-    if (rb + (lane & 15) >= L) {
+    if (ch + 1 < nch) stage_dma<NW>(sb[(ch + 1) & 1], c, ch + 1, w, lane, ko, qo, vo);
+    const WalkBuf<NW>& sm = sb[ch & 1];
+    // rows [0, L) of this chunk; a wave past dv gets an empty range
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        out + tb * out_rs, 0, active ? L * out_row : 0, kBufferFlags);
+    int lane_off = out_lane;
+    asm volatile("" : "+v"(lane_off));  // keep the 16 row offsets below out of the loop preheader
+
+    // ---- X = K St and QS = Q St (entry state), St split into B operands on the fly ----
+    f32x4 X[4], QS[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        R.q[kk] = make_uint4(0, 0, 0, 0);
-        R.k[kk] = make_uint4(0, 0, 0, 0);
+    for (int b = 0; b < 4; ++b) {
+      X[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      QS[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      x8 sh, sl;
+      pack_split<TIN>(St[2 * jj], St[2 * jj + 1], sh, sl);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int rb = 32 * (b >> 1) + 4 * (b & 1);
+        const x8 kf = *reinterpret_cast<const x8*>(sm.K + kqb[jj] + rb * DKC);
+        const x8 qf = *reinterpret_cast<const x8*>(sm.Q + kqb[jj] + rb * DKC);
+        X[b] = M::mma(kf, sh, X[b]);
+        QS[b] = M::mma(qf, sh, QS[b]);
+        X[b] = M::mma(kf, sl, X[b]);
+        QS[b] = M::mma(qf, sl, QS[b]);
       }
     }
 
-    // ---- X = K S^T and QS = Q S^T of the row block; K^T to LDS; Z ----
-    f32x4 accq[NT];
+    // ---- Z = V - diag(fz) X as B operands (k = token) ----
+    x8 Zh[2], Zl[2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 accx = {0.f, 0.f, 0.f, 0.f};
-      accq[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) {
+      f32x4 z[2];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const x8 shi = frag<TIN>(sm.Sh[cb], LDQ, 16 * nt, 32 * kk, lane);
-        const x8 slo = frag<TIN>(sm.Sl[cb], LDQ, 16 * nt, 32 * kk, lane);
-        const x8 kf = __builtin_bit_cast(x8, R.k[kk]);
-        const x8 qf = __builtin_bit_cast(x8, R.q[kk]);
-        accx = M::mma(kf, shi, accx);
-        accq[nt] = M::mma(qf, shi, accq[nt]);
-        accx = M::mma(kf, slo, accx);
-        accq[nt] = M::mma(qf, slo, accq[nt]);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int b = 2 * j + hh;
+        const int rb = 32 * (b >> 1) + 4 * (b & 1);
+        const float4 fz = *reinterpret_cast<const float4*>(sm.F + fb + rb);
+        const float fzr[4] = {fz.x, fz.y, fz.z, fz.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          z[hh][r] = M::dec(sm.V[vb + (rb + r) * 16 * NW]) - fzr[r] * X[b][r];
       }
-      uint16_t zh[4], zl[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = rb + 4 * (lane >> 4) + r;
-        const float vv = i < L ? M::dec(R.v[nt][r]) : 0.0f;
-        const float z = vv - f4(R.fz, r) * accx[r];
-        zh[r] = M::enc(z);
-        zl[r] = M::enc(z - M::dec(zh[r]));
-      }
-      const int off = (16 * nt + (lane & 15)) * LDT + rb + 4 * (lane >> 4);
-      store4(sm.Zh + off, zh);
-      store4(sm.Zl + off, zl);
+      pack_split<TIN>(z[0], z[1], Zh[j], Zl[j]);
     }
+
+    // ---- U = T_b Z (lower triangular in token blocks) ----
+    f32x4 U[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rb = 32 * (b >> 1) + 4 * (b & 1);
+      U[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j <= (b >> 1); ++j) {
+        const x8 th = *reinterpret_cast<const x8*>(sm.Th + tpb[j] + rb * CK);
+        const x8 tl = *reinterpret_cast<const x8*>(sm.Tl + tpb[j] + rb * CK);
+        U[b] = M::mma(th, Zh[j], U[b]);
+        U[b] = M::mma(th, Zl[j], U[b]);
+        U[b] = M::mma(tl, Zh[j], U[b]);
+      }
+    }
+    x8 Uh[2], Ul[2], Wh[2], Wl[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f32x4 wv[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int b = 2 * j + hh;
+        const int rb = 32 * (b >> 1) + 4 * (b & 1);
+        const float4 fw = *reinterpret_cast<const float4*>(sm.F + 2 * CK + fb + rb);
+        wv[hh] = (f32x4){fw.x * U[b][0], fw.y * U[b][1], fw.z * U[b][2], fw.w * U[b][3]};
+      }
+      pack_split<TIN>(U[2 * j], U[2 * j + 1], Uh[j], Ul[j]);
+      pack_split<TIN>(wv[0], wv[1], Wh[j], Wl[j]);
+    }
+
+    // ---- O = diag(fo) QS + P U, stored ----
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rb = 32 * (b >> 1) + 4 * (b & 1);
+      const float4 fo = *reinterpret_cast<const float4*>(sm.F + CK + fb + rb);
+      f32x4 o = {fo.x * QS[b][0], fo.y * QS[b][1], fo.z * QS[b][2], fo.w * QS[b][3]};
+#pragma unroll
+      for (int j = 0; j <= (b >> 1); ++j) {
+        const x8 pf = *reinterpret_cast<const x8*>(sm.P + tpb[j] + rb * CK);
+        o = M::mma(pf, Uh[j], o);
+        o = M::mma(pf, Ul[j], o);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) OutT<TOUT>::store(orsrc, lane_off + (rb + r) * out_row, o[r]);
+    }
+
+    // ---- St = e^{G_C} St + K^T W ----
     {
-      const int tok = rb + (lane & 15);
+      const float gc = sm.F[3 * CK];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t kw[4] = {R.k[kk].x, R.k[kk].y, R.k[kk].z, R.k[kk].w};
-        const int d0 = 32 * kk + 8 * (lane >> 4);
-        const int col = kt_col(d0, tok);
+      for (int kb = 0; kb < 8; ++kb) {
+        f32x4 acc = St[kb];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sm.Kt[(d0 + 2 * e) * LDT + col] = (uint16_t)(kw[e] & 0xffffu);
-          sm.Kt[(d0 + 2 * e + 1) * LDT + col] = (uint16_t)(kw[e] >> 16);
+        for (int r = 0; r < 4; ++r) acc[r] *= gc;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint16_t* p = sm.K + trb[kb >> 1] + 32 * j * DKC + 4 * (kb & 1);
+          const u16x4 t0 = lds_read_tr(p);
+          const u16x4 t1 = lds_read_tr(p + 4 * DKC);
+          const u16x8 kt = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+          const x8 kf = __builtin_bit_cast(x8, kt);
+          acc = M::mma(kf, Wh[j], acc);
+          acc = M::mma(kf, Wl[j], acc);
         }
+        St[kb] = acc;
       }
     }
-    lds_barrier();
 
-    // ---- U = T_b Z (row block); U^T and (diag(fw) U)^T to LDS ----
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 accu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        if (kt < nkt) {
-          const x8 th = __builtin_bit_cast(x8, R.th[kt]);
-          const x8 tl = __builtin_bit_cast(x8, R.tl[kt]);
-          const x8 zh = frag<TIN>(sm.Zh, LDT, 16 * nt, 32 * kt, lane);
-          const x8 zl = frag<TIN>(sm.Zl, LDT, 16 * nt, 32 * kt, lane);
-          accu = M::mma(th, zh, accu);
-          accu = M::mma(th, zl, accu);
-          accu = M::mma(tl, zh, accu);
-        }
-      }
-      uint16_t uh[4], ul[4], wh[4], wl[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float u = accu[r];
-        uh[r] = M::enc(u);
-        ul[r] = M::enc(u - M::dec(uh[r]));
-        const float up = u * f4(R.fw, r);
-        wh[r] = M::enc(up);
-        wl[r] = M::enc(up - M::dec(wh[r]));
-      }
-      const int off = (16 * nt + (lane & 15)) * LDT + rb + 4 * (lane >> 4);
-      store4(sm.Uh + off, uh);
-      store4(sm.Ul + off, ul);
-      store4(sm.Wh + off, wh);
-      store4(sm.Wl + off, wl);
-    }
-    lds_barrier();
-
-    // ---- outputs of the row block; state update; S to the other buffer ----
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 acco = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        if (kt < nkt) {
-          const x8 pf = __builtin_bit_cast(x8, R.p[kt]);
-          acco = M::mma(pf, frag<TIN>(sm.Uh, LDT, 16 * nt, 32 * kt, lane), acco);
-          acco = M::mma(pf, frag<TIN>(sm.Ul, LDT, 16 * nt, 32 * kt, lane), acco);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = rb + 4 * (lane >> 4) + r;
-        const float o = f4(R.fo, r) * accq[nt][r] + acco[r];
-        Ot* dst = i < L ? out + (tb + i) * out_rs + 16 * nt + (lane & 15)
-                        : dump_tile + i * BV + 16 * nt + (lane & 15);
-        *dst = OutT<TOUT>::cvt(o);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 2 * NT; ++q) {
-      const int mt = q >> 1, nt = 2 * w + (q & 1);
-      const int dk = 16 * nt + (lane & 15);
-      f32x4 acc = accs[q];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= R.gc;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const x8 kf = *reinterpret_cast<const x8*>(
-            sm.Kt + dk * LDT + kt_col(dk, 32 * kt + 8 * (lane >> 4)));
-        acc = M::mma(frag<TIN>(sm.Wh, LDT, 16 * mt, 32 * kt, lane), kf, acc);
-        acc = M::mma(frag<TIN>(sm.Wl, LDT, 16 * mt, 32 * kt, lane), kf, acc);
-      }
-      accs[q] = acc;
-    }
-    write_s_lds(cb ^ 1);
-    lds_barrier();
-  };
-
-  write_s_lds(0);
-  ChunkRegs<NT> RA, RB;
-  if (nch > 0) fetch_ahead(RA, 0);
-  __syncthreads();
-  for (int ch = 0; ch < nch; ch += 2) {
-    step(RA, RB, ch);
-    if (ch + 1 < nch) step(RB, RA, ch + 1);
+    stage_sync();
   }
 
-  // final state
-#pragma unroll
-  for (int q = 0; q < 2 * NT; ++q) {
-    const int mt = q >> 1, nt = 2 * w + (q & 1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      Sg[(16 * mt + 4 * (lane >> 4) + r) * DKC + 16 * nt + (lane & 15)] = accs[q][r];
-  }
+  store_state();
 }
 
 int64_t max_chunks(int64_t total_tokens, int64_t num_seqs) {
@@ -801,9 +849,8 @@ int64_t max_chunks(int64_t total_tokens, int64_t num_seqs) {
 
 size_t meta_bytes(int64_t num_seqs) { return (size_t)((2 * num_seqs + 1) * 4 + 255) / 256 * 256; }
 
-size_t dump_bytes(int64_t num_seqs, int hv, int dv) {
-  return (size_t)num_seqs * hv * (dv / BVT) * CK * BVT * sizeof(float);
-}
+int walk_tiles(int dv) { return (dv + WALK_BV - 1) / WALK_BV; }
+
 
 template <int TIN>
 hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) {
@@ -811,42 +858,47 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   int32_t* order = cs + a.num_seqs + 1;
   char* recs = static_cast<char*>(ws) + meta_bytes(a.num_seqs);
   const int64_t mc = max_chunks(a.total_tokens, a.num_seqs);
-  float* dump = reinterpret_cast<float*>(recs + (size_t)mc * a.hv * REC_BYTES);
   hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, cs, order);
   hipLaunchKernelGGL((chunk_prep_kernel<TIN>), dim3((unsigned)mc, (unsigned)a.hv), dim3(256), 0,
                      stream, a, (const int32_t*)cs, recs);
-  const int ntiles = a.dv / BVT;
+  const int ntiles = walk_tiles(a.dv);
   const int64_t units = a.num_seqs * a.hk;
   const int64_t blocks = (units + kXcds - 1) / kXcds * kXcds * (a.hv / a.hk) * ntiles;
   if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (a.out_dt == kF32)
-    hipLaunchKernelGGL((chunk_state_kernel<TIN, kF32, WALK_NT>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((chunk_state_kernel<TIN, kF32, WALK_NW, WALK_MINB>), dim3((unsigned)blocks),
+                       dim3(64 * WALK_NW), 0,
                        stream, a, (const int32_t*)cs, (const int32_t*)order, (const char*)recs,
-                       ntiles, (int)mc, dump);
+                       ntiles, (int)mc);
   else
-    hipLaunchKernelGGL((chunk_state_kernel<TIN, TIN, WALK_NT>), dim3((unsigned)blocks), dim3(256), 0,
+    hipLaunchKernelGGL((chunk_state_kernel<TIN, TIN, WALK_NW, WALK_MINB>), dim3((unsigned)blocks),
+                       dim3(64 * WALK_NW), 0,
                        stream, a, (const int32_t*)cs, (const int32_t*)order, (const char*)recs,
-                       ntiles, (int)mc, dump);
+                       ntiles, (int)mc);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool chunked_supported(int in_dt, int out_dt, int dk, int dv) {
+bool chunked_supported(int in_dt, int out_dt, int64_t hv, int dk, int dv) {
   (void)out_dt;
-  return (in_dt == kBF16 || in_dt == kF16) && dk == DKC && dv % BVT == 0;
+  // the state walk addresses a chunk of output rows with 32-bit byte offsets
+  const bool rows_fit = hv * dv * CK * (int64_t)sizeof(float) < ((int64_t)1 << 31);
+  return (in_dt == kBF16 || in_dt == kF16) && dk == DKC && dv % 16 == 0 && dv >= 16 && rows_fit;
 }
 
 bool chunked_layout_ok(const void* q, const void* k, const void* v, int64_t q_rs, int64_t k_rs,
                        int64_t v_rs) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  return al(q) && al(k) && al(v) && q_rs % 8 == 0 && k_rs % 8 == 0 && v_rs % 8 == 0;
+  // a chunk of rows is addressed with 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 24;
+  return al(q) && al(k) && al(v) && q_rs % 8 == 0 && k_rs % 8 == 0 && v_rs % 8 == 0 &&
+         q_rs < lim && k_rs < lim && v_rs < lim;
 }
 
 size_t chunked_workspace_bytes(int64_t total_tokens, int64_t num_seqs, int hv, int dk, int dv) {
   (void)dk; (void)dv;
-  return meta_bytes(num_seqs) + (size_t)max_chunks(total_tokens, num_seqs) * (size_t)hv * REC_BYTES +
-         dump_bytes(num_seqs, hv, dv);
+  return meta_bytes(num_seqs) + (size_t)max_chunks(total_tokens, num_seqs) * (size_t)hv * REC_BYTES;
 }
 
 hipError_t launch_prefill_chunked(const PrefillArgs& a, void* ws, size_t ws_bytes,

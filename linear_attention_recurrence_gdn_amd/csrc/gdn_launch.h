@@ -75,7 +75,7 @@ hipError_t launch_prefill_sequential(const PrefillArgs& a, hipStream_t stream);
 
 // Chunked prefill (MFMA).  Returns hipErrorNotSupported when the shape or
 // dtype has no chunked kernel (the caller then uses the sequential one).
-bool chunked_supported(int in_dt, int out_dt, int dk, int dv);
+bool chunked_supported(int in_dt, int out_dt, int64_t hv, int dk, int dv);
 // the chunked kernels stage q/k/v rows with 16-byte loads
 bool chunked_layout_ok(const void* q, const void* k, const void* v, int64_t q_rs, int64_t k_rs,
                        int64_t v_rs);
