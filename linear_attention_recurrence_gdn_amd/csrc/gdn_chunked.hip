@@ -55,9 +55,11 @@ constexpr int WALK_MINB = GDN_WALK_MINB;  // state-walk workgroups per CU the re
 constexpr int WALK_BV = 16 * WALK_NW;     // state rows per workgroup
 constexpr int LDQ = DKC + 8;  // padded LDS row (16-bit elements), token-major 128-wide tiles
 constexpr int LDF = CK + 4;   // padded LDS row (f32), 64 x 64 matrices
+constexpr int LDT = CK + 8;   // padded LDS row (16-bit elements), 64 x 64 matrices
 constexpr int kXcds = 8;      // accelerator complex dies (separate L2s) on MI355X
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int TIN>
 struct MT;
@@ -208,20 +210,31 @@ constexpr int REC_P = 2 * CK * CK * 2;
 constexpr int REC_F = 3 * CK * CK * 2;
 constexpr int REC_BYTES = REC_F + 4 * CK * 4;
 
+// One workgroup per (chunk, q/k head): the raw products K K^T and Q K^T of the
+// chunk are shared by the v-heads of the GQA group, so they are formed once
+// (each wave keeps its tiles in registers) and then, head by head, scaled by
+// that head's gates and betas, solved and written out.
 template <int TIN>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, const int32_t* cs,
-                                                         char* recs) {
-  __shared__ __align__(16) uint16_t Qs[CK * LDQ];
-  __shared__ __align__(16) uint16_t Ks[CK * LDQ];
-  __shared__ __align__(16) float Am[CK * LDF];
-  __shared__ __align__(16) float Tm[CK * LDF];
+__global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const int32_t* cs,
+                                                            char* recs) {
+  // Q and K are needed only for the products; A and T then reuse their space
+  union PrepLds {
+    struct {
+      uint16_t Qs[CK * LDQ], Ks[CK * LDQ];
+    } qk;
+    struct {
+      float Am[CK * LDF], Tm[CK * LDF];
+    } at;
+  };
+  __shared__ __align__(16) PrepLds u;
+  __shared__ __align__(16) uint16_t Ps[CK * LDT];
   __shared__ float Rs[4][16 * 17];
   __shared__ double Gd[CK];
   __shared__ float nq[CK], nk[CK], bt[CK];
   using M = MT<TIN>;
 
   const int c = blockIdx.x;
-  const int h = blockIdx.y;
+  const int hk = blockIdx.y;
   const int n = (int)a.num_seqs;
   if (c >= cs[n]) return;
   int lo = 0, hi = n - 1;  // largest s with cs[s] <= c
@@ -234,41 +247,44 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, const in
   chunk_bounds(a, s, t0, t1);
   const int64_t tb = t0 + (int64_t)(c - cs[s]) * CK;
   const int L = (int)min((int64_t)CK, t1 - tb);
-  const int hk = h / (a.hv / a.hk);
+  const int ratio = a.hv / a.hk;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
+  uint16_t* Qs = u.qk.Qs;
+  uint16_t* Ks = u.qk.Ks;
+  float* Am = u.at.Am;
+  float* Tm = u.at.Tm;
 
-  // stage Q and K (zero rows past the sequence), g, beta
+  // stage Q and K, rows past the sequence zeroed (all loads issued before any is used)
+  {
+    u32x4 qv[4], kv[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = tid + 256 * u;
-    const int row = idx >> 4, p = idx & 15;
-    uint4 qv = {0, 0, 0, 0}, kv = {0, 0, 0, 0};
-    if (row < L) {
-      qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) +
-                                           (tb + row) * a.q_rs + (int64_t)hk * DKC + 8 * p);
-      kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) +
-                                           (tb + row) * a.k_rs + (int64_t)hk * DKC + 8 * p);
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 256 * k;
+      const int64_t t = tb + min(idx >> 4, L - 1);
+      qv[k] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) + t * a.q_rs +
+                                              (int64_t)hk * DKC + 8 * (idx & 15));
+      kv[k] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.k) + t * a.k_rs +
+                                              (int64_t)hk * DKC + 8 * (idx & 15));
     }
-    *reinterpret_cast<uint4*>(Qs + row * LDQ + 8 * p) = qv;
-    *reinterpret_cast<uint4*>(Ks + row * LDQ + 8 * p) = kv;
-  }
-  if (w == 0) {
-    const float gv = lane < L ? a.g[(tb + lane) * a.g_rs + h] : 0.0f;
-    const float bv = lane < L ? a.beta[(tb + lane) * a.beta_rs + h] : 0.0f;
-    Gd[lane] = wave_prefix64((double)gv, lane);
-    bt[lane] = bv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 256 * k;
+      const int row = idx >> 4, p = idx & 15;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(Qs + row * LDQ + 8 * p) = row < L ? qv[k] : zero;
+      *reinterpret_cast<u32x4*>(Ks + row * LDQ + 8 * p) = row < L ? kv[k] : zero;
+    }
   }
   __syncthreads();
   {  // row norms: 4 lanes per row, 32 elements each
     const int row = tid >> 2, qq = tid & 3;
     float sq = 0.0f, sk = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint4 xq = *reinterpret_cast<const uint4*>(Qs + row * LDQ + 32 * qq + 8 * u);
-      const uint4 xk = *reinterpret_cast<const uint4*>(Ks + row * LDQ + 32 * qq + 8 * u);
+    for (int k = 0; k < 4; ++k) {
+      const uint4 xq = *reinterpret_cast<const uint4*>(Qs + row * LDQ + 32 * qq + 8 * k);
+      const uint4 xk = *reinterpret_cast<const uint4*>(Ks + row * LDQ + 32 * qq + 8 * k);
       const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w}, wk[4] = {xk.x, xk.y, xk.z, xk.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -287,121 +303,154 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrefillArgs a, const in
       nk[row] = a.l2norm ? 1.0f / sqrtf(sk + a.l2_eps) : 1.0f;
     }
   }
-  __syncthreads();
-  if (w == 0) {  // per-token factors
-    float* F = reinterpret_cast<float*>(rec + REC_F);
-    const double gl = Gd[L - 1];
-    const float eg = expf((float)Gd[lane]);
-    F[lane] = eg * nk[lane];
-    F[CK + lane] = eg * a.scale * nq[lane];
-    F[2 * CK + lane] = expf((float)(gl - Gd[lane])) * nk[lane];
-    F[3 * CK + lane] = lane == 0 ? expf((float)gl) : 0.0f;
-  }
 
-  // 20 tile products: K K^T (jobs 0..9) and Q K^T (jobs 10..19), lower tiles
-  uint16_t* P = reinterpret_cast<uint16_t*>(rec + REC_P);
-  for (int job = w; job < 20; job += 4) {
-    const bool is_p = job >= 10;
-    const int t = is_p ? job - 10 : job;
+  // the lower 16x16 tiles of K K^T (jobs 0..9) and Q K^T (jobs 10..19): wave w
+  // owns jobs w, w + 4, ..., element r of a tile at (4 (l/16) + r, l % 16)
+  f32x4 acc[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int job = w + 4 * k;
+    const int t = job >= 10 ? job - 10 : job;
     const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
     const int tj = t - (ti * (ti + 1)) / 2;
-    const uint16_t* X = is_p ? Qs : Ks;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* X = job >= 10 ? Qs : Ks;
+    acc[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      acc = M::mma(frag<TIN>(X, LDQ, 16 * ti, 32 * kk, lane),
-                   frag<TIN>(Ks, LDQ, 16 * tj, 32 * kk, lane), acc);
+      acc[k] = M::mma(frag<TIN>(X, LDQ, 16 * ti, 32 * kk, lane),
+                      frag<TIN>(Ks, LDQ, 16 * tj, 32 * kk, lane), acc[k]);
+  }
+  __syncthreads();  // Q and K are dead from here on: A and T take their space
+
+  for (int jh = 0; jh < ratio; ++jh) {
+    const int h = hk * ratio + jh;
+    char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
+    if (w == 0) {
+      const float gv = lane < L ? a.g[(tb + lane) * a.g_rs + h] : 0.0f;
+      const float bv = lane < L ? a.beta[(tb + lane) * a.beta_rs + h] : 0.0f;
+      const double gcum = wave_prefix64((double)gv, lane);
+      Gd[lane] = gcum;
+      bt[lane] = bv;
+      // per-token factors
+      const double gl = __shfl(gcum, L - 1, 64);
+      const float eg = expf((float)gcum);
+      float* F = reinterpret_cast<float*>(rec + REC_F);
+      F[lane] = eg * nk[lane];
+      F[CK + lane] = eg * a.scale * nq[lane];
+      F[2 * CK + lane] = expf((float)(gl - gcum)) * nk[lane];
+      F[3 * CK + lane] = lane == 0 ? expf((float)gl) : 0.0f;
+    }
+    __syncthreads();
+
+    // A (strictly lower, scaled) and P (lower incl. diagonal, scaled)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * ti + 4 * (lane >> 4) + r;
-      const int j = 16 * tj + (lane & 15);
-      const float e = expf((float)(Gd[i] - Gd[j]));
-      if (is_p) {
-        const float pv = j <= i ? acc[r] * a.scale * nq[i] * nk[j] * e : 0.0f;
-        P[i * CK + j] = M::enc(pv);
-      } else {
-        Am[i * LDF + j] = j < i ? bt[i] * e * nk[i] * nk[j] * acc[r] : 0.0f;
+    for (int k = 0; k < 5; ++k) {
+      const int job = w + 4 * k;
+      const bool is_p = job >= 10;
+      const int t = is_p ? job - 10 : job;
+      const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+      const int tj = t - (ti * (ti + 1)) / 2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + 4 * (lane >> 4) + r;
+        const int j = 16 * tj + (lane & 15);
+        const float e = expf((float)(Gd[i] - Gd[j]));
+        if (is_p) {
+          const float pv = j <= i ? acc[k][r] * a.scale * nq[i] * nk[j] * e : 0.0f;
+          Ps[i * LDT + j] = M::enc(pv);
+        } else {
+          Am[i * LDF + j] = j < i ? bt[i] * e * nk[i] * nk[j] * acc[k][r] : 0.0f;
+        }
       }
     }
-  }
-  // zero the strictly-upper 16x16 blocks of T and of P
-  for (int idx = tid; idx < 6 * 256; idx += 256) {
-    const int blk = idx >> 8, e = idx & 255;
-    const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-    const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-    const int i = 16 * bi + (e >> 4), j = 16 * bj + (e & 15);
-    Tm[i * LDF + j] = 0.0f;
-    P[i * CK + j] = 0;
-  }
-  __syncthreads();
-
-  // diagonal blocks of T = (I + A)^{-1}: forward substitution, one column per lane
-  if (lane < 16) {
-    const int b0 = 16 * w, col = lane;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = (r == col) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int m = 0; m < r; ++m) v -= Am[(b0 + r) * LDF + b0 + m] * x[m];
-      x[r] = v;
+    // zero the strictly-upper 16x16 blocks of T and of P
+    for (int idx = tid; idx < 6 * 256; idx += 256) {
+      const int blk = idx >> 8, e = idx & 255;
+      const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+      const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+      const int i = 16 * bi + (e >> 4), j = 16 * bj + (e & 15);
+      Tm[i * LDF + j] = 0.0f;
+      Ps[i * LDT + j] = 0;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDF + b0 + col] = x[r];
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
-  // 16x16x16 products on the f32 MFMA (A: lane (m = l%16, k = l/16),
-  // B: lane (k = l/16, n = l%16), D: lane (m = 4 (l/16) + r, n = l%16))
-  for (int d = 1; d < 4; ++d) {
-    const int j = w, i = w + d;
-    const bool active = i < 4;
-    f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      for (int k = j; k < i; ++k)
+    // diagonal blocks of T = (I + A)^{-1}: forward substitution, one column per lane
+    if (lane < 16) {
+      const int b0 = 16 * w, col = lane;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = (r == col) ? 1.0f : 0.0f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) v -= Am[(b0 + r) * LDF + b0 + m] * x[m];
+        x[r] = v;
+        asm volatile("" ::: "memory");  // load row r + 1 of A only now: bounds the live registers
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDF + b0 + col] = x[r];
+    }
+    __syncthreads();
+
+    // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
+    // 16x16x16 products on the f32 MFMA (A: lane (m = l%16, k = l/16),
+    // B: lane (k = l/16, n = l%16), D: lane (m = 4 (l/16) + r, n = l%16))
+    for (int d = 1; d < 4; ++d) {
+      const int j = w, i = w + d;
+      const bool active = i < 4;
+      f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
+      if (active) {
+        for (int k = j; k < i; ++k)
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+            r4 = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                Am[(16 * i + (lane & 15)) * LDF + 16 * k + 4 * s4 + (lane >> 4)],
+                Tm[(16 * k + 4 * s4 + (lane >> 4)) * LDF + 16 * j + (lane & 15)], r4, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Rs[w][(4 * (lane >> 4) + r) * 17 + (lane & 15)] = r4[r];
+      }
+      __syncthreads();
+      if (active) {
+        f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
-          r4 = __builtin_amdgcn_mfma_f32_16x16x4f32(
-              Am[(16 * i + (lane & 15)) * LDF + 16 * k + 4 * s4 + (lane >> 4)],
-              Tm[(16 * k + 4 * s4 + (lane >> 4)) * LDF + 16 * j + (lane & 15)], r4, 0, 0, 0);
+          t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(
+              Tm[(16 * i + (lane & 15)) * LDF + 16 * i + 4 * s4 + (lane >> 4)],
+              Rs[w][(4 * s4 + (lane >> 4)) * 17 + (lane & 15)], t4, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Rs[w][(4 * (lane >> 4) + r) * 17 + (lane & 15)] = r4[r];
+        for (int r = 0; r < 4; ++r)
+          Tm[(16 * i + 4 * (lane >> 4) + r) * LDF + 16 * j + (lane & 15)] = -t4[r];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (active) {
-      f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(
-            Tm[(16 * i + (lane & 15)) * LDF + 16 * i + 4 * s4 + (lane >> 4)],
-            Rs[w][(4 * s4 + (lane >> 4)) * 17 + (lane & 15)], t4, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        Tm[(16 * i + 4 * (lane >> 4) + r) * LDF + 16 * j + (lane & 15)] = -t4[r];
-    }
-    __syncthreads();
-  }
 
-  // T_b = T diag(beta), split into high and low 16-bit parts
-  uint16_t* Th = reinterpret_cast<uint16_t*>(rec + REC_TH);
-  uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + REC_TL);
+    // T_b = T diag(beta), split into high and low 16-bit parts; P copied out
+    uint16_t* Th = reinterpret_cast<uint16_t*>(rec + REC_TH);
+    uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + REC_TL);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = tid + 256 * u;
-    const int i = idx >> 4, j4 = 4 * (idx & 15);
-    const float4 t = *reinterpret_cast<const float4*>(Tm + i * LDF + j4);
-    const float x[4] = {t.x * bt[j4], t.y * bt[j4 + 1], t.z * bt[j4 + 2], t.w * bt[j4 + 3]};
-    uint16_t hh[4], ll[4];
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 256 * k;
+      const int i = idx >> 4, j4 = 4 * (idx & 15);
+      const float4 t = *reinterpret_cast<const float4*>(Tm + i * LDF + j4);
+      const float x[4] = {t.x * bt[j4], t.y * bt[j4 + 1], t.z * bt[j4 + 2], t.w * bt[j4 + 3]};
+      uint16_t hh[4], ll[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      hh[e] = M::enc(x[e]);
-      ll[e] = M::enc(x[e] - M::dec(hh[e]));
+      for (int e = 0; e < 4; ++e) {
+        hh[e] = M::enc(x[e]);
+        ll[e] = M::enc(x[e] - M::dec(hh[e]));
+      }
+      *reinterpret_cast<uint2*>(Th + i * CK + j4) =
+          make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
+      *reinterpret_cast<uint2*>(Tl + i * CK + j4) =
+          make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
     }
-    *reinterpret_cast<uint2*>(Th + i * CK + j4) =
-        make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
-    *reinterpret_cast<uint2*>(Tl + i * CK + j4) =
-        make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = tid + 256 * k;
+      const int i = idx >> 3, j8 = 8 * (idx & 7);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(rec + REC_P) + i * CK + j8) =
+          *reinterpret_cast<const uint4*>(Ps + i * LDT + j8);
+    }
+    __syncthreads();  // the next head rewrites Gd, bt, A, T and P
   }
 }
 
@@ -443,8 +492,6 @@ constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer resource word 3 on 
 // V of the chunk, [token][16 NW columns] 16-bit, 16-byte chunks XOR-swizzled so
 // the four rows 8 apart read by one D-layout access hit distinct banks
 __device__ __forceinline__ int v_swz(int row) { return ((row >> 3) & 3) << 1; }
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // One chunk's inputs in LDS.  The walk keeps two and fills one with direct
 // global-to-LDS loads while it computes on the other.
@@ -859,7 +906,7 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   char* recs = static_cast<char*>(ws) + meta_bytes(a.num_seqs);
   const int64_t mc = max_chunks(a.total_tokens, a.num_seqs);
   hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, cs, order);
-  hipLaunchKernelGGL((chunk_prep_kernel<TIN>), dim3((unsigned)mc, (unsigned)a.hv), dim3(256), 0,
+  hipLaunchKernelGGL((chunk_prep_kernel<TIN>), dim3((unsigned)mc, (unsigned)a.hk), dim3(256), 0,
                      stream, a, (const int32_t*)cs, recs);
   const int ntiles = walk_tiles(a.dv);
   const int64_t units = a.num_seqs * a.hk;
