@@ -51,11 +51,11 @@ constexpr int DKC = 128;      // key head size served here
 #define GDN_WALK_NB 1
 #endif
 #ifndef GDN_WALK_MINB
-#define GDN_WALK_MINB 1
+#define GDN_WALK_MINB 2
 #endif
 constexpr int WALK_NW = GDN_WALK_NW;      // waves per state-walk workgroup
 constexpr int WALK_NB = GDN_WALK_NB;      // 16-row state blocks per wave
-constexpr int WALK_MINB = GDN_WALK_MINB;  // state-walk workgroups per CU the registers allow
+constexpr int WALK_MINB = GDN_WALK_MINB;  // register budget: as for this many workgroups per CU
 constexpr int WALK_BV = 16 * WALK_NW * WALK_NB;  // state rows per workgroup
 constexpr int LDQ = DKC + 8;  // padded LDS row (16-bit elements), token-major 128-wide tiles
 constexpr int LDF = CK + 4;   // padded LDS row (f32), 64 x 64 matrices
@@ -670,7 +670,11 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     int max_chunks) {
   constexpr int NTH = 64 * NW;
   constexpr int VC = WalkBuf<NW, NB>::VC;
-  __shared__ __align__(16) WalkBuf<NW, NB> sb[2];
+  // the two chunk buffers are dynamic LDS: the static size would make the
+  // compiler assume one workgroup per CU and spread the registers over the
+  // accumulation file, costing a copy for every accumulator the VALU touches
+  extern __shared__ __align__(16) char walk_lds[];
+  WalkBuf<NW, NB>* sb = reinterpret_cast<WalkBuf<NW, NB>*>(walk_lds);
   using M = MT<TIN>;
   using x8 = typename M::x8;
 
@@ -758,7 +762,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   // rows past the end of a sequence arrive as zeros; clearing both buffers
   // first also keeps every row that the first chunk does not load finite
   {
-    u32x4* z = reinterpret_cast<u32x4*>(&sb[0]);
+    u32x4* z = reinterpret_cast<u32x4*>(walk_lds);
     constexpr int n16 = (int)(2 * sizeof(WalkBuf<NW, NB>) / 16);
     for (int i = tid; i < n16; i += NTH) z[i] = (u32x4){0u, 0u, 0u, 0u};
   }
@@ -1020,16 +1024,19 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   const int64_t units = a.num_seqs * a.hk;
   const int64_t blocks = (units + kXcds - 1) / kXcds * kXcds * (a.hv / a.hk) * ntiles;
   if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  if (a.out_dt == kF32)
-    hipLaunchKernelGGL((chunk_state_kernel<TIN, kF32, WALK_NW, WALK_NB, WALK_MINB>), dim3((unsigned)blocks),
-                       dim3(64 * WALK_NW), 0,
-                       stream, a, (const int32_t*)cs, (const int32_t*)order, (const char*)recs,
-                       ntiles, (int)mc);
-  else
-    hipLaunchKernelGGL((chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB>), dim3((unsigned)blocks),
-                       dim3(64 * WALK_NW), 0,
-                       stream, a, (const int32_t*)cs, (const int32_t*)order, (const char*)recs,
-                       ntiles, (int)mc);
+  const size_t lds = 2 * sizeof(WalkBuf<WALK_NW, WALK_NB>);
+  auto launch = [&](auto kern) -> hipError_t {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * WALK_NW), lds, stream, a,
+                       (const int32_t*)cs, (const int32_t*)order, (const char*)recs, ntiles, (int)mc);
+    return hipSuccess;
+  };
+  const hipError_t e = a.out_dt == kF32
+                           ? launch(chunk_state_kernel<TIN, kF32, WALK_NW, WALK_NB, WALK_MINB>)
+                           : launch(chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB>);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
