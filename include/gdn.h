@@ -117,7 +117,14 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
 
 /*
  * gdn_prefill_varlen_workspace_size -- bytes of device workspace that
- * gdn_prefill_varlen needs for these sizes and flags (0 if none).
+ * gdn_prefill_varlen needs for these sizes and flags (0 if none).  The
+ * chunked path (bf16/fp16 inputs, dk = 128, dv a multiple of 16) keeps one
+ * 25,600-byte record per (64-token chunk, v-head): about
+ * (total_tokens / 64 + num_seqs) * hv * 25,600 bytes plus about 8 bytes per
+ * sequence; the token-sequential path needs none.  Whether a call takes the
+ * chunked path also depends on its pointers (16-byte aligned q/k/v rows,
+ * strides multiples of 8 elements): with a smaller workspace it fails rather
+ * than falling back.
  */
 size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs, int64_t hk,
                                          int64_t hv, int64_t dk, int64_t dv, gdn_dtype in_dt,

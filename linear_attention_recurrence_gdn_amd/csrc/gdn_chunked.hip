@@ -1,5 +1,5 @@
 // gdn_chunked.hip -- chunk-parallel varlen prefill with the dense products on
-// MFMA (v_mfma_f32_16x16x32_{bf16,f16}), for Dk = 128, Dv a multiple of 32 and
+// MFMA (v_mfma_f32_16x16x32_{bf16,f16}), for Dk = 128, Dv a multiple of 16 and
 // bf16 / fp16 inputs.
 //
 // The recurrence (vllm.cpp tests/vt/test_ops_gdn.cpp, "gdn decode:
@@ -15,19 +15,22 @@
 //
 // Work split:
 //   chunk_meta_kernel   prefix count of chunks per sequence, from cu_seqlens on
-//                       the device (no host synchronisation);
-//   chunk_t_kernel      one workgroup per (chunk, v-head): K K^T on MFMA, the
-//                       strictly-lower A, T = (I + A)^{-1} by blocked forward
-//                       substitution (16x16 blocks), T_b = T diag(beta) to the
-//                       workspace -- all of it independent of the state;
-//   chunk_state_kernel  one workgroup per (sequence, v-head, 16-row tile of S)
-//                       walks the chunks in order with its S tile held in MFMA
-//                       accumulators:
+//                       the device (no host synchronisation), and the order
+//                       of the sequences by length;
+//   chunk_prep_kernel   one workgroup per (chunk, q/k head): K K^T and Q K^T on
+//                       MFMA once per GQA group, then per v-head the strictly
+//                       lower A, T = (I + A)^{-1} by blocked forward
+//                       substitution (16x16 blocks), T_b = T diag(beta), P and
+//                       the per-token factors to a record in the workspace --
+//                       all of it independent of the state;
+//   chunk_state_kernel  one workgroup per (sequence, v-head, block of 16 NW
+//                       state rows) walks the chunks in order; each wave keeps
+//                       its 16 rows of S for all keys in MFMA accumulators:
 //                         X = K S^T,  Z = V - diag(e^G n_k) X,  U = T_b Z,
 //                         O = diag(e^G scale n_q) Q S^T + P U,
 //                         S = e^{G_C} S + (diag(e^{G_C - G} n_k) U)^T K.
 //                       Forming U as T_b (V - ...) never builds the 64 x 128
-//                       matrix T diag(beta e^G) K, so each tile does only work
+//                       matrix T diag(beta e^G) K, so each wave does only work
 //                       proportional to its own 16 rows.
 // Precision: the raw 16-bit q/k/v are exact MFMA operands; the L2 norms enter
 // as diagonal scalings; an f32 operand (S, T_b, Z, U) is split into a 16-bit
