@@ -236,8 +236,8 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
   __shared__ __align__(16) PrepLds u;
   __shared__ __align__(16) uint16_t Ps[CK * LDT];
   __shared__ float Rs[4][16 * 17];
-  __shared__ double Gd[CK];
-  __shared__ float nq[CK], nk[CK], bt[CK];
+  __shared__ __align__(16) double Gd[CK];
+  __shared__ __align__(16) float nq[CK], nk[CK], bt[CK], rowA[CK], rowP[CK];
   using M = MT<TIN>;
 
   const int c = blockIdx.x;
@@ -262,6 +262,14 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
   uint16_t* Ks = u.qk.Ks;
   float* Am = u.at.Am;
   float* Tm = u.at.Tm;
+
+  // gate and beta of the first v-head, in flight while Q and K are staged
+  // (wave 0 holds one token per lane; the next head's are fetched one head ahead)
+  float gv = 0.0f, bv = 0.0f;
+  if (w == 0 && lane < L) {
+    gv = a.g[(tb + lane) * a.g_rs + hk * ratio];
+    bv = a.beta[(tb + lane) * a.beta_rs + hk * ratio];
+  }
 
   // stage Q and K, rows past the sequence zeroed (all loads issued before any is used)
   {
@@ -329,15 +337,30 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
   }
   __syncthreads();  // Q and K are dead from here on: A and T take their space
 
+  // the strictly-upper 16x16 blocks of T and of P are zero for every head
+  for (int idx = tid; idx < 6 * 256; idx += 256) {
+    const int blk = idx >> 8, e = idx & 255;
+    const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+    const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+    const int i = 16 * bi + (e >> 4), j = 16 * bj + (e & 15);
+    Tm[i * LDF + j] = 0.0f;
+    Ps[i * LDT + j] = 0;
+  }
+
   for (int jh = 0; jh < ratio; ++jh) {
     const int h = hk * ratio + jh;
     char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
     if (w == 0) {
-      const float gv = lane < L ? a.g[(tb + lane) * a.g_rs + h] : 0.0f;
-      const float bv = lane < L ? a.beta[(tb + lane) * a.beta_rs + h] : 0.0f;
+      float gn = 0.0f, bn = 0.0f;  // the next head's, one head ahead
+      if (jh + 1 < ratio && lane < L) {
+        gn = a.g[(tb + lane) * a.g_rs + h + 1];
+        bn = a.beta[(tb + lane) * a.beta_rs + h + 1];
+      }
       const double gcum = wave_prefix64((double)gv, lane);
       Gd[lane] = gcum;
       bt[lane] = bv;
+      rowA[lane] = bv * nk[lane];
+      rowP[lane] = a.scale * nq[lane];
       // per-token factors
       const double gl = __shfl(gcum, L - 1, 64);
       const float eg = expf((float)gcum);
@@ -346,10 +369,13 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
       F[CK + lane] = eg * a.scale * nq[lane];
       F[2 * CK + lane] = expf((float)(gl - gcum)) * nk[lane];
       F[3 * CK + lane] = lane == 0 ? expf((float)gl) : 0.0f;
+      gv = gn;
+      bv = bn;
     }
     __syncthreads();
 
-    // A (strictly lower, scaled) and P (lower incl. diagonal, scaled)
+    // A (strictly lower, scaled) and P (lower incl. diagonal, scaled):
+    // element (i, j) = acc * row factor(i) * n_k,j * exp(G_i - G_j)
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
       const int job = w + 4 * k;
@@ -357,27 +383,25 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
       const int t = is_p ? job - 10 : job;
       const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
       const int tj = t - (ti * (ti + 1)) / 2;
+      const int i0 = 16 * ti + 4 * (lane >> 4);
+      const int j = 16 * tj + (lane & 15);
+      const double2 ga = *reinterpret_cast<const double2*>(Gd + i0);
+      const double2 gb = *reinterpret_cast<const double2*>(Gd + i0 + 2);
+      const double gi[4] = {ga.x, ga.y, gb.x, gb.y};
+      const double gj = Gd[j];
+      const float4 rf = *reinterpret_cast<const float4*>((is_p ? rowP : rowA) + i0);
+      const float rfi[4] = {rf.x, rf.y, rf.z, rf.w};
+      const float cj = nk[j];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ti + 4 * (lane >> 4) + r;
-        const int j = 16 * tj + (lane & 15);
-        const float e = expf((float)(Gd[i] - Gd[j]));
-        if (is_p) {
-          const float pv = j <= i ? acc[k][r] * a.scale * nq[i] * nk[j] * e : 0.0f;
-          Ps[i * LDT + j] = M::enc(pv);
-        } else {
-          Am[i * LDF + j] = j < i ? bt[i] * e * nk[i] * nk[j] * acc[k][r] : 0.0f;
-        }
+        const int i = i0 + r;
+        const float e = expf((float)(gi[r] - gj));
+        const float x = acc[k][r] * rfi[r] * cj * e;
+        if (is_p)
+          Ps[i * LDT + j] = M::enc(j <= i ? x : 0.0f);
+        else
+          Am[i * LDF + j] = j < i ? x : 0.0f;
       }
-    }
-    // zero the strictly-upper 16x16 blocks of T and of P
-    for (int idx = tid; idx < 6 * 256; idx += 256) {
-      const int blk = idx >> 8, e = idx & 255;
-      const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-      const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-      const int i = 16 * bi + (e >> 4), j = 16 * bj + (e & 15);
-      Tm[i * LDF + j] = 0.0f;
-      Ps[i * LDT + j] = 0;
     }
     __syncthreads();
 
