@@ -677,8 +677,16 @@ __device__ __forceinline__ u16x4 lds_read_tr(const uint16_t* p) {
 }
 
 // Packs two D tiles (tile 2j: slots 0-3, tile 2j + 1: slots 4-7) into a B
-// operand, split into 16-bit high and low parts (lo = x - hi, rounded).
+// operand, rounded to 16 bits.
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+template <int TIN>
+__device__ __forceinline__ void pack_hi(const f32x4& t0, const f32x4& t1,
+                                        typename MT<TIN>::x8& hi) {
+  const f32x8 x = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  hi = __builtin_convertvector(x, typename MT<TIN>::x8);
+}
+
+// The same split into 16-bit high and low parts (lo = x - hi, rounded).
 template <int TIN>
 __device__ __forceinline__ void pack_split(const f32x4& t0, const f32x4& t1,
                                            typename MT<TIN>::x8& hi, typename MT<TIN>::x8& lo) {
@@ -704,6 +712,11 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   WalkBuf<NW, NB>* sb = reinterpret_cast<WalkBuf<NW, NB>*>(walk_lds);
   using M = MT<TIN>;
   using x8 = typename M::x8;
+  // A 16-bit output keeps about 8 (bf16) or 11 (fp16) significant bits, so
+  // its two history terms Q S^T and P U take the high part of S and of U only;
+  // an f32 output gets the full high/low products.  The state itself always
+  // gets them.
+  constexpr bool kFullOut = TOUT == kF32;
 
   // XCD-aware mapping.  Workgroups are dealt round-robin to the 8 XCDs, each
   // with its own L2; the tiles of one v-head re-read the same per-chunk
@@ -878,7 +891,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
           X[nb][b] = M::mma(kf[jj & 1][b], sh, X[nb][b]);
           QS[nb][b] = M::mma(qf[jj & 1][b], sh, QS[nb][b]);
           X[nb][b] = M::mma(kf[jj & 1][b], sl, X[nb][b]);
-          QS[nb][b] = M::mma(qf[jj & 1][b], sl, QS[nb][b]);
+          if constexpr (kFullOut) QS[nb][b] = M::mma(qf[jj & 1][b], sl, QS[nb][b]);
         }
       }
     }
@@ -940,7 +953,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
         const f32x4& u1 = U[nb][2 * j + 1];
         const f32x4 w0 = {fw[0].x * u0[0], fw[0].y * u0[1], fw[0].z * u0[2], fw[0].w * u0[3]};
         const f32x4 w1 = {fw[1].x * u1[0], fw[1].y * u1[1], fw[1].z * u1[2], fw[1].w * u1[3]};
-        pack_split<TIN>(u0, u1, Uh[nb][j], Ul[nb][j]);
+        if constexpr (kFullOut)
+          pack_split<TIN>(u0, u1, Uh[nb][j], Ul[nb][j]);
+        else
+          pack_hi<TIN>(u0, u1, Uh[nb][j]);
         pack_split<TIN>(w0, w1, Wh[nb][j], Wl[nb][j]);
       }
     }
@@ -961,7 +977,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           o[nb] = M::mma(pf, Uh[nb][j], o[nb]);
-          o[nb] = M::mma(pf, Ul[nb][j], o[nb]);
+          if constexpr (kFullOut) o[nb] = M::mma(pf, Ul[nb][j], o[nb]);
         }
       }
 #pragma unroll
