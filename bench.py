@@ -39,11 +39,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(B, hk, hv, dk, dv, in_bytes, out_bytes, alpha_bytes=4):
+def decode_bytes(B, hk, hv, dk, dv, in_bytes, out_bytes, alpha_bytes=4, state_bytes=4):
     """Algorithmic HBM bytes of one decode step: the state is read and written
     once per live (row, v-head); q/k once per (row, q/k head); v and out once;
     alpha, beta per (row, v-head); dt_bias, ssm_a per v-head; the slot index."""
-    state = 2 * B * hv * dv * dk * 4
+    state = 2 * B * hv * dv * dk * state_bytes
     qk = 2 * B * hk * dk * in_bytes
     vo = B * hv * dv * (in_bytes + out_bytes)
     gate = B * hv * (alpha_bytes + 4) + 2 * hv * 4 + B * 4
@@ -115,6 +115,8 @@ def main():
                     help="wall-clock budget of each CPU-oracle baseline leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-state16", action="store_true",
+                    help="skip the decode leg with a bf16 state pool")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale factor for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -158,23 +160,27 @@ def main():
     torch.cuda.synchronize()
     log(f"decode setup {time.time() - t_setup:.1f}s")
 
+    def timed(step, warmup, steps):
+        """Wall seconds over `steps` launches after `warmup`, and each launch's
+        duration (ms) from HIP events recorded on the launch stream."""
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(stream)
+            step(warmup + i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, np.array([a.elapsed_time(b) for a, b in ev])
+
     def decode_step(i):
         gdn.decode(qb, kb, vb, alpha, dt_bias, ssm_a, beta, pool, subsets[i % 4],
                    scale=case.scale, out=out, stream=stream)
 
-    for i in range(args.warmup):
-        decode_step(i)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        decode_step(args.warmup + i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    wall, kernel_ms = timed(decode_step, args.warmup, args.steps)
     step_bytes = decode_bytes(B, hk, hv, dk, dv, 2, 2)
     ms_per_step = wall * 1e3 / args.steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -214,6 +220,33 @@ def main():
             "kernel_avg_us": round(kavg * 1e3, 2),
         },
     }
+
+    # ---------------- decode with the pool stored as bf16 ----------------
+    if not args.no_state16:
+        pool16 = to_dev(W.encode(case.pool, W.BF16).view(np.int16)).view(torch.bfloat16)
+
+        def decode16_step(i):
+            gdn.decode(qb, kb, vb, alpha, dt_bias, ssm_a, beta, pool16, subsets[i % 4],
+                       scale=case.scale, out=out, stream=stream)
+
+        wall16, k16 = timed(decode16_step, args.warmup, args.steps)
+        bytes16 = decode_bytes(B, hk, hv, dk, dv, 2, 2, state_bytes=2)
+        ms16 = wall16 * 1e3 / args.steps
+        kavg16 = float(k16.mean())
+        result["decode_state_bf16"] = {
+            "workload": "the same decode with the 1024-slot state pool stored as bf16 "
+                        "(widened to f32 for the step, rounded on store)",
+            "ms_per_step": round(ms16, 5),
+            "tokens_per_s": round(B / (ms16 * 1e-3), 1),
+            "algorithmic_bytes_per_step": bytes16,
+            "kernel_avg_us": round(kavg16 * 1e3, 2),
+            "achieved_GBs": round(bytes16 / (kavg16 * 1e-3) / 1e9, 1),
+            "hbm_frac": round(bytes16 / (kavg16 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "speedup_vs_f32_state": round(kavg / kavg16, 3),
+        }
+        del pool16
+        log(f"decode bf16 state: kernel avg {kavg16 * 1e3:.1f} us -> "
+            f"{bytes16 / (kavg16 * 1e-3) / 1e9:.0f} GB/s")
 
     # ---------------- prefill leg ----------------
     if not args.no_prefill:

@@ -63,9 +63,21 @@ enum {
 };
 
 enum {
-  GDN_L2NORM_QK = 1u << 0,          /* L2-normalise q and k per head, eps = l2_eps */
-  GDN_PREFILL_SEQUENTIAL = 1u << 2  /* prefill: force the token-sequential kernel */
+  GDN_L2NORM_QK = 1u << 0,           /* L2-normalise q and k per head, eps = l2_eps */
+  GDN_PREFILL_SEQUENTIAL = 1u << 2,  /* prefill: force the token-sequential kernel */
+  GDN_STATE_F16 = 1u << 3,           /* state pool stored as IEEE binary16 */
+  GDN_STATE_BF16 = 1u << 4           /* state pool stored as bfloat16 */
 };
+/*
+ * State storage dtype (flags GDN_STATE_F16 / GDN_STATE_BF16, at most one;
+ * default f32).  vllm.cpp test_ops_gdn.cpp: "CUDA gdn decode corner fallback
+ * supports indexed compressed state", the packed-decode port's note that the
+ * op reads and writes persistent state in its declared FP16/BF16/F32 storage
+ * dtype, and "gdn indexed state I/O: dtype conversion".  A 16-bit state is
+ * widened to f32 when read, every step is computed in f32, and the new state
+ * is rounded to nearest-even when written back; slots that are not written
+ * keep their bytes.
+ */
 
 /*
  * gdn_gate -- g[r, h] = softplus(alpha[r, h] + dt_bias[h]) * ssm_a[h].
@@ -96,21 +108,23 @@ int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_
  *   alpha      [batch, hv] in alpha_dt, row stride alpha_row_stride.
  *   dt_bias, ssm_a  [hv] f32.   beta [batch, hv] f32 (post-sigmoid),
  *              row stride beta_row_stride.
- *   state_pool [num_slots, hv, dv, dk] f32, read and written in place.
+ *   state_pool [num_slots, hv, dv, dk] f32 (or binary16 / bfloat16 with
+ *              GDN_STATE_F16 / GDN_STATE_BF16), read and written in place.
  *   state_idx  [batch] int32: row b uses slot state_idx[b].  A negative
  *              index marks a padded row: its output row is written as zeros
  *              and no state is touched.  An index >= num_slots is a caller
  *              error; such a row's output is written as NaN and no state is
  *              touched.  Two rows naming the same slot race (undefined).
  *   scale      > 0 and finite (usually 1/sqrt(dk)).
- *   flags      GDN_L2NORM_QK to normalise q and k with l2_eps.
+ *   flags      GDN_L2NORM_QK to normalise q and k with l2_eps; at most one
+ *              of GDN_STATE_F16, GDN_STATE_BF16.
  * batch == 0 enqueues nothing and returns GDN_OK.
  */
 int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
                gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
                int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-               const float* beta, int64_t beta_row_stride, float* state_pool,
+               const float* beta, int64_t beta_row_stride, void* state_pool,
                int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
                uint32_t flags, hipStream_t stream);
@@ -140,7 +154,8 @@ size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs,
  *   q, k, v      as for gdn_decode with one row per token.
  *   g            [total_tokens, hv] f32 (from gdn_gate), row stride g_row_stride.
  *   beta         [total_tokens, hv] f32, row stride beta_row_stride.
- *   state_pool   [num_slots, hv, dv, dk] f32.  Sequence s starts from
+ *   state_pool   [num_slots, hv, dv, dk] f32 (binary16 / bfloat16 with
+ *                GDN_STATE_F16 / GDN_STATE_BF16).  Sequence s starts from
  *                pool[slot] (slot = state_idx[s], or s when state_idx is
  *                NULL) when has_initial_state[s] != 0 (NULL: all nonzero),
  *                else from zeros without reading the slot, and its final
@@ -153,14 +168,15 @@ size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs,
  *                gdn_prefill_varlen_workspace_size(...) bytes (may be NULL
  *                when that size is 0).
  *   flags        GDN_L2NORM_QK; GDN_PREFILL_SEQUENTIAL forces the
- *                token-sequential kernel instead of the chunked one.
+ *                token-sequential kernel instead of the chunked one; at most
+ *                one of GDN_STATE_F16, GDN_STATE_BF16.
  * num_seqs == 0 enqueues nothing and returns GDN_OK.
  */
 int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k,
                        const void* v, gdn_dtype in_dt, int64_t q_row_stride,
                        int64_t k_row_stride, int64_t v_row_stride, const float* g,
                        int64_t g_row_stride, const float* beta, int64_t beta_row_stride,
-                       float* state_pool, int64_t num_slots, const int32_t* state_idx,
+                       void* state_pool, int64_t num_slots, const int32_t* state_idx,
                        const int8_t* has_initial_state, const int32_t* cu_seqlens,
                        int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
                        int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,

@@ -73,6 +73,13 @@ int check_scale(const char* op, float scale, float eps) {
   return GDN_OK;
 }
 
+// storage dtype of the state pool from the flags, or -1 when both are set
+int state_dtype(uint32_t flags) {
+  const bool f16 = (flags & GDN_STATE_F16) != 0, bf16 = (flags & GDN_STATE_BF16) != 0;
+  if (f16 && bf16) return -1;
+  return f16 ? GDN_F16 : bf16 ? GDN_BF16 : GDN_F32;
+}
+
 int hip_status(const char* op, hipError_t e) {
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", op, hipGetErrorString(e));
   return ok();
@@ -102,7 +109,7 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
                gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
                int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-               const float* beta, int64_t beta_row_stride, float* state_pool,
+               const float* beta, int64_t beta_row_stride, void* state_pool,
                int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
                hipStream_t stream) {
@@ -115,7 +122,10 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
     return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
   if (out_dt != GDN_F32 && out_dt != in_dt)
     return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
-  if (flags & ~(uint32_t)GDN_L2NORM_QK) return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_STATE_F16 | GDN_STATE_BF16))
+    return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  const int state_dt = state_dtype(flags);
+  if (state_dt < 0) return fail(GDN_ERR_DTYPE, "%s: GDN_STATE_F16 and GDN_STATE_BF16 both set", op);
   if (batch == 0) return ok();
   if (!out || !q || !k || !v || !alpha || !dt_bias || !ssm_a || !beta || !state_pool ||
       !state_idx)
@@ -131,7 +141,8 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
   a.qk_vec = qk_vector_ok(q, k, in_dt, q_row_stride, k_row_stride) ? 1 : 0;
   a.alpha = alpha; a.alpha_dt = alpha_dt; a.alpha_rs = alpha_row_stride;
   a.dt_bias = dt_bias; a.ssm_a = ssm_a; a.beta = beta; a.beta_rs = beta_row_stride;
-  a.pool = state_pool; a.num_slots = num_slots; a.idx = state_idx; a.batch = batch;
+  a.pool = state_pool; a.state_dt = state_dt; a.num_slots = num_slots; a.idx = state_idx;
+  a.batch = batch;
   a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
   a.scale = scale; a.l2_eps = l2_eps; a.l2norm = (flags & GDN_L2NORM_QK) ? 1 : 0;
   return hip_status(op, gdn::launch_decode(a, stream));
@@ -154,7 +165,7 @@ size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs,
 int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
                        gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                        int64_t v_row_stride, const float* g, int64_t g_row_stride,
-                       const float* beta, int64_t beta_row_stride, float* state_pool,
+                       const float* beta, int64_t beta_row_stride, void* state_pool,
                        int64_t num_slots, const int32_t* state_idx,
                        const int8_t* has_initial_state, const int32_t* cu_seqlens,
                        int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
@@ -169,8 +180,10 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
   if (!valid_dt(in_dt) || !valid_dt(out_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
   if (out_dt != GDN_F32 && out_dt != in_dt)
     return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
-  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_PREFILL_SEQUENTIAL))
+  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_PREFILL_SEQUENTIAL | GDN_STATE_F16 | GDN_STATE_BF16))
     return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  const int state_dt = state_dtype(flags);
+  if (state_dt < 0) return fail(GDN_ERR_DTYPE, "%s: GDN_STATE_F16 and GDN_STATE_BF16 both set", op);
   if (num_seqs == 0) return ok();
   if (!state_pool || !cu_seqlens) return fail(GDN_ERR_ARG, "%s: null pointer", op);
   if (!state_idx && num_seqs > num_slots)
@@ -188,7 +201,7 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
   a.q_rs = q_row_stride; a.k_rs = k_row_stride; a.v_rs = v_row_stride;
   a.qk_vec = qk_vector_ok(q, k, in_dt, q_row_stride, k_row_stride) ? 1 : 0;
   a.g = g; a.g_rs = g_row_stride; a.beta = beta; a.beta_rs = beta_row_stride;
-  a.pool = state_pool; a.num_slots = num_slots; a.idx = state_idx;
+  a.pool = state_pool; a.state_dt = state_dt; a.num_slots = num_slots; a.idx = state_idx;
   a.has_init = has_initial_state; a.cu = cu_seqlens; a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
   a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;

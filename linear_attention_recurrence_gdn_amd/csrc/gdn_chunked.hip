@@ -765,7 +765,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     return;
   }
   const bool init = a.has_init ? a.has_init[s] != 0 : true;
-  float* Sg = a.pool + ((slot * a.hv + h) * a.dv + dvw + cl) * DKC;
+  const int64_t Sg = ((slot * a.hv + h) * a.dv + dvw + cl) * DKC;  // element offset in the pool
   using Ot = typename OutT<TOUT>::type;
   Ot* out = static_cast<Ot*>(a.out) + (int64_t)h * a.dv + dvw;  // this wave's column 0
 
@@ -776,7 +776,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     const bool ld = init && dvw + 16 * nb < a.dv;
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const float4 v = ld ? *reinterpret_cast<const float4*>(Sg + 16 * nb * DKC + blk_row(kb, 4 * g))
+      const float4 v = ld ? state_load4_rt(a.state_dt, a.pool, Sg + 16 * nb * DKC + blk_row(kb, 4 * g))
                           : make_float4(0.f, 0.f, 0.f, 0.f);
       St[nb][kb] = (f32x4){v.x, v.y, v.z, v.w};
     }
@@ -787,8 +787,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       if (dvw + 16 * nb < a.dv) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
-          *reinterpret_cast<float4*>(Sg + 16 * nb * DKC + blk_row(kb, 4 * g)) =
-              make_float4(St[nb][kb][0], St[nb][kb][1], St[nb][kb][2], St[nb][kb][3]);
+          state_store4_rt(a.state_dt, a.pool, Sg + 16 * nb * DKC + blk_row(kb, 4 * g),
+                          make_float4(St[nb][kb][0], St[nb][kb][1], St[nb][kb][2], St[nb][kb][3]));
       }
     }
   };

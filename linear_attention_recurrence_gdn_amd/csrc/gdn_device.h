@@ -85,6 +85,59 @@ __device__ __forceinline__ void state_store(float* p, float4 x) {
   }
 }
 
+// Four consecutive state elements in storage dtype TS (f32, binary16 or
+// bfloat16), widened to f32 on load and rounded to nearest-even on store.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int TS, bool NT>
+__device__ __forceinline__ float4 state_load4(const void* base, int64_t off) {
+  if constexpr (TS == kF32) {
+    return state_load<NT>(static_cast<const float*>(base) + off);
+  } else {
+    const u32x2_t* p = reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(base) + off);
+    u32x2_t r;
+    if constexpr (NT) r = __builtin_nontemporal_load(p);
+    else r = *p;
+    const uint32_t lo = r[0], hi = r[1];
+    if constexpr (TS == kBF16)
+      return make_float4(bf16_to_f32(lo & 0xffffu), bf16_to_f32(lo >> 16),
+                         bf16_to_f32(hi & 0xffffu), bf16_to_f32(hi >> 16));
+    else
+      return make_float4(f16_to_f32(lo & 0xffffu), f16_to_f32(lo >> 16),
+                         f16_to_f32(hi & 0xffffu), f16_to_f32(hi >> 16));
+  }
+}
+
+template <int TS, bool NT>
+__device__ __forceinline__ void state_store4(void* base, int64_t off, float4 x) {
+  if constexpr (TS == kF32) {
+    state_store<NT>(static_cast<float*>(base) + off, x);
+  } else {
+    uint32_t e[4];
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = TS == kBF16 ? f32_to_bf16(xs[i]) : f32_to_f16(xs[i]);
+    u32x2_t r = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+    u32x2_t* p = reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(base) + off);
+    if constexpr (NT) __builtin_nontemporal_store(r, p);
+    else *p = r;
+  }
+}
+
+// The same with the storage dtype known only at run time (state loaded or
+// stored once per kernel, outside any loop).
+__device__ __forceinline__ float4 state_load4_rt(int ts, const void* base, int64_t off) {
+  if (ts == kBF16) return state_load4<kBF16, false>(base, off);
+  if (ts == kF16) return state_load4<kF16, false>(base, off);
+  return state_load4<kF32, false>(base, off);
+}
+
+__device__ __forceinline__ void state_store4_rt(int ts, void* base, int64_t off, float4 x) {
+  if (ts == kBF16) state_store4<kBF16, false>(base, off, x);
+  else if (ts == kF16) state_store4<kF16, false>(base, off, x);
+  else state_store4<kF32, false>(base, off, x);
+}
+
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }

@@ -35,7 +35,8 @@ struct DecodeArgs {
   const float* ssm_a;
   const float* beta;
   int64_t beta_rs;
-  float* pool;
+  void* pool;     // [slots, hv, dv, dk] in state_dt
+  int state_dt;   // kF32, kF16 or kBF16 storage; the step is computed in f32
   int64_t num_slots;
   const int32_t* idx;
   int64_t batch;
@@ -57,7 +58,8 @@ struct PrefillArgs {
   int64_t g_rs;
   const float* beta;
   int64_t beta_rs;
-  float* pool;
+  void* pool;     // [slots, hv, dv, dk] in state_dt
+  int state_dt;
   int64_t num_slots;
   const int32_t* idx;       // may be null: slot s
   const int8_t* has_init;   // may be null: all 1

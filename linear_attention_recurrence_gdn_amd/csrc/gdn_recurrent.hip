@@ -115,7 +115,7 @@ __device__ __forceinline__ float tile_step(float4 (&s)[NL], float4 q4, float4 k4
 // waves of one head are neighbours.  All indices are wave-uniform (scalar
 // registers); the q/k/v/gate loads are issued before the slot index is
 // waited on, and the whole state tile is requested before any arithmetic.
-template <int DK, int NL, int TIN, int TAL, bool NT>
+template <int DK, int NL, int TIN, int TAL, int TS, bool NT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total_waves,
                                                      int tiles_per_head) {
   using T = Tile<DK, NL>;
@@ -151,12 +151,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total
     return;
   }
 
-  float* S = a.pool + (((int64_t)slot * a.hv + h) * a.dv) * DK + col;
+  // element offset of this lane's columns in the (slot, head) state
+  const int64_t S = (((int64_t)slot * a.hv + h) * a.dv) * DK + col;
   float4 s[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int row = min(r0 + i * T::RPI + sub, a.dv - 1);
-    s[i] = state_load<NT>(S + (int64_t)row * DK);
+    s[i] = state_load4<TS, NT>(a.pool, S + (int64_t)row * DK);
   }
 
   float4 q4 = raw_to_f32<TIN>(qr);
@@ -173,30 +174,38 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int row = r0 + i * T::RPI + sub;
-    if (row < a.dv) state_store<NT>(S + (int64_t)row * DK, s[i]);
+    if (row < a.dv) state_store4<TS, NT>(a.pool, S + (int64_t)row * DK, s[i]);
   }
 }
 
-template <int DK, int NL, int TIN, int TAL, bool NT>
+template <int DK, int NL, int TIN, int TAL, int TS, bool NT>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   using T = Tile<DK, NL>;
   const int tiles = (a.dv + T::BV - 1) / T::BV;
   const int64_t waves = a.batch * a.hv * tiles;
   if (waves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((decode_kernel<DK, NL, TIN, TAL, NT>), dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL((decode_kernel<DK, NL, TIN, TAL, TS, NT>), dim3((unsigned)blocks), dim3(256), 0,
                      stream, a, waves, tiles);
   return hipGetLastError();
 }
 
-template <int DK, int NL>
-static hipError_t launch_decode_dk(const DecodeArgs& a, hipStream_t stream) {
+template <int DK, int NL, int TS>
+static hipError_t launch_decode_ts(const DecodeArgs& a, hipStream_t stream) {
 #define GDN_DEC(TI, TA) \
-  if (a.in_dt == TI && a.alpha_dt == TA) return launch_decode_t<DK, NL, TI, TA, true>(a, stream);
+  if (a.in_dt == TI && a.alpha_dt == TA) return launch_decode_t<DK, NL, TI, TA, TS, true>(a, stream);
   GDN_DEC(kBF16, kF32) GDN_DEC(kF16, kF32) GDN_DEC(kF32, kF32)
   GDN_DEC(kBF16, kBF16) GDN_DEC(kF16, kBF16) GDN_DEC(kF32, kBF16)
   GDN_DEC(kBF16, kF16) GDN_DEC(kF16, kF16) GDN_DEC(kF32, kF16)
 #undef GDN_DEC
+  return hipErrorInvalidValue;
+}
+
+template <int DK, int NL>
+static hipError_t launch_decode_dk(const DecodeArgs& a, hipStream_t stream) {
+  if (a.state_dt == kF32) return launch_decode_ts<DK, NL, kF32>(a, stream);
+  if (a.state_dt == kBF16) return launch_decode_ts<DK, NL, kBF16>(a, stream);
+  if (a.state_dt == kF16) return launch_decode_ts<DK, NL, kF16>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -274,12 +283,12 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(PrefillArgs a, int64_t
   for (int u = 0; u < PF; ++u)
     cur[u] = load_token<DK, TIN>(a, min(t0 + u, t1 - 1 < t0 ? t0 : t1 - 1), hk, h, col, vrow);
 
-  float* S = a.pool + ((slot * a.hv + h) * a.dv) * DK + col;
+  const int64_t S = ((slot * a.hv + h) * a.dv) * DK + col;  // element offset in the pool
   float4 s[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int row = min(r0 + i * T::RPI + sub, a.dv - 1);
-    s[i] = init ? *reinterpret_cast<const float4*>(S + (int64_t)row * DK)
+    s[i] = init ? state_load4_rt(a.state_dt, a.pool, S + (int64_t)row * DK)
                 : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
@@ -309,7 +318,7 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(PrefillArgs a, int64_t
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int row = r0 + i * T::RPI + sub;
-    if (row < a.dv) *reinterpret_cast<float4*>(S + (int64_t)row * DK) = s[i];
+    if (row < a.dv) state_store4_rt(a.state_dt, a.pool, S + (int64_t)row * DK, s[i]);
   }
 }
 

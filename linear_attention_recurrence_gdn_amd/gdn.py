@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 GDN_L2NORM_QK = 1 << 0
 GDN_PREFILL_SEQUENTIAL = 1 << 2
+GDN_STATE_F16 = 1 << 3
+GDN_STATE_BF16 = 1 << 4
+_STATE_FLAGS = {torch.float32: 0, torch.float16: GDN_STATE_F16, torch.bfloat16: GDN_STATE_BF16}
 
 _TORCH_DT = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
 
@@ -105,6 +108,13 @@ def _rows2(t: torch.Tensor, name: str, width: int) -> int:
     return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), width)
 
 
+def _state_flags(pool: torch.Tensor) -> int:
+    try:
+        return _STATE_FLAGS[pool.dtype]
+    except KeyError:
+        raise GdnError(-2, f"state_pool dtype {pool.dtype} not supported") from None
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -133,7 +143,9 @@ def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale
 
     q, k: [B, Hk, Dk]; v: [B, Hv, Dv] (rows may be strided, e.g. views into one
     packed q|k|v buffer); alpha [B, Hv]; dt_bias, ssm_a [Hv] f32; beta [B, Hv] f32;
-    state_pool [slots, Hv, Dv, Dk] f32 contiguous; state_idx [B] int32."""
+    state_pool [slots, Hv, Dv, Dk] contiguous, f32 or 16-bit storage (float16 /
+    bfloat16: widened to f32 for the step, the new state rounded on store);
+    state_idx [B] int32."""
     lib = load_library()
     if state_pool.dim() != 4 or not state_pool.is_contiguous():
         raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
@@ -154,12 +166,12 @@ def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale
         out = torch.empty((B, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
     if not out.is_contiguous() or tuple(out.shape) != (B, hv, dv):
         raise GdnError(-3, "out: need contiguous [B, Hv, Dv]")
-    flags = GDN_L2NORM_QK if l2norm else 0
+    flags = (GDN_L2NORM_QK if l2norm else 0) | _state_flags(state_pool)
     _check(lib.gdn_decode(
         _dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
         q_rs, k_rs, v_rs, _dev(alpha, "alpha"), _dt(alpha), a_rs,
         _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
-        _dev(beta, "beta", torch.float32), b_rs, _dev(state_pool, "state_pool", torch.float32),
+        _dev(beta, "beta", torch.float32), b_rs, _dev(state_pool, "state_pool"),
         slots, _dev(state_idx, "state_idx", torch.int32), B, hk, hv, dk, dv, float(scale),
         float(l2_eps), flags, _stream(stream)))
     return out
@@ -182,7 +194,8 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
     """Varlen prefill over sequences packed back to back (cu_seqlens [N+1] int32).
 
     q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; g, beta: [T, Hv] f32; state_pool
-    [slots, Hv, Dv, Dk] f32 (initial states read, final states written)."""
+    [slots, Hv, Dv, Dk] f32, float16 or bfloat16 (initial states read, final
+    states written)."""
     lib = load_library()
     if state_pool.dim() != 4 or not state_pool.is_contiguous():
         raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
@@ -201,7 +214,8 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
         out = torch.empty((T, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
     if not out.is_contiguous() or tuple(out.shape) != (T, hv, dv):
         raise GdnError(-3, "out: need contiguous [T, Hv, Dv]")
-    flags = (GDN_L2NORM_QK if l2norm else 0) | (GDN_PREFILL_SEQUENTIAL if sequential else 0)
+    flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_PREFILL_SEQUENTIAL if sequential else 0) |
+             _state_flags(state_pool))
     ws_need = lib.gdn_prefill_varlen_workspace_size(T, N, hk, hv, dk, dv, _dt(q), flags)
     if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
@@ -210,7 +224,7 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
     _check(lib.gdn_prefill_varlen(
         _dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
         q_rs, k_rs, v_rs, _dev(g, "g", torch.float32), g_rs, _dev(beta, "beta", torch.float32),
-        b_rs, _dev(state_pool, "state_pool", torch.float32), slots,
+        b_rs, _dev(state_pool, "state_pool"), slots,
         _dev(state_idx, "state_idx", torch.int32),
         _dev(has_initial_state, "has_initial_state", torch.int8),
         _dev(cu_seqlens, "cu_seqlens", torch.int32), N, T, hk, hv, dk, dv, float(scale),

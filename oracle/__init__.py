@@ -55,11 +55,12 @@ def _load():
         lib.oracle_l2norm.argtypes = [vp, vp, i64, i64, dbl]
         lib.oracle_decode.restype = i32
         lib.oracle_decode.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, i32, i64, i64, i64,
-                                      vp, vp, i64, vp, i64, vp, dbl, dbl, i32, vp, vp, vp]
+                                      vp, vp, i64, vp, i32, i64, vp, dbl, dbl, i32, vp, vp,
+                                      vp]
         lib.oracle_prefill_varlen.restype = i32
         lib.oracle_prefill_varlen.argtypes = [i64, vp, i64, i64, i64, i64, vp, vp, vp, i32,
-                                              i64, i64, i64, vp, vp, i64, vp, i64, vp, vp,
-                                              dbl, dbl, i32, vp, vp, vp]
+                                              i64, i64, i64, vp, vp, i64, vp, i32, i64, vp,
+                                              vp, dbl, dbl, i32, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -75,6 +76,14 @@ def _p(a: Optional[np.ndarray]):
 def _need(a: np.ndarray, dtype) -> np.ndarray:
     assert a.dtype == dtype and a.flags.c_contiguous, (a.dtype, dtype)
     return a
+
+
+def _pool(pool: np.ndarray, state_dt: int) -> np.ndarray:
+    """The state pool as stored: float32 for F32, raw uint16 bits for F16/BF16."""
+    if state_dt == F32:
+        return _need(pool, np.float32)
+    assert state_dt in (F16, BF16), state_dt
+    return _need(pool, np.uint16)
 
 
 def decode_value(buf: np.ndarray, dt: int, off: int) -> float:
@@ -113,14 +122,15 @@ def gate(alpha: np.ndarray, alpha_dt: int, dt_bias: np.ndarray, ssm_a: np.ndarra
 
 def decode(*, batch, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs, v, v_off, v_rs, in_dt,
            g, beta, pool, idx, scale, l2_eps=1e-6, l2norm=True, head_mask=None,
-           state_out=None):
+           state_out=None, state_dt=F32):
     """One decode step.  q/k/v are storage buffers addressed as
-    buf.flat[off + row*rs + head*D + d].  Returns (out [B,hv,dv] f64,
-    state_out [B,hv,dv,dk] f64 = updated states of the live rows)."""
+    buf.flat[off + row*rs + head*D + d].  The pool [slots,hv,dv,dk] is stored
+    as state_dt (float32, or uint16 bits of f16/bf16).  Returns (out [B,hv,dv]
+    f64, state_out [B,hv,dv,dk] f64 = updated states of the live rows)."""
     lib = _load()
     g = np.ascontiguousarray(g, dtype=np.float64)
     beta = _need(beta, np.float32)
-    pool = _need(pool, np.float32)
+    pool = _pool(pool, state_dt)
     idx = _need(np.asarray(idx, dtype=np.int32), np.int32)
     out = np.zeros((batch, hv, dv), dtype=np.float64)
     if state_out is None:
@@ -130,7 +140,8 @@ def decode(*, batch, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs, v, v_off, v
     rc = lib.oracle_decode(batch, hk, hv, dk, dv,
                            q.ctypes.data + q_off * es, k.ctypes.data + k_off * es,
                            v.ctypes.data + v_off * es, in_dt, q_rs, k_rs, v_rs,
-                           _p(g), _p(beta), beta.shape[1], _p(pool), pool.shape[0], _p(idx),
+                           _p(g), _p(beta), beta.shape[1], _p(pool), int(state_dt),
+                           pool.shape[0], _p(idx),
                            float(scale), float(l2_eps), int(bool(l2norm)), _p(hm),
                            _p(out), _p(state_out))
     if rc:
@@ -140,15 +151,16 @@ def decode(*, batch, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs, v, v_off, v
 
 def prefill_varlen(*, cu_seqlens, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs, v, v_off,
                    v_rs, in_dt, g, beta, pool, idx, has_init, scale, l2_eps=1e-6,
-                   l2norm=True, head_mask=None):
-    """Varlen prefill.  Returns (out [T,hv,dv] f64, final states [N,hv,dv,dk] f64)."""
+                   l2norm=True, head_mask=None, state_dt=F32):
+    """Varlen prefill.  The pool is stored as state_dt (as for decode).
+    Returns (out [T,hv,dv] f64, final states [N,hv,dv,dk] f64)."""
     lib = _load()
     cu = _need(np.asarray(cu_seqlens, dtype=np.int32), np.int32)
     n = cu.shape[0] - 1
     t = int(cu[-1])
     g = np.ascontiguousarray(g, dtype=np.float64)
     beta = _need(beta, np.float32)
-    pool = _need(pool, np.float32)
+    pool = _pool(pool, state_dt)
     idx_a = None if idx is None else _need(np.asarray(idx, dtype=np.int32), np.int32)
     hi = None if has_init is None else _need(np.asarray(has_init, dtype=np.int8), np.int8)
     hm = None if head_mask is None else np.ascontiguousarray(head_mask, dtype=np.uint8)
@@ -158,7 +170,8 @@ def prefill_varlen(*, cu_seqlens, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs
     rc = lib.oracle_prefill_varlen(n, _p(cu), hk, hv, dk, dv,
                                    q.ctypes.data + q_off * es, k.ctypes.data + k_off * es,
                                    v.ctypes.data + v_off * es, in_dt, q_rs, k_rs, v_rs,
-                                   _p(g), _p(beta), beta.shape[1], _p(pool), pool.shape[0],
+                                   _p(g), _p(beta), beta.shape[1], _p(pool), int(state_dt),
+                                   pool.shape[0],
                                    _p(idx_a), _p(hi), float(scale), float(l2_eps),
                                    int(bool(l2norm)), _p(hm), _p(out), _p(st))
     if rc:
@@ -167,9 +180,10 @@ def prefill_varlen(*, cu_seqlens, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs
 
 
 # ---- convenience wrappers over the seeded workload cases ------------------
-def decode_case(case, head_mask=None, rows=None):
+def decode_case(case, head_mask=None, rows=None, pool=None, state_dt=F32):
     """Oracle for a workloads.DecodeCase: gate then one recurrence step.
-    `rows` (optional index array) restricts the batch to those rows."""
+    `rows` (optional index array) restricts the batch to those rows; `pool`
+    (stored as state_dt) replaces the case's f32 pool when given."""
     qv, kv, vv = case.q, case.k, case.v
     alpha, beta, idx = case.alpha, case.beta, case.idx
     qbuf, kbuf, vbuf = qv.buf, kv.buf, vv.buf
@@ -189,17 +203,20 @@ def decode_case(case, head_mask=None, rows=None):
                   q=qbuf, q_off=qv.offset, q_rs=qv.row_stride,
                   k=kbuf, k_off=kv.offset, k_rs=kv.row_stride,
                   v=vbuf, v_off=vv.offset, v_rs=vv.row_stride, in_dt=case.in_dtype,
-                  g=g, beta=beta, pool=case.pool, idx=idx, scale=case.scale,
-                  l2_eps=case.l2_eps, l2norm=case.l2norm, head_mask=head_mask)
+                  g=g, beta=beta, pool=case.pool if pool is None else pool, idx=idx,
+                  scale=case.scale, l2_eps=case.l2_eps, l2norm=case.l2norm,
+                  head_mask=head_mask, state_dt=state_dt)
 
 
-def prefill_case(case, head_mask=None):
-    """Oracle for a workloads.PrefillCase: gate then the varlen recurrence."""
+def prefill_case(case, head_mask=None, pool=None, state_dt=F32):
+    """Oracle for a workloads.PrefillCase: gate then the varlen recurrence;
+    `pool` (stored as state_dt) replaces the case's f32 pool when given."""
     g = gate(case.alpha, F32, case.dt_bias, case.ssm_a)
     return prefill_varlen(cu_seqlens=case.cu_seqlens, hk=case.hk, hv=case.hv, dk=case.dk,
                           dv=case.dv, q=case.q.buf, q_off=case.q.offset, q_rs=case.q.row_stride,
                           k=case.k.buf, k_off=case.k.offset, k_rs=case.k.row_stride,
                           v=case.v.buf, v_off=case.v.offset, v_rs=case.v.row_stride,
-                          in_dt=case.in_dtype, g=g, beta=case.beta, pool=case.pool,
-                          idx=case.idx, has_init=case.has_init, scale=case.scale,
-                          l2_eps=case.l2_eps, l2norm=case.l2norm, head_mask=head_mask)
+                          in_dt=case.in_dtype, g=g, beta=case.beta,
+                          pool=case.pool if pool is None else pool, idx=case.idx,
+                          has_init=case.has_init, scale=case.scale, l2_eps=case.l2_eps,
+                          l2norm=case.l2norm, head_mask=head_mask, state_dt=state_dt)

@@ -204,7 +204,8 @@ static int check_slots(const int32_t* idx, int64_t n, int64_t num_slots, int all
 
 /* ------------------------------------------------------------------------
  * Decode: one token for each of `batch` sequences.  Sequence b's state is
- * pool[idx[b]] ([hv][dv][dk] f32, read only here); idx[b] < 0 marks a padded
+ * pool[idx[b]] ([hv][dv][dk], read only here, stored as f32, f16 or bf16 per
+ * state_dt and widened exactly to f64); idx[b] < 0 marks a padded
  * row whose output is zero and whose state is not touched.
  * g is [batch, hv] (from oracle_gate), beta is [batch, hv] f32 with a row stride.
  * Outputs: out [batch, hv, dv] f64; state_out [batch, hv, dv, dk] f64 holding
@@ -215,11 +216,13 @@ static int check_slots(const int32_t* idx, int64_t n, int64_t num_slots, int all
 int oracle_decode(int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
                   const void* q, const void* k, const void* v, int in_dt, int64_t q_rs,
                   int64_t k_rs, int64_t v_rs, const double* g, const float* beta,
-                  int64_t beta_rs, const float* pool, int64_t num_slots, const int32_t* idx,
-                  double scale, double l2_eps, int l2norm, const uint8_t* head_mask,
+                  int64_t beta_rs, const void* pool, int state_dt, int64_t num_slots,
+                  const int32_t* idx, double scale, double l2_eps, int l2norm,
+                  const uint8_t* head_mask,
                   double* out, double* state_out) {
   int rc = check_common(hk, hv, dk, dv, scale);
   if (rc) return rc;
+  if (state_dt != OR_F32 && state_dt != OR_F16 && state_dt != OR_BF16) return OR_ERR_ARG;
   rc = check_slots(idx, batch, num_slots, 1);
   if (rc) return rc;
   const int64_t ratio = hv / hk;
@@ -242,8 +245,8 @@ int oracle_decode(int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
       load_qkv(q, k, v, in_dt, q_rs, k_rs, v_rs, b, hkh, h, dk, dv, l2norm, l2_eps, scale, qd,
                kd, vd);
       double* S = state_out + (b * hv + h) * head_elems;
-      const float* S0 = pool + ((int64_t)slot * hv + h) * head_elems;
-      for (int64_t e = 0; e < head_elems; ++e) S[e] = (double)S0[e];
+      const int64_t s0 = ((int64_t)slot * hv + h) * head_elems;
+      for (int64_t e = 0; e < head_elems; ++e) S[e] = load_elem(pool, state_dt, s0 + e);
       recurrence_step(S, dv, dk, kd, qd, vd, g[b * hv + h], (double)beta[b * beta_rs + h], o,
                       work);
     }
@@ -265,11 +268,13 @@ int oracle_prefill_varlen(int64_t num_seqs, const int32_t* cu, int64_t hk, int64
                           int64_t dk, int64_t dv, const void* q, const void* k, const void* v,
                           int in_dt, int64_t q_rs, int64_t k_rs, int64_t v_rs,
                           const double* g, const float* beta, int64_t beta_rs,
-                          const float* pool, int64_t num_slots, const int32_t* idx,
+                          const void* pool, int state_dt, int64_t num_slots,
+                          const int32_t* idx,
                           const int8_t* has_init, double scale, double l2_eps, int l2norm,
                           const uint8_t* head_mask, double* out, double* state_out) {
   int rc = check_common(hk, hv, dk, dv, scale);
   if (rc) return rc;
+  if (state_dt != OR_F32 && state_dt != OR_F16 && state_dt != OR_BF16) return OR_ERR_ARG;
   if (num_seqs < 0 || cu[0] != 0) return OR_ERR_SHAPE;
   for (int64_t s = 0; s < num_seqs; ++s)
     if (cu[s + 1] < cu[s]) return OR_ERR_SHAPE;
@@ -292,8 +297,9 @@ int oracle_prefill_varlen(int64_t num_seqs, const int32_t* cu, int64_t hk, int64
     for (int64_t h = 0; h < hv; ++h) {
       if (head_mask && !head_mask[h]) continue;
       double* S = state_out + (s * hv + h) * head_elems;
-      const float* S0 = pool + (slot * hv + h) * head_elems;
-      for (int64_t e = 0; e < head_elems; ++e) S[e] = init ? (double)S0[e] : 0.0;
+      const int64_t s0 = (slot * hv + h) * head_elems;
+      for (int64_t e = 0; e < head_elems; ++e)
+        S[e] = init ? load_elem(pool, state_dt, s0 + e) : 0.0;
       const int64_t hkh = h / ratio;
       for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
         load_qkv(q, k, v, in_dt, q_rs, k_rs, v_rs, t, hkh, h, dk, dv, l2norm, l2_eps, scale,
