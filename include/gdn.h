@@ -21,11 +21,12 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
- *     the return value of gdn_last_error().  The library allocates nothing,
- *     frees nothing and never synchronises: each call enqueues its kernels on
- *     `stream` and returns; results are visible after the stream completes.
- *     No call reads device data on the host, so calls can be captured into a
- *     HIP graph.
+ *     the return value of gdn_last_error().  The library allocates no device
+ *     memory, frees nothing and never synchronises: each call enqueues its
+ *     kernels on `stream` and returns; results are visible after the stream
+ *     completes.  No call reads device data on the host, so calls can be
+ *     captured into a HIP graph -- except with GDN_CHECK_SLOTS, which copies
+ *     the slot table (and cu_seqlens) to the host and waits for the stream.
  *   - Sizes and strides are in ELEMENTS of the named dtype.  A "row" is one
  *     token (prefill) or one sequence (decode).  Within a row, head h of a
  *     [rows, H, D] operand starts at element h*D and is contiguous.
@@ -58,17 +59,28 @@ enum {
   GDN_ERR_ARG = -1,    /* bad scalar argument, null pointer or misalignment */
   GDN_ERR_DTYPE = -2,  /* unsupported dtype or dtype combination */
   GDN_ERR_SHAPE = -3,  /* Hv not a multiple of Hk, unsupported Dk, stride < width */
-  GDN_ERR_SLOT = -4,   /* reserved for slot validation done by the caller */
+  GDN_ERR_SLOT = -4,   /* GDN_CHECK_SLOTS found a duplicate or out-of-range slot */
   GDN_ERR_HIP = -5     /* a kernel launch failed */
 };
 
 enum {
   GDN_L2NORM_QK = 1u << 0,           /* L2-normalise q and k per head, eps = l2_eps */
+  GDN_CHECK_SLOTS = 1u << 1,         /* check the slot table first (reads it; waits) */
   GDN_PREFILL_SEQUENTIAL = 1u << 2,  /* prefill: force the token-sequential kernel */
   GDN_STATE_F16 = 1u << 3,           /* state pool stored as IEEE binary16 */
   GDN_STATE_BF16 = 1u << 4           /* state pool stored as bfloat16 */
 };
 /*
+ * Slot check (flag GDN_CHECK_SLOTS).  vllm.cpp test_ops_gdn.cpp, "gdn packed
+ * decode rejects duplicate and out-of-range live slots".  Before enqueueing
+ * anything the call copies state_idx (prefill: also cu_seqlens) to the host,
+ * in order after the work already on `stream`, waits for it, and returns
+ * GDN_ERR_SLOT when a live slot is >= num_slots or named twice (prefill: any
+ * negative slot too) and GDN_ERR_SHAPE when cu_seqlens does not run
+ * non-decreasing from 0 to total_tokens.  It returns GDN_ERR_ARG while the
+ * stream is being captured.  Without the flag the slot table is trusted
+ * (see each entry point for what a bad entry does).
+ *
  * State storage dtype (flags GDN_STATE_F16 / GDN_STATE_BF16, at most one;
  * default f32).  vllm.cpp test_ops_gdn.cpp: "CUDA gdn decode corner fallback
  * supports indexed compressed state", the packed-decode port's note that the
@@ -116,8 +128,9 @@ int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_
  *              error; such a row's output is written as NaN and no state is
  *              touched.  Two rows naming the same slot race (undefined).
  *   scale      > 0 and finite (usually 1/sqrt(dk)).
- *   flags      GDN_L2NORM_QK to normalise q and k with l2_eps; at most one
- *              of GDN_STATE_F16, GDN_STATE_BF16.
+ *   flags      GDN_L2NORM_QK to normalise q and k with l2_eps; GDN_CHECK_SLOTS
+ *              to validate state_idx first (negative entries allowed); at
+ *              most one of GDN_STATE_F16, GDN_STATE_BF16.
  * batch == 0 enqueues nothing and returns GDN_OK.
  */
 int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
@@ -160,16 +173,20 @@ size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs,
  *                NULL) when has_initial_state[s] != 0 (NULL: all nonzero),
  *                else from zeros without reading the slot, and its final
  *                state is written to pool[slot].  Slots must be distinct and
- *                in range (caller's responsibility; not checked on device).
+ *                in [0, num_slots): checked with GDN_CHECK_SLOTS; otherwise
+ *                a sequence whose slot is out of range gets NaN outputs and
+ *                no state access, and two sequences naming one slot race.
  *   cu_seqlens   [num_seqs + 1] int32, cu_seqlens[0] = 0, non-decreasing,
- *                cu_seqlens[num_seqs] = total_tokens.  Read on the device.
+ *                cu_seqlens[num_seqs] = total_tokens.  Read on the device,
+ *                where every range is clamped to [0, total_tokens); checked
+ *                with GDN_CHECK_SLOTS.
  *                A zero-length sequence passes its state through unchanged.
  *   workspace    device buffer of at least
  *                gdn_prefill_varlen_workspace_size(...) bytes (may be NULL
  *                when that size is 0).
- *   flags        GDN_L2NORM_QK; GDN_PREFILL_SEQUENTIAL forces the
- *                token-sequential kernel instead of the chunked one; at most
- *                one of GDN_STATE_F16, GDN_STATE_BF16.
+ *   flags        GDN_L2NORM_QK; GDN_CHECK_SLOTS; GDN_PREFILL_SEQUENTIAL
+ *                forces the token-sequential kernel instead of the chunked
+ *                one; at most one of GDN_STATE_F16, GDN_STATE_BF16.
  * num_seqs == 0 enqueues nothing and returns GDN_OK.
  */
 int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k,

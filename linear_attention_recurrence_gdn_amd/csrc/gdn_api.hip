@@ -1,9 +1,13 @@
 // gdn_api.hip -- the C ABI declared in include/gdn.h: host-side argument
-// validation and dispatch to the kernel launchers.  Nothing here allocates,
-// synchronises or reads device memory.
+// validation and dispatch to the kernel launchers.  Nothing here allocates
+// device memory; only GDN_CHECK_SLOTS reads device data (the slot table and
+// cu_seqlens, copied to the host in stream order) and so waits on the stream.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+
+#include <algorithm>
+#include <vector>
 
 #include "../../include/gdn.h"
 #include "gdn_launch.h"
@@ -80,6 +84,48 @@ int state_dtype(uint32_t flags) {
   return f16 ? GDN_F16 : bf16 ? GDN_BF16 : GDN_F32;
 }
 
+// GDN_CHECK_SLOTS (vllm.cpp test_ops_gdn.cpp, the packed-decode case that
+// rejects duplicate and out-of-range live slots): copy `n` int32 entries of
+// device metadata to the host after the work already on `stream`, and wait.
+int fetch_i32(const char* op, const int32_t* dev, int64_t n, std::vector<int32_t>& host,
+              hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess)
+    return fail(GDN_ERR_HIP, "%s: stream query failed: %s", op, hipGetErrorString(e));
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(GDN_ERR_ARG, "%s: GDN_CHECK_SLOTS waits on the stream and cannot be captured",
+                op);
+  host.resize((size_t)n);
+  e = hipMemcpyAsync(host.data(), dev, (size_t)n * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(GDN_ERR_HIP, "%s: reading device metadata failed: %s", op, hipGetErrorString(e));
+  return GDN_OK;
+}
+
+// Live slots (>= 0; negative ones allowed only where they mark padded rows)
+// must lie in [0, num_slots) and be distinct.
+int check_slot_table(const char* op, const std::vector<int32_t>& idx, int64_t num_slots,
+                     bool allow_negative) {
+  std::vector<int32_t> live;
+  live.reserve(idx.size());
+  for (size_t i = 0; i < idx.size(); ++i) {
+    const int32_t s = idx[i];
+    if (s < 0 && allow_negative) continue;
+    if (s < 0 || s >= num_slots)
+      return fail(GDN_ERR_SLOT, "%s: row %zu names slot %d, outside [0, %lld)", op, i, (int)s,
+                  (long long)num_slots);
+    live.push_back(s);
+  }
+  std::sort(live.begin(), live.end());
+  const auto d = std::adjacent_find(live.begin(), live.end());
+  if (d != live.end())
+    return fail(GDN_ERR_SLOT, "%s: slot %d is named by more than one row", op, (int)*d);
+  return GDN_OK;
+}
+
 int hip_status(const char* op, hipError_t e) {
   if (e != hipSuccess) return fail(GDN_ERR_HIP, "%s: launch failed: %s", op, hipGetErrorString(e));
   return ok();
@@ -122,7 +168,7 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
     return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
   if (out_dt != GDN_F32 && out_dt != in_dt)
     return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
-  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_STATE_F16 | GDN_STATE_BF16))
+  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_CHECK_SLOTS | GDN_STATE_F16 | GDN_STATE_BF16))
     return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
   const int state_dt = state_dtype(flags);
   if (state_dt < 0) return fail(GDN_ERR_DTYPE, "%s: GDN_STATE_F16 and GDN_STATE_BF16 both set", op);
@@ -135,6 +181,11 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
     return fail(GDN_ERR_SHAPE, "%s: v/alpha/beta row stride below its row width", op);
   if (!aligned(state_pool, 16)) return fail(GDN_ERR_ARG, "%s: state pool must be 16-byte aligned", op);
   if (batch * hv > ((int64_t)1 << 40)) return fail(GDN_ERR_SHAPE, "%s: batch*hv too large", op);
+  if (flags & GDN_CHECK_SLOTS) {
+    std::vector<int32_t> h;
+    if ((rc = fetch_i32(op, state_idx, batch, h, stream))) return rc;
+    if ((rc = check_slot_table(op, h, num_slots, true))) return rc;
+  }
   gdn::DecodeArgs a{};
   a.out = out; a.out_dt = out_dt; a.q = q; a.k = k; a.v = v; a.in_dt = in_dt;
   a.q_rs = q_row_stride; a.k_rs = k_row_stride; a.v_rs = v_row_stride;
@@ -180,7 +231,8 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
   if (!valid_dt(in_dt) || !valid_dt(out_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
   if (out_dt != GDN_F32 && out_dt != in_dt)
     return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
-  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_PREFILL_SEQUENTIAL | GDN_STATE_F16 | GDN_STATE_BF16))
+  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_CHECK_SLOTS | GDN_PREFILL_SEQUENTIAL |
+                          GDN_STATE_F16 | GDN_STATE_BF16))
     return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
   const int state_dt = state_dtype(flags);
   if (state_dt < 0) return fail(GDN_ERR_DTYPE, "%s: GDN_STATE_F16 and GDN_STATE_BF16 both set", op);
@@ -195,6 +247,21 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
     if ((rc = check_qk(op, q, k, in_dt, q_row_stride, k_row_stride, hk, dk))) return rc;
     if (v_row_stride < hv * dv || g_row_stride < hv || beta_row_stride < hv)
       return fail(GDN_ERR_SHAPE, "%s: v/g/beta row stride below its row width", op);
+  }
+  if (flags & GDN_CHECK_SLOTS) {
+    std::vector<int32_t> h;
+    if ((rc = fetch_i32(op, cu_seqlens, num_seqs + 1, h, stream))) return rc;
+    if (h[0] != 0 || h[(size_t)num_seqs] != total_tokens)
+      return fail(GDN_ERR_SHAPE, "%s: cu_seqlens must run from 0 to total_tokens (%lld)", op,
+                  (long long)total_tokens);
+    for (int64_t s = 0; s < num_seqs; ++s)
+      if (h[(size_t)s + 1] < h[(size_t)s])
+        return fail(GDN_ERR_SHAPE, "%s: cu_seqlens decreases at sequence %lld", op,
+                    (long long)s);
+    if (state_idx) {
+      if ((rc = fetch_i32(op, state_idx, num_seqs, h, stream))) return rc;
+      if ((rc = check_slot_table(op, h, num_slots, false))) return rc;
+    }
   }
   gdn::PrefillArgs a{};
   a.out = out; a.out_dt = out_dt; a.q = q; a.k = k; a.v = v; a.in_dt = in_dt;

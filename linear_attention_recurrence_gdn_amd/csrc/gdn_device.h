@@ -19,14 +19,30 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
+// f32 -> bfloat16 / binary16, round to nearest even, converted in hardware
+// (v_cvt_pk_bf16_f32, v_cvt_f16_f32).  On gfx950 the bf16 conversion gives
+// exactly the rule above, NaN quieting included: checked on the device for
+// the bit patterns of Winery-Strata's bf16_bits_test list (NaNs of both
+// signs and payloads, infinities, the largest finite, ties, subnormals).
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
-  const uint32_t b = __float_as_uint(x);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((b >> 16) | 0x40u);
-  return static_cast<uint16_t>((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two values rounded and packed into one word, a in the low half.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+__device__ __forceinline__ uint32_t pack2_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
 }
 
 // Four consecutive elements starting at element `off` (16-byte aligned for f32,
@@ -113,11 +129,9 @@ __device__ __forceinline__ void state_store4(void* base, int64_t off, float4 x) 
   if constexpr (TS == kF32) {
     state_store<NT>(static_cast<float*>(base) + off, x);
   } else {
-    uint32_t e[4];
-    const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = TS == kBF16 ? f32_to_bf16(xs[i]) : f32_to_f16(xs[i]);
-    u32x2_t r = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+    u32x2_t r;
+    if constexpr (TS == kBF16) r = u32x2_t{pack2_bf16(x.x, x.y), pack2_bf16(x.z, x.w)};
+    else r = u32x2_t{pack2_f16(x.x, x.y), pack2_f16(x.z, x.w)};
     u32x2_t* p = reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(base) + off);
     if constexpr (NT) __builtin_nontemporal_store(r, p);
     else *p = r;

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 
 GDN_F32, GDN_F16, GDN_BF16 = 0, 1, 2
 GDN_L2NORM_QK = 1 << 0
+GDN_CHECK_SLOTS = 1 << 1
 GDN_PREFILL_SEQUENTIAL = 1 << 2
 GDN_STATE_F16 = 1 << 3
 GDN_STATE_BF16 = 1 << 4
@@ -138,14 +139,15 @@ def gate(alpha: torch.Tensor, dt_bias: torch.Tensor, ssm_a: torch.Tensor,
 
 def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale: float,
            l2norm: bool = True, l2_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
-           out_dtype=None, stream=None) -> torch.Tensor:
+           out_dtype=None, check_slots: bool = False, stream=None) -> torch.Tensor:
     """One decode step, gate fused, pool updated in place.
 
     q, k: [B, Hk, Dk]; v: [B, Hv, Dv] (rows may be strided, e.g. views into one
     packed q|k|v buffer); alpha [B, Hv]; dt_bias, ssm_a [Hv] f32; beta [B, Hv] f32;
     state_pool [slots, Hv, Dv, Dk] contiguous, f32 or 16-bit storage (float16 /
     bfloat16: widened to f32 for the step, the new state rounded on store);
-    state_idx [B] int32."""
+    state_idx [B] int32.  check_slots: validate state_idx first (GDN_CHECK_SLOTS:
+    reads it back and waits on the stream; not capturable)."""
     lib = load_library()
     if state_pool.dim() != 4 or not state_pool.is_contiguous():
         raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
@@ -166,7 +168,8 @@ def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale
         out = torch.empty((B, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
     if not out.is_contiguous() or tuple(out.shape) != (B, hv, dv):
         raise GdnError(-3, "out: need contiguous [B, Hv, Dv]")
-    flags = (GDN_L2NORM_QK if l2norm else 0) | _state_flags(state_pool)
+    flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_CHECK_SLOTS if check_slots else 0) |
+             _state_flags(state_pool))
     _check(lib.gdn_decode(
         _dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
         q_rs, k_rs, v_rs, _dev(alpha, "alpha"), _dt(alpha), a_rs,
@@ -190,12 +193,13 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
                    has_initial_state: Optional[torch.Tensor] = None, l2norm: bool = True,
                    l2_eps: float = 1e-6, out: Optional[torch.Tensor] = None, out_dtype=None,
                    sequential: bool = False, workspace: Optional[torch.Tensor] = None,
-                   stream=None) -> torch.Tensor:
+                   check_slots: bool = False, stream=None) -> torch.Tensor:
     """Varlen prefill over sequences packed back to back (cu_seqlens [N+1] int32).
 
     q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; g, beta: [T, Hv] f32; state_pool
     [slots, Hv, Dv, Dk] f32, float16 or bfloat16 (initial states read, final
-    states written)."""
+    states written).  check_slots: validate cu_seqlens and state_idx first
+    (GDN_CHECK_SLOTS: reads them back and waits on the stream)."""
     lib = load_library()
     if state_pool.dim() != 4 or not state_pool.is_contiguous():
         raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
@@ -215,7 +219,7 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
     if not out.is_contiguous() or tuple(out.shape) != (T, hv, dv):
         raise GdnError(-3, "out: need contiguous [T, Hv, Dv]")
     flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_PREFILL_SEQUENTIAL if sequential else 0) |
-             _state_flags(state_pool))
+             (GDN_CHECK_SLOTS if check_slots else 0) | _state_flags(state_pool))
     ws_need = lib.gdn_prefill_varlen_workspace_size(T, N, hk, hv, dk, dv, _dt(q), flags)
     if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)

@@ -121,3 +121,11 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(4, 32)
     with pytest.raises(B.GdnError):
         pkg.gate(x, torch.zeros(32), torch.zeros(32))
+
+
+def test_check_slots_flag_is_known():
+    lib = pkg.load_library()
+    # accepted by both entry points: validation goes on to the null-pointer check
+    assert _decode(lib, flags=1 | (1 << 1)) == -1 and "null pointer" in _err(lib)
+    assert _prefill(lib, flags=1 | (1 << 1)) == -1 and "null pointer" in _err(lib)
+    assert B.GDN_CHECK_SLOTS == 1 << 1
