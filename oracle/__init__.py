@@ -21,6 +21,7 @@ _SRC = os.path.join(_HERE, "gdn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, F16, BF16 = 0, 1, 2
+F64 = 3   # oracle-internal code: an array of doubles (e.g. an oracle output)
 
 
 def build(force: bool = True) -> str:
@@ -61,6 +62,9 @@ def _load():
         lib.oracle_prefill_varlen.argtypes = [i64, vp, i64, i64, i64, i64, vp, vp, vp, i32,
                                               i64, i64, i64, vp, vp, i64, vp, i32, i64, vp,
                                               vp, dbl, dbl, i32, vp, vp, vp]
+        lib.oracle_rmsnorm_gated.restype = i32
+        lib.oracle_rmsnorm_gated.argtypes = [i64, i64, i64, vp, i32, vp, i32, i64, vp, i32,
+                                             dbl, i32, vp]
         _lib = lib
     return _lib
 
@@ -177,6 +181,23 @@ def prefill_varlen(*, cu_seqlens, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs
     if rc:
         raise OracleError(f"oracle_prefill_varlen: error {rc}")
     return out, st
+
+
+def rmsnorm_gated(x, x_dt, z, z_dt, z_row_stride, w, w_dt, *, rows, hv, dv, eps,
+                  sigmoid=False):
+    """Gated RMSNorm of x [rows, hv, dv] (storage array of x_dt, or float64 with
+    x_dt = F64) with the gate z (token t's head h at z.flat[t*z_row_stride +
+    h*dv + i]) and weight w [dv].  Returns y [rows, hv, dv] f64."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    z = np.ascontiguousarray(z)
+    w = np.ascontiguousarray(w)
+    y = np.zeros((rows, hv, dv), dtype=np.float64)
+    rc = lib.oracle_rmsnorm_gated(rows, hv, dv, _p(x), x_dt, _p(z), z_dt, z_row_stride,
+                                  _p(w), w_dt, float(eps), int(bool(sigmoid)), _p(y))
+    if rc:
+        raise OracleError(f"oracle_rmsnorm_gated: error {rc}")
+    return y
 
 
 # ---- convenience wrappers over the seeded workload cases ------------------

@@ -26,7 +26,9 @@
  *       q scaled after normalising, GQA head hk = hv / (Hv/Hk), slot < 0 gives
  *       a zero output row and leaves the state alone, duplicate or
  *       out-of-range live slots are errors);
- *      "l2norm: plain sum of squares over the last dim".
+ *      "l2norm: plain sum of squares over the last dim";
+ *      "rmsnorm_gated: norm-then-gate, silu and sigmoid activations" and the
+ *       rank-3 padded-row gate case (the gated RMSNorm after the recurrence).
  *
  * Parity pins live in tests/test_oracle_pins.py (the pages' worked values and
  * the invariants listed there).
@@ -39,6 +41,7 @@
 #define OR_F32 0
 #define OR_F16 1
 #define OR_BF16 2
+#define OR_F64 3 /* oracle-internal: an array of doubles (e.g. an f64 output) */
 
 #define OR_OK 0
 #define OR_ERR_ARG -1
@@ -78,6 +81,7 @@ static double load_elem(const void* base, int dt, int64_t off) {
     case OR_F32: return (double)((const float*)base)[off];
     case OR_F16: return half_to_double(((const uint16_t*)base)[off]);
     case OR_BF16: return bf16_to_double(((const uint16_t*)base)[off]);
+    case OR_F64: return ((const double*)base)[off];
     default: return NAN;
   }
 }
@@ -310,5 +314,47 @@ int oracle_prefill_varlen(int64_t num_seqs, const int32_t* cu, int64_t hk, int64
     }
   }
   free(qd); free(kd); free(vd); free(work);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Gated RMSNorm (vllm.cpp "rmsnorm_gated: norm-then-gate, silu and sigmoid
+ * activations"; the rank-3 padded-row gate case).  For each token t and
+ * v-head h, with x the [dv] row x[t][h]:
+ *   ms      = (1/dv) sum_i x_i^2             (a mean, not a sum)
+ *   y_i     = x_i / sqrt(ms + eps) * w_i * act(z[t][h][i])
+ *   act     = silu(z) = z / (1 + exp(-z))   (default)
+ *             sigmoid(z) = 1 / (1 + exp(-z)) (sigmoid != 0)
+ * Normalise first, then gate.  x: [rows][hv][dv] (x_dt, OR_F64 allowed);
+ * z: row t's gate at z[t * z_row_stride + h * dv + i] (a padded token row);
+ * w: [dv].  y: [rows][hv][dv] f64.
+ * ------------------------------------------------------------------------ */
+static double act_gate(double z, int sigmoid) {
+  const double sg = 1.0 / (1.0 + exp(-z));
+  return sigmoid ? sg : z * sg;
+}
+
+int oracle_rmsnorm_gated(int64_t rows, int64_t hv, int64_t dv, const void* x, int x_dt,
+                         const void* z, int z_dt, int64_t z_row_stride, const void* w,
+                         int w_dt, double eps, int sigmoid, double* y) {
+  if (rows < 0 || hv <= 0 || dv <= 0 || z_row_stride < hv * dv) return OR_ERR_SHAPE;
+  if (!(eps >= 0.0)) return OR_ERR_ARG;
+  for (int64_t t = 0; t < rows; ++t) {
+    for (int64_t h = 0; h < hv; ++h) {
+      const int64_t xo = (t * hv + h) * dv;
+      double ms = 0.0;
+      for (int64_t i = 0; i < dv; ++i) {
+        const double xi = load_elem(x, x_dt, xo + i);
+        ms += xi * xi;
+      }
+      ms /= (double)dv;
+      const double inv = 1.0 / sqrt(ms + eps);
+      for (int64_t i = 0; i < dv; ++i) {
+        const double xi = load_elem(x, x_dt, xo + i);
+        const double zi = load_elem(z, z_dt, t * z_row_stride + h * dv + i);
+        y[xo + i] = xi * inv * load_elem(w, w_dt, i) * act_gate(zi, sigmoid);
+      }
+    }
+  }
   return OR_OK;
 }
