@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-state16", action="store_true",
                     help="skip the decode leg with a bf16 state pool")
+    ap.add_argument("--no-norm", action="store_true",
+                    help="skip the gated-RMSNorm legs (fused decode, norm after prefill)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale factor for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -248,6 +250,32 @@ def main():
         log(f"decode bf16 state: kernel avg {kavg16 * 1e3:.1f} us -> "
             f"{bytes16 / (kavg16 * 1e-3) / 1e9:.0f} GB/s")
 
+    # ---------------- decode with the gated RMSNorm fused ----------------
+    if not args.no_norm:
+        nrm = W.norm_inputs(202, B, hv, dv, W.BF16)
+        zb = to_dev(nrm.z.buf.view(np.int16)).view(torch.bfloat16).view(B, hv, dv)
+        wb = to_dev(nrm.w.view(np.int16)).view(torch.bfloat16)
+
+        def decode_norm_step(i):
+            gdn.decode_gated_norm(qb, kb, vb, alpha, dt_bias, ssm_a, beta, pool, subsets[i % 4],
+                                  zb, wb, scale=case.scale, norm_eps=nrm.eps, out=out,
+                                  stream=stream)
+
+        wall_n, kn = timed(decode_norm_step, args.warmup, args.steps)
+        bytes_n = step_bytes + B * hv * dv * 2 + dv * 2
+        kavg_n = float(kn.mean())
+        result["decode_gated_norm"] = {
+            "workload": "the same decode with the gated RMSNorm (silu gate, bf16 z and w) "
+                        "fused into the output store",
+            "ms_per_step": round(wall_n * 1e3 / args.steps, 5),
+            "algorithmic_bytes_per_step": bytes_n,
+            "kernel_avg_us": round(kavg_n * 1e3, 2),
+            "achieved_GBs": round(bytes_n / (kavg_n * 1e-3) / 1e9, 1),
+            "hbm_frac": round(bytes_n / (kavg_n * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "overhead_vs_plain_decode": round(kavg_n / kavg - 1.0, 4),
+        }
+        log(f"decode + gated norm: kernel avg {kavg_n * 1e3:.1f} us")
+
     # ---------------- prefill leg ----------------
     if not args.no_prefill:
         pre = W.prefill_varlen_gqa3()
@@ -302,6 +330,29 @@ def main():
             "path": "chunked" if ws_n > 0 else "token-sequential",
         }
         log(f"prefill: {p_ms_step:.3f} ms/step -> {T / (p_ms_step * 1e-3) / 1e6:.2f} M tokens/s")
+
+        # the gated RMSNorm over the prefill output (a separate HBM pass)
+        if not args.no_norm:
+            pn = W.norm_inputs(404, T, pre.hv, pre.dv, W.F16)
+            pz = to_dev(pn.z.buf).view(T, pre.hv, pre.dv)
+            pw = to_dev(pn.w)
+            nout = torch.empty_like(pout)
+
+            def norm_step(i):
+                gdn.rmsnorm_gated(pout, pz, pw, eps=pn.eps, out=nout, stream=stream)
+
+            nwall, nk = timed(norm_step, 3, args.prefill_steps)
+            nbytes = 3 * T * pre.hv * pre.dv * 2 + pre.dv * 2
+            navg = float(nk.mean())
+            result["prefill"]["rmsnorm_gated"] = {
+                "workload": "gated RMSNorm (silu) over the [32768, 24, 128] fp16 prefill output "
+                            "with an fp16 gate and weight",
+                "kernel_avg_us": round(navg * 1e3, 2),
+                "algorithmic_bytes": nbytes,
+                "achieved_GBs": round(nbytes / (navg * 1e-3) / 1e9, 1),
+                "hbm_frac": round(nbytes / (navg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            }
+            log(f"prefill gated norm: kernel avg {navg * 1e3:.1f} us")
 
     # ---------------- CPU oracle baseline ----------------
     if not args.no_cpu:

@@ -68,7 +68,8 @@ enum {
   GDN_CHECK_SLOTS = 1u << 1,         /* check the slot table first (reads it; waits) */
   GDN_PREFILL_SEQUENTIAL = 1u << 2,  /* prefill: force the token-sequential kernel */
   GDN_STATE_F16 = 1u << 3,           /* state pool stored as IEEE binary16 */
-  GDN_STATE_BF16 = 1u << 4           /* state pool stored as bfloat16 */
+  GDN_STATE_BF16 = 1u << 4,          /* state pool stored as bfloat16 */
+  GDN_NORM_SIGMOID = 1u << 5         /* gated norm: sigmoid gate instead of silu */
 };
 /*
  * Slot check (flag GDN_CHECK_SLOTS).  vllm.cpp test_ops_gdn.cpp, "gdn packed
@@ -141,6 +142,64 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
                int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
                uint32_t flags, hipStream_t stream);
+
+/*
+ * gdn_decode_gated_norm -- gdn_decode followed, in the same kernel, by the
+ * gated RMSNorm of each (row, v-head) output (see gdn_rmsnorm_gated):
+ *   out[b][h][i] = o[i] / sqrt(mean_i o^2 + norm_eps) * norm_w[i] * act(z[b][h][i])
+ * where o is the step's f32 output before any rounding.  vllm.cpp
+ * test_ops_gdn.cpp, "rmsnorm_gated: norm-then-gate, silu and sigmoid
+ * activations" and the rank-3 padded-row gate case (the gate is the z slice
+ * of a wider projection row).
+ *   all arguments of gdn_decode, plus
+ *   norm_z     [batch, hv, dv] gate in in_dt; row b's head h starts at
+ *              element b * norm_z_row_stride + h * dv (stride >= hv*dv, so a
+ *              padded row of a wider buffer can be passed).  Never written.
+ *   norm_w     [dv] weight in in_dt.
+ *   norm_eps   >= 0 and finite, added to the mean square.
+ *   flags      as gdn_decode, plus GDN_NORM_SIGMOID for a sigmoid gate
+ *              (default silu(z) = z * sigmoid(z)).
+ * Padded rows (negative slot) are written as zeros; rows with an
+ * out-of-range slot as NaN.  Each (row, v-head) is one workgroup of at most
+ * 8 waves, so dv <= 256 at dk = 128 (dk = 256: 128; dk = 16, 32, 64: 512);
+ * larger dv returns GDN_ERR_SHAPE.
+ */
+int gdn_decode_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                          const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                          int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
+                          gdn_dtype alpha_dt, int64_t alpha_row_stride, const float* dt_bias,
+                          const float* ssm_a, const float* beta, int64_t beta_row_stride,
+                          void* state_pool, int64_t num_slots, const int32_t* state_idx,
+                          int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
+                          float scale, float l2_eps, const void* norm_z,
+                          int64_t norm_z_row_stride, const void* norm_w, float norm_eps,
+                          uint32_t flags, hipStream_t stream);
+
+/*
+ * gdn_rmsnorm_gated -- gated RMSNorm over [rows, hv, dv] (vllm.cpp
+ * test_ops_gdn.cpp, "rmsnorm_gated: norm-then-gate, silu and sigmoid
+ * activations", the CPU-vs-CUDA rmsnorm_gated cases and the rank-3
+ * padded-row gate case):
+ *   out[t][h][i] = x[t][h][i] / sqrt(mean_i x[t][h][i]^2 + eps) * norm_w[i]
+ *                  * act(z[t][h][i]),   act = silu, or sigmoid with
+ *                  GDN_NORM_SIGMOID.
+ * The variance is a mean over dv; normalise first, then gate.
+ *   out     [rows, hv, dv] contiguous, out_dt (f32 or x_dt).
+ *   x       [rows, hv, dv] contiguous in x_dt (e.g. the prefill output).
+ *   z       gate in x_dt: token t's head h starts at t * z_row_stride + h*dv
+ *           (z_row_stride >= hv*dv); the buffer must hold
+ *           (rows - 1) * z_row_stride + hv*dv elements.  Never written.
+ *   norm_w  [dv] in x_dt.
+ *   eps     >= 0 and finite.
+ * Computed in f32, output rounded to nearest-even.  rows == 0 enqueues
+ * nothing.  Fast path: with N = 16 bytes of x_dt elements (8 for f16/bf16, 4
+ * for f32), dv / N a power of two <= 64, z_row_stride a multiple of N and
+ * every pointer 16-byte aligned; any other layout takes a slower
+ * wave-per-row kernel.
+ */
+int gdn_rmsnorm_gated(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt,
+                      const void* z, int64_t z_row_stride, const void* norm_w, int64_t rows,
+                      int64_t hv, int64_t dv, float eps, uint32_t flags, hipStream_t stream);
 
 /*
  * gdn_prefill_varlen_workspace_size -- bytes of device workspace that

@@ -151,15 +151,25 @@ int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_
   return hip_status(op, gdn::launch_gate(a, stream));
 }
 
-int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
-               gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
-               int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
-               int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-               const float* beta, int64_t beta_row_stride, void* state_pool,
-               int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
-               int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
-               hipStream_t stream) {
-  const char* op = "gdn_decode";
+}  // extern "C"
+
+namespace {
+
+struct NormIn {
+  const void* z;
+  int64_t z_rs;
+  const void* w;
+  float eps;
+};
+
+int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, const void* k,
+                const void* v, gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+                int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
+                int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
+                const float* beta, int64_t beta_row_stride, void* state_pool,
+                int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
+                int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
+                const NormIn* norm, uint32_t flags, hipStream_t stream) {
   int rc;
   if (batch < 0 || num_slots < 0) return fail(GDN_ERR_SHAPE, "%s: negative batch/num_slots", op);
   if ((rc = check_heads(op, hk, hv, dk, dv))) return rc;
@@ -168,8 +178,16 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
     return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
   if (out_dt != GDN_F32 && out_dt != in_dt)
     return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
-  if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_CHECK_SLOTS | GDN_STATE_F16 | GDN_STATE_BF16))
-    return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  const uint32_t known = GDN_L2NORM_QK | GDN_CHECK_SLOTS | GDN_STATE_F16 | GDN_STATE_BF16 |
+                         (norm ? (uint32_t)GDN_NORM_SIGMOID : 0u);
+  if (flags & ~known) return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (norm) {
+    if (!(norm->eps >= 0.0f) || !isfinite(norm->eps))
+      return fail(GDN_ERR_ARG, "%s: norm_eps must be finite and >= 0", op);
+    if (dv > gdn::decode_norm_max_dv((int)dk))
+      return fail(GDN_ERR_SHAPE, "%s: the fused norm takes dv <= %d at dk = %lld", op,
+                  gdn::decode_norm_max_dv((int)dk), (long long)dk);
+  }
   const int state_dt = state_dtype(flags);
   if (state_dt < 0) return fail(GDN_ERR_DTYPE, "%s: GDN_STATE_F16 and GDN_STATE_BF16 both set", op);
   if (batch == 0) return ok();
@@ -177,6 +195,14 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
       !state_idx)
     return fail(GDN_ERR_ARG, "%s: null pointer", op);
   if ((rc = check_qk(op, q, k, in_dt, q_row_stride, k_row_stride, hk, dk))) return rc;
+  if (norm) {
+    if (!norm->z || !norm->w) return fail(GDN_ERR_ARG, "%s: null pointer", op);
+    const size_t eb = (size_t)elem_bytes(in_dt);
+    if (!aligned(norm->z, eb) || !aligned(norm->w, eb))
+      return fail(GDN_ERR_ARG, "%s: norm_z/norm_w must be aligned to their element size", op);
+    if (norm->z_rs < hv * dv)
+      return fail(GDN_ERR_SHAPE, "%s: norm_z row stride below hv*dv", op);
+  }
   if (v_row_stride < hv * dv || alpha_row_stride < hv || beta_row_stride < hv)
     return fail(GDN_ERR_SHAPE, "%s: v/alpha/beta row stride below its row width", op);
   if (!aligned(state_pool, 16)) return fail(GDN_ERR_ARG, "%s: state pool must be 16-byte aligned", op);
@@ -196,8 +222,76 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
   a.batch = batch;
   a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
   a.scale = scale; a.l2_eps = l2_eps; a.l2norm = (flags & GDN_L2NORM_QK) ? 1 : 0;
+  if (norm) {
+    a.norm_z = norm->z; a.norm_z_rs = norm->z_rs; a.norm_w = norm->w;
+    a.norm_eps = norm->eps; a.norm_sigmoid = (flags & GDN_NORM_SIGMOID) ? 1 : 0;
+  }
   return hip_status(op, gdn::launch_decode(a, stream));
 }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
+               gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+               int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
+               int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
+               const float* beta, int64_t beta_row_stride, void* state_pool,
+               int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
+               int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+               hipStream_t stream) {
+  return decode_impl("gdn_decode", out, out_dt, q, k, v, in_dt, q_row_stride, k_row_stride,
+                     v_row_stride, alpha, alpha_dt, alpha_row_stride, dt_bias, ssm_a, beta,
+                     beta_row_stride, state_pool, num_slots, state_idx, batch, hk, hv, dk, dv,
+                     scale, l2_eps, nullptr, flags, stream);
+}
+
+int gdn_decode_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                          const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                          int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
+                          gdn_dtype alpha_dt, int64_t alpha_row_stride, const float* dt_bias,
+                          const float* ssm_a, const float* beta, int64_t beta_row_stride,
+                          void* state_pool, int64_t num_slots, const int32_t* state_idx,
+                          int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
+                          float scale, float l2_eps, const void* norm_z,
+                          int64_t norm_z_row_stride, const void* norm_w, float norm_eps,
+                          uint32_t flags, hipStream_t stream) {
+  const NormIn n{norm_z, norm_z_row_stride, norm_w, norm_eps};
+  return decode_impl("gdn_decode_gated_norm", out, out_dt, q, k, v, in_dt, q_row_stride,
+                     k_row_stride, v_row_stride, alpha, alpha_dt, alpha_row_stride, dt_bias,
+                     ssm_a, beta, beta_row_stride, state_pool, num_slots, state_idx, batch, hk,
+                     hv, dk, dv, scale, l2_eps, &n, flags, stream);
+}
+
+int gdn_rmsnorm_gated(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt,
+                      const void* z, int64_t z_row_stride, const void* norm_w, int64_t rows,
+                      int64_t hv, int64_t dv, float eps, uint32_t flags, hipStream_t stream) {
+  const char* op = "gdn_rmsnorm_gated";
+  if (rows < 0 || hv <= 0 || dv <= 0 || hv > (1 << 20) || dv > (1 << 20))
+    return fail(GDN_ERR_SHAPE, "%s: rows >= 0, hv and dv in [1, 2^20] required", op);
+  if (!valid_dt(x_dt) || !valid_dt(out_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
+  if (out_dt != GDN_F32 && out_dt != x_dt)
+    return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
+  if (flags & ~(uint32_t)GDN_NORM_SIGMOID)
+    return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (!(eps >= 0.0f) || !isfinite(eps))
+    return fail(GDN_ERR_ARG, "%s: eps must be finite and >= 0", op);
+  if (z_row_stride < hv * dv) return fail(GDN_ERR_SHAPE, "%s: z row stride below hv*dv", op);
+  if (rows == 0) return ok();
+  if (!out || !x || !z || !norm_w) return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  const size_t eb = (size_t)elem_bytes(x_dt);
+  if (!aligned(x, eb) || !aligned(z, eb) || !aligned(norm_w, eb) ||
+      !aligned(out, (size_t)elem_bytes(out_dt)))
+    return fail(GDN_ERR_ARG, "%s: pointers must be aligned to their element size", op);
+  if (rows * hv > ((int64_t)1 << 40)) return fail(GDN_ERR_SHAPE, "%s: rows*hv too large", op);
+  gdn::NormArgs a{};
+  a.out = out; a.out_dt = out_dt; a.x = x; a.x_dt = x_dt; a.z = z; a.z_rs = z_row_stride;
+  a.w = norm_w; a.rows = rows; a.hv = (int)hv; a.dv = (int)dv; a.eps = eps;
+  a.sigmoid = (flags & GDN_NORM_SIGMOID) ? 1 : 0;
+  return hip_status(op, gdn::launch_rmsnorm_gated(a, stream));
+}
+
 
 static bool use_chunked(int64_t hk, int64_t hv, int64_t dk, int64_t dv, int in_dt, int out_dt,
                         uint32_t flags) {

@@ -152,6 +152,12 @@ __device__ __forceinline__ void state_store4_rt(int ts, void* base, int64_t off,
   else state_store4<kF32, false>(base, off, x);
 }
 
+// Gate activation of the gated RMSNorm: silu(z) = z * sigmoid(z), or sigmoid(z).
+__device__ __forceinline__ float gate_act(float z, bool sigmoid) {
+  const float sg = 1.0f / (1.0f + expf(-z));
+  return sigmoid ? sg : z * sg;
+}
+
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }

@@ -43,6 +43,27 @@ struct DecodeArgs {
   int hk, hv, dk, dv;
   float scale, l2_eps;
   int l2norm;
+  // gated RMSNorm epilogue (norm_z == nullptr: none): out = o / rms(o) * w * act(z)
+  const void* norm_z;    // [batch, hv, dv] in in_dt, token row stride norm_z_rs
+  int64_t norm_z_rs;
+  const void* norm_w;    // [dv] in in_dt
+  float norm_eps;
+  int norm_sigmoid;      // act: 0 silu, 1 sigmoid
+};
+
+// Gated RMSNorm over [rows, hv, dv]: x, z and w share x_dt.
+struct NormArgs {
+  void* out;
+  int out_dt;
+  const void* x;       // [rows, hv, dv] contiguous
+  int x_dt;
+  const void* z;       // token t's head h at z[t * z_rs + h * dv]
+  int64_t z_rs;
+  const void* w;       // [dv]
+  int64_t rows;
+  int hv, dv;
+  float eps;
+  int sigmoid;
 };
 
 struct PrefillArgs {
@@ -73,6 +94,10 @@ struct PrefillArgs {
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// the fused-norm decode runs one workgroup (at most 16 waves) per (row,
+// v-head): the largest dv it takes at this dk
+int decode_norm_max_dv(int dk);
+hipError_t launch_rmsnorm_gated(const NormArgs& a, hipStream_t stream);
 hipError_t launch_prefill_sequential(const PrefillArgs& a, hipStream_t stream);
 
 // Chunked prefill (MFMA).  Returns hipErrorNotSupported when the shape or

@@ -57,6 +57,11 @@ hipError_t launch_gate(const GateArgs& a, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // shared per-token step on a wave's register tile
 // ---------------------------------------------------------------------------
+// The fused-norm decode runs one workgroup per (row, v-head) of at most this
+// many waves (512 threads leave each lane up to 256 VGPRs: the doubled tile
+// of the fused norm fits without spilling).
+constexpr int kNormMaxWaves = 8;
+
 template <int DK, int NL>
 struct Tile {
   static constexpr int LPR = DK / 4;    // lanes per state row
@@ -115,13 +120,21 @@ __device__ __forceinline__ float tile_step(float4 (&s)[NL], float4 q4, float4 k4
 // waves of one head are neighbours.  All indices are wave-uniform (scalar
 // registers); the q/k/v/gate loads are issued before the slot index is
 // waited on, and the whole state tile is requested before any arithmetic.
-template <int DK, int NL, int TIN, int TAL, int TS, bool NT>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total_waves,
-                                                     int tiles_per_head) {
+//
+// NORM adds the gated RMSNorm after the step (vllm.cpp test_ops_gdn.cpp,
+// "rmsnorm_gated: norm-then-gate"): the workgroup is then exactly the
+// tiles_per_head waves of one (row, v-head), which add their squared outputs
+// through LDS; each output is o / sqrt(mean(o^2) + eps) * w * act(z), from
+// the unrounded f32 o.
+template <int DK, int NL, int TIN, int TAL, int TS, bool NT, bool NORM>
+__global__ __launch_bounds__(NORM ? 64 * kNormMaxWaves : 256) void decode_kernel(DecodeArgs a,
+                                                                   int64_t total_waves,
+                                                                   int tiles_per_head) {
   using T = Tile<DK, NL>;
   const int lane = threadIdx.x & 63;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // the host keeps the wave count below 2^31, so 32-bit index math suffices
-  const uint32_t wave = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wave = blockIdx.x * (NORM ? (uint32_t)tiles_per_head : 4u) + wid;
   if (wave >= (uint32_t)total_waves) return;
   const int tile = (int)(wave % (uint32_t)tiles_per_head);
   const uint32_t bh = wave / (uint32_t)tiles_per_head;
@@ -144,7 +157,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total
   const float dtb = a.dt_bias[h];
   const float ssa = a.ssm_a[h];
   const float beta = a.beta[b * a.beta_rs + h];
+  uint32_t zr = 0, wr = 0;
+  if constexpr (NORM) {
+    const int row = min(myrow, a.dv - 1);
+    zr = load_raw1<TIN>(a.norm_z, b * a.norm_z_rs + (int64_t)h * a.dv + row);
+    wr = load_raw1<TIN>(a.norm_w, row);
+  }
 
+  // (block-uniform when NORM: every wave of the workgroup leaves here together)
   if (slot < 0 || slot >= a.num_slots) {
     // padded row: zeros; out-of-range slot (caller error): NaN.  No state access.
     if (writer) store1(a.out, a.out_dt, out_off, slot < 0 ? 0.0f : __builtin_nanf(""));
@@ -168,7 +188,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total
 #pragma unroll
   for (int i = 0; i < NL; ++i)
     if (r0 + i * T::RPI + sub >= a.dv) s[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float o = tile_step<DK, NL>(s, q4, k4, kq, decay, beta, vv, lane, sub);
+  float o = tile_step<DK, NL>(s, q4, k4, kq, decay, beta, vv, lane, sub);
+  if constexpr (NORM) {
+    __shared__ float part[kNormMaxWaves];
+    const float sq = group_sum<64>(writer ? o * o : 0.0f);
+    if (lane == 0) part[wid] = sq;
+    __syncthreads();
+    float tot = 0.0f;
+    for (int i = 0; i < tiles_per_head; ++i) tot += part[i];
+    const float inv = 1.0f / sqrtf(tot / (float)a.dv + a.norm_eps);
+    o = o * inv * raw1_to_f32<TIN>(wr) * gate_act(raw1_to_f32<TIN>(zr), a.norm_sigmoid != 0);
+  }
   if (writer) store1(a.out, a.out_dt, out_off, o);
 
 #pragma unroll
@@ -178,22 +208,30 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int64_t total
   }
 }
 
-template <int DK, int NL, int TIN, int TAL, int TS, bool NT>
+template <int DK, int NL, int TIN, int TAL, int TS, bool NORM>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   using T = Tile<DK, NL>;
   const int tiles = (a.dv + T::BV - 1) / T::BV;
   const int64_t waves = a.batch * a.hv * tiles;
   if (waves >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((decode_kernel<DK, NL, TIN, TAL, TS, NT>), dim3((unsigned)blocks), dim3(256), 0,
-                     stream, a, waves, tiles);
+  if constexpr (NORM) {
+    // one workgroup of `tiles` waves per (row, v-head)
+    if (tiles > kNormMaxWaves) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_kernel<DK, NL, TIN, TAL, TS, true, true>),
+                       dim3((unsigned)(a.batch * a.hv)), dim3(64 * tiles), 0, stream, a, waves,
+                       tiles);
+  } else {
+    const int64_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((decode_kernel<DK, NL, TIN, TAL, TS, true, false>),
+                       dim3((unsigned)blocks), dim3(256), 0, stream, a, waves, tiles);
+  }
   return hipGetLastError();
 }
 
-template <int DK, int NL, int TS>
+template <int DK, int NL, int TS, bool NORM>
 static hipError_t launch_decode_ts(const DecodeArgs& a, hipStream_t stream) {
 #define GDN_DEC(TI, TA) \
-  if (a.in_dt == TI && a.alpha_dt == TA) return launch_decode_t<DK, NL, TI, TA, TS, true>(a, stream);
+  if (a.in_dt == TI && a.alpha_dt == TA) return launch_decode_t<DK, NL, TI, TA, TS, NORM>(a, stream);
   GDN_DEC(kBF16, kF32) GDN_DEC(kF16, kF32) GDN_DEC(kF32, kF32)
   GDN_DEC(kBF16, kBF16) GDN_DEC(kF16, kBF16) GDN_DEC(kF32, kBF16)
   GDN_DEC(kBF16, kF16) GDN_DEC(kF16, kF16) GDN_DEC(kF32, kF16)
@@ -201,22 +239,48 @@ static hipError_t launch_decode_ts(const DecodeArgs& a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-template <int DK, int NL>
-static hipError_t launch_decode_dk(const DecodeArgs& a, hipStream_t stream) {
-  if (a.state_dt == kF32) return launch_decode_ts<DK, NL, kF32>(a, stream);
-  if (a.state_dt == kBF16) return launch_decode_ts<DK, NL, kBF16>(a, stream);
-  if (a.state_dt == kF16) return launch_decode_ts<DK, NL, kF16>(a, stream);
+template <int DK, int NL, bool NORM>
+static hipError_t launch_decode_st(const DecodeArgs& a, hipStream_t stream) {
+  if (a.state_dt == kF32) return launch_decode_ts<DK, NL, kF32, NORM>(a, stream);
+  if (a.state_dt == kBF16) return launch_decode_ts<DK, NL, kBF16, NORM>(a, stream);
+  if (a.state_dt == kF16) return launch_decode_ts<DK, NL, kF16, NORM>(a, stream);
   return hipErrorInvalidValue;
+}
+
+// Loads per lane of the decode tile, per dk (measured fastest).  The fused
+// norm doubles them where the row allows, so a head takes half the waves and
+// a workgroup's barrier waits on fewer of them.
+constexpr int decode_nl(int dk) { return dk == 16 ? 4 : 8; }
+constexpr int decode_norm_nl(int dk) {
+  return 2 * decode_nl(dk) <= dk / 4 ? 2 * decode_nl(dk) : decode_nl(dk);
+}
+
+template <int DK>
+static hipError_t launch_decode_dk(const DecodeArgs& a, hipStream_t stream) {
+  if (a.norm_z) return launch_decode_st<DK, decode_norm_nl(DK), true>(a, stream);
+  return launch_decode_st<DK, decode_nl(DK), false>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   switch (a.dk) {
-    case 16: return launch_decode_dk<16, 4>(a, stream);
-    case 32: return launch_decode_dk<32, 8>(a, stream);
-    case 64: return launch_decode_dk<64, 8>(a, stream);
-    case 128: return launch_decode_dk<128, 8>(a, stream);
-    case 256: return launch_decode_dk<256, 8>(a, stream);
+    case 16: return launch_decode_dk<16>(a, stream);
+    case 32: return launch_decode_dk<32>(a, stream);
+    case 64: return launch_decode_dk<64>(a, stream);
+    case 128: return launch_decode_dk<128>(a, stream);
+    case 256: return launch_decode_dk<256>(a, stream);
     default: return hipErrorInvalidValue;
+  }
+}
+
+// Largest dv the fused-norm decode takes for a given dk.
+int decode_norm_max_dv(int dk) {
+  switch (dk) {
+    case 16: return kNormMaxWaves * Tile<16, decode_norm_nl(16)>::BV;
+    case 32: return kNormMaxWaves * Tile<32, decode_norm_nl(32)>::BV;
+    case 64: return kNormMaxWaves * Tile<64, decode_norm_nl(64)>::BV;
+    case 128: return kNormMaxWaves * Tile<128, decode_norm_nl(128)>::BV;
+    case 256: return kNormMaxWaves * Tile<256, decode_norm_nl(256)>::BV;
+    default: return 0;
   }
 }
 

@@ -23,12 +23,13 @@ GDN_CHECK_SLOTS = 1 << 1
 GDN_PREFILL_SEQUENTIAL = 1 << 2
 GDN_STATE_F16 = 1 << 3
 GDN_STATE_BF16 = 1 << 4
+GDN_NORM_SIGMOID = 1 << 5
 _STATE_FLAGS = {torch.float32: 0, torch.float16: GDN_STATE_F16, torch.bfloat16: GDN_STATE_BF16}
 
 _TORCH_DT = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
 
-EXPORTS = ("gdn_gate", "gdn_decode", "gdn_prefill_varlen_workspace_size",
-           "gdn_prefill_varlen", "gdn_last_error")
+EXPORTS = ("gdn_gate", "gdn_decode", "gdn_decode_gated_norm", "gdn_rmsnorm_gated",
+           "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_last_error")
 
 
 class GdnError(RuntimeError):
@@ -57,6 +58,13 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode.restype = i32
     lib.gdn_decode.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i32, i64, vp, vp,
                                vp, i64, vp, i64, vp, i64, i64, i64, i64, i64, f32, f32, u32, vp]
+    lib.gdn_decode_gated_norm.restype = i32
+    lib.gdn_decode_gated_norm.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i32, i64,
+                                          vp, vp, vp, i64, vp, i64, vp, i64, i64, i64, i64, i64,
+                                          f32, f32, vp, i64, vp, f32, u32, vp]
+    lib.gdn_rmsnorm_gated.restype = i32
+    lib.gdn_rmsnorm_gated.argtypes = [vp, i32, vp, i32, vp, i64, vp, i64, i64, i64, f32, u32,
+                                      vp]
     lib.gdn_prefill_varlen_workspace_size.restype = sz
     lib.gdn_prefill_varlen_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32, u32]
     lib.gdn_prefill_varlen.restype = i32
@@ -148,6 +156,28 @@ def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale
     bfloat16: widened to f32 for the step, the new state rounded on store);
     state_idx [B] int32.  check_slots: validate state_idx first (GDN_CHECK_SLOTS:
     reads it back and waits on the stream; not capturable)."""
+    return _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, scale=scale,
+                   l2norm=l2norm, l2_eps=l2_eps, out=out, out_dtype=out_dtype,
+                   check_slots=check_slots, stream=stream, norm=None)
+
+
+def decode_gated_norm(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, norm_z,
+                      norm_w, *, scale: float, norm_eps: float = 1e-6, sigmoid: bool = False,
+                      l2norm: bool = True, l2_eps: float = 1e-6,
+                      out: Optional[torch.Tensor] = None, out_dtype=None,
+                      check_slots: bool = False, stream=None) -> torch.Tensor:
+    """decode() with the gated RMSNorm fused after the step:
+    out = o / sqrt(mean(o^2) + norm_eps) * norm_w * act(norm_z), act = silu or
+    sigmoid.  norm_z: [B, Hv, Dv] (rows may be padded views of a wider
+    buffer) and norm_w: [Dv], both in q's dtype."""
+    return _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, scale=scale,
+                   l2norm=l2norm, l2_eps=l2_eps, out=out, out_dtype=out_dtype,
+                   check_slots=check_slots, stream=stream,
+                   norm=(norm_z, norm_w, norm_eps, sigmoid))
+
+
+def _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale, l2norm,
+            l2_eps, out, out_dtype, check_slots, stream, norm):
     lib = load_library()
     if state_pool.dim() != 4 or not state_pool.is_contiguous():
         raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
@@ -170,13 +200,51 @@ def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale
         raise GdnError(-3, "out: need contiguous [B, Hv, Dv]")
     flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_CHECK_SLOTS if check_slots else 0) |
              _state_flags(state_pool))
-    _check(lib.gdn_decode(
-        _dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
-        q_rs, k_rs, v_rs, _dev(alpha, "alpha"), _dt(alpha), a_rs,
-        _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
-        _dev(beta, "beta", torch.float32), b_rs, _dev(state_pool, "state_pool"),
-        slots, _dev(state_idx, "state_idx", torch.int32), B, hk, hv, dk, dv, float(scale),
-        float(l2_eps), flags, _stream(stream)))
+    args = [_dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
+            q_rs, k_rs, v_rs, _dev(alpha, "alpha"), _dt(alpha), a_rs,
+            _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
+            _dev(beta, "beta", torch.float32), b_rs, _dev(state_pool, "state_pool"),
+            slots, _dev(state_idx, "state_idx", torch.int32), B, hk, hv, dk, dv, float(scale),
+            float(l2_eps)]
+    if norm is None:
+        _check(lib.gdn_decode(*args, flags, _stream(stream)))
+        return out
+    z, w, eps, sigmoid = norm
+    if z.shape[0] != B:
+        raise GdnError(-3, f"norm_z: {z.shape[0]} rows, state_idx has {B}")
+    z_rs = _rows(z, "norm_z", hv, dv)
+    if w.dim() != 1 or w.shape[0] != dv or not w.is_contiguous():
+        raise GdnError(-3, f"norm_w: need contiguous [{dv}]")
+    flags |= GDN_NORM_SIGMOID if sigmoid else 0
+    _check(lib.gdn_decode_gated_norm(*args, _dev(z, "norm_z", q.dtype), z_rs,
+                                     _dev(w, "norm_w", q.dtype), float(eps), flags,
+                                     _stream(stream)))
+    return out
+
+
+def rmsnorm_gated(x, z, w, *, eps: float = 1e-6, sigmoid: bool = False,
+                  out: Optional[torch.Tensor] = None, out_dtype=None,
+                  stream=None) -> torch.Tensor:
+    """Gated RMSNorm: out = x / sqrt(mean(x^2) + eps) * w * act(z) per
+    (row, head), act = silu or sigmoid.  x: [T, Hv, Dv] contiguous; z: [T, Hv, Dv]
+    (rows may be padded views of a wider buffer); w: [Dv]; all one dtype."""
+    lib = load_library()
+    if x.dim() != 3 or not x.is_contiguous():
+        raise GdnError(-3, "x: need contiguous [T, Hv, Dv]")
+    T, hv, dv = x.shape
+    if z.shape[0] != T:
+        raise GdnError(-3, f"z: {z.shape[0]} rows, x has {T}")
+    z_rs = _rows(z, "z", hv, dv)
+    if w.dim() != 1 or w.shape[0] != dv or not w.is_contiguous():
+        raise GdnError(-3, f"w: need contiguous [{dv}]")
+    if out is None:
+        out = torch.empty((T, hv, dv), dtype=out_dtype or x.dtype, device=x.device)
+    if not out.is_contiguous() or tuple(out.shape) != (T, hv, dv):
+        raise GdnError(-3, "out: need contiguous [T, Hv, Dv]")
+    _check(lib.gdn_rmsnorm_gated(_dev(out, "out"), _dt(out), _dev(x, "x"), _dt(x),
+                                 _dev(z, "z", x.dtype), z_rs, _dev(w, "w", x.dtype), T, hv, dv,
+                                 float(eps), GDN_NORM_SIGMOID if sigmoid else 0,
+                                 _stream(stream)))
     return out
 
 

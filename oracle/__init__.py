@@ -241,3 +241,32 @@ def prefill_case(case, head_mask=None, pool=None, state_dt=F32):
                           pool=case.pool if pool is None else pool, idx=case.idx,
                           has_init=case.has_init, scale=case.scale, l2_eps=case.l2_eps,
                           l2norm=case.l2norm, head_mask=head_mask, state_dt=state_dt)
+
+
+def _norm_rows(norm, total_rows, rows=None):
+    z = norm.z
+    assert z.offset == 0
+    zbuf = z.buf.reshape(total_rows, z.row_stride)
+    if rows is not None:
+        zbuf = zbuf[np.asarray(rows)]
+    return np.ascontiguousarray(zbuf)
+
+
+def decode_norm_case(case, norm, *, sigmoid=False, rows=None, pool=None, state_dt=F32):
+    """Oracle for a decode step followed by the gated RMSNorm of its f64
+    outputs (workloads.NormInputs supplies z and w).  Returns (y, states)."""
+    out, st = decode_case(case, rows=rows, pool=pool, state_dt=state_dt)
+    zb = _norm_rows(norm, case.batch, rows)
+    y = rmsnorm_gated(out, F64, zb, norm.dtype, norm.z.row_stride, norm.w, norm.dtype,
+                      rows=out.shape[0], hv=case.hv, dv=case.dv, eps=norm.eps, sigmoid=sigmoid)
+    return y, st
+
+
+def prefill_norm_case(case, norm, *, sigmoid=False, head_mask=None):
+    """Oracle for the varlen prefill followed by the gated RMSNorm of its f64
+    outputs.  Returns (y, final states)."""
+    out, st = prefill_case(case, head_mask=head_mask)
+    zb = _norm_rows(norm, case.total_tokens)
+    y = rmsnorm_gated(out, F64, zb, norm.dtype, norm.z.row_stride, norm.w, norm.dtype,
+                      rows=out.shape[0], hv=case.hv, dv=case.dv, eps=norm.eps, sigmoid=sigmoid)
+    return y, st

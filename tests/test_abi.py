@@ -129,3 +129,49 @@ def test_check_slots_flag_is_known():
     assert _decode(lib, flags=1 | (1 << 1)) == -1 and "null pointer" in _err(lib)
     assert _prefill(lib, flags=1 | (1 << 1)) == -1 and "null pointer" in _err(lib)
     assert B.GDN_CHECK_SLOTS == 1 << 1
+
+
+def _norm(lib, **kw):
+    a = dict(out=None, out_dt=2, x=None, x_dt=2, z=None, z_rs=3072, w=None, rows=16, hv=24,
+             dv=128, eps=1e-6, flags=0, stream=None)
+    a.update(kw)
+    return lib.gdn_rmsnorm_gated(*a.values())
+
+
+def test_rmsnorm_gated_argument_errors():
+    lib = pkg.load_library()
+    assert _norm(lib, x_dt=5) == -2
+    assert _norm(lib, out_dt=1) == -2                   # f16 out from bf16 x
+    assert _norm(lib, flags=1 << 6) == -1
+    assert _norm(lib, flags=1) == -1                    # not a norm flag
+    assert _norm(lib, eps=-1.0) == -1
+    assert _norm(lib, eps=float("nan")) == -1
+    assert _norm(lib, z_rs=3071) == -3
+    assert _norm(lib, hv=0) == -3
+    assert _norm(lib, flags=1 << 5) == -1 and "null pointer" in _err(lib)
+    assert _err(lib).startswith("gdn_rmsnorm_gated:")
+    assert _norm(lib, rows=0) == 0
+
+
+def _decode_norm(lib, **kw):
+    a = dict(out=None, out_dt=2, q=None, k=None, v=None, in_dt=2, q_rs=2048, k_rs=2048,
+             v_rs=4096, alpha=None, alpha_dt=0, alpha_rs=32, dt_bias=None, ssm_a=None,
+             beta=None, beta_rs=32, pool=None, slots=8, idx=None, batch=4, hk=16, hv=32,
+             dk=128, dv=128, scale=0.088, eps=1e-6, z=None, z_rs=4096, w=None, neps=1e-6,
+             flags=1, stream=None)
+    a.update(kw)
+    return lib.gdn_decode_gated_norm(*a.values())
+
+
+def test_decode_gated_norm_argument_errors():
+    lib = pkg.load_library()
+    assert _decode_norm(lib, dk=256, dv=136) == -3 and "dv <= 128" in _err(lib)
+    assert _decode_norm(lib, dk=128, dv=264) == -3 and "dv <= 256" in _err(lib)
+    assert _decode_norm(lib, dk=64, dv=520) == -3 and "dv <= 512" in _err(lib)
+    assert _decode_norm(lib, neps=-1.0) == -1
+    assert _decode_norm(lib, flags=1 | (1 << 6)) == -1
+    # the sigmoid flag belongs to the norm entry points only
+    assert _decode(lib, flags=1 | (1 << 5)) == -1 and "unknown flags" in _err(lib)
+    assert _decode_norm(lib, flags=1 | (1 << 5)) == -1 and "null pointer" in _err(lib)
+    assert _err(lib).startswith("gdn_decode_gated_norm:")
+    assert _decode_norm(lib, batch=0) == 0

@@ -341,3 +341,28 @@ def decode_packed_b1024(seed: int = 505) -> DecodeCase:
     return make_decode_case("decode-packed-B1024-Hk16-Hv32-D128-f16", seed, batch=1024,
                             hk=16, hv=32, dk=128, dv=128, in_dtype=F16, out_dtype=F16,
                             slots=4096, pool_std=0.05, packed_pad=256)
+
+
+# --------------------------------------------------------------------------
+# gated RMSNorm inputs (the norm after the recurrence)
+# --------------------------------------------------------------------------
+@dataclass
+class NormInputs:
+    z: View                  # gate [rows, hv, dv] inside padded token rows
+    w: np.ndarray            # [dv] weight, storage dtype
+    dtype: int
+    eps: float = 1e-6
+
+
+def norm_inputs(seed: int, rows: int, hv: int, dv: int, dtype: int, *, pad: int = 0,
+                z_range: float = 6.0) -> NormInputs:
+    """Gate z ~ U(-z_range, z_range) in token rows of hv*dv + pad elements (the
+    padding holds NaN, which must never be read) and weight w ~ U(-1, 1),
+    encoded in `dtype` (the ranges of the pages' gated-norm kernel tests)."""
+    rng = np.random.default_rng([seed, 0x9A7E])
+    z = rng.uniform(-z_range, z_range, size=(rows, hv * dv))
+    w = rng.uniform(-1.0, 1.0, size=dv)
+    buf = nan_fill((rows, hv * dv + pad), dtype)
+    buf[:, :hv * dv] = encode(z, dtype)
+    return NormInputs(z=View(np.ascontiguousarray(buf), 0, hv * dv + pad, dtype),
+                      w=encode(w, dtype), dtype=dtype)
