@@ -62,6 +62,13 @@ def _load():
         lib.oracle_prefill_varlen.argtypes = [i64, vp, i64, i64, i64, i64, vp, vp, vp, i32,
                                               i64, i64, i64, vp, vp, i64, vp, i32, i64, vp,
                                               vp, dbl, dbl, i32, vp, vp, vp]
+        lib.oracle_round_through.restype = dbl
+        lib.oracle_round_through.argtypes = [ctypes.c_float, i32]
+        lib.oracle_gate_beta.restype = i32
+        lib.oracle_gate_beta.argtypes = [i64, i64, vp, vp, i32, i64, i64, vp, vp, i32, vp, vp]
+        lib.oracle_post_conv.restype = i32
+        lib.oracle_post_conv.argtypes = [i64, i64, i64, i64, i64, vp, i32, i64, vp, vp, i32,
+                                         i64, i64, vp, vp, dbl, vp, vp, vp, vp, vp]
         lib.oracle_rmsnorm_gated.restype = i32
         lib.oracle_rmsnorm_gated.argtypes = [i64, i64, i64, vp, i32, vp, i32, i64, vp, i32,
                                              dbl, i32, vp]
@@ -181,6 +188,47 @@ def prefill_varlen(*, cu_seqlens, hk, hv, dk, dv, q, q_off, q_rs, k, k_off, k_rs
     if rc:
         raise OracleError(f"oracle_prefill_varlen: error {rc}")
     return out, st
+
+
+def round_through(x: float, dt: int) -> float:
+    return _load().oracle_round_through(float(x), dt)
+
+
+def gate_beta(a_buf, a_off, a_rs, b_buf, b_off, b_rs, ab_dt, dt_bias, ssm_a, *, rows, hv,
+              round_beta=False):
+    """g and beta [rows, hv] f64 from raw a and b read as buf.flat[off + r*rs + h]
+    (views of one merged row allowed).  round_beta: beta rounded through the
+    storage dtype (the packed decode's rule)."""
+    lib = _load()
+    g = np.empty((rows, hv), dtype=np.float64)
+    beta = np.empty((rows, hv), dtype=np.float64)
+    ea, eb = a_buf.itemsize, b_buf.itemsize
+    rc = lib.oracle_gate_beta(rows, hv, a_buf.ctypes.data + a_off * ea,
+                              b_buf.ctypes.data + b_off * eb, ab_dt, a_rs, b_rs,
+                              _p(_need(dt_bias, np.float32)), _p(_need(ssm_a, np.float32)),
+                              int(bool(round_beta)), _p(g), _p(beta))
+    if rc:
+        raise OracleError(f"oracle_gate_beta: error {rc}")
+    return g, beta
+
+
+def post_conv(conv, conv_dt, conv_rs, a_buf, a_off, a_rs, b_buf, b_off, b_rs, ab_dt, dt_bias,
+              ssm_a, *, T, hk, hv, dk, dv, l2_eps=1e-6):
+    """The post-conv front-end: (q, k normalised [T,hk,dk], v [T,hv,dv], g, beta
+    [T,hv]), all f64."""
+    lib = _load()
+    conv = np.ascontiguousarray(conv)
+    q = np.empty((T, hk, dk)); k = np.empty((T, hk, dk)); v = np.empty((T, hv, dv))
+    g = np.empty((T, hv)); beta = np.empty((T, hv))
+    ea, eb = a_buf.itemsize, b_buf.itemsize
+    rc = lib.oracle_post_conv(T, hk, hv, dk, dv, _p(conv), conv_dt, conv_rs,
+                              a_buf.ctypes.data + a_off * ea, b_buf.ctypes.data + b_off * eb,
+                              ab_dt, a_rs, b_rs, _p(_need(dt_bias, np.float32)),
+                              _p(_need(ssm_a, np.float32)), float(l2_eps), _p(q), _p(k), _p(v),
+                              _p(g), _p(beta))
+    if rc:
+        raise OracleError(f"oracle_post_conv: error {rc}")
+    return q, k, v, g, beta
 
 
 def rmsnorm_gated(x, x_dt, z, z_dt, z_row_stride, w, w_dt, *, rows, hv, dv, eps,

@@ -28,7 +28,11 @@
  *       out-of-range live slots are errors);
  *      "l2norm: plain sum of squares over the last dim";
  *      "rmsnorm_gated: norm-then-gate, silu and sigmoid activations" and the
- *       rank-3 padded-row gate case (the gated RMSNorm after the recurrence).
+ *       rank-3 padded-row gate case (the gated RMSNorm after the recurrence);
+ *      "gdn_post_conv fused == composed" and the packed in_proj_ba case (the
+ *       front-end: conv output split into q, k, v, q/k normalised, g and
+ *       beta = sigmoid(b) from a and b views of one merged row);
+ *      PackedDecodeReference's beta, sigmoid(b) rounded through b's dtype.
  *
  * Parity pins live in tests/test_oracle_pins.py (the pages' worked values and
  * the invariants listed there).
@@ -357,4 +361,100 @@ int oracle_rmsnorm_gated(int64_t rows, int64_t hv, int64_t dv, const void* x, in
     }
   }
   return OR_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Rounding a binary32 value through a 16-bit storage format (nearest, ties to
+ * even), returned widened.  Written from the format definitions:
+ *  bfloat16 keeps the top 16 bits of the binary32 pattern;
+ *  binary16 has a quantum of 2^(e-10) for 2^-14 <= |x| (e = floor(log2|x|)),
+ *  2^-24 below that, and overflows to infinity past 65504.
+ * ------------------------------------------------------------------------ */
+static double round_through(float x, int dt) {
+  if (dt == OR_F32 || isnan(x) || isinf(x)) return (double)x;
+  if (dt == OR_BF16) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    const uint32_t lsb = (u >> 16) & 1u;
+    u = (u + 0x7fffu + lsb) & 0xffff0000u;
+    float r;
+    memcpy(&r, &u, 4);
+    return (double)r;
+  }
+  /* binary16 */
+  const double ax = fabs((double)x);
+  if (ax == 0.0) return (double)x;
+  const int e = ilogb(ax);
+  const double quantum = e < -14 ? ldexp(1.0, -24) : ldexp(1.0, e - 10);
+  double r = nearbyint(ax / quantum) * quantum; /* default mode: ties to even */
+  if (r > 65504.0) r = INFINITY;
+  return x < 0 ? -r : r;
+}
+
+/* The pages' beta: the logistic function evaluated in binary32. */
+static float sigmoid_f32(float b) { return 1.0f / (1.0f + expf(-b)); }
+
+/* exported so the tests can pin the rounding against the format definitions */
+double oracle_round_through(float x, int dt) { return round_through(x, dt); }
+
+/* ------------------------------------------------------------------------
+ * Gate and beta from raw projections (vllm.cpp "GdnGBeta"; the packed
+ * in_proj_ba case: a and b are column views of one merged row, each with its
+ * own row stride and offset, in one dtype):
+ *   g    = softplus(a + dt_bias) * ssm_a             (as oracle_gate)
+ *   beta = sigmoid(b)                                 (round_beta == 0)
+ *        = sigmoid(b) rounded through b's dtype       (round_beta != 0,
+ *          PackedDecodeReference)
+ * sigmoid in binary32 as the pages compute it; g and beta returned in f64.
+ * ------------------------------------------------------------------------ */
+int oracle_gate_beta(int64_t rows, int64_t hv, const void* a, const void* b, int ab_dt,
+                     int64_t a_row_stride, int64_t b_row_stride, const float* dt_bias,
+                     const float* ssm_a, int round_beta, double* g, double* beta) {
+  if (rows < 0 || hv <= 0 || a_row_stride < hv || b_row_stride < hv) return OR_ERR_SHAPE;
+  if (ab_dt != OR_F32 && ab_dt != OR_F16 && ab_dt != OR_BF16) return OR_ERR_ARG;
+  int rc = oracle_gate(rows, hv, a, ab_dt, a_row_stride, dt_bias, ssm_a, g);
+  if (rc) return rc;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t h = 0; h < hv; ++h) {
+      const float bv = (float)load_elem(b, ab_dt, r * b_row_stride + h);
+      const float s = sigmoid_f32(bv);
+      beta[r * hv + h] = round_beta ? round_through(s, ab_dt) : (double)s;
+    }
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Post-conv front-end (vllm.cpp "gdn_post_conv fused == composed"): token t's
+ * conv output row (conv_dt, row stride conv_row_stride) holds q in columns
+ * [0, Hk*Dk), k in [Hk*Dk, 2*Hk*Dk) and v in [2*Hk*Dk, 2*Hk*Dk + Hv*Dv).
+ *   q_out, k_out [T][Hk][Dk]: x / sqrt(sum x^2 + l2_eps) per head (no scale)
+ *   v_out [T][Hv][Dv]: copied
+ *   g, beta [T][Hv]: oracle_gate_beta with round_beta = 0
+ * All outputs f64.
+ * ------------------------------------------------------------------------ */
+int oracle_post_conv(int64_t T, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
+                     const void* conv, int conv_dt, int64_t conv_row_stride, const void* a,
+                     const void* b, int ab_dt, int64_t a_row_stride, int64_t b_row_stride,
+                     const float* dt_bias, const float* ssm_a, double l2_eps, double* q_out,
+                     double* k_out, double* v_out, double* g, double* beta) {
+  if (T < 0 || hk <= 0 || hv <= 0 || dk <= 0 || dv <= 0) return OR_ERR_SHAPE;
+  if (conv_row_stride < 2 * hk * dk + hv * dv) return OR_ERR_SHAPE;
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t row = t * conv_row_stride;
+    for (int64_t h = 0; h < hk; ++h) {
+      double* qo = q_out + (t * hk + h) * dk;
+      double* ko = k_out + (t * hk + h) * dk;
+      for (int64_t j = 0; j < dk; ++j) {
+        qo[j] = load_elem(conv, conv_dt, row + h * dk + j);
+        ko[j] = load_elem(conv, conv_dt, row + hk * dk + h * dk + j);
+      }
+      l2_normalize(qo, dk, l2_eps);
+      l2_normalize(ko, dk, l2_eps);
+    }
+    for (int64_t i = 0; i < hv * dv; ++i)
+      v_out[t * hv * dv + i] = load_elem(conv, conv_dt, row + 2 * hk * dk + i);
+  }
+  return oracle_gate_beta(T, hv, a, b, ab_dt, a_row_stride, b_row_stride, dt_bias, ssm_a, 0, g,
+                          beta);
 }
