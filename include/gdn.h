@@ -69,7 +69,9 @@ enum {
   GDN_PREFILL_SEQUENTIAL = 1u << 2,  /* prefill: force the token-sequential kernel */
   GDN_STATE_F16 = 1u << 3,           /* state pool stored as IEEE binary16 */
   GDN_STATE_BF16 = 1u << 4,          /* state pool stored as bfloat16 */
-  GDN_NORM_SIGMOID = 1u << 5         /* gated norm: sigmoid gate instead of silu */
+  GDN_NORM_SIGMOID = 1u << 5,        /* gated norm: sigmoid gate instead of silu */
+  GDN_BETA_RAW = 1u << 6,            /* decode: beta is the raw projection b */
+  GDN_BETA_ROUNDED = 1u << 7         /* gate_beta/post_conv: round sigmoid(b) to b's dtype */
 };
 /*
  * Slot check (flag GDN_CHECK_SLOTS).  vllm.cpp test_ops_gdn.cpp, "gdn packed
@@ -107,6 +109,44 @@ int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_
              int64_t rows, int64_t hv, hipStream_t stream);
 
 /*
+ * gdn_gate_beta -- g and beta from the raw projections a and b (vllm.cpp
+ * test_ops_gdn.cpp, GdnGBeta and the packed in_proj_ba case):
+ *   g[r][h]    = softplus(a[r][h] + dt_bias[h]) * ssm_a[h]      (as gdn_gate)
+ *   beta[r][h] = sigmoid(b[r][h]) in f32; with GDN_BETA_ROUNDED rounded
+ *                through ab_dt (the packed decode's rule).
+ *   g, beta    [rows, hv] f32 outputs, row stride out_row_stride (>= hv).
+ *   a_raw, b_raw  [rows, hv] in ab_dt with their own row strides (>= hv):
+ *                 e.g. column views of one merged [rows, 2*hv] b|a row.
+ *   dt_bias, ssm_a  [hv] f32.
+ * rows == 0 enqueues nothing.
+ */
+int gdn_gate_beta(float* g, float* beta, int64_t out_row_stride, const void* a_raw,
+                  const void* b_raw, gdn_dtype ab_dt, int64_t a_row_stride,
+                  int64_t b_row_stride, const float* dt_bias, const float* ssm_a, int64_t rows,
+                  int64_t hv, uint32_t flags, hipStream_t stream);
+
+/*
+ * gdn_post_conv -- the front-end after the causal conv (vllm.cpp
+ * test_ops_gdn.cpp, "gdn_post_conv fused == composed"): token t's conv row
+ * (conv_dt, row stride conv_row_stride >= 2*hk*dk + hv*dv) holds q in columns
+ * [0, hk*dk), k in [hk*dk, 2*hk*dk), v in [2*hk*dk, 2*hk*dk + hv*dv).
+ *   q_out, k_out [T, hk, dk] contiguous, out_dt: q and k L2-normalised per
+ *                head with l2_eps inside the root (no scale).
+ *   v_out        [T, hv, dv] contiguous, out_dt: v converted.
+ *   g_out, beta_out  [T, hv] f32 contiguous: as gdn_gate_beta from a_raw /
+ *                b_raw (ab_dt, own row strides); flags: GDN_BETA_ROUNDED.
+ * gdn_decode and gdn_prefill_varlen can read the conv rows directly (q, k, v
+ * as row-strided views, norm in-kernel), so this pass is for callers that
+ * want q, k, v materialised.  total_tokens == 0 enqueues nothing.
+ */
+int gdn_post_conv(void* q_out, void* k_out, void* v_out, gdn_dtype out_dt, float* g_out,
+                  float* beta_out, const void* conv, gdn_dtype conv_dt, int64_t conv_row_stride,
+                  const void* a_raw, const void* b_raw, gdn_dtype ab_dt, int64_t a_row_stride,
+                  int64_t b_row_stride, const float* dt_bias, const float* ssm_a,
+                  int64_t total_tokens, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
+                  float l2_eps, uint32_t flags, hipStream_t stream);
+
+/*
  * gdn_decode -- one token for each of `batch` sequences, gate fused, states
  * updated in place in a slot-indexed pool.
  * vllm.cpp test_ops_gdn.cpp: "gdn decode: hand-computed single step" (the
@@ -120,7 +160,11 @@ int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_
  *              into the same buffer with the same row stride.
  *   alpha      [batch, hv] in alpha_dt, row stride alpha_row_stride.
  *   dt_bias, ssm_a  [hv] f32.   beta [batch, hv] f32 (post-sigmoid),
- *              row stride beta_row_stride.
+ *              row stride beta_row_stride; with GDN_BETA_RAW it is instead
+ *              the raw projection b in alpha_dt (e.g. the b columns of the
+ *              merged b|a row that alpha also points into) and the step uses
+ *              sigmoid(b) computed in f32 and rounded through alpha_dt
+ *              (vllm.cpp PackedDecodeReference).
  *   state_pool [num_slots, hv, dv, dk] f32 (or binary16 / bfloat16 with
  *              GDN_STATE_F16 / GDN_STATE_BF16), read and written in place.
  *   state_idx  [batch] int32: row b uses slot state_idx[b].  A negative
@@ -130,15 +174,16 @@ int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_
  *              touched.  Two rows naming the same slot race (undefined).
  *   scale      > 0 and finite (usually 1/sqrt(dk)).
  *   flags      GDN_L2NORM_QK to normalise q and k with l2_eps; GDN_CHECK_SLOTS
- *              to validate state_idx first (negative entries allowed); at
- *              most one of GDN_STATE_F16, GDN_STATE_BF16.
+ *              to validate state_idx first (negative entries allowed);
+ *              GDN_BETA_RAW (see beta); at most one of GDN_STATE_F16,
+ *              GDN_STATE_BF16.
  * batch == 0 enqueues nothing and returns GDN_OK.
  */
 int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
                gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
                int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-               const float* beta, int64_t beta_row_stride, void* state_pool,
+               const void* beta, int64_t beta_row_stride, void* state_pool,
                int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
                uint32_t flags, hipStream_t stream);
@@ -168,7 +213,7 @@ int gdn_decode_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void
                           const void* v, gdn_dtype in_dt, int64_t q_row_stride,
                           int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
                           gdn_dtype alpha_dt, int64_t alpha_row_stride, const float* dt_bias,
-                          const float* ssm_a, const float* beta, int64_t beta_row_stride,
+                          const float* ssm_a, const void* beta, int64_t beta_row_stride,
                           void* state_pool, int64_t num_slots, const int32_t* state_idx,
                           int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
                           float scale, float l2_eps, const void* norm_z,

@@ -147,7 +147,81 @@ int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_
     return fail(GDN_ERR_SHAPE, "%s: row strides must be >= hv", op);
   if (rows == 0) return ok();
   if (!g || !alpha || !dt_bias || !ssm_a) return fail(GDN_ERR_ARG, "%s: null pointer", op);
-  gdn::GateArgs a{g, g_row_stride, alpha, alpha_dt, alpha_row_stride, dt_bias, ssm_a, rows, hv};
+  gdn::GateArgs a{};
+  a.g = g; a.g_rs = g_row_stride; a.alpha = alpha; a.alpha_dt = alpha_dt;
+  a.alpha_rs = alpha_row_stride; a.dt_bias = dt_bias; a.ssm_a = ssm_a; a.rows = rows; a.hv = hv;
+  return hip_status(op, gdn::launch_gate(a, stream));
+}
+
+int gdn_gate_beta(float* g, float* beta, int64_t out_row_stride, const void* a_raw,
+                  const void* b_raw, gdn_dtype ab_dt, int64_t a_row_stride,
+                  int64_t b_row_stride, const float* dt_bias, const float* ssm_a, int64_t rows,
+                  int64_t hv, uint32_t flags, hipStream_t stream) {
+  const char* op = "gdn_gate_beta";
+  if (rows < 0 || hv <= 0) return fail(GDN_ERR_SHAPE, "%s: rows >= 0 and hv > 0 required", op);
+  if (!valid_dt(ab_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown a/b dtype %d", op, ab_dt);
+  if (flags & ~(uint32_t)GDN_BETA_ROUNDED)
+    return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (out_row_stride < hv || a_row_stride < hv || b_row_stride < hv)
+    return fail(GDN_ERR_SHAPE, "%s: row strides must be >= hv", op);
+  if (rows == 0) return ok();
+  if (!g || !beta || !a_raw || !b_raw || !dt_bias || !ssm_a)
+    return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  const size_t eb = (size_t)elem_bytes(ab_dt);
+  if (!aligned(a_raw, eb) || !aligned(b_raw, eb) || !aligned(g, 4) || !aligned(beta, 4))
+    return fail(GDN_ERR_ARG, "%s: pointers must be aligned to their element size", op);
+  gdn::GateArgs a{};
+  a.g = g; a.g_rs = out_row_stride; a.alpha = a_raw; a.alpha_dt = ab_dt;
+  a.alpha_rs = a_row_stride; a.dt_bias = dt_bias; a.ssm_a = ssm_a; a.rows = rows; a.hv = hv;
+  a.b = b_raw; a.b_rs = b_row_stride; a.beta = beta; a.beta_rs = out_row_stride;
+  a.round_beta = (flags & GDN_BETA_ROUNDED) ? 1 : 0;
+  return hip_status(op, gdn::launch_gate(a, stream));
+}
+
+int gdn_post_conv(void* q_out, void* k_out, void* v_out, gdn_dtype out_dt, float* g_out,
+                  float* beta_out, const void* conv, gdn_dtype conv_dt, int64_t conv_row_stride,
+                  const void* a_raw, const void* b_raw, gdn_dtype ab_dt, int64_t a_row_stride,
+                  int64_t b_row_stride, const float* dt_bias, const float* ssm_a,
+                  int64_t total_tokens, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
+                  float l2_eps, uint32_t flags, hipStream_t stream) {
+  const char* op = "gdn_post_conv";
+  const int64_t T = total_tokens;
+  if (T < 0) return fail(GDN_ERR_SHAPE, "%s: negative total_tokens", op);
+  if (hk <= 0 || hv <= 0 || dk <= 0 || dv <= 0 || hv % hk != 0)
+    return fail(GDN_ERR_SHAPE, "%s: positive sizes and Hv a multiple of Hk required", op);
+  if (hk > (1 << 16) || hv > (1 << 20) || dk > (1 << 16) || dv > (1 << 20))
+    return fail(GDN_ERR_SHAPE, "%s: head counts or sizes too large", op);
+  if (!valid_dt(out_dt) || !valid_dt(conv_dt) || !valid_dt(ab_dt))
+    return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
+  if (flags & ~(uint32_t)GDN_BETA_ROUNDED)
+    return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (!(l2_eps >= 0.0f) || !isfinite(l2_eps))
+    return fail(GDN_ERR_ARG, "%s: l2_eps must be finite and >= 0", op);
+  if (conv_row_stride < 2 * hk * dk + hv * dv)
+    return fail(GDN_ERR_SHAPE, "%s: conv row stride below 2*Hk*Dk + Hv*Dv", op);
+  if (a_row_stride < hv || b_row_stride < hv)
+    return fail(GDN_ERR_SHAPE, "%s: a/b row strides must be >= hv", op);
+  if (T == 0) return ok();
+  if (!q_out || !k_out || !v_out || !g_out || !beta_out || !conv || !a_raw || !b_raw ||
+      !dt_bias || !ssm_a)
+    return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  const size_t eo = (size_t)elem_bytes(out_dt), ec = (size_t)elem_bytes(conv_dt),
+               eab = (size_t)elem_bytes(ab_dt);
+  if (!aligned(q_out, eo) || !aligned(k_out, eo) || !aligned(v_out, eo) || !aligned(conv, ec) ||
+      !aligned(a_raw, eab) || !aligned(b_raw, eab) || !aligned(g_out, 4) || !aligned(beta_out, 4))
+    return fail(GDN_ERR_ARG, "%s: pointers must be aligned to their element size", op);
+  if (T >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "%s: total_tokens too large", op);
+  gdn::PostConvArgs p{};
+  p.q = q_out; p.k = k_out; p.v = v_out; p.out_dt = out_dt; p.conv = conv; p.conv_dt = conv_dt;
+  p.conv_rs = conv_row_stride; p.T = T; p.hk = (int)hk; p.hv = (int)hv; p.dk = (int)dk;
+  p.dv = (int)dv; p.l2_eps = l2_eps;
+  const int rc = hip_status(op, gdn::launch_post_conv(p, stream));
+  if (rc) return rc;
+  gdn::GateArgs a{};
+  a.g = g_out; a.g_rs = hv; a.alpha = a_raw; a.alpha_dt = ab_dt; a.alpha_rs = a_row_stride;
+  a.dt_bias = dt_bias; a.ssm_a = ssm_a; a.rows = T; a.hv = hv;
+  a.b = b_raw; a.b_rs = b_row_stride; a.beta = beta_out; a.beta_rs = hv;
+  a.round_beta = (flags & GDN_BETA_ROUNDED) ? 1 : 0;
   return hip_status(op, gdn::launch_gate(a, stream));
 }
 
@@ -166,7 +240,7 @@ int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, cons
                 const void* v, gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                 int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
                 int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-                const float* beta, int64_t beta_row_stride, void* state_pool,
+                const void* beta, int64_t beta_row_stride, void* state_pool,
                 int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                 int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
                 const NormIn* norm, uint32_t flags, hipStream_t stream) {
@@ -179,7 +253,7 @@ int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, cons
   if (out_dt != GDN_F32 && out_dt != in_dt)
     return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
   const uint32_t known = GDN_L2NORM_QK | GDN_CHECK_SLOTS | GDN_STATE_F16 | GDN_STATE_BF16 |
-                         (norm ? (uint32_t)GDN_NORM_SIGMOID : 0u);
+                         GDN_BETA_RAW | (norm ? (uint32_t)GDN_NORM_SIGMOID : 0u);
   if (flags & ~known) return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
   if (norm) {
     if (!(norm->eps >= 0.0f) || !isfinite(norm->eps))
@@ -206,6 +280,9 @@ int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, cons
   if (v_row_stride < hv * dv || alpha_row_stride < hv || beta_row_stride < hv)
     return fail(GDN_ERR_SHAPE, "%s: v/alpha/beta row stride below its row width", op);
   if (!aligned(state_pool, 16)) return fail(GDN_ERR_ARG, "%s: state pool must be 16-byte aligned", op);
+  if (!aligned(alpha, (size_t)elem_bytes(alpha_dt)) ||
+      !aligned(beta, (flags & GDN_BETA_RAW) ? (size_t)elem_bytes(alpha_dt) : 4))
+    return fail(GDN_ERR_ARG, "%s: alpha/beta must be aligned to their element size", op);
   if (batch * hv > ((int64_t)1 << 40)) return fail(GDN_ERR_SHAPE, "%s: batch*hv too large", op);
   if (flags & GDN_CHECK_SLOTS) {
     std::vector<int32_t> h;
@@ -218,6 +295,7 @@ int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, cons
   a.qk_vec = qk_vector_ok(q, k, in_dt, q_row_stride, k_row_stride) ? 1 : 0;
   a.alpha = alpha; a.alpha_dt = alpha_dt; a.alpha_rs = alpha_row_stride;
   a.dt_bias = dt_bias; a.ssm_a = ssm_a; a.beta = beta; a.beta_rs = beta_row_stride;
+  a.beta_raw = (flags & GDN_BETA_RAW) ? 1 : 0;
   a.pool = state_pool; a.state_dt = state_dt; a.num_slots = num_slots; a.idx = state_idx;
   a.batch = batch;
   a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
@@ -237,7 +315,7 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
                gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
                int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-               const float* beta, int64_t beta_row_stride, void* state_pool,
+               const void* beta, int64_t beta_row_stride, void* state_pool,
                int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
                hipStream_t stream) {
@@ -251,7 +329,7 @@ int gdn_decode_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void
                           const void* v, gdn_dtype in_dt, int64_t q_row_stride,
                           int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
                           gdn_dtype alpha_dt, int64_t alpha_row_stride, const float* dt_bias,
-                          const float* ssm_a, const float* beta, int64_t beta_row_stride,
+                          const float* ssm_a, const void* beta, int64_t beta_row_stride,
                           void* state_pool, int64_t num_slots, const int32_t* state_idx,
                           int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
                           float scale, float l2_eps, const void* norm_z,

@@ -305,4 +305,14 @@ __device__ __forceinline__ float gate_value(float x, float ssm_a) {
   return sp * ssm_a;
 }
 
+// beta from the raw projection b: the logistic function in f32, optionally
+// rounded through b's 16-bit storage format (nearest even) and widened back.
+template <int DT>
+__device__ __forceinline__ float beta_from_raw(float b, bool round) {
+  const float s = 1.0f / (1.0f + expf(-b));
+  if constexpr (DT == kBF16) return round ? bf16_to_f32(f32_to_bf16(s)) : s;
+  else if constexpr (DT == kF16) return round ? f16_to_f32(f32_to_f16(s)) : s;
+  else return s;
+}
+
 }  // namespace gdn

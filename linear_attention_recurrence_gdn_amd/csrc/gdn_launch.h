@@ -17,6 +17,27 @@ struct GateArgs {
   const float* ssm_a;
   int64_t rows;
   int64_t hv;
+  // optional beta from the raw projection b (same dtype as alpha)
+  const void* b;       // nullptr: no beta
+  int64_t b_rs;
+  float* beta;
+  int64_t beta_rs;
+  int round_beta;      // sigmoid rounded through b's dtype
+};
+
+// Post-conv front-end: conv output rows [T, 2*hk*dk + hv*dv (+ padding)] ->
+// q, k normalised [T, hk, dk], v [T, hv, dv] (contiguous, out_dt).
+struct PostConvArgs {
+  void* q;
+  void* k;
+  void* v;
+  int out_dt;
+  const void* conv;
+  int conv_dt;
+  int64_t conv_rs;
+  int64_t T;
+  int hk, hv, dk, dv;
+  float l2_eps;
 };
 
 struct DecodeArgs {
@@ -33,8 +54,9 @@ struct DecodeArgs {
   int64_t alpha_rs;
   const float* dt_bias;
   const float* ssm_a;
-  const float* beta;
+  const void* beta;  // f32 post-sigmoid, or (beta_raw) the raw b in alpha_dt
   int64_t beta_rs;
+  int beta_raw;      // beta = sigmoid(b) rounded through alpha_dt
   void* pool;     // [slots, hv, dv, dk] in state_dt
   int state_dt;   // kF32, kF16 or kBF16 storage; the step is computed in f32
   int64_t num_slots;
@@ -93,6 +115,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
+hipError_t launch_post_conv(const PostConvArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // the fused-norm decode runs one workgroup (at most 16 waves) per (row,
 // v-head): the largest dv it takes at this dk

@@ -42,6 +42,13 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     const int64_t h = i - r * a.hv;
     const float x = load1(a.alpha, a.alpha_dt, r * a.alpha_rs + h) + a.dt_bias[h];
     a.g[r * a.g_rs + h] = gate_value(x, a.ssm_a[h]);
+    if (a.b) {
+      const float bv = load1(a.b, a.alpha_dt, r * a.b_rs + h);
+      const bool rnd = a.round_beta != 0;
+      a.beta[r * a.beta_rs + h] = a.alpha_dt == kBF16 ? beta_from_raw<kBF16>(bv, rnd)
+                                  : a.alpha_dt == kF16 ? beta_from_raw<kF16>(bv, rnd)
+                                                       : beta_from_raw<kF32>(bv, rnd);
+    }
   }
 }
 
@@ -156,7 +163,11 @@ __global__ __launch_bounds__(NORM ? 64 * kNormMaxWaves : 256) void decode_kernel
   const uint32_t ar = load_raw1<TAL>(a.alpha, b * a.alpha_rs + h);
   const float dtb = a.dt_bias[h];
   const float ssa = a.ssm_a[h];
-  const float beta = a.beta[b * a.beta_rs + h];
+  // beta is one value per (row, v-head): a wave-uniform scalar load either way
+  const float beta =
+      a.beta_raw ? beta_from_raw<TAL>(raw1_to_f32<TAL>(load_raw1<TAL>(a.beta, b * a.beta_rs + h)),
+                                      true)
+                 : static_cast<const float*>(a.beta)[b * a.beta_rs + h];
   uint32_t zr = 0, wr = 0;
   if constexpr (NORM) {
     const int row = min(myrow, a.dv - 1);

@@ -24,11 +24,14 @@ GDN_PREFILL_SEQUENTIAL = 1 << 2
 GDN_STATE_F16 = 1 << 3
 GDN_STATE_BF16 = 1 << 4
 GDN_NORM_SIGMOID = 1 << 5
+GDN_BETA_RAW = 1 << 6
+GDN_BETA_ROUNDED = 1 << 7
 _STATE_FLAGS = {torch.float32: 0, torch.float16: GDN_STATE_F16, torch.bfloat16: GDN_STATE_BF16}
 
 _TORCH_DT = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
 
-EXPORTS = ("gdn_gate", "gdn_decode", "gdn_decode_gated_norm", "gdn_rmsnorm_gated",
+EXPORTS = ("gdn_gate", "gdn_gate_beta", "gdn_post_conv", "gdn_decode", "gdn_decode_gated_norm",
+           "gdn_rmsnorm_gated",
            "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_last_error")
 
 
@@ -58,6 +61,11 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode.restype = i32
     lib.gdn_decode.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i32, i64, vp, vp,
                                vp, i64, vp, i64, vp, i64, i64, i64, i64, i64, f32, f32, u32, vp]
+    lib.gdn_gate_beta.restype = i32
+    lib.gdn_gate_beta.argtypes = [vp, vp, i64, vp, vp, i32, i64, i64, vp, vp, i64, i64, u32, vp]
+    lib.gdn_post_conv.restype = i32
+    lib.gdn_post_conv.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i64, vp, vp, i32, i64, i64,
+                                  vp, vp, i64, i64, i64, i64, i64, f32, u32, vp]
     lib.gdn_decode_gated_norm.restype = i32
     lib.gdn_decode_gated_norm.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i32, i64,
                                           vp, vp, vp, i64, vp, i64, vp, i64, i64, i64, i64, i64,
@@ -147,7 +155,8 @@ def gate(alpha: torch.Tensor, dt_bias: torch.Tensor, ssm_a: torch.Tensor,
 
 def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale: float,
            l2norm: bool = True, l2_eps: float = 1e-6, out: Optional[torch.Tensor] = None,
-           out_dtype=None, check_slots: bool = False, stream=None) -> torch.Tensor:
+           out_dtype=None, check_slots: bool = False, beta_raw: bool = False,
+           stream=None) -> torch.Tensor:
     """One decode step, gate fused, pool updated in place.
 
     q, k: [B, Hk, Dk]; v: [B, Hv, Dv] (rows may be strided, e.g. views into one
@@ -155,29 +164,32 @@ def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale
     state_pool [slots, Hv, Dv, Dk] contiguous, f32 or 16-bit storage (float16 /
     bfloat16: widened to f32 for the step, the new state rounded on store);
     state_idx [B] int32.  check_slots: validate state_idx first (GDN_CHECK_SLOTS:
-    reads it back and waits on the stream; not capturable)."""
+    reads it back and waits on the stream; not capturable).  beta_raw: beta is
+    the raw projection b in alpha's dtype (GDN_BETA_RAW: sigmoid(b) rounded
+    through that dtype)."""
     return _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, scale=scale,
                    l2norm=l2norm, l2_eps=l2_eps, out=out, out_dtype=out_dtype,
-                   check_slots=check_slots, stream=stream, norm=None)
+                   check_slots=check_slots, beta_raw=beta_raw, stream=stream, norm=None)
 
 
 def decode_gated_norm(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, norm_z,
                       norm_w, *, scale: float, norm_eps: float = 1e-6, sigmoid: bool = False,
                       l2norm: bool = True, l2_eps: float = 1e-6,
                       out: Optional[torch.Tensor] = None, out_dtype=None,
-                      check_slots: bool = False, stream=None) -> torch.Tensor:
+                      check_slots: bool = False, beta_raw: bool = False,
+                      stream=None) -> torch.Tensor:
     """decode() with the gated RMSNorm fused after the step:
     out = o / sqrt(mean(o^2) + norm_eps) * norm_w * act(norm_z), act = silu or
     sigmoid.  norm_z: [B, Hv, Dv] (rows may be padded views of a wider
     buffer) and norm_w: [Dv], both in q's dtype."""
     return _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, scale=scale,
                    l2norm=l2norm, l2_eps=l2_eps, out=out, out_dtype=out_dtype,
-                   check_slots=check_slots, stream=stream,
+                   check_slots=check_slots, beta_raw=beta_raw, stream=stream,
                    norm=(norm_z, norm_w, norm_eps, sigmoid))
 
 
 def _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale, l2norm,
-            l2_eps, out, out_dtype, check_slots, stream, norm):
+            l2_eps, out, out_dtype, check_slots, beta_raw, stream, norm):
     lib = load_library()
     if state_pool.dim() != 4 or not state_pool.is_contiguous():
         raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
@@ -199,11 +211,12 @@ def _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scal
     if not out.is_contiguous() or tuple(out.shape) != (B, hv, dv):
         raise GdnError(-3, "out: need contiguous [B, Hv, Dv]")
     flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_CHECK_SLOTS if check_slots else 0) |
-             _state_flags(state_pool))
+             (GDN_BETA_RAW if beta_raw else 0) | _state_flags(state_pool))
     args = [_dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
             q_rs, k_rs, v_rs, _dev(alpha, "alpha"), _dt(alpha), a_rs,
             _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
-            _dev(beta, "beta", torch.float32), b_rs, _dev(state_pool, "state_pool"),
+            _dev(beta, "beta", alpha.dtype if beta_raw else torch.float32), b_rs,
+            _dev(state_pool, "state_pool"),
             slots, _dev(state_idx, "state_idx", torch.int32), B, hk, hv, dk, dv, float(scale),
             float(l2_eps)]
     if norm is None:
@@ -220,6 +233,60 @@ def _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scal
                                      _dev(w, "norm_w", q.dtype), float(eps), flags,
                                      _stream(stream)))
     return out
+
+
+def gate_beta(a, b, dt_bias, ssm_a, *, rounded: bool = False, g=None, beta=None,
+              stream=None):
+    """g = softplus(a + dt_bias) * ssm_a and beta = sigmoid(b) ([rows, hv] f32 each)
+    from raw a and b ([rows, hv], one dtype, rows may be strided: e.g. column
+    views of one merged b|a row).  rounded: beta rounded through b's dtype."""
+    lib = load_library()
+    rows, hv = a.shape[0], dt_bias.shape[0]
+    a_rs = _rows2(a, "a", hv)
+    b_rs = _rows2(b, "b", hv)
+    if b.shape[0] != rows:
+        raise GdnError(-3, f"b: {b.shape[0]} rows, a has {rows}")
+    if g is None:
+        g = torch.empty((rows, hv), dtype=torch.float32, device=a.device)
+    if beta is None:
+        beta = torch.empty((rows, hv), dtype=torch.float32, device=a.device)
+    for name, t in (("g", g), ("beta", beta)):
+        if not t.is_contiguous() or tuple(t.shape) != (rows, hv):
+            raise GdnError(-3, f"{name}: need contiguous [{rows}, {hv}]")
+    _check(lib.gdn_gate_beta(_dev(g, "g", torch.float32), _dev(beta, "beta", torch.float32), hv,
+                             _dev(a, "a"), _dev(b, "b", a.dtype), _dt(a), a_rs, b_rs,
+                             _dev(dt_bias, "dt_bias", torch.float32),
+                             _dev(ssm_a, "ssm_a", torch.float32), rows, hv,
+                             GDN_BETA_ROUNDED if rounded else 0, _stream(stream)))
+    return g, beta
+
+
+def post_conv(conv, a, b, dt_bias, ssm_a, *, hk: int, dk: int, dv: int, l2_eps: float = 1e-6,
+              out_dtype=None, rounded: bool = False, stream=None):
+    """The post-conv front-end: conv [T, >= 2*hk*dk + hv*dv] (rows contiguous, may
+    be padded) -> (q, k [T, hk, dk] normalised, v [T, hv, dv], g, beta [T, hv])."""
+    lib = load_library()
+    T = conv.shape[0]
+    hv = dt_bias.shape[0]
+    if conv.dim() != 2 or conv.stride(1) != 1 or conv.shape[1] < 2 * hk * dk + hv * dv:
+        raise GdnError(-3, "conv: need [T, >= 2*hk*dk + hv*dv] with contiguous rows")
+    conv_rs = conv.stride(0) if T > 1 else max(conv.stride(0), conv.shape[1])
+    a_rs = _rows2(a, "a", hv)
+    b_rs = _rows2(b, "b", hv)
+    od = out_dtype or conv.dtype
+    q = torch.empty((T, hk, dk), dtype=od, device=conv.device)
+    k = torch.empty((T, hk, dk), dtype=od, device=conv.device)
+    v = torch.empty((T, hv, dv), dtype=od, device=conv.device)
+    g = torch.empty((T, hv), dtype=torch.float32, device=conv.device)
+    beta = torch.empty((T, hv), dtype=torch.float32, device=conv.device)
+    _check(lib.gdn_post_conv(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q), _dev(g, "g"),
+                             _dev(beta, "beta"), _dev(conv, "conv"), _dt(conv), conv_rs,
+                             _dev(a, "a"), _dev(b, "b", a.dtype), _dt(a), a_rs, b_rs,
+                             _dev(dt_bias, "dt_bias", torch.float32),
+                             _dev(ssm_a, "ssm_a", torch.float32), T, hk, hv, dk, dv,
+                             float(l2_eps), GDN_BETA_ROUNDED if rounded else 0,
+                             _stream(stream)))
+    return q, k, v, g, beta
 
 
 def rmsnorm_gated(x, z, w, *, eps: float = 1e-6, sigmoid: bool = False,

@@ -175,3 +175,28 @@ def test_decode_gated_norm_argument_errors():
     assert _decode_norm(lib, flags=1 | (1 << 5)) == -1 and "null pointer" in _err(lib)
     assert _err(lib).startswith("gdn_decode_gated_norm:")
     assert _decode_norm(lib, batch=0) == 0
+
+
+def test_gate_beta_and_post_conv_argument_errors():
+    lib = pkg.load_library()
+    gb = lambda **kw: lib.gdn_gate_beta(*dict(dict(
+        g=None, beta=None, out_rs=24, a=None, b=None, ab_dt=2, a_rs=48, b_rs=48, dt_bias=None,
+        ssm_a=None, rows=8, hv=24, flags=0, stream=None), **kw).values())
+    assert gb(ab_dt=7) == -2
+    assert gb(flags=1 << 6) == -1                  # the decode-only raw-beta flag
+    assert gb(out_rs=23) == -3 and gb(a_rs=23) == -3 and gb(b_rs=23) == -3
+    assert gb(flags=1 << 7) == -1 and "null pointer" in _err(lib)
+    assert _err(lib).startswith("gdn_gate_beta:")
+    assert gb(rows=0) == 0
+    pc = lambda **kw: lib.gdn_post_conv(*dict(dict(
+        q=None, k=None, v=None, out_dt=2, g=None, beta=None, conv=None, conv_dt=2,
+        conv_rs=8192, a=None, b=None, ab_dt=2, a_rs=64, b_rs=64, dt_bias=None, ssm_a=None,
+        t=16, hk=16, hv=32, dk=128, dv=128, eps=1e-6, flags=0, stream=None), **kw).values())
+    assert pc(conv_rs=8191) == -3
+    assert pc(hv=33) == -3
+    assert pc(conv_dt=9) == -2
+    assert pc(eps=-1.0) == -1
+    assert pc(flags=1) == -1
+    assert pc() == -1 and "null pointer" in _err(lib)
+    assert _err(lib).startswith("gdn_post_conv:")
+    assert pc(t=0) == 0

@@ -366,3 +366,31 @@ def norm_inputs(seed: int, rows: int, hv: int, dv: int, dtype: int, *, pad: int 
     buf[:, :hv * dv] = encode(z, dtype)
     return NormInputs(z=View(np.ascontiguousarray(buf), 0, hv * dv + pad, dtype),
                       w=encode(w, dtype), dtype=dtype)
+
+
+# --------------------------------------------------------------------------
+# merged b|a projection rows (the packed in_proj_ba layout)
+# --------------------------------------------------------------------------
+@dataclass
+class MergedBA:
+    buf: np.ndarray          # [rows, prefix + 2*hv + suffix] storage, NaN canaries around
+    b_off: int               # column of b[., 0]
+    a_off: int               # column of a[., 0]
+    row_stride: int
+    dtype: int
+
+
+def merged_ba(seed: int, alpha: np.ndarray, dtype: int, *, prefix: int = 1, suffix: int = 3,
+              b_range: float = 3.0) -> MergedBA:
+    """Rows holding b in columns [prefix, prefix+hv) and a (= alpha, the raw
+    gate projection) in [prefix+hv, prefix+2hv), NaN elsewhere; raw b ~
+    U(-b_range, b_range), all encoded in `dtype`."""
+    rows, hv = alpha.shape
+    rng = np.random.default_rng([seed, 0xBA])
+    b = rng.uniform(-b_range, b_range, size=(rows, hv))
+    width = prefix + 2 * hv + suffix
+    buf = nan_fill((rows, width), dtype)
+    buf[:, prefix:prefix + hv] = encode(b, dtype)
+    buf[:, prefix + hv:prefix + 2 * hv] = encode(alpha, dtype)
+    return MergedBA(buf=np.ascontiguousarray(buf), b_off=prefix, a_off=prefix + hv,
+                    row_stride=width, dtype=dtype)
