@@ -69,6 +69,12 @@ def _load():
         lib.oracle_post_conv.restype = i32
         lib.oracle_post_conv.argtypes = [i64, i64, i64, i64, i64, vp, i32, i64, vp, vp, i32,
                                          i64, i64, vp, vp, dbl, vp, vp, vp, vp, vp]
+        lib.oracle_conv1d_fwd.restype = i32
+        lib.oracle_conv1d_fwd.argtypes = [i64, vp, i64, i64, vp, i32, i64, vp, vp, vp, i32, i64,
+                                          i64, vp, vp, i32, vp, vp]
+        lib.oracle_conv1d_update.restype = i32
+        lib.oracle_conv1d_update.argtypes = [i64, i64, i64, vp, i32, i64, vp, vp, vp, i32, i64,
+                                             i64, vp, i32, vp, vp, vp]
         lib.oracle_rmsnorm_gated.restype = i32
         lib.oracle_rmsnorm_gated.argtypes = [i64, i64, i64, vp, i32, vp, i32, i64, vp, i32,
                                              dbl, i32, vp]
@@ -318,3 +324,49 @@ def prefill_norm_case(case, norm, *, sigmoid=False, head_mask=None):
     y = rmsnorm_gated(out, F64, zb, norm.dtype, norm.z.row_stride, norm.w, norm.dtype,
                       rows=out.shape[0], hv=case.hv, dv=case.dv, eps=norm.eps, sigmoid=sigmoid)
     return y, st
+
+
+def conv1d_fwd(*, cu_seqlens, C, K, x, x_dt, x_rs, w, bias, state, st_dt, state_len,
+               idx=None, has_init=None, silu=True):
+    """Varlen depthwise causal conv.  x: storage buffer addressed as
+    x.flat[t*x_rs + c]; w [C, K], bias [C] or None (x_dt); state [slots, C,
+    state_len] (st_dt).  Returns (out [T, C] f64, new states [N, C, K-1] f64)."""
+    lib = _load()
+    cu = _need(np.asarray(cu_seqlens, dtype=np.int32), np.int32)
+    n = cu.shape[0] - 1
+    T = int(cu[-1])
+    out = np.zeros((T, C), dtype=np.float64)
+    st = np.zeros((n, C, max(K - 1, 0)), dtype=np.float64)
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    b = None if bias is None else np.ascontiguousarray(bias)
+    state = np.ascontiguousarray(state)
+    ia = None if idx is None else _need(np.asarray(idx, dtype=np.int32), np.int32)
+    hi = None if has_init is None else _need(np.asarray(has_init, dtype=np.int8), np.int8)
+    rc = lib.oracle_conv1d_fwd(n, _p(cu), C, K, _p(x), x_dt, x_rs, _p(w), _p(b), _p(state),
+                               st_dt, state_len, state.shape[0], _p(ia), _p(hi), int(bool(silu)),
+                               _p(out), _p(st))
+    if rc:
+        raise OracleError(f"oracle_conv1d_fwd: error {rc}")
+    return out, st
+
+
+def conv1d_update(*, batch, C, K, x, x_dt, x_rs, w, bias, state, st_dt, state_len, idx=None,
+                  silu=True):
+    """Single-token conv update.  Returns (out [B, C] f64, rolled states
+    [B, C, K-1] f64, written [B] bool: False for rows with a negative slot)."""
+    lib = _load()
+    out = np.zeros((batch, C), dtype=np.float64)
+    st = np.zeros((batch, C, max(K - 1, 0)), dtype=np.float64)
+    wr = np.zeros(batch, dtype=np.int8)
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    b = None if bias is None else np.ascontiguousarray(bias)
+    state = np.ascontiguousarray(state)
+    ia = None if idx is None else _need(np.asarray(idx, dtype=np.int32), np.int32)
+    rc = lib.oracle_conv1d_update(batch, C, K, _p(x), x_dt, x_rs, _p(w), _p(b), _p(state), st_dt,
+                                  state_len, state.shape[0], _p(ia), int(bool(silu)), _p(out),
+                                  _p(st), _p(wr))
+    if rc:
+        raise OracleError(f"oracle_conv1d_update: error {rc}")
+    return out, st, wr.astype(bool)

@@ -32,7 +32,10 @@
  *      "gdn_post_conv fused == composed" and the packed in_proj_ba case (the
  *       front-end: conv output split into q, k, v, q/k normalised, g and
  *       beta = sigmoid(b) from a and b views of one merged row);
- *      PackedDecodeReference's beta, sigmoid(b) rounded through b's dtype.
+ *      PackedDecodeReference's beta, sigmoid(b) rounded through b's dtype;
+ *      the causal_conv1d_fwd / causal_conv1d_update cases (depthwise causal
+ *       conv with a K-1 state per channel, bias, silu, varlen with
+ *       has_initial_state, the T < K-1 write-back, indexed and widened caches).
  *
  * Parity pins live in tests/test_oracle_pins.py (the pages' worked values and
  * the invariants listed there).
@@ -457,4 +460,103 @@ int oracle_post_conv(int64_t T, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
   }
   return oracle_gate_beta(T, hv, a, b, ab_dt, a_row_stride, b_row_stride, dt_bias, ssm_a, 0, g,
                           beta);
+}
+
+/* ------------------------------------------------------------------------
+ * Depthwise causal conv1d (vllm.cpp "causal_conv1d_fwd: bias + initial state,
+ * hand-computed", the short-sequence write-back case, "causal_conv1d_update:
+ * bias + rolling state", the indexed, widened-cache and padded-row cases).
+ * For channel c with taps w[c][0..K-1] (w[c][K-1] multiplies the current
+ * token) and the token's window (the K-1 inputs before it, then itself):
+ *   y = act(bias[c] + sum_j w[c][j] * window[j]),   act = silu or identity
+ * The state holds the K-1 raw (pre-activation) inputs before the next token;
+ * slot s's row for channel c starts at state[(s * C + c) * state_len]
+ * (state_len >= K-1; only the leading K-1 entries are used).
+ * Storage: x, w, bias in x_dt; state in st_dt (read widened, returned f64).
+ * ------------------------------------------------------------------------ */
+static double conv_act(double v, int silu) { return silu ? v / (1.0 + exp(-v)) : v; }
+
+/* Varlen forward.  Sequence s covers tokens [cu[s], cu[s+1]); its window
+ * before its first token is state row idx[s] (idx NULL: s) when has_init[s]
+ * (NULL: all 1), else zeros.  out [T][C] f64; state_out [num_seqs][C][K-1]
+ * f64: the last K-1 entries of (initial window, then the sequence's inputs). */
+int oracle_conv1d_fwd(int64_t num_seqs, const int32_t* cu, int64_t C, int64_t K,
+                      const void* x, int x_dt, int64_t x_row_stride, const void* w,
+                      const void* bias, const void* state, int st_dt, int64_t state_len,
+                      int64_t num_slots, const int32_t* idx, const int8_t* has_init, int silu,
+                      double* out, double* state_out) {
+  if (num_seqs < 0 || C <= 0 || K <= 0 || x_row_stride < C || state_len < K - 1)
+    return OR_ERR_SHAPE;
+  if (cu[0] != 0) return OR_ERR_SHAPE;
+  for (int64_t s = 0; s < num_seqs; ++s)
+    if (cu[s + 1] < cu[s]) return OR_ERR_SHAPE;
+  if (idx) {
+    int rc = check_slots(idx, num_seqs, num_slots, 0);
+    if (rc) return rc;
+  } else if (num_seqs > num_slots) {
+    return OR_ERR_SLOT;
+  }
+  double* win = (double*)malloc((size_t)K * sizeof(double));
+  if (!win) return OR_ERR_ARG;
+  for (int64_t s = 0; s < num_seqs; ++s) {
+    const int64_t slot = idx ? idx[s] : s;
+    const int init = has_init ? has_init[s] != 0 : 1;
+    for (int64_t c = 0; c < C; ++c) {
+      /* win[0..K-2]: the K-1 inputs before the current token */
+      for (int64_t j = 0; j < K - 1; ++j)
+        win[j] = init ? load_elem(state, st_dt, (slot * C + c) * state_len + j) : 0.0;
+      const double wc_last = load_elem(w, x_dt, c * K + K - 1);
+      const double b = bias ? load_elem(bias, x_dt, c) : 0.0;
+      for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
+        const double xt = load_elem(x, x_dt, t * x_row_stride + c);
+        double acc = b;
+        for (int64_t j = 0; j < K - 1; ++j) acc += load_elem(w, x_dt, c * K + j) * win[j];
+        acc += wc_last * xt;
+        out[t * C + c] = conv_act(acc, silu);
+        for (int64_t j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+        if (K > 1) win[K - 2] = xt;
+      }
+      for (int64_t j = 0; j < K - 1; ++j) state_out[(s * C + c) * (K - 1) + j] = win[j];
+    }
+  }
+  free(win);
+  return OR_OK;
+}
+
+/* Single-token update for `batch` rows: row r uses state slot idx[r] (idx
+ * NULL: r); a negative slot leaves its output row and every state alone (the
+ * caller's out is then kept, and out_written[r] = 0).  out [batch][C] f64;
+ * state_out [batch][C][K-1] f64: the rolled window (old entries shifted left,
+ * the raw input appended). */
+int oracle_conv1d_update(int64_t batch, int64_t C, int64_t K, const void* x, int x_dt,
+                         int64_t x_row_stride, const void* w, const void* bias,
+                         const void* state, int st_dt, int64_t state_len, int64_t num_slots,
+                         const int32_t* idx, int silu, double* out, double* state_out,
+                         int8_t* out_written) {
+  if (batch < 0 || C <= 0 || K <= 0 || x_row_stride < C || state_len < K - 1)
+    return OR_ERR_SHAPE;
+  if (idx) {
+    int rc = check_slots(idx, batch, num_slots, 1);
+    if (rc) return rc;
+  } else if (batch > num_slots) {
+    return OR_ERR_SLOT;
+  }
+  for (int64_t r = 0; r < batch; ++r) {
+    const int64_t slot = idx ? idx[r] : r;
+    out_written[r] = slot >= 0;
+    if (slot < 0) continue;
+    for (int64_t c = 0; c < C; ++c) {
+      const int64_t srow = (slot * C + c) * state_len;
+      const double xt = load_elem(x, x_dt, r * x_row_stride + c);
+      double acc = bias ? load_elem(bias, x_dt, c) : 0.0;
+      for (int64_t j = 0; j < K - 1; ++j)
+        acc += load_elem(w, x_dt, c * K + j) * load_elem(state, st_dt, srow + j);
+      acc += load_elem(w, x_dt, c * K + K - 1) * xt;
+      out[r * C + c] = conv_act(acc, silu);
+      double* so = state_out + (r * C + c) * (K - 1);
+      for (int64_t j = 0; j + 1 < K - 1; ++j) so[j] = load_elem(state, st_dt, srow + j + 1);
+      if (K > 1) so[K - 2] = xt;
+    }
+  }
+  return OR_OK;
 }
