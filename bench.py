@@ -119,6 +119,7 @@ def main():
                     help="skip the decode leg with a bf16 state pool")
     ap.add_argument("--no-norm", action="store_true",
                     help="skip the gated-RMSNorm legs (fused decode, norm after prefill)")
+    ap.add_argument("--no-conv", action="store_true", help="skip the conv1d legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale factor for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -276,6 +277,34 @@ def main():
         }
         log(f"decode + gated norm: kernel avg {kavg_n * 1e3:.1f} us")
 
+    # ---------------- conv1d update at the decode batch ----------------
+    if not args.no_conv:
+        C, K = 2 * hk * dk + hv * dv, 4
+        crng = np.random.default_rng([202, 0xC0])
+        ux = to_dev(W.encode(crng.normal(size=(B, C)).astype(np.float32), W.BF16).view(np.int16)
+                    ).view(torch.bfloat16)
+        uw = to_dev(W.encode(crng.uniform(-1, 1, size=(C, K)), W.BF16).view(np.int16)
+                    ).view(torch.bfloat16)
+        ust = torch.zeros((case.num_slots, C, K - 1), dtype=torch.bfloat16, device=dev)
+        uout = torch.empty_like(ux)
+
+        def conv_upd_step(i):
+            gdn.conv1d_update(ux, uw, None, ust, state_idx=subsets[i % 4], out=uout,
+                              stream=stream)
+
+        _, uk = timed(conv_upd_step, args.warmup, args.steps)
+        ubytes = 2 * B * C * 2 + 2 * B * C * (K - 1) * 2 + C * K * 2 + B * 4
+        uavg = float(uk.mean())
+        result["conv1d_update"] = {
+            "workload": f"conv1d update (K=4, silu) for the B=256 decode batch, {C} bf16 "
+                        f"channels, bf16 state rows from the 1024-slot cache",
+            "kernel_avg_us": round(uavg * 1e3, 2),
+            "algorithmic_bytes": ubytes,
+            "achieved_GBs": round(ubytes / (uavg * 1e-3) / 1e9, 1),
+        }
+        log(f"conv1d_update: kernel avg {uavg * 1e3:.1f} us")
+        del ust
+
     # ---------------- prefill leg ----------------
     if not args.no_prefill:
         pre = W.prefill_varlen_gqa3()
@@ -330,6 +359,33 @@ def main():
             "path": "chunked" if ws_n > 0 else "token-sequential",
         }
         log(f"prefill: {p_ms_step:.3f} ms/step -> {T / (p_ms_step * 1e-3) / 1e6:.2f} M tokens/s")
+
+        # the causal conv1d before the front-end, over the same tokens
+        if not args.no_conv:
+            C, K = 2 * pre.hk * pre.dk + pre.hv * pre.dv, 4
+            crng = np.random.default_rng([404, 0xC0])
+            cx = to_dev(W.encode(crng.normal(size=(T, C)).astype(np.float32), W.F16))
+            cw = to_dev(W.encode(crng.uniform(-1, 1, size=(C, K)), W.F16))
+            cst = torch.zeros((64, C, K - 1), dtype=torch.float16, device=dev)
+            cout = torch.empty_like(cx)
+
+            def conv_step(i):
+                gdn.conv1d_fwd(cx, cw, None, cst, pcu, state_idx=pidx, has_initial_state=phi,
+                               out=cout, stream=stream)
+
+            cwall, ck = timed(conv_step, 3, args.prefill_steps)
+            cbytes = 2 * T * C * 2 + 2 * N * C * (K - 1) * 2 + C * K * 2
+            cavg = float(ck.mean())
+            result["prefill"]["conv1d_fwd"] = {
+                "workload": f"depthwise causal conv1d (K=4, silu) over the 32768 packed tokens, "
+                            f"{C} fp16 channels (q|k|v), fp16 state from the 64-slot cache",
+                "kernel_avg_us": round(cavg * 1e3, 2),
+                "algorithmic_bytes": cbytes,
+                "achieved_GBs": round(cbytes / (cavg * 1e-3) / 1e9, 1),
+                "hbm_frac": round(cbytes / (cavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            }
+            log(f"prefill conv1d_fwd: kernel avg {cavg * 1e3:.1f} us")
+            del cx, cout
 
         # the gated RMSNorm over the prefill output (a separate HBM pass)
         if not args.no_norm:

@@ -71,7 +71,8 @@ enum {
   GDN_STATE_BF16 = 1u << 4,          /* state pool stored as bfloat16 */
   GDN_NORM_SIGMOID = 1u << 5,        /* gated norm: sigmoid gate instead of silu */
   GDN_BETA_RAW = 1u << 6,            /* decode: beta is the raw projection b */
-  GDN_BETA_ROUNDED = 1u << 7         /* gate_beta/post_conv: round sigmoid(b) to b's dtype */
+  GDN_BETA_ROUNDED = 1u << 7,        /* gate_beta/post_conv: round sigmoid(b) to b's dtype */
+  GDN_CONV_SILU = 1u << 8            /* conv1d: silu activation (else identity) */
 };
 /*
  * Slot check (flag GDN_CHECK_SLOTS).  vllm.cpp test_ops_gdn.cpp, "gdn packed
@@ -107,6 +108,63 @@ enum {
 int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_dt,
              int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
              int64_t rows, int64_t hv, hipStream_t stream);
+
+/*
+ * gdn_conv1d_fwd -- depthwise causal conv1d over sequences packed back to back
+ * (vllm.cpp test_ops_gdn.cpp, "causal_conv1d_fwd: bias + initial state,
+ * hand-computed", the short-sequence write-back case, the padded-row case
+ * and the CUDA varlen cases).  For channel c of token t in sequence s:
+ *   out[t][c] = act(bias[c] + sum_{j<K} weight[c][j] * window[j])
+ * where window[K-1] is x[t][c] and window[0..K-2] the K-1 inputs before it in
+ * the same sequence, taken from the state row before the sequence's first
+ * token (zeros when has_initial_state[s] == 0); act = silu with
+ * GDN_CONV_SILU, else identity.  Afterwards the state row holds the last
+ * K-1 raw inputs of (old window, the sequence's tokens): a sequence shorter
+ * than K-1 shifts the old window left (zeros without an initial state).
+ *   out          [total_tokens, channels] contiguous, out_dt (f32 or x_dt).
+ *   x            row t at x + t * x_row_stride (>= channels), x_dt.
+ *   weight       [channels, width] in x_dt;  bias [channels] in x_dt or NULL.
+ *   conv_state   [num_slots, channels, state_len] (state_len >= width-1;
+ *                only the leading width-1 entries are read or written, so a
+ *                widened cache keeps its extra columns), f32 or GDN_STATE_F16
+ *                / GDN_STATE_BF16; NULL allowed when width == 1.
+ *   state_idx    [num_seqs] slot per sequence, or NULL (slot s).
+ *   has_initial_state  [num_seqs] int8, or NULL (all 1).
+ *   cu_seqlens   [num_seqs + 1] int32 as for gdn_prefill_varlen (read on the
+ *                device; checked with GDN_CHECK_SLOTS, as are the slots).
+ *   width        1..8 (width 1 keeps no state: conv_state, state_idx and
+ *                num_slots are then unused).  flags: GDN_CONV_SILU,
+ *                GDN_CHECK_SLOTS, GDN_STATE_*.
+ * A sequence with an out-of-range slot gets NaN outputs and keeps no state.
+ * num_seqs == 0 enqueues nothing.
+ */
+int gdn_conv1d_fwd(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt,
+                   int64_t x_row_stride, const void* weight, const void* bias,
+                   void* conv_state, int64_t state_len, int64_t num_slots,
+                   const int32_t* state_idx, const int8_t* has_initial_state,
+                   const int32_t* cu_seqlens, int64_t num_seqs, int64_t total_tokens,
+                   int64_t channels, int64_t width, uint32_t flags, hipStream_t stream);
+
+/*
+ * gdn_conv1d_update -- one token per row through the conv, rolling each
+ * row's state (vllm.cpp test_ops_gdn.cpp, "causal_conv1d_update: bias +
+ * rolling state", the indexed in-place and widened-cache cases):
+ *   out[r][c] = act(bias[c] + sum_{j<K-1} weight[c][j] * state[j] +
+ *                   weight[c][K-1] * x[r][c]),
+ * then the state row shifts left by one and takes x[r][c] last.
+ *   out        [batch, channels] contiguous, out_dt.
+ *   x          row r at x + r * x_row_stride, x_dt.
+ *   conv_state as for gdn_conv1d_fwd; state_idx [batch] or NULL (row r).
+ *              A negative slot leaves that row's output and every state
+ *              untouched; an out-of-range slot writes NaN and touches no
+ *              state (GDN_CHECK_SLOTS rejects both duplicates and it).
+ * batch == 0 enqueues nothing.
+ */
+int gdn_conv1d_update(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt,
+                      int64_t x_row_stride, const void* weight, const void* bias,
+                      void* conv_state, int64_t state_len, int64_t num_slots,
+                      const int32_t* state_idx, int64_t batch, int64_t channels, int64_t width,
+                      uint32_t flags, hipStream_t stream);
 
 /*
  * gdn_gate_beta -- g and beta from the raw projections a and b (vllm.cpp

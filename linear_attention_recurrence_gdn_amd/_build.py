@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.hip", "gdn_recurrent.hip", "gdn_chunked.hip", "gdn_norm.hip",
-           "gdn_frontend.hip"]
+           "gdn_frontend.hip", "gdn_conv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

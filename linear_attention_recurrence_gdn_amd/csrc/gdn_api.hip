@@ -229,6 +229,28 @@ int gdn_post_conv(void* q_out, void* k_out, void* v_out, gdn_dtype out_dt, float
 
 namespace {
 
+int conv_common(const char* op, gdn_dtype out_dt, gdn_dtype x_dt, int64_t x_row_stride,
+                int64_t state_len, int64_t num_slots, int64_t channels, int64_t width,
+                uint32_t flags, uint32_t extra_flags) {
+  if (!valid_dt(x_dt) || !valid_dt(out_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
+  if (out_dt != GDN_F32 && out_dt != x_dt)
+    return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
+  if (flags & ~(uint32_t)(GDN_CONV_SILU | GDN_CHECK_SLOTS | GDN_STATE_F16 | GDN_STATE_BF16 |
+                          extra_flags))
+    return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (state_dtype(flags) < 0)
+    return fail(GDN_ERR_DTYPE, "%s: GDN_STATE_F16 and GDN_STATE_BF16 both set", op);
+  if (channels <= 0 || channels > ((int64_t)65535 * 256))
+    return fail(GDN_ERR_SHAPE, "%s: channels must be in [1, %d]", op, 65535 * 256);
+  if (width < 1 || width > gdn::kConvMaxK)
+    return fail(GDN_ERR_SHAPE, "%s: width %lld not in [1, %d]", op, (long long)width,
+                gdn::kConvMaxK);
+  if (x_row_stride < channels) return fail(GDN_ERR_SHAPE, "%s: x row stride below channels", op);
+  if (state_len < width - 1) return fail(GDN_ERR_SHAPE, "%s: state_len below width - 1", op);
+  if (num_slots < 0) return fail(GDN_ERR_SHAPE, "%s: negative num_slots", op);
+  return GDN_OK;
+}
+
 struct NormIn {
   const void* z;
   int64_t z_rs;
@@ -370,6 +392,93 @@ int gdn_rmsnorm_gated(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt
   return hip_status(op, gdn::launch_rmsnorm_gated(a, stream));
 }
 
+
+int gdn_conv1d_fwd(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt,
+                   int64_t x_row_stride, const void* weight, const void* bias,
+                   void* conv_state, int64_t state_len, int64_t num_slots,
+                   const int32_t* state_idx, const int8_t* has_initial_state,
+                   const int32_t* cu_seqlens, int64_t num_seqs, int64_t total_tokens,
+                   int64_t channels, int64_t width, uint32_t flags, hipStream_t stream) {
+  const char* op = "gdn_conv1d_fwd";
+  int rc;
+  if (num_seqs < 0 || total_tokens < 0) return fail(GDN_ERR_SHAPE, "%s: negative size", op);
+  if ((rc = conv_common(op, out_dt, x_dt, x_row_stride, state_len, num_slots, channels, width,
+                        flags, 0)))
+    return rc;
+  if (total_tokens >= ((int64_t)1 << 31) * 16)
+    return fail(GDN_ERR_SHAPE, "%s: total_tokens too large", op);
+  if (num_seqs >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "%s: too many sequences", op);
+  if (num_seqs == 0) return ok();
+  if (width > 1 && !state_idx && num_seqs > num_slots)   // width 1 keeps no state
+    return fail(GDN_ERR_SLOT, "%s: %lld sequences but %lld slots", op, (long long)num_seqs,
+                (long long)num_slots);
+  if (!cu_seqlens || !weight || (width > 1 && !conv_state))
+    return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  if (total_tokens > 0 && (!out || !x)) return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  const size_t ex = (size_t)elem_bytes(x_dt);
+  if (!aligned(x, ex) || !aligned(weight, ex) || !aligned(bias, ex) ||
+      !aligned(out, (size_t)elem_bytes(out_dt)) ||
+      !aligned(conv_state, (size_t)elem_bytes(state_dtype(flags))))
+    return fail(GDN_ERR_ARG, "%s: pointers must be aligned to their element size", op);
+  if (flags & GDN_CHECK_SLOTS) {
+    std::vector<int32_t> h;
+    if ((rc = fetch_i32(op, cu_seqlens, num_seqs + 1, h, stream))) return rc;
+    if (h[0] != 0 || h[(size_t)num_seqs] != total_tokens)
+      return fail(GDN_ERR_SHAPE, "%s: cu_seqlens must run from 0 to total_tokens (%lld)", op,
+                  (long long)total_tokens);
+    for (int64_t s = 0; s < num_seqs; ++s)
+      if (h[(size_t)s + 1] < h[(size_t)s])
+        return fail(GDN_ERR_SHAPE, "%s: cu_seqlens decreases at sequence %lld", op,
+                    (long long)s);
+    if (state_idx && width > 1) {
+      if ((rc = fetch_i32(op, state_idx, num_seqs, h, stream))) return rc;
+      if ((rc = check_slot_table(op, h, num_slots, false))) return rc;
+    }
+  }
+  gdn::ConvArgs a{};
+  a.out = out; a.out_dt = out_dt; a.x = x; a.x_dt = x_dt; a.x_rs = x_row_stride; a.w = weight;
+  a.bias = bias; a.state = conv_state; a.state_dt = state_dtype(flags);
+  a.state_len = state_len; a.num_slots = num_slots; a.idx = state_idx;
+  a.has_init = has_initial_state; a.cu = cu_seqlens; a.n = num_seqs; a.T = total_tokens;
+  a.C = channels; a.K = (int)width; a.silu = (flags & GDN_CONV_SILU) ? 1 : 0;
+  return hip_status(op, gdn::launch_conv_fwd(a, stream));
+}
+
+int gdn_conv1d_update(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt,
+                      int64_t x_row_stride, const void* weight, const void* bias,
+                      void* conv_state, int64_t state_len, int64_t num_slots,
+                      const int32_t* state_idx, int64_t batch, int64_t channels, int64_t width,
+                      uint32_t flags, hipStream_t stream) {
+  const char* op = "gdn_conv1d_update";
+  int rc;
+  if (batch < 0) return fail(GDN_ERR_SHAPE, "%s: negative batch", op);
+  if ((rc = conv_common(op, out_dt, x_dt, x_row_stride, state_len, num_slots, channels, width,
+                        flags, 0)))
+    return rc;
+  if (batch >= ((int64_t)1 << 31)) return fail(GDN_ERR_SHAPE, "%s: batch too large", op);
+  if (batch == 0) return ok();
+  if (width > 1 && !state_idx && batch > num_slots)   // width 1 keeps no state
+    return fail(GDN_ERR_SLOT, "%s: %lld rows but %lld slots", op, (long long)batch,
+                (long long)num_slots);
+  if (!out || !x || !weight || (width > 1 && !conv_state))
+    return fail(GDN_ERR_ARG, "%s: null pointer", op);
+  const size_t ex = (size_t)elem_bytes(x_dt);
+  if (!aligned(x, ex) || !aligned(weight, ex) || !aligned(bias, ex) ||
+      !aligned(out, (size_t)elem_bytes(out_dt)) ||
+      !aligned(conv_state, (size_t)elem_bytes(state_dtype(flags))))
+    return fail(GDN_ERR_ARG, "%s: pointers must be aligned to their element size", op);
+  if ((flags & GDN_CHECK_SLOTS) && state_idx && width > 1) {
+    std::vector<int32_t> h;
+    if ((rc = fetch_i32(op, state_idx, batch, h, stream))) return rc;
+    if ((rc = check_slot_table(op, h, num_slots, true))) return rc;
+  }
+  gdn::ConvArgs a{};
+  a.out = out; a.out_dt = out_dt; a.x = x; a.x_dt = x_dt; a.x_rs = x_row_stride; a.w = weight;
+  a.bias = bias; a.state = conv_state; a.state_dt = state_dtype(flags);
+  a.state_len = state_len; a.num_slots = num_slots; a.idx = state_idx; a.n = batch;
+  a.C = channels; a.K = (int)width; a.silu = (flags & GDN_CONV_SILU) ? 1 : 0;
+  return hip_status(op, gdn::launch_conv_update(a, stream));
+}
 
 static bool use_chunked(int64_t hk, int64_t hv, int64_t dk, int64_t dv, int in_dt, int out_dt,
                         uint32_t flags) {

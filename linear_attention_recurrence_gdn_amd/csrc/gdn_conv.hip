@@ -1,0 +1,206 @@
+// gdn_conv.hip -- depthwise causal conv1d before the GDN front-end (vllm.cpp
+// tests/vt/test_ops_gdn.cpp, the causal_conv1d_fwd / causal_conv1d_update
+// cases): for channel c with taps w[c][0..K-1], the last on the current token,
+//   y = act(bias[c] + sum_j w[c][j] * window[j]),  act = silu or identity,
+// where the window is the K-1 inputs before the token, then the token.  The
+// state row of a sequence holds the K-1 raw inputs before its next token.
+//
+// Forward (varlen prefill): HBM-bound, read x once and write y once.  Each
+// thread owns one channel of a 16-token span of the packed token axis (lanes
+// = consecutive channels, so every load is a contiguous row segment), finds
+// the sequence of its first token by binary search in cu_seqlens, preloads
+// its 16 inputs and the K-1 before them (from x, or from the state row at a
+// sequence start), and walks the span, restarting the window at every
+// sequence boundary inside it.  A second kernel, ordered after the first on
+// the stream, writes each sequence's new state row, so no thread overwrites
+// a state another thread still has to read.
+//
+// Update (decode): one thread per (row, channel): read the state row, the
+// input and the taps, write y and the rolled state.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kSpan = 16;   // tokens per thread in the forward pass
+
+__device__ __forceinline__ float conv_act(float v, bool silu) {
+  return silu ? v / (1.0f + expf(-v)) : v;
+}
+
+// Sequence containing token t: the largest s with cu[s] <= t (zero-length
+// sequences share their start with the next one; the last of them wins).
+__device__ __forceinline__ int64_t seq_of(const int32_t* cu, int64_t n, int64_t t) {
+  int64_t lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int TX, int K>
+__global__ __launch_bounds__(256) void conv_fwd_kernel(ConvArgs a) {
+  const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  if (c >= a.C) return;
+  const int64_t t0 = (int64_t)blockIdx.x * kSpan;
+  const int64_t t1 = min(t0 + kSpan, a.T);
+  const bool silu = a.silu != 0;
+
+  float w[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) w[j] = raw1_to_f32<TX>(load_raw1<TX>(a.w, c * K + j));
+  const float bias = a.bias ? raw1_to_f32<TX>(load_raw1<TX>(a.bias, c)) : 0.0f;
+
+  // inputs of the span (clamped to T; the tail is never used)
+  float xs[kSpan];
+#pragma unroll
+  for (int i = 0; i < kSpan; ++i)
+    xs[i] = raw1_to_f32<TX>(load_raw1<TX>(a.x, min(t0 + i, a.T - 1) * a.x_rs + c));
+
+  int64_t s = seq_of(a.cu, a.n, t0);
+  int64_t s_begin = a.cu[s], s_end = a.cu[s + 1];
+  // the window before t0
+  float win[K > 1 ? K - 1 : 1];
+  auto load_window = [&](int64_t t) {
+    // inputs at positions t-(K-1) .. t-1 of sequence s (state or zeros before it)
+    const int64_t slot = a.idx ? (int64_t)a.idx[s] : s;
+    const bool ok = slot >= 0 && slot < a.num_slots;
+    const bool init = ok && (a.has_init ? a.has_init[s] != 0 : true);
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+      const int64_t pos = t - (K - 1) + j - s_begin;
+      float v = 0.0f;
+      // (clamped: a malformed cu_seqlens must not index outside x)
+      if (pos >= 0)
+        v = raw1_to_f32<TX>(load_raw1<TX>(
+            a.x, max((int64_t)0, min(s_begin + pos, a.T - 1)) * a.x_rs + c));
+      else if (init)
+        v = load1(a.state, a.state_dt,
+                  (slot * a.C + c) * a.state_len + max((int64_t)0, (K - 1) + pos));
+      win[j] = ok ? v : __builtin_nanf("");
+    }
+  };
+  load_window(t0);
+
+#pragma unroll
+  for (int i = 0; i < kSpan; ++i) {
+    const int64_t t = t0 + i;
+    if (t < t1) {
+      if (t >= s_end && s + 1 < a.n) {   // next sequence(s): skip empty ones
+        while (t >= s_end && s + 1 < a.n) { ++s; s_begin = a.cu[s]; s_end = a.cu[s + 1]; }
+        load_window(t);
+      }
+      float acc = bias;
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) acc += w[j] * win[j];
+      acc += w[K - 1] * xs[i];
+      store1(a.out, a.out_dt, t * a.C + c, conv_act(acc, silu));
+#pragma unroll
+      for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
+      if constexpr (K > 1) win[K - 2] = xs[i];
+    }
+  }
+}
+
+// New state rows: the last K-1 entries of (initial window, the inputs).
+__global__ __launch_bounds__(256) void conv_state_kernel(ConvArgs a) {
+  const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  const int64_t s = blockIdx.x;
+  if (c >= a.C) return;
+  const int64_t slot = a.idx ? (int64_t)a.idx[s] : s;
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t b0 = max((int64_t)0, min((int64_t)a.cu[s], a.T));
+  const int64_t len = max((int64_t)0, min((int64_t)a.cu[s + 1], a.T) - b0);
+  const bool init = a.has_init ? a.has_init[s] != 0 : true;
+  const int64_t row = (slot * a.C + c) * a.state_len;
+  const int km1 = a.K - 1;
+  float nv[7];
+  for (int j = 0; j < km1; ++j) {
+    const int64_t e = len + j;   // index into (window of K-1 | inputs)
+    nv[j] = e >= km1 ? load1(a.x, a.x_dt, (b0 + e - km1) * a.x_rs + c)
+                     : (init ? load1(a.state, a.state_dt, row + e) : 0.0f);
+  }
+  for (int j = 0; j < km1; ++j) store1(a.state, a.state_dt, row + j, nv[j]);
+}
+
+template <int TX, int K>
+__global__ __launch_bounds__(256) void conv_update_kernel(ConvArgs a) {
+  const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  const int64_t r = blockIdx.x;
+  if (c >= a.C) return;
+  const int64_t slot = a.idx ? (int64_t)a.idx[r] : r;
+  if (slot < 0) return;                     // padded row: output and state untouched
+  if (K > 1 && slot >= a.num_slots) {       // caller error: NaN, no state access
+    store1(a.out, a.out_dt, r * a.C + c, __builtin_nanf(""));
+    return;
+  }
+  const int64_t row = (slot * a.C + c) * a.state_len;
+  float st[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) st[j] = load1(a.state, a.state_dt, row + j);
+  const float xv = raw1_to_f32<TX>(load_raw1<TX>(a.x, r * a.x_rs + c));
+  float acc = a.bias ? raw1_to_f32<TX>(load_raw1<TX>(a.bias, c)) : 0.0f;
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) acc += raw1_to_f32<TX>(load_raw1<TX>(a.w, c * K + j)) * st[j];
+  acc += raw1_to_f32<TX>(load_raw1<TX>(a.w, c * K + K - 1)) * xv;
+  store1(a.out, a.out_dt, r * a.C + c, conv_act(acc, a.silu != 0));
+#pragma unroll
+  for (int j = 0; j + 1 < K - 1; ++j) store1(a.state, a.state_dt, row + j, st[j + 1]);
+  if constexpr (K > 1) store1(a.state, a.state_dt, row + K - 2, xv);
+}
+
+template <int TX>
+hipError_t launch_fwd_tx(const ConvArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.T + kSpan - 1) / kSpan), (unsigned)((a.C + 255) / 256));
+  switch (a.K) {
+#define GDN_CONV_K(KK) \
+    case KK: hipLaunchKernelGGL((conv_fwd_kernel<TX, KK>), grid, dim3(256), 0, stream, a); break;
+    GDN_CONV_K(1) GDN_CONV_K(2) GDN_CONV_K(3) GDN_CONV_K(4) GDN_CONV_K(5) GDN_CONV_K(6)
+    GDN_CONV_K(7) GDN_CONV_K(8)
+#undef GDN_CONV_K
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int TX>
+hipError_t launch_update_tx(const ConvArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.n, (unsigned)((a.C + 255) / 256));
+  switch (a.K) {
+#define GDN_CONV_K(KK) \
+    case KK: hipLaunchKernelGGL((conv_update_kernel<TX, KK>), grid, dim3(256), 0, stream, a); break;
+    GDN_CONV_K(1) GDN_CONV_K(2) GDN_CONV_K(3) GDN_CONV_K(4) GDN_CONV_K(5) GDN_CONV_K(6)
+    GDN_CONV_K(7) GDN_CONV_K(8)
+#undef GDN_CONV_K
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t stream) {
+  if (a.n == 0) return hipSuccess;
+  if (a.T > 0) {
+    hipError_t e = a.x_dt == kBF16 ? launch_fwd_tx<kBF16>(a, stream)
+                 : a.x_dt == kF16  ? launch_fwd_tx<kF16>(a, stream)
+                                   : launch_fwd_tx<kF32>(a, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (a.K > 1) {
+    const dim3 grid((unsigned)a.n, (unsigned)((a.C + 255) / 256));
+    hipLaunchKernelGGL(conv_state_kernel, grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_update(const ConvArgs& a, hipStream_t stream) {
+  if (a.n == 0) return hipSuccess;
+  return a.x_dt == kBF16 ? launch_update_tx<kBF16>(a, stream)
+       : a.x_dt == kF16  ? launch_update_tx<kF16>(a, stream)
+                         : launch_update_tx<kF32>(a, stream);
+}
+
+}  // namespace gdn

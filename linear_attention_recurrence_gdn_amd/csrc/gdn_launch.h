@@ -88,6 +88,29 @@ struct NormArgs {
   int sigmoid;
 };
 
+// Depthwise causal conv1d (forward over packed sequences, or single-token update).
+struct ConvArgs {
+  void* out;             // [T or batch, C] contiguous, out_dt
+  int out_dt;
+  const void* x;         // row t at x + t * x_rs, x_dt
+  int x_dt;
+  int64_t x_rs;
+  const void* w;         // [C, K] in x_dt
+  const void* bias;      // [C] in x_dt, or nullptr
+  void* state;           // [num_slots, C, state_len] in state_dt (leading K-1 used)
+  int state_dt;
+  int64_t state_len;
+  int64_t num_slots;
+  const int32_t* idx;      // [n] slot per sequence / row, or nullptr (s)
+  const int8_t* has_init;  // forward: [n] or nullptr (all 1)
+  const int32_t* cu;       // forward: [n + 1]
+  int64_t n;               // sequences (forward) or rows (update)
+  int64_t T;               // tokens (forward)
+  int64_t C;
+  int K;
+  int silu;
+};
+
 struct PrefillArgs {
   void* out;
   int out_dt;
@@ -116,6 +139,9 @@ struct PrefillArgs {
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
 hipError_t launch_post_conv(const PostConvArgs& a, hipStream_t stream);
+constexpr int kConvMaxK = 8;
+hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_conv_update(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // the fused-norm decode runs one workgroup (at most 16 waves) per (row,
 // v-head): the largest dv it takes at this dk

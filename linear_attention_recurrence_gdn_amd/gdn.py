@@ -26,11 +26,12 @@ GDN_STATE_BF16 = 1 << 4
 GDN_NORM_SIGMOID = 1 << 5
 GDN_BETA_RAW = 1 << 6
 GDN_BETA_ROUNDED = 1 << 7
+GDN_CONV_SILU = 1 << 8
 _STATE_FLAGS = {torch.float32: 0, torch.float16: GDN_STATE_F16, torch.bfloat16: GDN_STATE_BF16}
 
 _TORCH_DT = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
 
-EXPORTS = ("gdn_gate", "gdn_gate_beta", "gdn_post_conv", "gdn_decode", "gdn_decode_gated_norm",
+EXPORTS = ("gdn_conv1d_fwd", "gdn_conv1d_update", "gdn_gate", "gdn_gate_beta", "gdn_post_conv", "gdn_decode", "gdn_decode_gated_norm",
            "gdn_rmsnorm_gated",
            "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_last_error")
 
@@ -61,6 +62,12 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode.restype = i32
     lib.gdn_decode.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i32, i64, vp, vp,
                                vp, i64, vp, i64, vp, i64, i64, i64, i64, i64, f32, f32, u32, vp]
+    lib.gdn_conv1d_fwd.restype = i32
+    lib.gdn_conv1d_fwd.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp, i64, i64, vp, vp, vp, i64,
+                                   i64, i64, i64, u32, vp]
+    lib.gdn_conv1d_update.restype = i32
+    lib.gdn_conv1d_update.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp, i64, i64, vp, i64, i64,
+                                      i64, u32, vp]
     lib.gdn_gate_beta.restype = i32
     lib.gdn_gate_beta.argtypes = [vp, vp, i64, vp, vp, i32, i64, i64, vp, vp, i64, i64, u32, vp]
     lib.gdn_post_conv.restype = i32
@@ -232,6 +239,64 @@ def _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scal
     _check(lib.gdn_decode_gated_norm(*args, _dev(z, "norm_z", q.dtype), z_rs,
                                      _dev(w, "norm_w", q.dtype), float(eps), flags,
                                      _stream(stream)))
+    return out
+
+
+def _conv_common(x, weight, conv_state, name):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise GdnError(-3, f"{name}: x needs [rows, C] with contiguous rows")
+    rows, C = x.shape
+    x_rs = x.stride(0) if rows > 1 else max(x.stride(0), C)
+    if weight.dim() != 2 or weight.shape[0] != C or not weight.is_contiguous():
+        raise GdnError(-3, f"{name}: weight needs contiguous [C, K]")
+    K = weight.shape[1]
+    if conv_state is None:
+        return rows, C, x_rs, K, 0, 0, 0
+    if conv_state.dim() != 3 or conv_state.shape[1] != C or not conv_state.is_contiguous():
+        raise GdnError(-3, f"{name}: conv_state needs contiguous [slots, C, state_len]")
+    return rows, C, x_rs, K, conv_state.shape[2], conv_state.shape[0], _state_flags(conv_state)
+
+
+def conv1d_fwd(x, weight, bias, conv_state, cu_seqlens, *, state_idx=None,
+               has_initial_state=None, silu: bool = True, out=None, out_dtype=None,
+               check_slots: bool = False, stream=None) -> torch.Tensor:
+    """Depthwise causal conv over sequences packed back to back: x [T, C]
+    (rows may be strided), weight [C, K], bias [C] or None, conv_state
+    [slots, C, state_len] (f32/f16/bf16, read then written back in place)."""
+    lib = load_library()
+    T, C, x_rs, K, sl, slots, sflags = _conv_common(x, weight, conv_state, "conv1d_fwd")
+    N = cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, C), dtype=out_dtype or x.dtype, device=x.device)
+    if not out.is_contiguous() or tuple(out.shape) != (T, C):
+        raise GdnError(-3, "out: need contiguous [T, C]")
+    flags = (GDN_CONV_SILU if silu else 0) | (GDN_CHECK_SLOTS if check_slots else 0) | sflags
+    _check(lib.gdn_conv1d_fwd(_dev(out, "out"), _dt(out), _dev(x, "x"), _dt(x), x_rs,
+                              _dev(weight, "weight", x.dtype), _dev(bias, "bias", x.dtype),
+                              _dev(conv_state, "conv_state"), sl, slots,
+                              _dev(state_idx, "state_idx", torch.int32),
+                              _dev(has_initial_state, "has_initial_state", torch.int8),
+                              _dev(cu_seqlens, "cu_seqlens", torch.int32), N, T, C, K, flags,
+                              _stream(stream)))
+    return out
+
+
+def conv1d_update(x, weight, bias, conv_state, *, state_idx=None, silu: bool = True, out=None,
+                  out_dtype=None, check_slots: bool = False, stream=None) -> torch.Tensor:
+    """One token per row through the conv: x [B, C] (rows may be strided), the
+    state rows (state_idx [B] int32 or None: row r) rolled in place."""
+    lib = load_library()
+    B, C, x_rs, K, sl, slots, sflags = _conv_common(x, weight, conv_state, "conv1d_update")
+    if out is None:
+        out = torch.empty((B, C), dtype=out_dtype or x.dtype, device=x.device)
+    if not out.is_contiguous() or tuple(out.shape) != (B, C):
+        raise GdnError(-3, "out: need contiguous [B, C]")
+    flags = (GDN_CONV_SILU if silu else 0) | (GDN_CHECK_SLOTS if check_slots else 0) | sflags
+    _check(lib.gdn_conv1d_update(_dev(out, "out"), _dt(out), _dev(x, "x"), _dt(x), x_rs,
+                                 _dev(weight, "weight", x.dtype), _dev(bias, "bias", x.dtype),
+                                 _dev(conv_state, "conv_state"), sl, slots,
+                                 _dev(state_idx, "state_idx", torch.int32), B, C, K, flags,
+                                 _stream(stream)))
     return out
 
 

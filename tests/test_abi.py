@@ -200,3 +200,30 @@ def test_gate_beta_and_post_conv_argument_errors():
     assert pc() == -1 and "null pointer" in _err(lib)
     assert _err(lib).startswith("gdn_post_conv:")
     assert pc(t=0) == 0
+
+
+def test_conv1d_argument_errors():
+    lib = pkg.load_library()
+    cf = lambda **kw: lib.gdn_conv1d_fwd(*dict(dict(
+        out=None, out_dt=2, x=None, x_dt=2, x_rs=5120, w=None, b=None, st=None, sl=3, slots=64,
+        idx=None, hi=None, cu=None, n=8, t=32768, c=5120, k=4, flags=1 << 8,
+        stream=None), **kw).values())
+    assert cf(k=9) == -3 and "width" in _err(lib)
+    assert cf(k=0) == -3
+    assert cf(sl=2) == -3 and "state_len" in _err(lib)
+    assert cf(x_rs=5119) == -3
+    assert cf(out_dt=1) == -2
+    assert cf(flags=(1 << 3) | (1 << 4)) == -2
+    assert cf(flags=1) == -1                       # not a conv flag
+    assert cf(n=65, slots=64) == -4                # more sequences than slots, no index
+    assert cf() == -1 and "null pointer" in _err(lib)
+    assert _err(lib).startswith("gdn_conv1d_fwd:")
+    assert cf(n=0) == 0
+    cu = lambda **kw: lib.gdn_conv1d_update(*dict(dict(
+        out=None, out_dt=2, x=None, x_dt=2, x_rs=8192, w=None, b=None, st=None, sl=3,
+        slots=1024, idx=None, batch=256, c=8192, k=4, flags=1 << 8, stream=None), **kw).values())
+    assert cu(k=9) == -3 and cu(sl=1) == -3
+    assert cu(batch=2048) == -4
+    assert cu(batch=2048, k=1) == -1 and "null pointer" in _err(lib)   # width 1: no state
+    assert cu() == -1 and _err(lib).startswith("gdn_conv1d_update:")
+    assert cu(batch=0) == 0
