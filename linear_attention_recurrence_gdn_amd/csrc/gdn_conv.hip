@@ -104,6 +104,133 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvArgs a) {
   }
 }
 
+// The same forward pass with 16-byte lanes: each thread owns V consecutive
+// channels (V = 8 for 16-bit data, 4 for f32) of an 8-token span, so every
+// x load and y store of a wave moves 1 KiB of contiguous row.  Used when the
+// channel count, the x row stride and the pointers allow 16-byte access.
+template <int TX>
+struct ConvVec {
+  static constexpr int V = TX == kF32 ? 4 : 8;
+  static constexpr int EB = TX == kF32 ? 4 : 2;
+};
+
+template <int TX>
+__device__ __forceinline__ uint4 ld16x(const void* p, int64_t elem) {
+  return *reinterpret_cast<const uint4*>(static_cast<const char*>(p) + elem * ConvVec<TX>::EB);
+}
+
+template <int TX>
+__device__ __forceinline__ void widen_v(uint4 u, float* v) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if constexpr (TX == kF32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = TX == kBF16 ? bf16_to_f32(w[i] & 0xffffu) : f16_to_f32(w[i] & 0xffffu);
+      v[2 * i + 1] = TX == kBF16 ? bf16_to_f32(w[i] >> 16) : f16_to_f32(w[i] >> 16);
+    }
+  }
+}
+
+template <int TX, int K, bool OF32>
+__global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
+  constexpr int V = ConvVec<TX>::V;
+  constexpr int SPAN = 8;
+  const int64_t c0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * V;
+  if (c0 >= a.C) return;
+  const int64_t t0 = (int64_t)blockIdx.x * SPAN;
+  const int64_t t1 = min(t0 + SPAN, a.T);
+  const bool silu = a.silu != 0;
+
+  uint4 xr[SPAN];
+#pragma unroll
+  for (int i = 0; i < SPAN; ++i) xr[i] = ld16x<TX>(a.x, min(t0 + i, a.T - 1) * a.x_rs + c0);
+  // taps of the V channels: V*K contiguous elements, K 16-byte chunks
+  float wf[V * K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) widen_v<TX>(ld16x<TX>(a.w, c0 * K + i * V), wf + i * V);
+  float bias[V];
+  if (a.bias) {
+    widen_v<TX>(ld16x<TX>(a.bias, c0), bias);
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) bias[v] = 0.0f;
+  }
+
+  int64_t s = seq_of(a.cu, a.n, t0);
+  int64_t s_begin = a.cu[s], s_end = a.cu[s + 1];
+  float win[K > 1 ? K - 1 : 1][V];
+  auto load_window = [&](int64_t t) {
+    const int64_t slot = a.idx ? (int64_t)a.idx[s] : s;
+    const bool ok = slot >= 0 && slot < a.num_slots;
+    const bool init = ok && (a.has_init ? a.has_init[s] != 0 : true);
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) {
+      const int64_t pos = t - (K - 1) + j - s_begin;
+      if (pos >= 0) {
+        widen_v<TX>(ld16x<TX>(a.x, max((int64_t)0, min(s_begin + pos, a.T - 1)) * a.x_rs + c0),
+                    win[j]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          win[j][v] = init ? load1(a.state, a.state_dt,
+                                   ((slot * a.C + c0 + v) * a.state_len) +
+                                       max((int64_t)0, (K - 1) + pos))
+                           : 0.0f;
+      }
+      if (!ok) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) win[j][v] = __builtin_nanf("");
+      }
+    }
+  };
+  load_window(t0);
+
+#pragma unroll
+  for (int i = 0; i < SPAN; ++i) {
+    const int64_t t = t0 + i;
+    if (t < t1) {
+      if (t >= s_end && s + 1 < a.n) {
+        while (t >= s_end && s + 1 < a.n) { ++s; s_begin = a.cu[s]; s_end = a.cu[s + 1]; }
+        load_window(t);
+      }
+      float xv[V], y[V];
+      widen_v<TX>(xr[i], xv);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float acc = bias[v];
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) acc += wf[v * K + j] * win[j][v];
+        acc += wf[v * K + K - 1] * xv[v];
+        y[v] = conv_act(acc, silu);
+      }
+      if constexpr (OF32 || TX == kF32) {
+        float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + t * a.C + c0);
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q)
+          o[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+      } else {
+        uint32_t pk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pk[q] = TX == kBF16 ? pack2_bf16(y[2 * q], y[2 * q + 1]) : pack2_f16(y[2 * q], y[2 * q + 1]);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + t * a.C + c0) =
+            make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
+#pragma unroll
+      for (int j = 0; j + 1 < K - 1; ++j)
+#pragma unroll
+        for (int v = 0; v < V; ++v) win[j][v] = win[j + 1][v];
+      if constexpr (K > 1) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) win[K - 2][v] = xv[v];
+      }
+    }
+  }
+}
+
 // New state rows: the last K-1 entries of (initial window, the inputs).
 __global__ __launch_bounds__(256) void conv_state_kernel(ConvArgs a) {
   const int64_t c = (int64_t)blockIdx.y * 256 + threadIdx.x;
@@ -151,8 +278,36 @@ __global__ __launch_bounds__(256) void conv_update_kernel(ConvArgs a) {
   if constexpr (K > 1) store1(a.state, a.state_dt, row + K - 2, xv);
 }
 
+template <int TX, bool OF32>
+hipError_t launch_fwd_vec(const ConvArgs& a, hipStream_t stream) {
+  constexpr int V = ConvVec<TX>::V;
+  const dim3 grid((unsigned)((a.T + 7) / 8), (unsigned)((a.C / V + 255) / 256));
+  switch (a.K) {
+#define GDN_CONV_K(KK) \
+    case KK: \
+      hipLaunchKernelGGL((conv_fwd_vec_kernel<TX, KK, OF32>), grid, dim3(256), 0, stream, a); \
+      break;
+    GDN_CONV_K(1) GDN_CONV_K(2) GDN_CONV_K(3) GDN_CONV_K(4) GDN_CONV_K(5) GDN_CONV_K(6)
+    GDN_CONV_K(7) GDN_CONV_K(8)
+#undef GDN_CONV_K
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// 16-byte lanes need V-aligned channel counts, x rows and pointers.
+bool conv_vec_ok(const ConvArgs& a) {
+  const int v = a.x_dt == kF32 ? 4 : 8;
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; };
+  return a.C % v == 0 && a.x_rs % v == 0 && al(a.x) && al(a.w) && al(a.bias) && al(a.out) &&
+         (a.out_dt == kF32 || a.out_dt == a.x_dt);
+}
+
 template <int TX>
 hipError_t launch_fwd_tx(const ConvArgs& a, hipStream_t stream) {
+  if (conv_vec_ok(a))
+    return a.out_dt == kF32 ? launch_fwd_vec<TX, true>(a, stream)
+                            : launch_fwd_vec<TX, false>(a, stream);
   const dim3 grid((unsigned)((a.T + kSpan - 1) / kSpan), (unsigned)((a.C + 255) / 256));
   switch (a.K) {
 #define GDN_CONV_K(KK) \

@@ -67,6 +67,9 @@ FWD_CASES = [
     ([40], 64, 1, W.BF16, W.BF16, W.F32, True, False, [1], False, 0, 0),
     ([16, 16, 5], 96, 5, W.BF16, W.F32, W.F16, False, True, [0, 1, 1], True, 3, 1),
     ([70, 2, 130], 264, 8, W.F32, W.F32, W.BF16, True, True, [1, 1, 1], True, 0, 0),
+    # 16-byte lanes with padded rows, zero-length and short sequences, a widened cache
+    ([0, 3, 1, 20], 128, 4, W.BF16, W.BF16, W.BF16, True, True, [1, 0, 1, 1], True, 8, 1),
+    ([9, 33], 64, 2, W.F16, W.F32, W.F16, False, False, [0, 1], False, 16, 0),
 ]
 
 
