@@ -848,11 +848,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) blk_off[nb] = dvw + 16 * nb < a.dv ? 0 : kDropOffset;
 
-  for (int ch = 0; ch < nch; ++ch) {
+  // One chunk step: `cur` holds chunk ch, `nxt` receives chunk ch + 1.  The
+  // restrict-qualified buffers tell the compiler that this step's LDS reads
+  // never alias the loads into the other buffer, so it does not wait for
+  // those loads before reading the current chunk.
+  auto chunk_step = [&](WalkBuf<NW, NB>* __restrict__ cur, WalkBuf<NW, NB>* __restrict__ nxt,
+                        int ch) {
     const int64_t tb = c.t_begin + (int64_t)ch * CK;
     const int L = chunk_len(c, ch);
-    if (ch + 1 < nch) stage_dma<NW, NB>(sb[(ch + 1) & 1], c, ch + 1, w, lane, so);
-    WalkBuf<NW, NB>& sm = sb[ch & 1];
+    if (ch + 1 < nch) stage_dma<NW, NB>(*nxt, c, ch + 1, w, lane, so);
+    WalkBuf<NW, NB>& sm = *cur;
     // rows [0, L) of this chunk
     const __amdgpu_buffer_rsrc_t orsrc =
         __builtin_amdgcn_make_buffer_rsrc(out + tb * out_rs, 0, L * out_row, kBufferFlags);
@@ -1040,7 +1045,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     }
 
     stage_sync();
-  }
+  };
+  for (int ch = 0; ch < nch; ++ch) chunk_step(&sb[ch & 1], &sb[(ch + 1) & 1], ch);
 
   store_state();
 }
