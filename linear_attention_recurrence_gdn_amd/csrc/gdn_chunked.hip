@@ -192,13 +192,26 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, int32_t*
   }
 }
 
-// inclusive prefix sum of 64 values held one per lane of a wave, in f64
-__device__ __forceinline__ double wave_prefix64(double x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+// A DPP move of an f64 (both halves); lanes the move does not reach read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xF, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xF,
+                                             true);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// inclusive prefix sum of 64 values held one per lane of a wave, in f64:
+// shifts by 1, 2, 4, 8 within each row of 16 lanes, then the last lane of
+// row 0 (row 2) added to row 1 (row 3), then lane 31 added to rows 2 and 3
+__device__ __forceinline__ double wave_prefix64(double x) {
+  x += dpp_f64<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_f64<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_f64<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_f64<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_f64<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_f64<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 
@@ -356,7 +369,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
         gn = a.g[(tb + lane) * a.g_rs + h + 1];
         bn = a.beta[(tb + lane) * a.beta_rs + h + 1];
       }
-      const double gcum = wave_prefix64((double)gv, lane);
+      const double gcum = wave_prefix64((double)gv);
       Gd[lane] = gcum;
       bt[lane] = bv;
       rowA[lane] = bv * nk[lane];
