@@ -619,42 +619,60 @@ __device__ __forceinline__ void stage_offsets(StageOffsets<NW, NB>& o, const Pre
   }
 }
 
-// Issues the loads of chunk `ch` into B.  The q/k/v rows go through buffer
-// resources that end at the chunk's last token, so rows past the end of the
-// sequence arrive as zeros.
-template <int NW, int NB>
-__device__ __forceinline__ void stage_dma(WalkBuf<NW, NB>& B, const WalkCtx& c, int ch, int w,
-                                          int lane, const StageOffsets<NW, NB>& o) {
+// Issues part PART of the loads of chunk `ch` into B: 0 = K, 1 = Q, 2 = T_b
+// high/low and P, 3 = the V columns and the factors.  The q/k/v rows go
+// through buffer resources that end at the chunk's last token, so rows past
+// the end of the sequence arrive as zeros.  The walk spreads the parts over
+// a chunk step so the CU's load path works while the wave computes.
+template <int NW, int NB, int PART>
+__device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx& c, int ch,
+                                               int w, int lane, const StageOffsets<NW, NB>& o) {
   using SO = StageOffsets<NW, NB>;
   const PrefillArgs& a = *c.a;
   const int64_t tb = c.t_begin + (int64_t)ch * CK;
   const int L = chunk_len(c, ch);
-  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + tb * a.k_rs + (int64_t)c.hk * DKC),
-      0, (int)(L * a.k_rs * 2), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.q) + tb * a.q_rs + (int64_t)c.hk * DKC),
-      0, (int)(L * a.q_rs * 2), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + tb * a.v_rs + (int64_t)c.h * a.dv),
-      0, (int)(L * a.v_rs * 2), kBufferFlags);
+  if constexpr (PART == 0) {
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + tb * a.k_rs +
+                              (int64_t)c.hk * DKC),
+        0, (int)(L * a.k_rs * 2), kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < SO::NKQ; ++i) {
-    const int u = NW * i + w;
-    dma16_buf(kr, o.k[i], B.K + 512 * u);
-    dma16_buf(qr, o.q[i], B.Q + 512 * u);
+    for (int i = 0; i < SO::NKQ; ++i) dma16_buf(kr, o.k[i], B.K + 512 * (NW * i + w));
+  } else if constexpr (PART == 1) {
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(static_cast<const uint16_t*>(a.q) + tb * a.q_rs +
+                              (int64_t)c.hk * DKC),
+        0, (int)(L * a.q_rs * 2), kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < SO::NKQ; ++i) dma16_buf(qr, o.q[i], B.Q + 512 * (NW * i + w));
+  } else if constexpr (PART == 2) {
+    const char* rec = chunk_rec(c, ch);
+#pragma unroll
+    for (int i = 0; i < SO::NTP; ++i) {
+      const int u = NW * i + w;
+      dma16(rec + REC_TH + o.tp[i], B.Th + 512 * u);
+      dma16(rec + REC_TL + o.tp[i], B.Tl + 512 * u);
+      dma16(rec + REC_P + o.tp[i], B.P + 512 * u);
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + tb * a.v_rs +
+                              (int64_t)c.h * a.dv),
+        0, (int)(L * a.v_rs * 2), kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < SO::NVL; ++i) dma16_buf(vr, o.v[i], B.V + 512 * (NW * i + w));
+    if (w == 0) dma16(chunk_rec(c, ch) + REC_F + 16 * lane, B.F);
   }
-  const char* rec = chunk_rec(c, ch);
-#pragma unroll
-  for (int i = 0; i < SO::NTP; ++i) {
-    const int u = NW * i + w;
-    dma16(rec + REC_TH + o.tp[i], B.Th + 512 * u);
-    dma16(rec + REC_TL + o.tp[i], B.Tl + 512 * u);
-    dma16(rec + REC_P + o.tp[i], B.P + 512 * u);
-  }
-#pragma unroll
-  for (int i = 0; i < SO::NVL; ++i) dma16_buf(vr, o.v[i], B.V + 512 * (NW * i + w));
-  if (w == 0) dma16(rec + REC_F + 16 * lane, B.F);
+}
+
+// All loads of chunk `ch` into B.
+template <int NW, int NB>
+__device__ __forceinline__ void stage_dma(WalkBuf<NW, NB>& B, const WalkCtx& c, int ch, int w,
+                                          int lane, const StageOffsets<NW, NB>& o) {
+  stage_dma_part<NW, NB, 0>(B, c, ch, w, lane, o);
+  stage_dma_part<NW, NB, 1>(B, c, ch, w, lane, o);
+  stage_dma_part<NW, NB, 2>(B, c, ch, w, lane, o);
+  stage_dma_part<NW, NB, 3>(B, c, ch, w, lane, o);
 }
 
 // Waits for this wave's outstanding global accesses (the chunk loads above)
@@ -869,7 +887,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
                         int ch) {
     const int64_t tb = c.t_begin + (int64_t)ch * CK;
     const int L = chunk_len(c, ch);
-    if (ch + 1 < nch) stage_dma<NW, NB>(*nxt, c, ch + 1, w, lane, so);
+    const bool more = ch + 1 < nch;  // the next chunk's loads go out in three groups
     WalkBuf<NW, NB>& sm = *cur;
     // rows [0, L) of this chunk
     const __amdgpu_buffer_rsrc_t orsrc =
@@ -900,6 +918,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       if (jj < 3) read_kq(kf[(jj + 1) & 1], qf[(jj + 1) & 1], jj + 1);
+      if (more && jj == 0) {
+        stage_dma_part<NW, NB, 0>(*nxt, c, ch + 1, w, lane, so);
+        stage_dma_part<NW, NB, 1>(*nxt, c, ch + 1, w, lane, so);
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         x8 sh, sl;
@@ -939,6 +961,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
+    if (more) stage_dma_part<NW, NB, 2>(*nxt, c, ch + 1, w, lane, so);
     // ---- U = T_b Z (lower triangular in token blocks) ----
     f32x4 U[NB][4];
 #pragma unroll
@@ -979,6 +1002,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
+    if (more) stage_dma_part<NW, NB, 3>(*nxt, c, ch + 1, w, lane, so);
     // ---- O = diag(fo) QS + P U, stored ----
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
