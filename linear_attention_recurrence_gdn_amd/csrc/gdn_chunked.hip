@@ -879,6 +879,23 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) blk_off[nb] = dvw + 16 * nb < a.dv ? 0 : kDropOffset;
 
+  // 16-bit outputs of a chunk are staged as rows in that chunk's V space and
+  // leave during the next step (or after the last one), so the wait for the
+  // next chunk's loads at the end of a step does not also wait for the stores.
+  auto store_rows = [&](const WalkBuf<NW, NB>* __restrict__ buf, int chp) {
+    if constexpr (TOUT != kF32) {
+      const int64_t tbp = c.t_begin + (int64_t)chp * CK;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          out + tbp * out_rs, 0, chunk_len(c, chp) * out_row, kBufferFlags);
+      u32x4 row8[2 * NB];
+#pragma unroll
+      for (int k = 0; k < 2 * NB; ++k) row8[k] = *reinterpret_cast<const u32x4*>(buf->V + orow_lds[k]);
+#pragma unroll
+      for (int k = 0; k < 2 * NB; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(row8[k], rs, orow_off + 16 * k + blk_off[k >> 1], 0, 0);
+    }
+  };
+
   // One chunk step: `cur` holds chunk ch, `nxt` receives chunk ch + 1.  The
   // restrict-qualified buffers tell the compiler that this step's LDS reads
   // never alias the loads into the other buffer, so it does not wait for
@@ -889,11 +906,28 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     const int L = chunk_len(c, ch);
     const bool more = ch + 1 < nch;  // the next chunk's loads go out in three groups
     WalkBuf<NW, NB>& sm = *cur;
+    if (ch > 0) store_rows(nxt, ch - 1);  // before the V loads below overwrite them
     // rows [0, L) of this chunk
     const __amdgpu_buffer_rsrc_t orsrc =
         __builtin_amdgcn_make_buffer_rsrc(out + tb * out_rs, 0, L * out_row, kBufferFlags);
     int lane_off = out_lane;
     asm volatile("" : "+v"(lane_off));  // keep the row offsets below out of the loop preheader
+
+    // Operands that do not depend on this step's products are read from LDS
+    // well ahead of their use, so their latency hides under the MFMAs before
+    // them: here the V values and fz factors of Z, and e^{G_C}.
+    uint16_t vraw[NB][4][4];
+    float4 fz4[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rb = 32 * (b >> 1) + 4 * (b & 1);
+      fz4[b] = *reinterpret_cast<const float4*>(sm.F + fb + rb);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vraw[nb][b][r] = sm.V[vb[nb] + (rb + r) * VC];
+    }
+    const float gc = sm.F[3 * CK];
 
     // ---- X = K St and QS = Q St (entry state), St split into B operands on the fly ----
     f32x4 X[NB][4], QS[NB][4];
@@ -936,26 +970,34 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
+    // T_b fragments of U (token blocks b, j <= b / 2) and the fw factors, read
+    // while the last products of X finish
+    x8 thf[4][2], tlf[4][2];
+    float4 fw4[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rb = 32 * (b >> 1) + 4 * (b & 1);
+#pragma unroll
+      for (int j = 0; j <= (b >> 1); ++j) {
+        thf[b][j] = *reinterpret_cast<const x8*>(sm.Th + tpb[j] + rb * CK);
+        tlf[b][j] = *reinterpret_cast<const x8*>(sm.Tl + tpb[j] + rb * CK);
+      }
+      fw4[b] = *reinterpret_cast<const float4*>(sm.F + 2 * CK + fb + rb);
+    }
+
     // ---- Z = V - diag(fz) X as B operands (k = token) ----
     x8 Zh[NB][2], Zl[NB][2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      float fzr[2][4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int rb = 32 * j + 4 * hh;
-        const float4 fz = *reinterpret_cast<const float4*>(sm.F + fb + rb);
-        fzr[hh][0] = fz.x; fzr[hh][1] = fz.y; fzr[hh][2] = fz.z; fzr[hh][3] = fz.w;
-      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 z[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int b = 2 * j + hh, rb = 32 * j + 4 * hh;
+          const int b = 2 * j + hh;
+          const float fzr[4] = {fz4[b].x, fz4[b].y, fz4[b].z, fz4[b].w};
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            z[hh][r] = M::dec(sm.V[vb[nb] + (rb + r) * VC]) - fzr[hh][r] * X[nb][b][r];
+          for (int r = 0; r < 4; ++r) z[hh][r] = M::dec(vraw[nb][b][r]) - fzr[r] * X[nb][b][r];
         }
         pack_split<TIN>(z[0], z[1], Zh[nb][j], Zl[nb][j]);
       }
@@ -966,28 +1008,32 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     f32x4 U[NB][4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int rb = 32 * (b >> 1) + 4 * (b & 1);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) U[nb][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j <= (b >> 1); ++j) {
-        const x8 th = *reinterpret_cast<const x8*>(sm.Th + tpb[j] + rb * CK);
-        const x8 tl = *reinterpret_cast<const x8*>(sm.Tl + tpb[j] + rb * CK);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          U[nb][b] = M::mma(th, Zh[nb][j], U[nb][b]);
-          U[nb][b] = M::mma(th, Zl[nb][j], U[nb][b]);
-          U[nb][b] = M::mma(tl, Zh[nb][j], U[nb][b]);
+          U[nb][b] = M::mma(thf[b][j], Zh[nb][j], U[nb][b]);
+          U[nb][b] = M::mma(thf[b][j], Zl[nb][j], U[nb][b]);
+          U[nb][b] = M::mma(tlf[b][j], Zh[nb][j], U[nb][b]);
         }
       }
+    }
+    // P fragments and fo factors of O, read while U finishes
+    x8 pff[4][2];
+    float4 fo4[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rb = 32 * (b >> 1) + 4 * (b & 1);
+#pragma unroll
+      for (int j = 0; j <= (b >> 1); ++j) pff[b][j] = *reinterpret_cast<const x8*>(sm.P + tpb[j] + rb * CK);
+      fo4[b] = *reinterpret_cast<const float4*>(sm.F + CK + fb + rb);
     }
     x8 Uh[NB][2], Ul[NB][2], Wh[NB][2], Wl[NB][2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      float4 fw[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        fw[hh] = *reinterpret_cast<const float4*>(sm.F + 2 * CK + fb + 32 * j + 4 * hh);
+      const float4 fw[2] = {fw4[2 * j], fw4[2 * j + 1]};
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const f32x4& u0 = U[nb][2 * j];
@@ -1007,7 +1053,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int rb = 32 * (b >> 1) + 4 * (b & 1);
-      const float4 fo = *reinterpret_cast<const float4*>(sm.F + CK + fb + rb);
+      const float4 fo = fo4[b];
       f32x4 o[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -1015,11 +1061,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
                         fo.w * QS[nb][b][3]};
 #pragma unroll
       for (int j = 0; j <= (b >> 1); ++j) {
-        const x8 pf = *reinterpret_cast<const x8*>(sm.P + tpb[j] + rb * CK);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          o[nb] = M::mma(pf, Uh[nb][j], o[nb]);
-          if constexpr (kFullOut) o[nb] = M::mma(pf, Ul[nb][j], o[nb]);
+          o[nb] = M::mma(pff[b][j], Uh[nb][j], o[nb]);
+          if constexpr (kFullOut) o[nb] = M::mma(pff[b][j], Ul[nb][j], o[nb]);
         }
       }
 #pragma unroll
@@ -1038,18 +1083,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
         }
       }
     }
-    if constexpr (TOUT != kF32) {
-#pragma unroll
-      for (int k = 0; k < 2 * NB; ++k) {
-        const u32x4 row8 = *reinterpret_cast<const u32x4*>(sm.V + orow_lds[k]);
-        __builtin_amdgcn_raw_buffer_store_b128(row8, orsrc, orow_off + 16 * k + blk_off[k >> 1],
-                                               0, 0);
-      }
-    }
 
     // ---- St = e^{G_C} St + K^T W ----
     {
-      const float gc = sm.F[3 * CK];
       // K^T fragments of key block kb + 1 are read while block kb multiplies
       auto read_kt = [&](x8 (&kd)[2], int kb) {
 #pragma unroll
@@ -1084,6 +1120,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     stage_sync();
   };
   for (int ch = 0; ch < nch; ++ch) chunk_step(&sb[ch & 1], &sb[(ch + 1) & 1], ch);
+  store_rows(&sb[(nch - 1) & 1], nch - 1);
 
   store_state();
 }
