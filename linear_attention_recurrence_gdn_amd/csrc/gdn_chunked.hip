@@ -913,22 +913,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     int lane_off = out_lane;
     asm volatile("" : "+v"(lane_off));  // keep the row offsets below out of the loop preheader
 
-    // Operands that do not depend on this step's products are read from LDS
-    // well ahead of their use, so their latency hides under the MFMAs before
-    // them: here the V values and fz factors of Z, and e^{G_C}.
-    uint16_t vraw[NB][4][4];
-    float4 fz4[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int rb = 32 * (b >> 1) + 4 * (b & 1);
-      fz4[b] = *reinterpret_cast<const float4*>(sm.F + fb + rb);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vraw[nb][b][r] = sm.V[vb[nb] + (rb + r) * VC];
-    }
-    const float gc = sm.F[3 * CK];
-
     // ---- X = K St and QS = Q St (entry state), St split into B operands on the fly ----
     f32x4 X[NB][4], QS[NB][4];
 #pragma unroll
@@ -949,10 +933,26 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     };
     read_kq(kf[0], qf[0], 0);
+    // Operands that do not depend on this step's products are read from LDS
+    // well ahead of their use, so their latency hides under the MFMAs before
+    // them: here (after the first K and Q fragments) the V values and fz
+    // factors of Z, and e^{G_C}.
+    uint16_t vraw[NB][4][4];
+    float4 fz4[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rb = 32 * (b >> 1) + 4 * (b & 1);
+      fz4[b] = *reinterpret_cast<const float4*>(sm.F + fb + rb);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vraw[nb][b][r] = sm.V[vb[nb] + (rb + r) * VC];
+    }
+    const float gc = sm.F[3 * CK];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       if (jj < 3) read_kq(kf[(jj + 1) & 1], qf[(jj + 1) & 1], jj + 1);
-      if (more && jj == 0) {
+      if (more && jj == 1) {
         stage_dma_part<NW, NB, 0>(*nxt, c, ch + 1, w, lane, so);
         stage_dma_part<NW, NB, 1>(*nxt, c, ch + 1, w, lane, so);
       }
