@@ -60,9 +60,6 @@ constexpr int WALK_NW = GDN_WALK_NW;      // waves per state-walk workgroup
 constexpr int WALK_NB = GDN_WALK_NB;      // 16-row state blocks per wave
 constexpr int WALK_MINB = GDN_WALK_MINB;  // register budget: as for this many workgroups per CU
 constexpr int WALK_BV = 16 * WALK_NW * WALK_NB;  // state rows per workgroup
-constexpr int LDQ = DKC + 8;  // padded LDS row (16-bit elements), token-major 128-wide tiles
-constexpr int LDF = CK + 4;   // padded LDS row (f32), 64 x 64 matrices
-constexpr int LDT = CK + 8;   // padded LDS row (16-bit elements), 64 x 64 matrices
 constexpr int kXcds = 8;      // accelerator complex dies (separate L2s) on MI355X
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -95,35 +92,7 @@ struct MT<kF16> {
   static __device__ __forceinline__ float dec(uint32_t u) { return f16_to_f32(u); }
 };
 
-// MFMA operand (16 rows x 32 k) from a row-major 16-bit LDS matrix: lane l
-// takes row r0 + l%16, elements k0 + 8 (l/16) .. +8.  Serves both the A
-// operand (rows = M) and the B operand stored transposed (rows = N).
-template <int TIN>
-__device__ __forceinline__ typename MT<TIN>::x8 frag(const uint16_t* m, int ld, int r0, int k0,
-                                                     int lane) {
-  return *reinterpret_cast<const typename MT<TIN>::x8*>(m + (r0 + (lane & 15)) * ld + k0 +
-                                                        8 * (lane >> 4));
-}
-
-// The same operand from an f32 LDS matrix, split into high and low 16-bit parts.
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-
-template <int TIN>
-__device__ __forceinline__ void frag_split(const float* m, int ld, int r0, int k0, int lane,
-                                           typename MT<TIN>::x8& hi, typename MT<TIN>::x8& lo) {
-  const float* p = m + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4);
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  u16x8 h, l;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = MT<TIN>::enc(x[e]);
-    l[e] = MT<TIN>::enc(x[e] - MT<TIN>::dec(h[e]));
-  }
-  hi = __builtin_bit_cast(typename MT<TIN>::x8, h);
-  lo = __builtin_bit_cast(typename MT<TIN>::x8, l);
-}
 
 // Workgroup barrier ordering LDS only.  __syncthreads() also waits for every
 // outstanding global access, which would force the next chunk's prefetched
@@ -232,25 +201,53 @@ constexpr int REC_BYTES = REC_F + 4 * CK * 4;
 
 // One workgroup per (chunk, q/k head): the raw products K K^T and Q K^T of the
 // chunk are shared by the v-heads of the GQA group, so they are formed once
-// (each wave keeps its tiles in registers) and then, head by head, scaled by
-// that head's gates and betas, solved and written out.
-template <int TIN>
-__global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const int32_t* cs,
-                                                            char* recs) {
-  // Q and K are needed only for the products; A and T then reuse their space
-  union PrepLds {
+// (each wave keeps the A and P tiles of the same blocks in registers, so one
+// exponential serves both) and then, head by head, scaled by that head's
+// gates and betas, solved and written out.  The gate prefix sums and per-token
+// factors of up to four heads are formed at once, one head per wave.
+//
+// LDS: Q and K are needed only for the products; the lower 16x16 blocks of A
+// and T and the per-wave partial products then reuse their space.  About
+// 36 KB in all, so four workgroups share a CU.
+constexpr int LDB = 20;         // padded f32 row of a 16x16 block of A or T
+constexpr int kPrepHeads = 4;   // v-heads whose factors are formed at once (one per wave)
+
+struct PrepLds {
+  union {
     struct {
-      uint16_t Qs[CK * LDQ], Ks[CK * LDQ];
+      uint16_t Q[CK * DKC], K[CK * DKC];  // [token][key], 16-byte chunks XOR-swizzled by row
     } qk;
     struct {
-      float Am[CK * LDF], Tm[CK * LDF];
+      float A[10][16 * LDB];  // lower blocks (bi >= bj) at bi (bi + 1) / 2 + bj
+      float T[10][16 * LDB];
+      float R[4][16 * 17];    // each wave's partial sum of an off-diagonal block
     } at;
-  };
-  __shared__ __align__(16) PrepLds u;
-  __shared__ __align__(16) uint16_t Ps[CK * LDT];
-  __shared__ float Rs[4][16 * 17];
-  __shared__ __align__(16) double Gd[CK];
-  __shared__ __align__(16) float nq[CK], nk[CK], bt[CK], rowA[CK], rowP[CK];
+  } u;
+  float nq[CK], nk[CK];
+  double Gd[kPrepHeads][CK];
+  float bt[kPrepHeads][CK];
+};
+
+// the 16-byte chunk of a Q/K row where logical chunk `chunk` is kept: a
+// 16-row operand read (or a row's four quarter reads) then touches 16
+// distinct 4-bank groups
+__device__ __forceinline__ int qk_chunk(int row, int chunk) { return chunk ^ (row & 15); }
+
+// MFMA operand (16 rows x 32 k) from swizzled Q or K: lane l takes row
+// r0 + l % 16, elements k0 + 8 (l / 16) .. +8
+template <int TIN>
+__device__ __forceinline__ typename MT<TIN>::x8 frag_qk(const uint16_t* m, int r0, int k0, int lane) {
+  const int row = r0 + (lane & 15);
+  return *reinterpret_cast<const typename MT<TIN>::x8*>(
+      m + row * DKC + 8 * qk_chunk(row, (k0 >> 3) + (lane >> 4)));
+}
+
+__device__ __forceinline__ int lower_blk(int bi, int bj) { return (bi * (bi + 1)) / 2 + bj; }
+
+template <int TIN>
+__global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, const int32_t* cs,
+                                                            char* recs) {
+  __shared__ __align__(16) PrepLds sh;
   using M = MT<TIN>;
 
   const int c = blockIdx.x;
@@ -271,18 +268,22 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint16_t* Qs = u.qk.Qs;
-  uint16_t* Ks = u.qk.Ks;
-  float* Am = u.at.Am;
-  float* Tm = u.at.Tm;
+  uint16_t* Qs = sh.u.qk.Q;
+  uint16_t* Ks = sh.u.qk.K;
 
-  // gate and beta of the first v-head, in flight while Q and K are staged
-  // (wave 0 holds one token per lane; the next head's are fetched one head ahead)
+  // gate and beta of this wave's head in the first group (one token per
+  // lane), in flight while Q and K are staged
   float gv = 0.0f, bv = 0.0f;
-  if (w == 0 && lane < L) {
-    gv = a.g[(tb + lane) * a.g_rs + hk * ratio];
-    bv = a.beta[(tb + lane) * a.beta_rs + hk * ratio];
-  }
+  auto load_gb = [&](int q) {
+    const int jh = kPrepHeads * q + w;
+    gv = 0.0f;
+    bv = 0.0f;
+    if (jh < ratio && lane < L) {
+      gv = a.g[(tb + lane) * a.g_rs + hk * ratio + jh];
+      bv = a.beta[(tb + lane) * a.beta_rs + hk * ratio + jh];
+    }
+  };
+  load_gb(0);
 
   // stage Q and K, rows past the sequence zeroed (all loads issued before any is used)
   {
@@ -299,10 +300,10 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int idx = tid + 256 * k;
-      const int row = idx >> 4, p = idx & 15;
+      const int row = idx >> 4, p = qk_chunk(row, idx & 15);
       const u32x4 zero = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(Qs + row * LDQ + 8 * p) = row < L ? qv[k] : zero;
-      *reinterpret_cast<u32x4*>(Ks + row * LDQ + 8 * p) = row < L ? kv[k] : zero;
+      *reinterpret_cast<u32x4*>(Qs + row * DKC + 8 * p) = row < L ? qv[k] : zero;
+      *reinterpret_cast<u32x4*>(Ks + row * DKC + 8 * p) = row < L ? kv[k] : zero;
     }
   }
   __syncthreads();
@@ -311,8 +312,9 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
     float sq = 0.0f, sk = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint4 xq = *reinterpret_cast<const uint4*>(Qs + row * LDQ + 32 * qq + 8 * k);
-      const uint4 xk = *reinterpret_cast<const uint4*>(Ks + row * LDQ + 32 * qq + 8 * k);
+      const int p = qk_chunk(row, 4 * qq + k);
+      const uint4 xq = *reinterpret_cast<const uint4*>(Qs + row * DKC + 8 * p);
+      const uint4 xk = *reinterpret_cast<const uint4*>(Ks + row * DKC + 8 * p);
       const uint32_t wq[4] = {xq.x, xq.y, xq.z, xq.w}, wk[4] = {xk.x, xk.y, xk.z, xk.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -327,155 +329,184 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
     sk += xor_lane<1>(sk);
     sk += xor_lane<2>(sk);
     if (qq == 0) {
-      nq[row] = a.l2norm ? 1.0f / sqrtf(sq + a.l2_eps) : 1.0f;
-      nk[row] = a.l2norm ? 1.0f / sqrtf(sk + a.l2_eps) : 1.0f;
+      sh.nq[row] = a.l2norm ? 1.0f / sqrtf(sq + a.l2_eps) : 1.0f;
+      sh.nk[row] = a.l2norm ? 1.0f / sqrtf(sk + a.l2_eps) : 1.0f;
     }
   }
 
-  // the lower 16x16 tiles of K K^T (jobs 0..9) and Q K^T (jobs 10..19): wave w
-  // owns jobs w, w + 4, ..., element r of a tile at (4 (l/16) + r, l % 16)
-  f32x4 acc[5];
+  // the lower 16x16 blocks t = 0..9 of K K^T and Q K^T: wave w owns blocks
+  // w, w + 4, w + 8 (< 10); element r of a tile at (4 (l/16) + r, l % 16)
+  f32x4 accA[3], accP[3];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int job = w + 4 * k;
-    const int t = job >= 10 ? job - 10 : job;
-    const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-    const int tj = t - (ti * (ti + 1)) / 2;
-    const uint16_t* X = job >= 10 ? Qs : Ks;
-    acc[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < 3; ++k) {
+    const int t = w + 4 * k;
+    accA[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    accP[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (t < 10) {
+      const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+      const int tj = t - (ti * (ti + 1)) / 2;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc[k] = M::mma(frag<TIN>(X, LDQ, 16 * ti, 32 * kk, lane),
-                      frag<TIN>(Ks, LDQ, 16 * tj, 32 * kk, lane), acc[k]);
-  }
-  __syncthreads();  // Q and K are dead from here on: A and T take their space
-
-  // the strictly-upper 16x16 blocks of T and of P are zero for every head
-  for (int idx = tid; idx < 6 * 256; idx += 256) {
-    const int blk = idx >> 8, e = idx & 255;
-    const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-    const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-    const int i = 16 * bi + (e >> 4), j = 16 * bj + (e & 15);
-    Tm[i * LDF + j] = 0.0f;
-    Ps[i * LDT + j] = 0;
-  }
-
-  for (int jh = 0; jh < ratio; ++jh) {
-    const int h = hk * ratio + jh;
-    char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
-    if (w == 0) {
-      float gn = 0.0f, bn = 0.0f;  // the next head's, one head ahead
-      if (jh + 1 < ratio && lane < L) {
-        gn = a.g[(tb + lane) * a.g_rs + h + 1];
-        bn = a.beta[(tb + lane) * a.beta_rs + h + 1];
+      for (int kk = 0; kk < 4; ++kk) {
+        const typename M::x8 kb = frag_qk<TIN>(Ks, 16 * tj, 32 * kk, lane);
+        accA[k] = M::mma(frag_qk<TIN>(Ks, 16 * ti, 32 * kk, lane), kb, accA[k]);
+        accP[k] = M::mma(frag_qk<TIN>(Qs, 16 * ti, 32 * kk, lane), kb, accP[k]);
       }
+    }
+  }
+  __syncthreads();  // Q and K are dead from here on; the norms are visible
+
+  // prefix sums of the gates and the per-token factors of heads
+  // kPrepHeads q .. +3, wave w forming head kPrepHeads q + w
+  auto factors = [&](int q) {
+    const int jh = kPrepHeads * q + w;
+    if (jh < ratio) {
+      const int h = hk * ratio + jh;
+      char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
       const double gcum = wave_prefix64((double)gv);
-      Gd[lane] = gcum;
-      bt[lane] = bv;
-      rowA[lane] = bv * nk[lane];
-      rowP[lane] = a.scale * nq[lane];
-      // per-token factors
+      sh.Gd[w][lane] = gcum;
+      sh.bt[w][lane] = bv;
       const double gl = __shfl(gcum, L - 1, 64);
       const float eg = expf((float)gcum);
       float* F = reinterpret_cast<float*>(rec + REC_F);
-      F[lane] = eg * nk[lane];
-      F[CK + lane] = eg * a.scale * nq[lane];
-      F[2 * CK + lane] = expf((float)(gl - gcum)) * nk[lane];
+      F[lane] = eg * sh.nk[lane];
+      F[CK + lane] = eg * a.scale * sh.nq[lane];
+      F[2 * CK + lane] = expf((float)(gl - gcum)) * sh.nk[lane];
       F[3 * CK + lane] = lane == 0 ? expf((float)gl) : 0.0f;
-      gv = gn;
-      bv = bn;
     }
-    __syncthreads();
+    load_gb(q + 1);  // the next group's, a group ahead
+  };
+  factors(0);
+  __syncthreads();
 
-    // A (strictly lower, scaled) and P (lower incl. diagonal, scaled):
-    // element (i, j) = acc * row factor(i) * n_k,j * exp(G_i - G_j)
+  float* const Ab = &sh.u.at.A[0][0];
+  float* const Tb = &sh.u.at.T[0][0];
+  constexpr int BLK = 16 * LDB;
+  for (int jh = 0; jh < ratio; ++jh) {
+    const int hs = jh % kPrepHeads;
+    if (jh > 0 && hs == 0) {
+      factors(jh / kPrepHeads);
+      __syncthreads();
+    }
+    // lane-derived indices are formed afresh for each head: hoisted out of
+    // the loop they would hold more registers than four workgroups per CU allow
+    int tid_h = tid;
+    asm volatile("" : "+v"(tid_h));
+    const int lane = tid_h & 63;
+    const int g = lane >> 4, cl = lane & 15;
+    const int h = hk * ratio + jh;
+    char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
+    uint16_t* Pg = reinterpret_cast<uint16_t*>(rec + REC_P);
+
+    // A (strictly lower, scaled) into LDS and P (lower incl. diagonal,
+    // scaled) straight to the record: element (i, j) = acc * row factor(i) *
+    // n_k,j * exp(G_i - G_j), the exponential shared by the two
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      const int job = w + 4 * k;
-      const bool is_p = job >= 10;
-      const int t = is_p ? job - 10 : job;
-      const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-      const int tj = t - (ti * (ti + 1)) / 2;
-      const int i0 = 16 * ti + 4 * (lane >> 4);
-      const int j = 16 * tj + (lane & 15);
-      const double2 ga = *reinterpret_cast<const double2*>(Gd + i0);
-      const double2 gb = *reinterpret_cast<const double2*>(Gd + i0 + 2);
-      const double gi[4] = {ga.x, ga.y, gb.x, gb.y};
-      const double gj = Gd[j];
-      const float4 rf = *reinterpret_cast<const float4*>((is_p ? rowP : rowA) + i0);
-      const float rfi[4] = {rf.x, rf.y, rf.z, rf.w};
-      const float cj = nk[j];
+    for (int k = 0; k < 3; ++k) {
+      const int t = w + 4 * k;
+      if (t < 10) {
+        const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int tj = t - (ti * (ti + 1)) / 2;
+        const int i0 = 16 * ti + 4 * g;
+        const int j = 16 * tj + cl;
+        const double2 ga = *reinterpret_cast<const double2*>(&sh.Gd[hs][i0]);
+        const double2 gb = *reinterpret_cast<const double2*>(&sh.Gd[hs][i0 + 2]);
+        const double gi[4] = {ga.x, ga.y, gb.x, gb.y};
+        const double gj = sh.Gd[hs][j];
+        const float4 b4 = *reinterpret_cast<const float4*>(&sh.bt[hs][i0]);
+        const float4 k4 = *reinterpret_cast<const float4*>(&sh.nk[i0]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&sh.nq[i0]);
+        const float rfa[4] = {b4.x * k4.x, b4.y * k4.y, b4.z * k4.z, b4.w * k4.w};
+        const float rfp[4] = {a.scale * q4.x, a.scale * q4.y, a.scale * q4.z, a.scale * q4.w};
+        const float cj = sh.nk[j];
+        float* At = Ab + t * BLK;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + r;
-        const float e = expf((float)(gi[r] - gj));
-        const float x = acc[k][r] * rfi[r] * cj * e;
-        if (is_p)
-          Ps[i * LDT + j] = M::enc(j <= i ? x : 0.0f);
-        else
-          Am[i * LDF + j] = j < i ? x : 0.0f;
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + r;
+          const float e = expf((float)(gi[r] - gj));
+          const float xa = accA[k][r] * rfa[r] * cj * e;
+          const float xp = accP[k][r] * rfp[r] * cj * e;
+          At[(4 * g + r) * LDB + cl] = j < i ? xa : 0.0f;
+          Pg[i * CK + j] = M::enc(j <= i ? xp : 0.0f);
+        }
       }
+    }
+    // the six strictly-upper 16x16 blocks of P are zero
+    if (tid_h < 192) {
+      const int blk = tid_h >> 5, e = tid_h & 31;
+      const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+      const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+      const int i = 16 * bi + (e >> 1), j8 = 16 * bj + 8 * (e & 1);
+      *reinterpret_cast<uint4*>(Pg + i * CK + j8) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
     // diagonal blocks of T = (I + A)^{-1}: forward substitution, one column per lane
     if (lane < 16) {
-      const int b0 = 16 * w, col = lane;
+      const float* Ad = Ab + lower_blk(w, w) * BLK;
+      const int col = lane;
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float v = (r == col) ? 1.0f : 0.0f;
 #pragma unroll
-        for (int m = 0; m < r; ++m) v -= Am[(b0 + r) * LDF + b0 + m] * x[m];
+        for (int m = 0; m < r; ++m) v -= Ad[r * LDB + m] * x[m];
         x[r] = v;
         asm volatile("" ::: "memory");  // load row r + 1 of A only now: bounds the live registers
       }
+      float* Td = Tb + lower_blk(w, w) * BLK;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Tm[(b0 + r) * LDF + b0 + col] = x[r];
+      for (int r = 0; r < 16; ++r) Td[r * LDB + col] = x[r];
     }
     __syncthreads();
 
     // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
     // 16x16x16 products on the f32 MFMA (A: lane (m = l%16, k = l/16),
-    // B: lane (k = l/16, n = l%16), D: lane (m = 4 (l/16) + r, n = l%16))
+    // B: lane (k = l/16, n = l%16), D: lane (m = 4 (l/16) + r, n = l%16)).
+    // The partial sum goes through this wave's own slot of R, so only the
+    // finished block needs a workgroup barrier.
     for (int d = 1; d < 4; ++d) {
       const int j = w, i = w + d;
-      const bool active = i < 4;
-      f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
-      if (active) {
-        for (int k = j; k < i; ++k)
+      if (i < 4) {
+        f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
+        for (int k = j; k < i; ++k) {
+          const float* Aik = Ab + lower_blk(i, k) * BLK;
+          const float* Tkj = Tb + lower_blk(k, j) * BLK;
 #pragma unroll
           for (int s4 = 0; s4 < 4; ++s4)
-            r4 = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                Am[(16 * i + (lane & 15)) * LDF + 16 * k + 4 * s4 + (lane >> 4)],
-                Tm[(16 * k + 4 * s4 + (lane >> 4)) * LDF + 16 * j + (lane & 15)], r4, 0, 0, 0);
+            r4 = __builtin_amdgcn_mfma_f32_16x16x4f32(Aik[cl * LDB + 4 * s4 + g],
+                                                      Tkj[(4 * s4 + g) * LDB + cl], r4, 0, 0, 0);
+        }
+        float* Rw = sh.u.at.R[w];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Rs[w][(4 * (lane >> 4) + r) * 17 + (lane & 15)] = r4[r];
-      }
-      __syncthreads();
-      if (active) {
+        for (int r = 0; r < 4; ++r) Rw[(4 * g + r) * 17 + cl] = r4[r];
+        __builtin_amdgcn_wave_barrier();
+        const float* Tii = Tb + lower_blk(i, i) * BLK;
         f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
-          t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(
-              Tm[(16 * i + (lane & 15)) * LDF + 16 * i + 4 * s4 + (lane >> 4)],
-              Rs[w][(4 * s4 + (lane >> 4)) * 17 + (lane & 15)], t4, 0, 0, 0);
+          t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(Tii[cl * LDB + 4 * s4 + g],
+                                                    Rw[(4 * s4 + g) * 17 + cl], t4, 0, 0, 0);
+        float* Tij = Tb + lower_blk(i, j) * BLK;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          Tm[(16 * i + 4 * (lane >> 4) + r) * LDF + 16 * j + (lane & 15)] = -t4[r];
+        for (int r = 0; r < 4; ++r) Tij[(4 * g + r) * LDB + cl] = -t4[r];
       }
       __syncthreads();
     }
 
-    // T_b = T diag(beta), split into high and low 16-bit parts; P copied out
+    // T_b = T diag(beta), split into high and low 16-bit parts (blocks above
+    // the diagonal are zero)
     uint16_t* Th = reinterpret_cast<uint16_t*>(rec + REC_TH);
     uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + REC_TL);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int idx = tid + 256 * k;
+      const int idx = tid_h + 256 * k;
       const int i = idx >> 4, j4 = 4 * (idx & 15);
-      const float4 t = *reinterpret_cast<const float4*>(Tm + i * LDF + j4);
-      const float x[4] = {t.x * bt[j4], t.y * bt[j4 + 1], t.z * bt[j4 + 2], t.w * bt[j4 + 3]};
+      const int bi = i >> 4, bj = j4 >> 4;
+      const float4 t = bj <= bi ? *reinterpret_cast<const float4*>(
+                                      Tb + lower_blk(bi, bj) * BLK + (i & 15) * LDB + (j4 & 15))
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b4 = *reinterpret_cast<const float4*>(&sh.bt[hs][j4]);
+      const float x[4] = {t.x * b4.x, t.y * b4.y, t.z * b4.z, t.w * b4.w};
       uint16_t hh[4], ll[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -487,14 +518,7 @@ __global__ __launch_bounds__(256, 3) void chunk_prep_kernel(PrefillArgs a, const
       *reinterpret_cast<uint2*>(Tl + i * CK + j4) =
           make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
     }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int idx = tid + 256 * k;
-      const int i = idx >> 3, j8 = 8 * (idx & 7);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(rec + REC_P) + i * CK + j8) =
-          *reinterpret_cast<const uint4*>(Ps + i * LDT + j8);
-    }
-    __syncthreads();  // the next head rewrites Gd, bt, A, T and P
+    __syncthreads();  // the next head rewrites A and T (and, per group, Gd and bt)
   }
 }
 
