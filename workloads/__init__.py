@@ -204,11 +204,13 @@ def make_decode_case(name: str, seed: int, *, batch: int, hk: int, hv: int, dk: 
                      pool_std: float = 0.05, large_every_third: bool = False,
                      head0_offset: float = 40.0, a_log_hi: float = 2.0,
                      packed_pad: Optional[int] = None, null_rows=(),
-                     scale: Optional[float] = None) -> DecodeCase:
+                     scale: Optional[float] = None, with_pool: bool = True) -> DecodeCase:
     """One decode step for `batch` single-token sequences whose states live in a
     `slots`-slot pool.  idx = prefix of a seeded permutation of the slots, with
     the rows listed in `null_rows` set to -1.  With `packed_pad`, q|k|v share
-    one row of width 2*hk*dk + hv*dv + packed_pad (padding = NaN canaries)."""
+    one row of width 2*hk*dk + hv*dv + packed_pad (padding = NaN canaries).
+    `with_pool=False` leaves `pool` as an empty [0, hv, dv, dk] array, for a
+    caller that fills the slots itself (timing only)."""
     assert slots >= batch
     rng = np.random.default_rng(seed)
     q = rng.normal(0.0, 1.0, size=(batch, hk, dk))
@@ -235,7 +237,8 @@ def make_decode_case(name: str, seed: int, *, batch: int, hk: int, hv: int, dk: 
         qv = View(buf, 0, stride, in_dtype)
         kv = View(buf, hk * dk, stride, in_dtype)
         vv = View(buf, 2 * hk * dk, stride, in_dtype)
-    pool = make_pool(seed, slots, hv, dv, dk, pool_std)
+    pool = (make_pool(seed, slots, hv, dv, dk, pool_std) if with_pool
+            else np.empty((0, hv, dv, dk), np.float32))
     return DecodeCase(name=name, batch=batch, hk=hk, hv=hv, dk=dk, dv=dv,
                       in_dtype=in_dtype, out_dtype=out_dtype, q=qv, k=kv, v=vv,
                       alpha=alpha, dt_bias=dt_bias, ssm_a=ssm_a, beta=beta, pool=pool,
@@ -335,12 +338,12 @@ def prefill_varlen_gqa3(seed: int = 404) -> PrefillCase:
                              in_dtype=F16, out_dtype=F16, slots=64, pool_std=0.05)
 
 
-def decode_packed_b1024(seed: int = 505) -> DecodeCase:
+def decode_packed_b1024(seed: int = 505, with_pool: bool = True) -> DecodeCase:
     """B=1024 decode from one packed fp16 q|k|v row per sequence (stride padded by
     256 NaN columns), Hk=16, Hv=32, D=128, fp32 pool of 4096 slots."""
     return make_decode_case("decode-packed-B1024-Hk16-Hv32-D128-f16", seed, batch=1024,
                             hk=16, hv=32, dk=128, dv=128, in_dtype=F16, out_dtype=F16,
-                            slots=4096, pool_std=0.05, packed_pad=256)
+                            slots=4096, pool_std=0.05, packed_pad=256, with_pool=with_pool)
 
 
 # --------------------------------------------------------------------------
