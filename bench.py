@@ -110,7 +110,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=12)
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of each CPU-oracle baseline leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
@@ -373,7 +373,7 @@ def main():
                                state_idx=pidx, has_initial_state=phi, out=pout,
                                workspace=ws, stream=stream)
 
-        for _ in range(2):
+        for _ in range(8):
             prefill_step()
         torch.cuda.synchronize()
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

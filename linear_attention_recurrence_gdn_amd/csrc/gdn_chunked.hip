@@ -39,6 +39,9 @@
 // 16 significant bits -- the state is accumulated in f32 throughout.  The
 // cumulative gate G is summed in f64 so differences G_i - G_j stay exact even
 // when a head's gate is thousands per chunk.
+#include <algorithm>
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -113,52 +116,139 @@ __device__ __forceinline__ void chunk_bounds(const PrefillArgs& a, int64_t s, in
 }
 
 // ---------------------------------------------------------------------------
-// chunk offsets: cs[s] = number of chunks of sequences before s; cs[n] = total.
-// order[k] = the sequence with the k-th most chunks (ties by index) when
-// n <= kOrderMax, else k: the state walk starts the longest sequences first,
-// since the longest one bounds the whole prefill.
+// Per-call metadata in the workspace, formed on the device from cu_seqlens
+// (no host synchronisation):
+//   cs[s]    number of chunks of sequences before s; cs[n] = total;
+//   order[r] the sequence with the r-th most chunks (ties by index) when
+//            n <= kOrderMax, else r;
+//   ocs[r]   number of chunks of the sequences ranked before r;
+//   info[0]  split rank k: ranks [0, k) (the longest sequences) are walked as
+//            soon as their own records exist, while the records and walks of
+//            the other ranks proceed beside them on the remaining CUs.
+
+// The walk starts the longest sequences first, since the longest one bounds
+// the whole prefill.
 // ---------------------------------------------------------------------------
 constexpr int kOrderMax = 1024;
+constexpr int kSplitMax = 8;  // most ranks the early walk may take
 
-__global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, int32_t* cs,
-                                                         int32_t* order) {
+struct MetaPtrs {
+  int32_t *cs, *order, *ocs, *info;
+};
+
+__host__ __device__ inline MetaPtrs meta_ptrs(void* ws, int64_t n) {
+  int32_t* p = static_cast<int32_t*>(ws);
+  return {p, p + n + 1, p + 2 * n + 1, p + 3 * n + 2};
+}
+
+// block-wide inclusive scan of one value per thread (256 threads)
+__device__ __forceinline__ int32_t block_scan256(int32_t v, int32_t* part) {
+  part[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int32_t add = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  const int32_t r = part[threadIdx.x];
+  __syncthreads();
+  return r;
+}
+
+// The split rank from a cost model in units of one chunk step of one walk
+// workgroup (measured: a walk step costs about as much as the prep of one
+// (chunk, v-head) record on one CU):
+//   together:  all records on all CUs, then the walks;
+//   split k:   the records of ranks [0, k) on all CUs, then their walks on
+//              k hv ntiles CUs, beside the other records and walks on the
+//              remaining F CUs.
+// A walk phase takes max(longest sequence, its work / CUs).
+__device__ int split_rank(const int32_t* ocs, int n, int hv, int ntiles, int ncu, int kmax) {
+  const double C = ocs[n], H = hv, NT = ntiles, NC = ncu;
+  const double c0 = ocs[1] - ocs[0];
+  double best = C * H / NC + fmax(c0, C * H * NT / NC);
+  int kbest = 0;
+  for (int k = 1; k <= kmax && k < n; ++k) {
+    const double F = NC - (double)k * H * NT;
+    if (F < NC / 2) break;
+    const double CL = ocs[k], ck = ocs[k + 1] - ocs[k];
+    const double head = CL * H / NC;
+    const double tl = head + c0;
+    const double tr = head + (C - CL) * H / F + fmax(ck, (C - CL) * H * NT / F);
+    const double t = fmax(tl, tr) + 4.0;  // the second stream's launches and joins
+    if (t < best) {
+      best = t;
+      kbest = k;
+    }
+  }
+  return kbest;
+}
+
+__global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs m, int ntiles,
+                                                         int ncu, int kmax) {
   __shared__ int32_t part[256];
+  const int n = (int)a.num_seqs;
   int32_t carry = 0;
-  if (threadIdx.x == 0) cs[0] = 0;
-  for (int64_t base = 0; base < a.num_seqs; base += 256) {
-    const int64_t s = base + threadIdx.x;
+  if (threadIdx.x == 0) m.cs[0] = 0;
+  for (int base = 0; base < n; base += 256) {
+    const int s = base + (int)threadIdx.x;
     int32_t c = 0;
-    if (s < a.num_seqs) {
+    if (s < n) {
       int64_t t0, t1;
       chunk_bounds(a, s, t0, t1);
       c = (int32_t)((t1 - t0 + CK - 1) / CK);
     }
-    part[threadIdx.x] = c;
+    const int32_t incl = block_scan256(c, part);
+    if (s < n) m.cs[s + 1] = carry + incl;
+    if (threadIdx.x == 255) part[0] = incl;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int32_t add = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
-      __syncthreads();
-      part[threadIdx.x] += add;
-      __syncthreads();
-    }
-    if (s < a.num_seqs) cs[s + 1] = carry + part[threadIdx.x];
-    carry += part[255];
+    carry += part[0];
     __syncthreads();
   }
   __syncthreads();
-  const int n = (int)a.num_seqs;
   for (int s = threadIdx.x; s < n; s += 256) {
     int rank = s;
     if (n <= kOrderMax) {
-      const int cnt = cs[s + 1] - cs[s];
+      const int cnt = m.cs[s + 1] - m.cs[s];
       rank = 0;
       for (int t = 0; t < n; ++t) {
-        const int ct = cs[t + 1] - cs[t];
+        const int ct = m.cs[t + 1] - m.cs[t];
         rank += (ct > cnt) || (ct == cnt && t < s);
       }
     }
-    order[rank] = s;
+    m.order[rank] = s;
   }
+  __syncthreads();
+  // chunk offsets in rank order
+  carry = 0;
+  if (threadIdx.x == 0) m.ocs[0] = 0;
+  for (int base = 0; base < n; base += 256) {
+    const int r = base + (int)threadIdx.x;
+    int32_t c = 0;
+    if (r < n) {
+      const int s = m.order[r];
+      c = m.cs[s + 1] - m.cs[s];
+    }
+    const int32_t incl = block_scan256(c, part);
+    if (r < n) m.ocs[r + 1] = carry + incl;
+    if (threadIdx.x == 255) part[0] = incl;
+    __syncthreads();
+    carry += part[0];
+    __syncthreads();
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m.info[0] = n <= kOrderMax ? split_rank(m.ocs, n, a.hv, ntiles, ncu, kmax) : 0;
+  }
+}
+
+// The range of rank-order chunks [c0, c1) of a launch part: 0 = the ranks
+// walked early, 1 = the others, 2 = all.
+__device__ __forceinline__ void part_chunks(const MetaPtrs& m, int n, int part, int& c0, int& c1) {
+  const int k = part == 2 ? 0 : m.info[0];
+  c0 = part == 1 ? m.ocs[k] : 0;
+  c1 = part == 0 ? m.ocs[k] : m.ocs[n];
 }
 
 // A DPP move of an f64 (both halves); lanes the move does not reach read 0.
@@ -244,26 +334,11 @@ __device__ __forceinline__ typename MT<TIN>::x8 frag_qk(const uint16_t* m, int r
 
 __device__ __forceinline__ int lower_blk(int bi, int bj) { return (bi * (bi + 1)) / 2 + bj; }
 
+// One (chunk, q/k head) unit: chunk c (record index) of tokens [tb, tb + L).
 template <int TIN>
-__global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, const int32_t* cs,
-                                                            char* recs) {
-  __shared__ __align__(16) PrepLds sh;
+__device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, PrepLds& sh, int c,
+                                          int hk, int64_t tb, int L) {
   using M = MT<TIN>;
-
-  const int c = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int n = (int)a.num_seqs;
-  if (c >= cs[n]) return;
-  int lo = 0, hi = n - 1;  // largest s with cs[s] <= c
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cs[mid] <= c) lo = mid; else hi = mid - 1;
-  }
-  const int s = lo;
-  int64_t t0, t1;
-  chunk_bounds(a, s, t0, t1);
-  const int64_t tb = t0 + (int64_t)(c - cs[s]) * CK;
-  const int L = (int)min((int64_t)CK, t1 - tb);
   const int ratio = a.hv / a.hk;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -522,6 +597,34 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, const
   }
 }
 
+// One workgroup per (chunk, q/k head) unit of one launch part, the chunks
+// taken in rank order (longest sequences first); the grid covers every chunk
+// the call can have, and workgroups past the part's units leave at once.
+template <int TIN>
+__global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, MetaPtrs m,
+                                                            char* recs, int part) {
+  __shared__ __align__(16) PrepLds sh;
+  const int n = (int)a.num_seqs;
+  int c0, c1;
+  part_chunks(m, n, part, c0, c1);
+  const int64_t u = blockIdx.x;
+  if (u >= (int64_t)(c1 - c0) * a.hk) return;
+  const int cr = c0 + (int)(u / a.hk);
+  const int hk = (int)(u % a.hk);
+  int lo = 0, hi = n - 1;  // largest rank r with ocs[r] <= cr
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (m.ocs[mid] <= cr) lo = mid; else hi = mid - 1;
+  }
+  const int s = m.order[lo];
+  const int j = cr - m.ocs[lo];
+  int64_t t0, t1;
+  chunk_bounds(a, s, t0, t1);
+  const int64_t tb = t0 + (int64_t)j * CK;
+  const int L = (int)min((int64_t)CK, t1 - tb);
+  prep_unit<TIN>(a, recs, sh, m.cs[s] + j, hk, tb, L);
+}
+
 // ---------------------------------------------------------------------------
 // the state walk
 // ---------------------------------------------------------------------------
@@ -756,8 +859,7 @@ __device__ __forceinline__ void pack_split(const f32x4& t0, const f32x4& t1,
 // fall outside it and are dropped by the hardware, with no branch per row.
 template <int TIN, int TOUT, int NW, int NB, int MINB>
 __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
-    PrefillArgs a, const int32_t* cs, const int32_t* order, const char* recs, int ntiles,
-    int max_chunks) {
+    PrefillArgs a, MetaPtrs m, const char* recs, int ntiles, int max_chunks, int part) {
   constexpr int NTH = 64 * NW;
   constexpr int VC = WalkBuf<NW, NB>::VC;
   // the two chunk buffers are dynamic LDS: the static size would make the
@@ -783,12 +885,16 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   const int xcd = blockIdx.x % kXcds;
   const int rblk = blockIdx.x / kXcds;
   const int unit = (rblk / per_unit) * kXcds + xcd;
-  if (unit >= a.num_seqs * a.hk) return;
+  // this launch part's ranks: 0 = [0, k), 1 = [k, n), 2 = all
+  const int n = (int)a.num_seqs;
+  const int ksplit = part == 2 ? 0 : m.info[0];
+  const int rbeg = part == 1 ? ksplit : 0, rend = part == 0 ? ksplit : n;
+  const int s_rank = rbeg + unit / a.hk;
+  if (s_rank >= rend) return;
   const int j0 = rblk % per_unit;
   const int tile = j0 % ntiles;
   const int h = (unit % a.hk) * ratio + j0 / ntiles;
-  const int s_rank = unit / a.hk;
-  const int s = order[s_rank];
+  const int s = m.order[s_rank];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = lane >> 4, cl = lane & 15;
@@ -797,7 +903,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   c.a = &a;
   c.recs = recs;
   chunk_bounds(a, s, c.t_begin, c.t_end);
-  c.c0 = cs[s];
+  c.c0 = m.cs[s];
   c.h = h;
   c.hk = h / ratio;
   c.dv0 = tile * VC;
@@ -1153,37 +1259,111 @@ int64_t max_chunks(int64_t total_tokens, int64_t num_seqs) {
   return (total_tokens + CK - 1) / CK + num_seqs;
 }
 
-size_t meta_bytes(int64_t num_seqs) { return (size_t)((2 * num_seqs + 1) * 4 + 255) / 256 * 256; }
+size_t meta_bytes(int64_t num_seqs) { return (size_t)((3 * num_seqs + 6) * 4 + 255) / 256 * 256; }
 
 int walk_tiles(int dv) { return (dv + WALK_BV - 1) / WALK_BV; }
 
 
+// Per device: the CU count, and a second stream with two events for the split
+// schedule (created on first use, kept for the life of the process).
+struct SplitRes {
+  bool tried = false, ok = false;
+  int ncu = 0;
+  hipStream_t aux = nullptr;
+  hipEvent_t records_early = nullptr, rest_done = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SplitRes g_split[kMaxDevices];
+std::mutex g_split_mu;
+
+// Returns the device's resources, or nullptr when the split schedule is unavailable.
+SplitRes* split_res(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  SplitRes& r = g_split[dev];
+  if (!r.tried) {
+    r.tried = true;
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        ncu <= 0)
+      return nullptr;
+    r.ncu = ncu;
+    r.ok = hipStreamCreateWithFlags(&r.aux, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&r.records_early, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&r.rest_done, hipEventDisableTiming) == hipSuccess;
+  }
+  return r.ok ? &r : nullptr;
+}
+
 template <int TIN>
 hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) {
-  int32_t* cs = static_cast<int32_t*>(ws);
-  int32_t* order = cs + a.num_seqs + 1;
+  const MetaPtrs m = meta_ptrs(ws, a.num_seqs);
   char* recs = static_cast<char*>(ws) + meta_bytes(a.num_seqs);
   const int64_t mc = max_chunks(a.total_tokens, a.num_seqs);
-  hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, cs, order);
-  hipLaunchKernelGGL((chunk_prep_kernel<TIN>), dim3((unsigned)mc, (unsigned)a.hk), dim3(256), 0,
-                     stream, a, (const int32_t*)cs, recs);
   const int ntiles = walk_tiles(a.dv);
-  const int64_t units = a.num_seqs * a.hk;
-  const int64_t blocks = (units + kXcds - 1) / kXcds * kXcds * (a.hv / a.hk) * ntiles;
-  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const size_t lds = 2 * sizeof(WalkBuf<WALK_NW, WALK_NB>);
-  auto launch = [&](auto kern) -> hipError_t {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * WALK_NW), lds, stream, a,
-                       (const int32_t*)cs, (const int32_t*)order, (const char*)recs, ntiles, (int)mc);
-    return hipSuccess;
+  const int per_seq_wgs = a.hv * ntiles;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  // The split schedule needs its second stream; the early walk may take at
+  // most half of the CUs, so the records of the other ranks always have room.
+  std::unique_lock<std::mutex> lock(g_split_mu);
+  SplitRes* sr = split_res(dev);
+  int ncu = sr ? sr->ncu : 256;
+  int kmax = 0;
+  if (sr && a.num_seqs >= 2 && a.num_seqs <= kOrderMax)
+    kmax = (int)std::min<int64_t>({(int64_t)kSplitMax, a.num_seqs - 1,
+                                   (int64_t)(ncu / 2 / per_seq_wgs)});
+  if (kmax == 0) lock.unlock();
+
+  hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, m, ntiles, ncu, kmax);
+
+  const int64_t prep_units = mc * a.hk;
+  if (prep_units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const unsigned prep_grid = (unsigned)prep_units;
+  auto prep = [&](int part, hipStream_t st) {
+    hipLaunchKernelGGL((chunk_prep_kernel<TIN>), dim3(prep_grid), dim3(256), 0, st, a, m, recs,
+                       part);
   };
-  const hipError_t e = a.out_dt == kF32
-                           ? launch(chunk_state_kernel<TIN, kF32, WALK_NW, WALK_NB, WALK_MINB>)
-                           : launch(chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB>);
-  if (e != hipSuccess) return e;
+  const int ratio = a.hv / a.hk;
+  const size_t lds = 2 * sizeof(WalkBuf<WALK_NW, WALK_NB>);
+  auto walk_blocks = [&](int64_t ranks) {
+    return (ranks * a.hk + kXcds - 1) / kXcds * kXcds * ratio * ntiles;
+  };
+  if (walk_blocks(a.num_seqs) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  auto walk = [&](int part, int64_t ranks, hipStream_t st) -> hipError_t {
+    auto go = [&](auto kern) -> hipError_t {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)walk_blocks(ranks)), dim3(64 * WALK_NW), lds, st,
+                         a, m, (const char*)recs, ntiles, (int)mc, part);
+      return hipSuccess;
+    };
+    return a.out_dt == kF32 ? go(chunk_state_kernel<TIN, kF32, WALK_NW, WALK_NB, WALK_MINB>)
+                            : go(chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB>);
+  };
+
+  hipError_t e;
+  if (kmax == 0) {
+    prep(2, stream);
+    if ((e = walk(2, a.num_seqs, stream)) != hipSuccess) return e;
+    return hipGetLastError();
+  }
+  // Split schedule (the rank k is chosen on the device; k = 0 leaves parts 0
+  // empty and runs everything as part 1):
+  //   caller's stream: meta, records of ranks [0, k), their walks
+  //   second stream:   (after those records) the other records, their walks
+  // and the caller's stream then waits for the second.  The early walks are
+  // queued right behind their records on the caller's stream, so they take
+  // their CUs before the other records fill the device.
+  prep(0, stream);
+  if ((e = hipEventRecord(sr->records_early, stream)) != hipSuccess) return e;
+  if ((e = walk(0, kmax, stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sr->aux, sr->records_early, 0)) != hipSuccess) return e;
+  prep(1, sr->aux);
+  if ((e = walk(1, a.num_seqs, sr->aux)) != hipSuccess) return e;
+  if ((e = hipEventRecord(sr->rest_done, sr->aux)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(stream, sr->rest_done, 0)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
