@@ -282,6 +282,9 @@ __device__ __forceinline__ double wave_prefix64(double x) {
 //         16-bit (high part only; it multiplies U in the output term only)
 //   F   = f32 [4][64]: fz_i = e^{G_i} n_k,i,  fo_i = e^{G_i} scale n_q,i,
 //         fw_i = e^{G_last - G_i} n_k,i,  and F[3][0] = e^{G_last}
+// The walk multiplies T_b and P only in 32-token block pairs on or below the
+// diagonal, so their upper-right 32 x 32 quadrants (rows 0-31, columns 32-63)
+// are never read and never written.
 // ---------------------------------------------------------------------------
 constexpr int REC_TH = 0;
 constexpr int REC_TL = CK * CK * 2;
@@ -505,12 +508,11 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
         }
       }
     }
-    // the six strictly-upper 16x16 blocks of P are zero
-    if (tid_h < 192) {
+    // the strictly-upper 16x16 blocks of P that the walk reads, (0, 1) and
+    // (2, 3), are zero
+    if (tid_h < 64) {
       const int blk = tid_h >> 5, e = tid_h & 31;
-      const int bi = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-      const int bj = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-      const int i = 16 * bi + (e >> 1), j8 = 16 * bj + 8 * (e & 1);
+      const int i = 32 * blk + (e >> 1), j8 = 32 * blk + 16 + 8 * (e & 1);
       *reinterpret_cast<uint4*>(Pg + i * CK + j8) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
@@ -569,13 +571,14 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     }
 
     // T_b = T diag(beta), split into high and low 16-bit parts (blocks above
-    // the diagonal are zero)
+    // the diagonal are zero; the unread upper-right quadrant is skipped)
     uint16_t* Th = reinterpret_cast<uint16_t*>(rec + REC_TH);
     uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + REC_TL);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int idx = tid_h + 256 * k;
       const int i = idx >> 4, j4 = 4 * (idx & 15);
+      if (i < 32 && j4 >= 32) continue;
       const int bi = i >> 4, bj = j4 >> 4;
       const float4 t = bj <= bi ? *reinterpret_cast<const float4*>(
                                       Tb + lower_blk(bi, bj) * BLK + (i & 15) * LDB + (j4 & 15))
