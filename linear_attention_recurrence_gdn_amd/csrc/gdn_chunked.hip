@@ -736,8 +736,9 @@ __device__ __forceinline__ void stage_offsets(StageOffsets<NW, NB>& o, const Pre
   }
 #pragma unroll
   for (int i = 0; i < SO::NTP; ++i) {
-    const int p = 64 * (NW * i + w) + lane, row = p >> 3;
-    o.tp[i] = 2 * (row * CK + 8 * ((p & 7) ^ tp_swz(row)));
+    const int p = 64 * (NW * i + w) + lane, row = p >> 3, chunk = (p & 7) ^ tp_swz(row);
+    // the unread upper-right quadrant is not fetched: its offset lies past the record
+    o.tp[i] = row < 32 && chunk >= 4 ? kDropOffset : 2 * (row * CK + 8 * chunk);
   }
   constexpr int VCH = 2 * NW * NB;  // 16-byte chunks per V row
 #pragma unroll
@@ -776,13 +777,14 @@ __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx
 #pragma unroll
     for (int i = 0; i < SO::NKQ; ++i) dma16_buf(qr, o.q[i], B.Q + 512 * (NW * i + w));
   } else if constexpr (PART == 2) {
-    const char* rec = chunk_rec(c, ch);
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(chunk_rec(c, ch)), 0, REC_BYTES, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < SO::NTP; ++i) {
       const int u = NW * i + w;
-      dma16(rec + REC_TH + o.tp[i], B.Th + 512 * u);
-      dma16(rec + REC_TL + o.tp[i], B.Tl + 512 * u);
-      dma16(rec + REC_P + o.tp[i], B.P + 512 * u);
+      dma16_buf(rr, REC_TH + o.tp[i], B.Th + 512 * u);
+      dma16_buf(rr, REC_TL + o.tp[i], B.Tl + 512 * u);
+      dma16_buf(rr, REC_P + o.tp[i], B.P + 512 * u);
     }
   } else {
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
