@@ -309,6 +309,44 @@ def test_prefill_varlen_gqa3_sampled_heads(dev):
           flush=True)
 
 
+def test_prefill_skewed_batch_split_schedule_sampled_heads(dev):
+    """One 8192-token sequence beside seven of 2048 (GQA 3, fp16): the longest
+    sequence bounds the call, so the chunked path walks it as soon as its own
+    records exist while the others' records and walks run beside it on a
+    second stream.  The split rank is read back from the metadata the call
+    leaves in the workspace (int32 words cs[n+1], order[n], ocs[n+1], then
+    the split rank)."""
+    announce("prefill skewed batch [8192, 7 x 2048] Hk8 Hv24 fp16: split schedule, sampled heads")
+    lengths = [8192] + [2048] * 7
+    case = W.make_prefill_case("skew", 4242, lengths=lengths, hk=8, hv=24, dk=128, dv=128,
+                               in_dtype=W.F16, out_dtype=W.F16, slots=12,
+                               has_init=[1, 0, 1, 1, 0, 1, 1, 1])
+    T, N = case.total_tokens, case.num_seqs
+    _, q, k, v = H.upload_views(case, dev, T)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    g = gdn.gate(t(case.alpha), t(case.dt_bias), t(case.ssm_a))
+    pool = t(case.pool)
+    pool0 = pool.clone()
+    ws_n = gdn.prefill_workspace_size(T, N, case.hk, case.hv, case.dk, case.dv, torch.float16)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    out = gdn.prefill_varlen(q, k, v, g, t(case.beta), pool, t(case.cu_seqlens),
+                             scale=case.scale, state_idx=t(case.idx),
+                             has_initial_state=t(case.has_init), workspace=ws)
+    torch.cuda.synchronize()
+    words = ws[:4 * (3 * N + 3)].view(torch.int32).cpu().numpy()
+    split_rank = int(words[3 * N + 2])
+    assert list(words[N + 1:2 * N + 1][:1]) == [0]      # the 8192-token sequence ranks first
+    assert split_rank == 1, f"split rank {split_rank}"
+    heads = [0, 13]
+    mask = np.zeros(case.hv, np.uint8)
+    mask[heads] = 1
+    want_out, want_state = oracle.prefill_case(case, head_mask=mask)
+    res = H.PrefillResult(H.out_to_f64(out), pool, pool0, True)
+    r_out, r_st = H.check_prefill(case, res, want_out, want_state, heads=heads)
+    print(f"  split rank {split_rank}  out rel-L1 {r_out:.3e}  state rel-L1 {r_st:.3e}",
+          flush=True)
+
+
 @pytest.mark.parametrize("ind", [W.BF16, W.F16], ids=["bf16", "f16"])
 def test_prefill_chunked_matches_sequential(dev, ind):
     announce(f"prefill: chunked MFMA path vs token-sequential path ({W.DTYPE_NAMES[ind]})")
