@@ -70,6 +70,10 @@ FWD_CASES = [
     # 16-byte lanes with padded rows, zero-length and short sequences, a widened cache
     ([0, 3, 1, 20], 128, 4, W.BF16, W.BF16, W.BF16, True, True, [1, 0, 1, 1], True, 8, 1),
     ([9, 33], 64, 2, W.F16, W.F32, W.F16, False, False, [0, 1], False, 16, 0),
+    # 16-byte lanes in 256- and 128-lane workgroups: sequences starting inside
+    # 8-token spans and a partial last span
+    ([37, 100, 5, 3], 2048, 4, W.BF16, W.BF16, W.BF16, True, True, [1, 0, 1, 1], True, 0, 0),
+    ([25, 0, 41], 1024, 3, W.F16, W.F16, W.F32, False, True, [0, 1, 1], False, 0, 0),
 ]
 
 
