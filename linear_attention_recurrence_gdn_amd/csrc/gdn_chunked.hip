@@ -536,39 +536,56 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     }
     __syncthreads();
 
-    // off-diagonal blocks by distance d: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj,
-    // 16x16x16 products on the f32 MFMA (A: lane (m = l%16, k = l/16),
-    // B: lane (k = l/16, n = l%16), D: lane (m = 4 (l/16) + r, n = l%16)).
-    // The partial sum goes through this wave's own slot of R, so only the
-    // finished block needs a workgroup barrier.
-    for (int d = 1; d < 4; ++d) {
-      const int j = w, i = w + d;
-      if (i < 4) {
-        f32x4 r4 = {0.f, 0.f, 0.f, 0.f};
-        for (int k = j; k < i; ++k) {
-          const float* Aik = Ab + lower_blk(i, k) * BLK;
-          const float* Tkj = Tb + lower_blk(k, j) * BLK;
+    // off-diagonal blocks, on 16x16x16 products of the f32 MFMA (A: lane
+    // (m = l%16, k = l/16), B: lane (k = l/16, n = l%16), D: lane
+    // (m = 4 (l/16) + r, n = l%16)), in 32 x 32 halves: with T1, T2 the
+    // inverses of the upper-left and lower-right halves and A21 the
+    // lower-left half of A, T21 = -T2 A21 T1, so
+    //   round 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (two waves),
+    //   round 2: Y = A21 T1, one 16x16 block per wave,
+    //   round 3: T21 = -T2 Y, one block per wave.
+    // Partial products go through the waves' slots of R.
+    auto mma_blk = [&](const float* X, int ldx, const float* Y, int ldy, f32x4 acc) {
 #pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4)
-            r4 = __builtin_amdgcn_mfma_f32_16x16x4f32(Aik[cl * LDB + 4 * s4 + g],
-                                                      Tkj[(4 * s4 + g) * LDB + cl], r4, 0, 0, 0);
-        }
-        float* Rw = sh.u.at.R[w];
+      for (int s4 = 0; s4 < 4; ++s4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[cl * ldx + 4 * s4 + g],
+                                                   Y[(4 * s4 + g) * ldy + cl], acc, 0, 0, 0);
+      return acc;
+    };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    float* Rw = sh.u.at.R[w];
+    if (w < 2) {
+      const int i = 2 * w + 1, j = 2 * w;
+      const f32x4 r4 = mma_blk(Ab + lower_blk(i, j) * BLK, LDB, Tb + lower_blk(j, j) * BLK, LDB,
+                               zero4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Rw[(4 * g + r) * 17 + cl] = r4[r];
-        __builtin_amdgcn_wave_barrier();
-        const float* Tii = Tb + lower_blk(i, i) * BLK;
-        f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) Rw[(4 * g + r) * 17 + cl] = r4[r];
+      __builtin_amdgcn_wave_barrier();
+      const f32x4 t4 = mma_blk(Tb + lower_blk(i, i) * BLK, LDB, Rw, 17, zero4);
+      float* Tij = Tb + lower_blk(i, j) * BLK;
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          t4 = __builtin_amdgcn_mfma_f32_16x16x4f32(Tii[cl * LDB + 4 * s4 + g],
-                                                    Rw[(4 * s4 + g) * 17 + cl], t4, 0, 0, 0);
-        float* Tij = Tb + lower_blk(i, j) * BLK;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Tij[(4 * g + r) * LDB + cl] = -t4[r];
-      }
-      __syncthreads();
+      for (int r = 0; r < 4; ++r) Tij[(4 * g + r) * LDB + cl] = -t4[r];
     }
+    __syncthreads();
+    {
+      const int i = 2 + (w >> 1), j = w & 1;
+      f32x4 y4 = zero4;
+      for (int k = j; k < 2; ++k)
+        y4 = mma_blk(Ab + lower_blk(i, k) * BLK, LDB, Tb + lower_blk(k, j) * BLK, LDB, y4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Rw[(4 * g + r) * 17 + cl] = y4[r];
+    }
+    __syncthreads();
+    {
+      const int i = 2 + (w >> 1), j = w & 1;
+      f32x4 t4 = zero4;
+      for (int k = 2; k <= i; ++k)
+        t4 = mma_blk(Tb + lower_blk(i, k) * BLK, LDB, sh.u.at.R[2 * (k - 2) + j], 17, t4);
+      float* Tij = Tb + lower_blk(i, j) * BLK;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Tij[(4 * g + r) * LDB + cl] = -t4[r];
+    }
+    __syncthreads();
 
     // T_b = T diag(beta), split into high and low 16-bit parts (blocks above
     // the diagonal are zero; the unread upper-right quadrant is skipped)
