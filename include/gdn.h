@@ -309,7 +309,7 @@ int gdn_rmsnorm_gated(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt
  * gdn_prefill_varlen needs for these sizes and flags (0 if none).  The
  * chunked path (bf16/fp16 inputs, dk = 128, dv a multiple of 16) keeps one
  * 25,600-byte record per (64-token chunk, v-head): about
- * (total_tokens / 64 + num_seqs) * hv * 25,600 bytes plus about 8 bytes per
+ * (total_tokens / 64 + num_seqs) * hv * 25,600 bytes plus about 12 bytes per
  * sequence; the token-sequential path needs none.  Whether a call takes the
  * chunked path also depends on its pointers (16-byte aligned q/k/v rows,
  * strides multiples of 8 elements): with a smaller workspace it fails rather
@@ -350,6 +350,13 @@ size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs,
  *                forces the token-sequential kernel instead of the chunked
  *                one; at most one of GDN_STATE_F16, GDN_STATE_BF16.
  * num_seqs == 0 enqueues nothing and returns GDN_OK.
+ * Streams: everything is ordered on `stream`.  When the lengths are skewed
+ * the chunked path may run part of the work on a second stream the library
+ * owns (one per device, created on first use and kept for the life of the
+ * process, default priority), forked from and joined back into `stream`
+ * with events, so later work on `stream` still sees every result.  It does
+ * not do so while `stream` is being captured or when `stream` belongs to
+ * another device than the current one.
  */
 int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k,
                        const void* v, gdn_dtype in_dt, int64_t q_row_stride,
