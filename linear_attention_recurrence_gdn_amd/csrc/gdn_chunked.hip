@@ -125,7 +125,6 @@ __device__ __forceinline__ void chunk_bounds(const PrefillArgs& a, int64_t s, in
 //   info[0]  split rank k: ranks [0, k) (the longest sequences) are walked as
 //            soon as their own records exist, while the records and walks of
 //            the other ranks proceed beside them on the remaining CUs.
-
 // The walk starts the longest sequences first, since the longest one bounds
 // the whole prefill.
 // ---------------------------------------------------------------------------
@@ -1325,13 +1324,23 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   const int per_seq_wgs = a.hv * ntiles;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-  // The split schedule needs its second stream; the early walk may take at
-  // most half of the CUs, so the records of the other ranks always have room.
+  // The split schedule needs its second stream on the caller's stream's
+  // device (the current one), and is not used while the caller's stream is
+  // being captured; the early walk may take at most half of the CUs, so the
+  // records of the other ranks always have room.
+  bool can_split = a.num_seqs >= 2 && a.num_seqs <= kOrderMax;
+  if (can_split) {
+    hipDevice_t sdev = -1;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    can_split = hipStreamGetDevice(stream, &sdev) == hipSuccess && sdev == dev &&
+                hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+                cap == hipStreamCaptureStatusNone;
+  }
   std::unique_lock<std::mutex> lock(g_split_mu);
   SplitRes* sr = split_res(dev);
   int ncu = sr ? sr->ncu : 256;
   int kmax = 0;
-  if (sr && a.num_seqs >= 2 && a.num_seqs <= kOrderMax)
+  if (sr && can_split)
     kmax = (int)std::min<int64_t>({(int64_t)kSplitMax, a.num_seqs - 1,
                                    (int64_t)(ncu / 2 / per_seq_wgs)});
   if (kmax == 0) lock.unlock();

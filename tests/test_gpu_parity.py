@@ -347,6 +347,56 @@ def test_prefill_skewed_batch_split_schedule_sampled_heads(dev):
           flush=True)
 
 
+def test_prefill_skewed_batch_in_a_captured_graph(dev):
+    """The same skewed batch captured into a graph (the library keeps the whole
+    call on the captured stream then): every replay, from a restored pool,
+    gives the eager call's outputs and final states."""
+    announce("prefill skewed batch captured into a graph: replays equal the eager call")
+    lengths = [1500] + [300] * 5
+    case = W.make_prefill_case("skewg", 4343, lengths=lengths, hk=2, hv=6, dk=128, dv=64,
+                               in_dtype=W.BF16, out_dtype=W.BF16, slots=8,
+                               has_init=[1, 1, 0, 1, 1, 1])
+    T, N = case.total_tokens, case.num_seqs
+    _, q, k, v = H.upload_views(case, dev, T)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    g = gdn.gate(t(case.alpha), t(case.dt_bias), t(case.ssm_a))
+    beta, cu, idx, hi = t(case.beta), t(case.cu_seqlens), t(case.idx), t(case.has_init)
+    pool0 = t(case.pool)
+    ws = torch.empty(gdn.prefill_workspace_size(T, N, case.hk, case.hv, case.dk, case.dv,
+                                                torch.bfloat16), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, case.hv, case.dv), dtype=torch.bfloat16, device=dev)
+    pool = pool0.clone()
+
+    def call():
+        gdn.prefill_varlen(q, k, v, g, beta, pool, cu, scale=case.scale, state_idx=idx,
+                           has_initial_state=hi, out=out, workspace=ws,
+                           stream=torch.cuda.current_stream())
+
+    call()
+    torch.cuda.synchronize()
+    want_out, want_pool = out.clone(), pool.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        pool.copy_(pool0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        pool.copy_(pool0)
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want_out), f"replay {rep}: outputs differ"
+        assert H.bytes_equal(pool, want_pool), f"replay {rep}: states differ"
+    want_o, want_s = oracle.prefill_case(case)
+    H.check_prefill(case, H.PrefillResult(H.out_to_f64(want_out), want_pool, pool0, True),
+                    want_o, want_s)
+
+
 @pytest.mark.parametrize("ind", [W.BF16, W.F16], ids=["bf16", "f16"])
 def test_prefill_chunked_matches_sequential(dev, ind):
     announce(f"prefill: chunked MFMA path vs token-sequential path ({W.DTYPE_NAMES[ind]})")
