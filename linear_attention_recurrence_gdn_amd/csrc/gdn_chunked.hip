@@ -516,10 +516,12 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     }
     __syncthreads();
 
-    // diagonal blocks of T = (I + A)^{-1}: forward substitution, one column per lane
-    if (lane < 16) {
-      const float* Ad = Ab + lower_blk(w, w) * BLK;
-      const int col = lane;
+    // diagonal blocks of T = (I + A)^{-1}: forward substitution, one column per
+    // lane, all four blocks on wave 0 (lane group g takes block g), so the
+    // other waves leave their SIMDs to the workgroups sharing the CU
+    if (w == 0) {
+      const float* Ad = Ab + lower_blk(g, g) * BLK;
+      const int col = cl;
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -529,7 +531,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
         x[r] = v;
         asm volatile("" ::: "memory");  // load row r + 1 of A only now: bounds the live registers
       }
-      float* Td = Tb + lower_blk(w, w) * BLK;
+      float* Td = Tb + lower_blk(g, g) * BLK;
 #pragma unroll
       for (int r = 0; r < 16; ++r) Td[r * LDB + col] = x[r];
     }
