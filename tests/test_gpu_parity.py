@@ -397,6 +397,22 @@ def test_prefill_skewed_batch_in_a_captured_graph(dev):
                     want_o, want_s)
 
 
+@pytest.mark.parametrize("nseq", [300, 1100], ids=["n300", "n1100"])
+def test_prefill_many_short_sequences(dev, nseq):
+    """Hundreds of short sequences (zero-length ones among them): the chunked
+    path's per-call metadata spans several 256-wide scans, and beyond 1024
+    sequences the walk keeps index order instead of ranking by length."""
+    announce(f"prefill {nseq} short sequences (0..20 tokens), GQA 2, bf16")
+    rng = np.random.default_rng(nseq)
+    lengths = [int(x) for x in rng.integers(0, 21, size=nseq)]
+    case = W.make_prefill_case("many", 5000 + nseq, lengths=lengths, hk=1, hv=2, dk=128, dv=32,
+                               in_dtype=W.BF16, out_dtype=W.BF16, slots=nseq + 3,
+                               has_init=[int(x) for x in rng.integers(0, 2, size=nseq)])
+    res = H.run_prefill(case, dev)
+    want_out, want_state = oracle.prefill_case(case)
+    H.check_prefill(case, res, want_out, want_state)
+
+
 @pytest.mark.parametrize("ind", [W.BF16, W.F16], ids=["bf16", "f16"])
 def test_prefill_chunked_matches_sequential(dev, ind):
     announce(f"prefill: chunked MFMA path vs token-sequential path ({W.DTYPE_NAMES[ind]})")
