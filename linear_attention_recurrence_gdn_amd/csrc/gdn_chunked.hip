@@ -40,6 +40,7 @@
 // cumulative gate G is summed in f64 so differences G_i - G_j stay exact even
 // when a head's gate is thousands per chunk.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "gdn_device.h"
@@ -1364,10 +1365,16 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   if (walk_blocks(a.num_seqs) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   auto walk = [&](int part, int64_t ranks, hipStream_t st) -> hipError_t {
     auto go = [&](auto kern) -> hipError_t {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)lds);
-      if (e != hipSuccess) return e;
+      // the dynamic-LDS limit is raised once per device and kernel
+      static std::atomic<uint64_t> raised{0};
+      const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+      if (!bit || !(raised.load(std::memory_order_acquire) & bit)) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+        raised.fetch_or(bit, std::memory_order_acq_rel);
+      }
       hipLaunchKernelGGL(kern, dim3((unsigned)walk_blocks(ranks)), dim3(64 * WALK_NW), lds, st,
                          a, m, (const char*)recs, ntiles, (int)mc, part);
       return hipSuccess;
