@@ -404,6 +404,19 @@ def main():
             "mfma_frac_algorithmic": round(pflops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "path": "chunked" if ws_n > 0 else "token-sequential",
         }
+        if ws_n > 0:
+            # the call leaves its per-call metadata at the front of the workspace:
+            # int32 cs[N+1], order[N], ocs[N+1], then the split rank it chose
+            words = ws[:4 * (3 * N + 3)].view(torch.int32).cpu().numpy()
+            k = int(words[3 * N + 2])
+            order = [int(x) for x in words[N + 1:2 * N + 1]]
+            result["prefill"]["schedule"] = {
+                "split_rank": k,
+                "walked_early": [pre.meta["lengths"][s] for s in order[:k]],
+                "note": "the records of the k longest sequences are formed first and their "
+                        "walks start at once; the other sequences' records and walks run "
+                        "beside them on a second stream",
+            }
         log(f"prefill: {p_ms_step:.3f} ms/step -> {T / (p_ms_step * 1e-3) / 1e6:.2f} M tokens/s")
 
         # the causal conv1d before the front-end, over the same tokens
