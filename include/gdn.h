@@ -135,7 +135,8 @@ int gdn_gate(float* g, int64_t g_row_stride, const void* alpha, gdn_dtype alpha_
  *   width        1..8 (width 1 keeps no state: conv_state, state_idx and
  *                num_slots are then unused).  flags: GDN_CONV_SILU,
  *                GDN_CHECK_SLOTS, GDN_STATE_*.
- * A sequence with an out-of-range slot gets NaN outputs and keeps no state.
+ * Unchecked (no GDN_CHECK_SLOTS), a sequence whose slot lies outside
+ * [0, num_slots) gets NaN in every output row and keeps no state (width >= 2).
  * num_seqs == 0 enqueues nothing.
  */
 int gdn_conv1d_fwd(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt,

@@ -67,10 +67,11 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvArgs a) {
   int64_t s_begin = a.cu[s], s_end = a.cu[s + 1];
   // the window before t0
   float win[K > 1 ? K - 1 : 1];
+  bool ok = true;   // the sequence's slot is in range (else all its outputs are NaN)
   auto load_window = [&](int64_t t) {
     // inputs at positions t-(K-1) .. t-1 of sequence s (state or zeros before it)
     const int64_t slot = a.idx ? (int64_t)a.idx[s] : s;
-    const bool ok = slot >= 0 && slot < a.num_slots;
+    ok = K == 1 || (slot >= 0 && slot < a.num_slots);   // width 1 keeps no state
     const bool init = ok && (a.has_init ? a.has_init[s] != 0 : true);
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) {
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvArgs a) {
       else if (init)
         v = load1(a.state, a.state_dt,
                   (slot * a.C + c) * a.state_len + max((int64_t)0, (K - 1) + pos));
-      win[j] = ok ? v : __builtin_nanf("");
+      win[j] = v;
     }
   };
   load_window(t0);
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvArgs a) {
 #pragma unroll
       for (int j = 0; j < K - 1; ++j) acc += w[j] * win[j];
       acc += w[K - 1] * xs[i];
-      store1(a.out, a.out_dt, t * a.C + c, conv_act(acc, silu));
+      store1(a.out, a.out_dt, t * a.C + c, ok ? conv_act(acc, silu) : __builtin_nanf(""));
 #pragma unroll
       for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
       if constexpr (K > 1) win[K - 2] = xs[i];
@@ -116,7 +117,8 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvArgs a) {
 // 128 or 64 lanes); spans are dealt to the XCDs in contiguous ranges so the
 // K-1 rows before a span come from L2 (measured: x is fetched from HBM once,
 // not 11/8 times); a span inside one sequence (all but a few) runs as
-// straight-line code.
+// straight-line code.  Rows no other thread reads again, and every output
+// row, carry the nontemporal hint (measured 4-5 % faster than plain access).
 template <int TX>
 struct ConvVec {
   static constexpr int V = TX == kF32 ? 4 : 8;
@@ -126,6 +128,17 @@ struct ConvVec {
 template <int TX>
 __device__ __forceinline__ uint4 ld16x(const void* p, int64_t elem) {
   return *reinterpret_cast<const uint4*>(static_cast<const char*>(p) + elem * ConvVec<TX>::EB);
+}
+
+// The same 16 bytes with the nontemporal (streaming) hint, for rows no other
+// thread reads again.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int TX>
+__device__ __forceinline__ uint4 ld16x_stream(const void* p, int64_t elem) {
+  const u32x4_t r = __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p) + elem * ConvVec<TX>::EB));
+  return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 template <int TX>
@@ -164,9 +177,14 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
   const int64_t t1 = min(t0 + SPAN, a.T);
   const bool silu = a.silu != 0;
 
+  // The last K-1 rows of the span are read again as the next span's window
+  // (from L2); the rows before them stream past the caches.
   uint4 xr[SPAN];
 #pragma unroll
-  for (int i = 0; i < SPAN; ++i) xr[i] = ld16x<TX>(a.x, min(t0 + i, a.T - 1) * a.x_rs + c0);
+  for (int i = 0; i < SPAN; ++i) {
+    const int64_t e = min(t0 + i, a.T - 1) * a.x_rs + c0;
+    xr[i] = i < SPAN - (K - 1) ? ld16x_stream<TX>(a.x, e) : ld16x<TX>(a.x, e);
+  }
   // taps of the V channels: V*K contiguous elements, K 16-byte chunks
   float wf[V * K];
 #pragma unroll
@@ -182,9 +200,10 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
   int64_t s = seq_of(a.cu, a.n, t0);
   int64_t s_begin = a.cu[s], s_end = a.cu[s + 1];
   float win[K > 1 ? K - 1 : 1][V];
+  bool ok = true;   // the sequence's slot is in range (else all its outputs are NaN)
   auto load_window = [&](int64_t t) {
     const int64_t slot = a.idx ? (int64_t)a.idx[s] : s;
-    const bool ok = slot >= 0 && slot < a.num_slots;
+    ok = K == 1 || (slot >= 0 && slot < a.num_slots);   // width 1 keeps no state
     const bool init = ok && (a.has_init ? a.has_init[s] != 0 : true);
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) {
@@ -200,10 +219,6 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
                                        max((int64_t)0, (K - 1) + pos))
                            : 0.0f;
       }
-      if (!ok) {
-#pragma unroll
-        for (int v = 0; v < V; ++v) win[j][v] = __builtin_nanf("");
-      }
     }
   };
   load_window(t0);
@@ -218,20 +233,24 @@ __global__ __launch_bounds__(256) void conv_fwd_vec_kernel(ConvArgs a) {
 #pragma unroll
       for (int j = 0; j < K - 1; ++j) acc += wf[v * K + j] * win[j][v];
       acc += wf[v * K + K - 1] * xv[v];
-      y[v] = conv_act(acc, silu);
+      y[v] = ok ? conv_act(acc, silu) : __builtin_nanf("");
     }
+    // output rows are written once and not read back: streaming stores
     if constexpr (OF32 || TX == kF32) {
-      float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + t * a.C + c0);
+      float* o = static_cast<float*>(a.out) + t * a.C + c0;
 #pragma unroll
-      for (int q = 0; q < V / 4; ++q)
-        o[q] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+      for (int q = 0; q < V / 4; ++q) {
+        const f32x4_t r = {y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]};
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4_t*>(o + 4 * q));
+      }
     } else {
       uint32_t pk[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         pk[q] = TX == kBF16 ? pack2_bf16(y[2 * q], y[2 * q + 1]) : pack2_f16(y[2 * q], y[2 * q + 1]);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + t * a.C + c0) =
-          make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      const u32x4_t r = {pk[0], pk[1], pk[2], pk[3]};
+      __builtin_nontemporal_store(
+          r, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + t * a.C + c0));
     }
 #pragma unroll
     for (int j = 0; j + 1 < K - 1; ++j)

@@ -24,9 +24,20 @@ struct V16 {
   static constexpr int EB = DT == kF32 ? 4 : 2;
 };
 
+// x and z are read once and the output written once: every access carries
+// the nontemporal (streaming) hint, except the weight row, which all rows share.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 template <int DT>
 __device__ __forceinline__ uint4 ld16(const void* p, int64_t elem) {
   return *reinterpret_cast<const uint4*>(static_cast<const char*>(p) + elem * V16<DT>::EB);
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 ld16_stream(const void* p, int64_t elem) {
+  const u32x4_t r = __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p) + elem * V16<DT>::EB));
+  return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 template <int DT>
@@ -49,15 +60,19 @@ template <int DT, bool OF32>
 __device__ __forceinline__ void st_out(void* p, int64_t elem, const float (&y)[V16<DT>::N]) {
   constexpr int N = V16<DT>::N;
   if constexpr (OF32 || DT == kF32) {
-    float4* o = reinterpret_cast<float4*>(static_cast<float*>(p) + elem);
+    float* o = static_cast<float*>(p) + elem;
 #pragma unroll
-    for (int i = 0; i < N / 4; ++i) o[i] = make_float4(y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]);
+    for (int i = 0; i < N / 4; ++i) {
+      const f32x4_t r = {y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+      __builtin_nontemporal_store(r, reinterpret_cast<f32x4_t*>(o + 4 * i));
+    }
   } else {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = DT == kBF16 ? pack2_bf16(y[2 * i], y[2 * i + 1]) : pack2_f16(y[2 * i], y[2 * i + 1]);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + elem) = make_uint4(w[0], w[1], w[2], w[3]);
+    const u32x4_t r = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p) + elem));
   }
 }
 
@@ -79,8 +94,8 @@ __global__ __launch_bounds__(256) void rmsnorm_gated_kernel(NormArgs a, int64_t 
     const int64_t r = min(r0 + u * RPW + sub, nrows - 1);   // r = t * hv + h
     const int64_t t = r / a.hv;
     const int64_t h = r - t * a.hv;
-    xr[u] = ld16<DT>(a.x, r * DV + col);
-    zr[u] = ld16<DT>(a.z, t * a.z_rs + h * DV + col);
+    xr[u] = ld16_stream<DT>(a.x, r * DV + col);
+    zr[u] = ld16_stream<DT>(a.z, t * a.z_rs + h * DV + col);
   }
   float w[N];
   widen16<DT>(ld16<DT>(a.w, col), w);

@@ -120,6 +120,43 @@ def test_conv1d_fwd_matrix(dev, spec):
             assert H.bytes_equal(dstate[:, :, K - 1:], st0[:, :, K - 1:])
 
 
+@pytest.mark.parametrize("C,xd", [(256, W.BF16), (10, W.F32)], ids=["vec16B", "scalar"])
+def test_conv1d_fwd_out_of_range_slot(dev, C, xd):
+    """Unchecked slots: a sequence whose slot lies outside [0, num_slots) gets
+    NaN in every output row (not only where its window would have been read)
+    and keeps no state; its neighbours are unaffected."""
+    announce(f"conv1d_fwd out-of-range slot C={C} {W.DTYPE_NAMES[xd]}")
+    lengths, K = [20, 37, 11, 9], 4
+    T, N, slots = sum(lengths), len(lengths), 6
+    x, w, b, st = make_inputs(77 + C, T, C, K, xd, 0, slots, K - 1, W.F32, True)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    idx = np.asarray([4, slots + 5, 0, -1], np.int32)     # sequences 1 and 3 out of range
+    hi = np.ones(N, np.int8)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    dstate = H.to_dev(st, W.F32, dev)
+    st0 = dstate.clone()
+    out = gdn.conv1d_fwd(H.to_dev(x, xd, dev), H.to_dev(w, xd, dev), H.to_dev(b, xd, dev), dstate,
+                         t(cu), state_idx=t(idx), has_initial_state=t(hi), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # the oracle checks slots: give the two bad sequences valid slots there
+    # (their neighbours' outputs and states do not depend on them)
+    ok_idx = np.asarray([4, 1, 0, 2], np.int32)
+    want, want_st = oracle.conv1d_fwd(cu_seqlens=cu, C=C, K=K, x=x, x_dt=xd, x_rs=C, w=w, bias=b,
+                                      state=st, st_dt=W.F32, state_len=K - 1, idx=ok_idx,
+                                      has_init=hi, silu=True)
+    got = H.out_to_f64(out)
+    for s in range(N):
+        rows = slice(cu[s], cu[s + 1])
+        if s in (1, 3):
+            assert np.isnan(got[rows]).all(), f"sequence {s} not all NaN"
+        else:
+            assert H.rel_l1(got[rows], want[rows]) <= tol(xd, W.F32)
+    gst = state_f64(dstate)
+    np.testing.assert_array_equal(gst[[4, 0]], stored(want_st[[0, 2]], W.F32))
+    ut = torch.tensor([1, 2, 3, 5], device=dev)
+    assert H.bytes_equal(dstate[ut], st0[ut])
+
+
 UPD_CASES = [
     # (batch, C, K, x dtype, out dtype, state dtype, bias, silu, indexed, x pad, extra)
     (4, 7, 4, W.F32, W.F32, W.F32, True, True, False, 0, 0),
