@@ -83,6 +83,33 @@ def test_rmsnorm_gated_matrix(dev, spec):
     assert H.bytes_equal(xd, x0) and H.bytes_equal(zd, z0)
 
 
+def test_rmsnorm_gated_prefill_size_sampled_rows(dev):
+    """The launch the benchmark times: the [32768, 24, 128] fp16 prefill output
+    (about 786k rows, thousands of workgroups) with an fp16 gate and weight;
+    every output finite, 4096 sampled rows and the last one against the oracle."""
+    T, hv, dv = 32768, 24, 128
+    announce(f"rmsnorm_gated [{T}, {hv}, {dv}] fp16 sampled rows")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4040)
+    x = torch.randn((T, hv, dv), generator=gen, device=dev, dtype=torch.float32).to(torch.float16)
+    norm = W.norm_inputs(404, T, hv, dv, W.F16)
+    z = z_view(norm, T, hv, dv, dev)
+    w = H.to_dev(norm.w, W.F16, dev)
+    out = gdn.rmsnorm_gated(x, z, w, eps=norm.eps)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(4041)
+    rows = np.concatenate([rng.choice(T * hv, size=4096, replace=False), [T * hv - 1]])
+    ti, hi = rows // hv, rows % hv
+    xs = x[torch.from_numpy(ti).to(dev), torch.from_numpy(hi).to(dev)].cpu().numpy()
+    zs = norm.z.buf.reshape(T, -1)[ti[:, None], hi[:, None] * dv + np.arange(dv)]
+    want = oracle.rmsnorm_gated(xs.reshape(-1, 1, dv), W.F16, np.ascontiguousarray(zs), W.F16, dv,
+                                norm.w, W.F16, rows=rows.size, hv=1, dv=dv, eps=norm.eps)
+    got = H.out_to_f64(out[torch.from_numpy(ti).to(dev), torch.from_numpy(hi).to(dev)])
+    r = H.rel_l1(got, want.reshape(-1, dv))
+    assert r <= H.OUT_TOL_HALF, f"rel-L1 {r:.3e}"
+
+
 def test_rmsnorm_gated_hand_values(dev):
     announce("rmsnorm_gated: the pages' hand values")
     x = torch.tensor([[[3.0, 4.0]]], device=dev)
