@@ -29,8 +29,14 @@ constexpr int kConvXcds = 8;  // accelerator complex dies (separate L2s) on MI35
 #define GDN_CONV_SPAN 8
 #endif
 
+// silu(v) = v * sigmoid(v), sigmoid(v) = 1 / (1 + 2^(-v log2 e)), on the
+// hardware base-2 exponential and reciprocal (about 1 ulp each; the result
+// is within a few ulp of the correctly rounded value).  The library expf and
+// an IEEE division cost about 20 instructions per output and made the
+// forward pass ALU-bound (195 -> 141 us over 32768 x 5120 fp16).
 __device__ __forceinline__ float conv_act(float v, bool silu) {
-  return silu ? v / (1.0f + expf(-v)) : v;
+  return silu ? v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f))
+              : v;
 }
 
 // Sequence containing token t: the largest s with cu[s] <= t (zero-length
