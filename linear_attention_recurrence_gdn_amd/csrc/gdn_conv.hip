@@ -383,8 +383,132 @@ hipError_t launch_fwd_tx(const ConvArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The update with 16-byte lanes (16-bit x, state_len == K-1): each thread
+// owns 8 channels of one row, whose state rows are 8(K-1) contiguous
+// elements, read and written back as whole 16-byte chunks; x, the taps and
+// the output move 16 bytes per lane as in the forward pass.
+template <int TX, int K, int TS>
+__global__ __launch_bounds__(256) void conv_update_vec_kernel(ConvArgs a) {
+  constexpr int V = ConvVec<TX>::V;
+  static_assert(V == 8 && K >= 2, "16-bit inputs, width >= 2");
+  constexpr int ES = TS == kF32 ? 4 : 2;
+  constexpr int NS = V * (K - 1);          // state elements of the thread's channels
+  constexpr int NQ = NS * ES / 16;         // 16-byte chunks of them
+  const int64_t c0 = ((int64_t)blockIdx.y * blockDim.x + threadIdx.x) * V;
+  const int64_t r = blockIdx.x;
+  if (c0 >= a.C) return;
+  const int64_t slot = a.idx ? (int64_t)a.idx[r] : r;
+  if (slot < 0) return;                     // padded row: output and state untouched
+  const bool of32 = a.out_dt == kF32;
+  if (slot >= a.num_slots) {                // caller error: NaN, no state access
+    for (int v = 0; v < V; ++v) store1(a.out, a.out_dt, r * a.C + c0 + v, __builtin_nanf(""));
+    return;
+  }
+  uint4* sp = reinterpret_cast<uint4*>(static_cast<char*>(a.state) +
+                                       (slot * a.C + c0) * (int64_t)(K - 1) * ES);
+  uint4 sq[NQ];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) sq[i] = sp[i];
+  float xv[V], wf[V * K], st[NS];
+  widen_v<TX>(ld16x<TX>(a.x, r * a.x_rs + c0), xv);
+#pragma unroll
+  for (int i = 0; i < K; ++i) widen_v<TX>(ld16x<TX>(a.w, c0 * K + i * V), wf + i * V);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    if constexpr (TS == kF32) widen_v<kF32>(sq[i], st + 4 * i);
+    else widen_v<TS>(sq[i], st + 8 * i);
+  }
+  float bias[V];
+  if (a.bias) {
+    widen_v<TX>(ld16x<TX>(a.bias, c0), bias);
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) bias[v] = 0.0f;
+  }
+  const bool silu = a.silu != 0;
+  float y[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float acc = bias[v];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) acc += wf[v * K + j] * st[v * (K - 1) + j];
+    acc += wf[v * K + K - 1] * xv[v];
+    y[v] = conv_act(acc, silu);
+  }
+  if (of32) {
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + r * a.C + c0);
+    o[0] = make_float4(y[0], y[1], y[2], y[3]);
+    o[1] = make_float4(y[4], y[5], y[6], y[7]);
+  } else {
+    uint32_t pk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      pk[q] = TX == kBF16 ? pack2_bf16(y[2 * q], y[2 * q + 1]) : pack2_f16(y[2 * q], y[2 * q + 1]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + r * a.C + c0) =
+        make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+  // rolled rows: the last K-2 entries move up, the input enters at the end
+  float ns[NS];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int j = 0; j + 1 < K - 1; ++j) ns[v * (K - 1) + j] = st[v * (K - 1) + j + 1];
+    ns[v * (K - 1) + K - 2] = xv[v];
+  }
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    uint4 q;
+    if constexpr (TS == kF32) {
+      q = make_uint4(__float_as_uint(ns[4 * i]), __float_as_uint(ns[4 * i + 1]),
+                     __float_as_uint(ns[4 * i + 2]), __float_as_uint(ns[4 * i + 3]));
+    } else {
+      const float* e = ns + 8 * i;
+      auto p2 = [](float lo, float hi) {
+        return TS == kBF16 ? pack2_bf16(lo, hi) : pack2_f16(lo, hi);
+      };
+      q = make_uint4(p2(e[0], e[1]), p2(e[2], e[3]), p2(e[4], e[5]), p2(e[6], e[7]));
+    }
+    sp[i] = q;
+  }
+}
+
+// The 16-byte update applies when x is 16-bit, the width is 2..5, the state
+// rows hold exactly K-1 entries, the channels and x's row stride are
+// multiples of 8 and every buffer is 16-byte aligned.
+template <int TX>
+static bool update_vec_ok(const ConvArgs& a) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; };
+  return TX != kF32 && a.K >= 2 && a.K <= 5 && a.state_len == a.K - 1 && a.C % 8 == 0 &&
+         a.x_rs % 8 == 0 && al(a.x) && al(a.w) && (a.bias == nullptr || al(a.bias)) &&
+         al(a.out) && al(a.state);
+}
+
+template <int TX, int TS>
+hipError_t launch_update_vec(const ConvArgs& a, hipStream_t stream) {
+  const int64_t lanes = a.C / 8;
+  const unsigned nthr = lanes >= 256 ? 256 : lanes >= 128 ? 128 : 64;
+  const dim3 grid((unsigned)a.n, (unsigned)((lanes + nthr - 1) / nthr));
+  switch (a.K) {
+#define GDN_CONV_K(KK) \
+    case KK: \
+      hipLaunchKernelGGL((conv_update_vec_kernel<TX, KK, TS>), grid, dim3(nthr), 0, stream, a); \
+      break;
+    GDN_CONV_K(2) GDN_CONV_K(3) GDN_CONV_K(4) GDN_CONV_K(5)
+#undef GDN_CONV_K
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int TX>
 hipError_t launch_update_tx(const ConvArgs& a, hipStream_t stream) {
+  if constexpr (TX != kF32) {
+    if (update_vec_ok<TX>(a)) {
+      return a.state_dt == kF32  ? launch_update_vec<TX, kF32>(a, stream)
+           : a.state_dt == kBF16 ? launch_update_vec<TX, kBF16>(a, stream)
+                                 : launch_update_vec<TX, kF16>(a, stream);
+    }
+  }
   const dim3 grid((unsigned)a.n, (unsigned)((a.C + 255) / 256));
   switch (a.K) {
 #define GDN_CONV_K(KK) \

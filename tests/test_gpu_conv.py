@@ -164,6 +164,13 @@ UPD_CASES = [
     (5, 100, 3, W.F16, W.F32, W.F32, True, False, True, 5, 1),
     (6, 256, 5, W.BF16, W.F32, W.F16, True, True, True, 0, 0),
     (2, 33, 1, W.F32, W.F32, W.F32, True, True, False, 0, 0),
+    # 16-byte lanes: f32 / bf16 / f16 state rows of exactly K-1 entries, padded x rows,
+    # a 64-lane workgroup at width 2, and the decode batch's shape
+    (64, 1024, 4, W.F16, W.F16, W.F32, True, True, True, 8, 0),
+    (7, 64, 2, W.BF16, W.BF16, W.F32, False, False, False, 0, 0),
+    (256, 8192, 4, W.BF16, W.BF16, W.BF16, False, True, True, 0, 0),
+    # a widened cache keeps the per-channel kernel
+    (4, 512, 4, W.BF16, W.BF16, W.BF16, True, True, True, 0, 1),
 ]
 
 
