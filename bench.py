@@ -127,7 +127,7 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        sys.exit("bench.py: this build measures one GPU only (the decode and prefill kernels "
+        sys.exit("bench.py: one GPU only (the decode and prefill kernels "
                  "shard by sequence with no exchange); run with --gpus 1")
 
     import torch

@@ -543,9 +543,9 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     // (m = 4 (l/16) + r, n = l%16)), in 32 x 32 halves: with T1, T2 the
     // inverses of the upper-left and lower-right halves and A21 the
     // lower-left half of A, T21 = -T2 A21 T1, so
-    //   round 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (two waves),
-    //   round 2: Y = A21 T1, one 16x16 block per wave,
-    //   round 3: T21 = -T2 Y, one block per wave.
+    //   pass 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22 (two waves),
+    //   pass 2: Y = A21 T1, one 16x16 block per wave,
+    //   pass 3: T21 = -T2 Y, one block per wave.
     // Partial products go through the waves' slots of R.
     auto mma_blk = [&](const float* X, int ldx, const float* Y, int ldy, f32x4 acc) {
 #pragma unroll
