@@ -347,6 +347,7 @@ def main():
             "kernel_avg_us": round(uavg * 1e3, 2),
             "algorithmic_bytes": ubytes,
             "achieved_GBs": round(ubytes / (uavg * 1e-3) / 1e9, 1),
+            "hbm_frac": round(ubytes / (uavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
         log(f"conv1d_update: kernel avg {uavg * 1e3:.1f} us")
         del ust
