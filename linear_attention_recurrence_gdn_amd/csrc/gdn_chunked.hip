@@ -188,9 +188,16 @@ __device__ int split_rank(const int32_t* ocs, int n, int hv, int ntiles, int ncu
 __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs m, int ntiles,
                                                          int ncu, int kmax) {
   __shared__ int32_t part[256];
+  // Up to kOrderMax sequences the three tables are built in LDS and copied
+  // out once at the end (no global round trips between the steps).
+  __shared__ int32_t l_cs[kOrderMax + 1], l_order[kOrderMax], l_ocs[kOrderMax + 1];
   const int n = (int)a.num_seqs;
+  const bool small = n <= kOrderMax;
+  int32_t* const cs = small ? l_cs : m.cs;
+  int32_t* const order = small ? l_order : m.order;
+  int32_t* const ocs = small ? l_ocs : m.ocs;
   int32_t carry = 0;
-  if (threadIdx.x == 0) m.cs[0] = 0;
+  if (threadIdx.x == 0) cs[0] = 0;
   for (int base = 0; base < n; base += 256) {
     const int s = base + (int)threadIdx.x;
     int32_t c = 0;
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
       c = (int32_t)((t1 - t0 + CK - 1) / CK);
     }
     const int32_t incl = block_scan256(c, part);
-    if (s < n) m.cs[s + 1] = carry + incl;
+    if (s < n) cs[s + 1] = carry + incl;
     if (threadIdx.x == 255) part[0] = incl;
     __syncthreads();
     carry += part[0];
@@ -209,29 +216,29 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
   __syncthreads();
   for (int s = threadIdx.x; s < n; s += 256) {
     int rank = s;
-    if (n <= kOrderMax) {
-      const int cnt = m.cs[s + 1] - m.cs[s];
+    if (small) {
+      const int cnt = cs[s + 1] - cs[s];
       rank = 0;
       for (int t = 0; t < n; ++t) {
-        const int ct = m.cs[t + 1] - m.cs[t];
+        const int ct = cs[t + 1] - cs[t];
         rank += (ct > cnt) || (ct == cnt && t < s);
       }
     }
-    m.order[rank] = s;
+    order[rank] = s;
   }
   __syncthreads();
   // chunk offsets in rank order
   carry = 0;
-  if (threadIdx.x == 0) m.ocs[0] = 0;
+  if (threadIdx.x == 0) ocs[0] = 0;
   for (int base = 0; base < n; base += 256) {
     const int r = base + (int)threadIdx.x;
     int32_t c = 0;
     if (r < n) {
-      const int s = m.order[r];
-      c = m.cs[s + 1] - m.cs[s];
+      const int s = order[r];
+      c = cs[s + 1] - cs[s];
     }
     const int32_t incl = block_scan256(c, part);
-    if (r < n) m.ocs[r + 1] = carry + incl;
+    if (r < n) ocs[r + 1] = carry + incl;
     if (threadIdx.x == 255) part[0] = incl;
     __syncthreads();
     carry += part[0];
@@ -239,7 +246,14 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    m.info[0] = n <= kOrderMax ? split_rank(m.ocs, n, a.hv, ntiles, ncu, kmax) : 0;
+    m.info[0] = small ? split_rank(ocs, n, a.hv, ntiles, ncu, kmax) : 0;
+  }
+  if (small) {
+    for (int i = threadIdx.x; i <= n; i += 256) {
+      m.cs[i] = l_cs[i];
+      m.ocs[i] = l_ocs[i];
+      if (i < n) m.order[i] = l_order[i];
+    }
   }
 }
 
