@@ -213,6 +213,36 @@ def test_conv1d_update_matrix(dev, spec):
             assert H.bytes_equal(dstate[:, :, K - 1:], st0[:, :, K - 1:])
 
 
+@pytest.mark.parametrize("C,xd", [(512, W.BF16), (36, W.F16)], ids=["vec16B", "scalar"])
+def test_conv1d_update_out_of_range_slot(dev, C, xd):
+    """Unchecked slots in the update: a row whose slot is past num_slots gets a
+    NaN output row and touches no state; a negative slot leaves its output row
+    and every state alone; the other rows match the oracle."""
+    announce(f"conv1d_update out-of-range slot C={C} {W.DTYPE_NAMES[xd]}")
+    B, K, slots = 5, 4, 6
+    x, w, b, st = make_inputs(91 + C, B, C, K, xd, 0, slots, K - 1, W.BF16, True)
+    idx = np.asarray([3, slots + 2, 0, -1, 5], np.int32)
+    dstate = H.to_dev(st, W.BF16, dev)
+    st0 = dstate.clone()
+    out = torch.full((B, C), 5.0, dtype=torch.float32, device=dev)
+    gdn.conv1d_update(H.to_dev(x, xd, dev), H.to_dev(w, xd, dev), H.to_dev(b, xd, dev), dstate,
+                      state_idx=torch.from_numpy(idx).to(dev), out=out)
+    torch.cuda.synchronize()
+    ok_idx = np.asarray([3, 1, 0, -1, 5], np.int32)   # the oracle checks slots
+    want, want_st, written = oracle.conv1d_update(batch=B, C=C, K=K, x=x, x_dt=xd, x_rs=C, w=w,
+                                                  bias=b, state=st, st_dt=W.BF16,
+                                                  state_len=K - 1, idx=ok_idx, silu=True)
+    got = H.out_to_f64(out)
+    assert np.isnan(got[1]).all()
+    assert np.all(got[3] == 5.0)
+    live = [0, 2, 4]
+    assert H.rel_l1(got[live], want[live]) <= tol(xd, W.F32)
+    gst = state_f64(dstate)
+    np.testing.assert_array_equal(gst[[3, 0, 5]], stored(want_st[live], W.BF16))
+    ut = torch.tensor([1, 2, 4], device=dev)
+    assert H.bytes_equal(dstate[ut], st0[ut])
+
+
 def test_conv1d_update_chain_equals_fwd(dev):
     announce("conv1d: update chain == fwd over the same tokens")
     T, C, K = 12, 130, 4
