@@ -29,7 +29,7 @@ def build(force: bool = True) -> str:
     no FMA contraction, so every product and sum is rounded as written)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-O2", "-std=gnu99", "-pthread", "-fPIC", "-shared",
                                "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
@@ -78,8 +78,37 @@ def _load():
         lib.oracle_rmsnorm_gated.restype = i32
         lib.oracle_rmsnorm_gated.argtypes = [i64, i64, i64, vp, i32, vp, i32, i64, vp, i32,
                                              dbl, i32, vp]
+        lib.oracle_set_threads.restype = None
+        lib.oracle_set_threads.argtypes = [i32]
+        lib.oracle_get_threads.restype = i32
+        lib.oracle_get_threads.argtypes = []
+        lib.oracle_set_threads(default_threads())
         _lib = lib
     return _lib
+
+
+def default_threads() -> int:
+    """Host threads for the (row or sequence, v-head) units of decode and
+    prefill: the CPUs this process may run on, at most 16 (one GPU's share of
+    a host), or ORACLE_THREADS when set."""
+    env = os.environ.get("ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def set_threads(n: int) -> None:
+    """Threads for decode and prefill units (the arithmetic of a unit does not
+    depend on it)."""
+    _load().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().oracle_get_threads())
 
 
 class OracleError(RuntimeError):

@@ -41,6 +41,7 @@
  * the invariants listed there).
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -214,6 +215,60 @@ static int check_slots(const int32_t* idx, int64_t n, int64_t num_slots, int all
 }
 
 /* ------------------------------------------------------------------------
+ * Independent units on several host threads.  The recurrence never mixes
+ * sequences or v-heads, so each (row or sequence, v-head) unit is computed
+ * alone, in the order written above, by whichever thread takes it; the
+ * arithmetic of a unit does not depend on the thread count.  Every thread
+ * owns its own scratch vectors.
+ * ------------------------------------------------------------------------ */
+static int g_threads = 1;
+
+void oracle_set_threads(int n) { g_threads = n < 1 ? 1 : (n > 256 ? 256 : n); }
+int oracle_get_threads(void) { return g_threads; }
+
+typedef void (*unit_fn)(const void* ctx, int64_t unit, double* scratch);
+
+struct unit_job {
+  unit_fn fn;
+  const void* ctx;
+  int64_t n_units;
+  int64_t next; /* taken with an atomic add */
+  size_t scratch_len;
+  int failed;
+};
+
+static void* unit_worker(void* arg) {
+  struct unit_job* job = (struct unit_job*)arg;
+  double* scratch = (double*)malloc(job->scratch_len * sizeof(double));
+  if (!scratch) {
+    __atomic_store_n(&job->failed, 1, __ATOMIC_RELAXED);
+    return NULL;
+  }
+  for (;;) {
+    const int64_t u = __atomic_fetch_add(&job->next, 1, __ATOMIC_RELAXED);
+    if (u >= job->n_units) break;
+    job->fn(job->ctx, u, scratch);
+  }
+  free(scratch);
+  return NULL;
+}
+
+static int run_units(unit_fn fn, const void* ctx, int64_t n_units, size_t scratch_len) {
+  struct unit_job job = {fn, ctx, n_units, 0, scratch_len, 0};
+  int nt = g_threads;
+  if ((int64_t)nt > n_units) nt = n_units > 0 ? (int)n_units : 1;
+  pthread_t tids[256];
+  int started = 0;
+  for (int i = 1; i < nt; ++i) {
+    if (pthread_create(&tids[started], NULL, unit_worker, &job) != 0) break;
+    ++started;
+  }
+  unit_worker(&job); /* the calling thread works too */
+  for (int i = 0; i < started; ++i) pthread_join(tids[i], NULL);
+  return job.failed ? OR_ERR_ARG : OR_OK;
+}
+
+/* ------------------------------------------------------------------------
  * Decode: one token for each of `batch` sequences.  Sequence b's state is
  * pool[idx[b]] ([hv][dv][dk], read only here, stored as f32, f16 or bf16 per
  * state_dt and widened exactly to f64); idx[b] < 0 marks a padded
@@ -224,6 +279,45 @@ static int check_slots(const int32_t* idx, int64_t n, int64_t num_slots, int all
  * head_mask [hv] (NULL = all heads) restricts the work to the marked v-heads;
  * entries of other heads are left as given.
  * ------------------------------------------------------------------------ */
+struct decode_ctx {
+  int64_t hk, hv, dk, dv, ratio;
+  const void *q, *k, *v;
+  int in_dt;
+  int64_t q_rs, k_rs, v_rs;
+  const double* g;
+  const float* beta;
+  int64_t beta_rs;
+  const void* pool;
+  int state_dt;
+  const int32_t* idx;
+  double scale, l2_eps;
+  int l2norm;
+  const uint8_t* head_mask;
+  double *out, *state_out;
+};
+
+/* unit = (row b, v-head h) */
+static void decode_unit(const void* cp, int64_t u, double* scratch) {
+  const struct decode_ctx* c = (const struct decode_ctx*)cp;
+  const int64_t b = u / c->hv, h = u % c->hv;
+  if (c->head_mask && !c->head_mask[h]) return;
+  const int64_t dk = c->dk, dv = c->dv, head_elems = dv * dk;
+  double *qd = scratch, *kd = qd + dk, *vd = kd + dk, *work = vd + dv;
+  double* o = c->out + (b * c->hv + h) * dv;
+  const int32_t slot = c->idx[b];
+  if (slot < 0) {
+    for (int64_t i = 0; i < dv; ++i) o[i] = 0.0;
+    return;
+  }
+  load_qkv(c->q, c->k, c->v, c->in_dt, c->q_rs, c->k_rs, c->v_rs, b, h / c->ratio, h, dk, dv,
+           c->l2norm, c->l2_eps, c->scale, qd, kd, vd);
+  double* S = c->state_out + (b * c->hv + h) * head_elems;
+  const int64_t s0 = ((int64_t)slot * c->hv + h) * head_elems;
+  for (int64_t e = 0; e < head_elems; ++e) S[e] = load_elem(c->pool, c->state_dt, s0 + e);
+  recurrence_step(S, dv, dk, kd, qd, vd, c->g[b * c->hv + h],
+                  (double)c->beta[b * c->beta_rs + h], o, work);
+}
+
 int oracle_decode(int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
                   const void* q, const void* k, const void* v, int in_dt, int64_t q_rs,
                   int64_t k_rs, int64_t v_rs, const double* g, const float* beta,
@@ -236,34 +330,10 @@ int oracle_decode(int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
   if (state_dt != OR_F32 && state_dt != OR_F16 && state_dt != OR_BF16) return OR_ERR_ARG;
   rc = check_slots(idx, batch, num_slots, 1);
   if (rc) return rc;
-  const int64_t ratio = hv / hk;
-  double* qd = (double*)malloc((size_t)dk * sizeof(double));
-  double* kd = (double*)malloc((size_t)dk * sizeof(double));
-  double* vd = (double*)malloc((size_t)dv * sizeof(double));
-  double* work = (double*)malloc((size_t)dv * sizeof(double));
-  if (!qd || !kd || !vd || !work) { free(qd); free(kd); free(vd); free(work); return OR_ERR_ARG; }
-  const int64_t head_elems = dv * dk;
-  for (int64_t b = 0; b < batch; ++b) {
-    const int32_t slot = idx[b];
-    for (int64_t h = 0; h < hv; ++h) {
-      if (head_mask && !head_mask[h]) continue;
-      double* o = out + (b * hv + h) * dv;
-      if (slot < 0) {
-        for (int64_t i = 0; i < dv; ++i) o[i] = 0.0;
-        continue;
-      }
-      const int64_t hkh = h / ratio;
-      load_qkv(q, k, v, in_dt, q_rs, k_rs, v_rs, b, hkh, h, dk, dv, l2norm, l2_eps, scale, qd,
-               kd, vd);
-      double* S = state_out + (b * hv + h) * head_elems;
-      const int64_t s0 = ((int64_t)slot * hv + h) * head_elems;
-      for (int64_t e = 0; e < head_elems; ++e) S[e] = load_elem(pool, state_dt, s0 + e);
-      recurrence_step(S, dv, dk, kd, qd, vd, g[b * hv + h], (double)beta[b * beta_rs + h], o,
-                      work);
-    }
-  }
-  free(qd); free(kd); free(vd); free(work);
-  return OR_OK;
+  const struct decode_ctx c = {hk, hv, dk, dv, hv / hk, q, k, v, in_dt, q_rs, k_rs, v_rs,
+                               g, beta, beta_rs, pool, state_dt, idx, scale, l2_eps, l2norm,
+                               head_mask, out, state_out};
+  return run_units(decode_unit, &c, batch * hv, (size_t)(2 * dk + 2 * dv));
 }
 
 /* ------------------------------------------------------------------------
@@ -275,6 +345,47 @@ int oracle_decode(int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
  * g, beta: [T, hv] (g f64 from oracle_gate; beta f32 with a row stride).
  * out: [T, hv, dv] f64.  head_mask as for oracle_decode.
  * ------------------------------------------------------------------------ */
+struct prefill_ctx {
+  const int32_t* cu;
+  int64_t hk, hv, dk, dv, ratio;
+  const void *q, *k, *v;
+  int in_dt;
+  int64_t q_rs, k_rs, v_rs;
+  const double* g;
+  const float* beta;
+  int64_t beta_rs;
+  const void* pool;
+  int state_dt;
+  const int32_t* idx;
+  const int8_t* has_init;
+  double scale, l2_eps;
+  int l2norm;
+  const uint8_t* head_mask;
+  double *out, *state_out;
+};
+
+/* unit = (sequence s, v-head h): the whole token loop of that head */
+static void prefill_unit(const void* cp, int64_t u, double* scratch) {
+  const struct prefill_ctx* c = (const struct prefill_ctx*)cp;
+  const int64_t s = u / c->hv, h = u % c->hv;
+  if (c->head_mask && !c->head_mask[h]) return;
+  const int64_t dk = c->dk, dv = c->dv, head_elems = dv * dk;
+  double *qd = scratch, *kd = qd + dk, *vd = kd + dk, *work = vd + dv;
+  const int64_t slot = c->idx ? c->idx[s] : s;
+  const int init = c->has_init ? c->has_init[s] != 0 : 1;
+  double* S = c->state_out + (s * c->hv + h) * head_elems;
+  const int64_t s0 = (slot * c->hv + h) * head_elems;
+  for (int64_t e = 0; e < head_elems; ++e)
+    S[e] = init ? load_elem(c->pool, c->state_dt, s0 + e) : 0.0;
+  const int64_t hkh = h / c->ratio;
+  for (int64_t t = c->cu[s]; t < c->cu[s + 1]; ++t) {
+    load_qkv(c->q, c->k, c->v, c->in_dt, c->q_rs, c->k_rs, c->v_rs, t, hkh, h, dk, dv,
+             c->l2norm, c->l2_eps, c->scale, qd, kd, vd);
+    recurrence_step(S, dv, dk, kd, qd, vd, c->g[t * c->hv + h],
+                    (double)c->beta[t * c->beta_rs + h], c->out + (t * c->hv + h) * dv, work);
+  }
+}
+
 int oracle_prefill_varlen(int64_t num_seqs, const int32_t* cu, int64_t hk, int64_t hv,
                           int64_t dk, int64_t dv, const void* q, const void* k, const void* v,
                           int in_dt, int64_t q_rs, int64_t k_rs, int64_t v_rs,
@@ -295,33 +406,10 @@ int oracle_prefill_varlen(int64_t num_seqs, const int32_t* cu, int64_t hk, int64
   } else if (num_seqs > num_slots) {
     return OR_ERR_SLOT;
   }
-  const int64_t ratio = hv / hk;
-  double* qd = (double*)malloc((size_t)dk * sizeof(double));
-  double* kd = (double*)malloc((size_t)dk * sizeof(double));
-  double* vd = (double*)malloc((size_t)dv * sizeof(double));
-  double* work = (double*)malloc((size_t)dv * sizeof(double));
-  if (!qd || !kd || !vd || !work) { free(qd); free(kd); free(vd); free(work); return OR_ERR_ARG; }
-  const int64_t head_elems = dv * dk;
-  for (int64_t s = 0; s < num_seqs; ++s) {
-    const int64_t slot = idx ? idx[s] : s;
-    const int init = has_init ? has_init[s] != 0 : 1;
-    for (int64_t h = 0; h < hv; ++h) {
-      if (head_mask && !head_mask[h]) continue;
-      double* S = state_out + (s * hv + h) * head_elems;
-      const int64_t s0 = (slot * hv + h) * head_elems;
-      for (int64_t e = 0; e < head_elems; ++e)
-        S[e] = init ? load_elem(pool, state_dt, s0 + e) : 0.0;
-      const int64_t hkh = h / ratio;
-      for (int64_t t = cu[s]; t < cu[s + 1]; ++t) {
-        load_qkv(q, k, v, in_dt, q_rs, k_rs, v_rs, t, hkh, h, dk, dv, l2norm, l2_eps, scale,
-                 qd, kd, vd);
-        recurrence_step(S, dv, dk, kd, qd, vd, g[t * hv + h], (double)beta[t * beta_rs + h],
-                        out + (t * hv + h) * dv, work);
-      }
-    }
-  }
-  free(qd); free(kd); free(vd); free(work);
-  return OR_OK;
+  const struct prefill_ctx c = {cu, hk, hv, dk, dv, hv / hk, q, k, v, in_dt, q_rs, k_rs, v_rs,
+                                g, beta, beta_rs, pool, state_dt, idx, has_init, scale, l2_eps,
+                                l2norm, head_mask, out, state_out};
+  return run_units(prefill_unit, &c, num_seqs * hv, (size_t)(2 * dk + 2 * dv));
 }
 
 /* ------------------------------------------------------------------------

@@ -490,3 +490,25 @@ def test_tiny_prefill_equals_sixty_four_decode_steps():
         np.testing.assert_allclose(o[0], out[t], rtol=1e-5, atol=1e-8)  # f32 state between steps
         S = s.astype(np.float32)
     np.testing.assert_allclose(S[0], st[0], rtol=1e-5, atol=1e-8)
+
+
+def test_threads_do_not_change_results():
+    """The oracle's decode and prefill run independent (row or sequence,
+    v-head) units on several host threads; every unit's arithmetic is the same
+    whatever the thread count, so the results are bit-identical."""
+    pre = W.make_prefill_case("thr", 77, lengths=[9, 0, 33, 2], hk=2, hv=6, dk=16, dv=8,
+                              in_dtype=W.BF16, out_dtype=W.BF16, slots=6, has_init=[1, 1, 0, 1])
+    dec = W.make_decode_case("thr", 78, batch=5, hk=1, hv=3, dk=16, dv=16, in_dtype=W.F16,
+                             out_dtype=W.F16, slots=7, null_rows=(1,))
+    n0 = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        p1 = oracle.prefill_case(pre)
+        d1 = oracle.decode_case(dec)
+        oracle.set_threads(5)
+        p5 = oracle.prefill_case(pre)
+        d5 = oracle.decode_case(dec)
+    finally:
+        oracle.set_threads(n0)
+    for a, b in zip(p1 + d1, p5 + d5):
+        assert np.array_equal(a, b)
