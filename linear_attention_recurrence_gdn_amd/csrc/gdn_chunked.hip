@@ -298,7 +298,11 @@ __device__ __forceinline__ double wave_prefix64(double x) {
 //         fw_i = e^{G_last - G_i} n_k,i,  and F[3][0] = e^{G_last}
 // The walk multiplies T_b and P only in 32-token block pairs on or below the
 // diagonal, so their upper-right 32 x 32 quadrants (rows 0-31, columns 32-63)
-// are never read and never written.
+// are free.  A 16-bit output needs only P's high part; for an f32 output the
+// low part of P (P - high, rounded to 16 bits) is kept there: its quadrant
+// (0, 0) in T_b-high's free quadrant, (1, 0) in T_b-low's and (1, 1) in P's,
+// element (i, j) at row i % 32, column 32 + j % 32.  For 16-bit outputs the
+// free quadrants are never written or read.
 // ---------------------------------------------------------------------------
 constexpr int REC_TH = 0;
 constexpr int REC_TL = CK * CK * 2;
@@ -360,6 +364,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool plo = a.out_dt == kF32;
   uint16_t* Qs = sh.u.qk.Q;
   uint16_t* Ks = sh.u.qk.K;
 
@@ -488,6 +493,13 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     const int h = hk * ratio + jh;
     char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
     uint16_t* Pg = reinterpret_cast<uint16_t*>(rec + REC_P);
+    // an f32 output also keeps P's low part, in the free quadrants (quadrant
+    // (qi, qj) in the free quadrant of record part qi + qj)
+    auto plo_dst = [&](int i, int j) {
+      const int part = (i >> 5) + (j >> 5);
+      return reinterpret_cast<uint16_t*>(rec + (part == 0 ? REC_TH : part == 1 ? REC_TL : REC_P)) +
+             (i & 31) * CK + 32 + (j & 31);
+    };
 
     // A (strictly lower, scaled) into LDS and P (lower incl. diagonal,
     // scaled) straight to the record: element (i, j) = acc * row factor(i) *
@@ -518,7 +530,10 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
           const float xa = accA[k][r] * rfa[r] * cj * e;
           const float xp = accP[k][r] * rfp[r] * cj * e;
           At[(4 * g + r) * LDB + cl] = j < i ? xa : 0.0f;
-          Pg[i * CK + j] = M::enc(j <= i ? xp : 0.0f);
+          const float pv = j <= i ? xp : 0.0f;
+          const uint16_t ph = M::enc(pv);
+          Pg[i * CK + j] = ph;
+          if (plo) *plo_dst(i, j) = M::enc(pv - M::dec(ph));
         }
       }
     }
@@ -528,6 +543,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
       const int blk = tid_h >> 5, e = tid_h & 31;
       const int i = 32 * blk + (e >> 1), j8 = 32 * blk + 16 + 8 * (e & 1);
       *reinterpret_cast<uint4*>(Pg + i * CK + j8) = make_uint4(0u, 0u, 0u, 0u);
+      if (plo) *reinterpret_cast<uint4*>(plo_dst(i, j8)) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
@@ -756,7 +772,7 @@ struct StageOffsets {
   int k[NKQ], q[NKQ], tp[NTP], v[NVL];
 };
 
-template <int NW, int NB>
+template <int NW, int NB, bool FULL>
 __device__ __forceinline__ void stage_offsets(StageOffsets<NW, NB>& o, const PrefillArgs& a,
                                               int dv0, int w, int lane) {
   using SO = StageOffsets<NW, NB>;
@@ -770,8 +786,9 @@ __device__ __forceinline__ void stage_offsets(StageOffsets<NW, NB>& o, const Pre
 #pragma unroll
   for (int i = 0; i < SO::NTP; ++i) {
     const int p = 64 * (NW * i + w) + lane, row = p >> 3, chunk = (p & 7) ^ tp_swz(row);
-    // the unread upper-right quadrant is not fetched: its offset lies past the record
-    o.tp[i] = row < 32 && chunk >= 4 ? kDropOffset : 2 * (row * CK + 8 * chunk);
+    // the free upper-right quadrants hold P's low part for an f32 output and
+    // are otherwise not fetched (their offset then lies past the record)
+    o.tp[i] = !FULL && row < 32 && chunk >= 4 ? kDropOffset : 2 * (row * CK + 8 * chunk);
   }
   constexpr int VCH = 2 * NW * NB;  // 16-byte chunks per V row
 #pragma unroll
@@ -907,10 +924,12 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   WalkBuf<NW, NB>* sb = reinterpret_cast<WalkBuf<NW, NB>*>(walk_lds);
   using M = MT<TIN>;
   using x8 = typename M::x8;
-  // A 16-bit output keeps about 8 (bf16) or 11 (fp16) significant bits, so
-  // its two history terms Q S^T and P U take the high part of S and of U only;
-  // an f32 output gets the full high/low products.  The state itself always
-  // gets them.
+  // The state's history term Q S^T always takes the high and low parts of S:
+  // with the high part only, an output row whose terms nearly cancel (a few
+  // in 10^5 at T = 4096) lost up to 2e-2 of its size, ten times a bf16
+  // rounding.  The in-chunk term P U takes the high parts of P and U for a
+  // 16-bit output (a row of it errs by about one 16-bit rounding), the full
+  // high/low products for an f32 output.
   constexpr bool kFullOut = TOUT == kF32;
 
   // XCD-aware mapping.  Workgroups are dealt round-robin to the 8 XCDs, each
@@ -997,7 +1016,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   }
 
   StageOffsets<NW, NB> so;
-  stage_offsets<NW, NB>(so, a, c.dv0, w, lane);
+  stage_offsets<NW, NB, kFullOut>(so, a, c.dv0, w, lane);
   // rows past the end of a sequence arrive as zeros; clearing both buffers
   // first also keeps every row that the first chunk does not load finite
   {
@@ -1133,7 +1152,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
           X[nb][b] = M::mma(kf[jj & 1][b], sh, X[nb][b]);
           QS[nb][b] = M::mma(qf[jj & 1][b], sh, QS[nb][b]);
           X[nb][b] = M::mma(kf[jj & 1][b], sl, X[nb][b]);
-          if constexpr (kFullOut) QS[nb][b] = M::mma(qf[jj & 1][b], sl, QS[nb][b]);
+          QS[nb][b] = M::mma(qf[jj & 1][b], sl, QS[nb][b]);
         }
       }
     }
@@ -1232,7 +1251,13 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           o[nb] = M::mma(pff[b][j], Uh[nb][j], o[nb]);
-          if constexpr (kFullOut) o[nb] = M::mma(pff[b][j], Ul[nb][j], o[nb]);
+          if constexpr (kFullOut) {
+            // P's low part, from the free quadrant of record part b / 2 + j
+            const uint16_t* pq = (b >> 1) == 0 ? sm.Th : j == 0 ? sm.Tl : sm.P;
+            const x8 pl = *reinterpret_cast<const x8*>(pq + tpb[1] + 4 * (b & 1) * CK);
+            o[nb] = M::mma(pff[b][j], Ul[nb][j], o[nb]);
+            o[nb] = M::mma(pl, Uh[nb][j], o[nb]);
+          }
         }
       }
 #pragma unroll
@@ -1345,7 +1370,7 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   // device (the current one), and is not used while the caller's stream is
   // being captured; the early walk may take at most half of the CUs, so the
   // records of the other ranks always have room.
-  bool can_split = a.num_seqs >= 2 && a.num_seqs <= kOrderMax;
+  bool can_split = !a.no_split && a.num_seqs >= 2 && a.num_seqs <= kOrderMax;
   if (can_split) {
     hipDevice_t sdev = -1;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -1377,10 +1402,11 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
     return (ranks * a.hk + kXcds - 1) / kXcds * kXcds * ratio * ntiles;
   };
   if (walk_blocks(a.num_seqs) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  // the dynamic-LDS limit is raised once per device and kernel: one mask per
+  // output type, since the two walk kernels are distinct functions
+  static std::atomic<uint64_t> raised_f32{0}, raised_16{0};
   auto walk = [&](int part, int64_t ranks, hipStream_t st) -> hipError_t {
-    auto go = [&](auto kern) -> hipError_t {
-      // the dynamic-LDS limit is raised once per device and kernel
-      static std::atomic<uint64_t> raised{0};
+    auto go = [&](auto kern, std::atomic<uint64_t>& raised) -> hipError_t {
       const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
       if (!bit || !(raised.load(std::memory_order_acquire) & bit)) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1393,8 +1419,9 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
                          a, m, (const char*)recs, ntiles, (int)mc, part);
       return hipSuccess;
     };
-    return a.out_dt == kF32 ? go(chunk_state_kernel<TIN, kF32, WALK_NW, WALK_NB, WALK_MINB>)
-                            : go(chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB>);
+    return a.out_dt == kF32
+               ? go(chunk_state_kernel<TIN, kF32, WALK_NW, WALK_NB, WALK_MINB>, raised_f32)
+               : go(chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB>, raised_16);
   };
 
   hipError_t e;

@@ -135,6 +135,7 @@ struct PrefillArgs {
   int hk, hv, dk, dv;
   float scale, l2_eps;
   int l2norm;
+  int no_split;   // keep the whole chunked call on `stream` (no second stream)
 };
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);

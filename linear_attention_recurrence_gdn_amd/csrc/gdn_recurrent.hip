@@ -352,13 +352,29 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(PrefillArgs a, int64_t
   }
   const bool init = a.has_init ? a.has_init[sq] != 0 : true;
   const int hk = h / (a.hv / a.hk);
+  const int64_t S = ((slot * a.hv + h) * a.dv) * DK + col;  // element offset in the pool
 
+  if (t1 <= t0) {
+    // a zero-length sequence reads no token row (with total_tokens == 0 the
+    // token pointers may be null): its state passes through, or is zeroed
+    // without an initial state
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int row = r0 + i * T::RPI + sub;
+      if (row < a.dv)
+        state_store4_rt(a.state_dt, a.pool, S + (int64_t)row * DK,
+                        init ? state_load4_rt(a.state_dt, a.pool, S + (int64_t)row * DK)
+                             : make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+    return;
+  }
+
+  // token rows t0 .. t1 - 1 exist from here on
   TokenRaw<TIN> cur[PF], nxt[PF];
 #pragma unroll
   for (int u = 0; u < PF; ++u)
-    cur[u] = load_token<DK, TIN>(a, min(t0 + u, t1 - 1 < t0 ? t0 : t1 - 1), hk, h, col, vrow);
+    cur[u] = load_token<DK, TIN>(a, min(t0 + u, t1 - 1), hk, h, col, vrow);
 
-  const int64_t S = ((slot * a.hv + h) * a.dv) * DK + col;  // element offset in the pool
   float4 s[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
