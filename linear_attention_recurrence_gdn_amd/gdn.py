@@ -145,6 +145,17 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _new(shape, dtype, device, stream) -> torch.Tensor:
+    """A tensor the binding allocates for a call.  When the call runs on a
+    stream other than the current one, the caching allocator is told that the
+    memory is in use on that stream, so it is not handed to other work before
+    the call's kernels are done with it."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+    return t
+
+
 def gate(alpha: torch.Tensor, dt_bias: torch.Tensor, ssm_a: torch.Tensor,
          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """g[r, h] = softplus(alpha[r, h] + dt_bias[h]) * ssm_a[h]  ->  [rows, hv] f32."""
@@ -152,7 +163,7 @@ def gate(alpha: torch.Tensor, dt_bias: torch.Tensor, ssm_a: torch.Tensor,
     rows, hv = alpha.shape[0], dt_bias.shape[0]
     a_rs = _rows2(alpha, "alpha", hv)
     if out is None:
-        out = torch.empty((rows, hv), dtype=torch.float32, device=alpha.device)
+        out = _new((rows, hv), torch.float32, alpha.device, stream)
     g_rs = _rows2(out, "g", hv)
     _check(lib.gdn_gate(_dev(out, "g", torch.float32), g_rs, _dev(alpha, "alpha"), _dt(alpha),
                         a_rs, _dev(dt_bias, "dt_bias", torch.float32),
@@ -214,7 +225,7 @@ def _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scal
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise GdnError(-2, "q, k, v must share a dtype")
     if out is None:
-        out = torch.empty((B, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
+        out = _new((B, hv, dv), out_dtype or q.dtype, q.device, stream)
     if not out.is_contiguous() or tuple(out.shape) != (B, hv, dv):
         raise GdnError(-3, "out: need contiguous [B, Hv, Dv]")
     flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_CHECK_SLOTS if check_slots else 0) |
@@ -267,7 +278,7 @@ def conv1d_fwd(x, weight, bias, conv_state, cu_seqlens, *, state_idx=None,
     T, C, x_rs, K, sl, slots, sflags = _conv_common(x, weight, conv_state, "conv1d_fwd")
     N = cu_seqlens.shape[0] - 1
     if out is None:
-        out = torch.empty((T, C), dtype=out_dtype or x.dtype, device=x.device)
+        out = _new((T, C), out_dtype or x.dtype, x.device, stream)
     if not out.is_contiguous() or tuple(out.shape) != (T, C):
         raise GdnError(-3, "out: need contiguous [T, C]")
     flags = (GDN_CONV_SILU if silu else 0) | (GDN_CHECK_SLOTS if check_slots else 0) | sflags
@@ -288,7 +299,7 @@ def conv1d_update(x, weight, bias, conv_state, *, state_idx=None, silu: bool = T
     lib = load_library()
     B, C, x_rs, K, sl, slots, sflags = _conv_common(x, weight, conv_state, "conv1d_update")
     if out is None:
-        out = torch.empty((B, C), dtype=out_dtype or x.dtype, device=x.device)
+        out = _new((B, C), out_dtype or x.dtype, x.device, stream)
     if not out.is_contiguous() or tuple(out.shape) != (B, C):
         raise GdnError(-3, "out: need contiguous [B, C]")
     flags = (GDN_CONV_SILU if silu else 0) | (GDN_CHECK_SLOTS if check_slots else 0) | sflags
@@ -312,9 +323,9 @@ def gate_beta(a, b, dt_bias, ssm_a, *, rounded: bool = False, g=None, beta=None,
     if b.shape[0] != rows:
         raise GdnError(-3, f"b: {b.shape[0]} rows, a has {rows}")
     if g is None:
-        g = torch.empty((rows, hv), dtype=torch.float32, device=a.device)
+        g = _new((rows, hv), torch.float32, a.device, stream)
     if beta is None:
-        beta = torch.empty((rows, hv), dtype=torch.float32, device=a.device)
+        beta = _new((rows, hv), torch.float32, a.device, stream)
     for name, t in (("g", g), ("beta", beta)):
         if not t.is_contiguous() or tuple(t.shape) != (rows, hv):
             raise GdnError(-3, f"{name}: need contiguous [{rows}, {hv}]")
@@ -339,11 +350,11 @@ def post_conv(conv, a, b, dt_bias, ssm_a, *, hk: int, dk: int, dv: int, l2_eps: 
     a_rs = _rows2(a, "a", hv)
     b_rs = _rows2(b, "b", hv)
     od = out_dtype or conv.dtype
-    q = torch.empty((T, hk, dk), dtype=od, device=conv.device)
-    k = torch.empty((T, hk, dk), dtype=od, device=conv.device)
-    v = torch.empty((T, hv, dv), dtype=od, device=conv.device)
-    g = torch.empty((T, hv), dtype=torch.float32, device=conv.device)
-    beta = torch.empty((T, hv), dtype=torch.float32, device=conv.device)
+    q = _new((T, hk, dk), od, conv.device, stream)
+    k = _new((T, hk, dk), od, conv.device, stream)
+    v = _new((T, hv, dv), od, conv.device, stream)
+    g = _new((T, hv), torch.float32, conv.device, stream)
+    beta = _new((T, hv), torch.float32, conv.device, stream)
     _check(lib.gdn_post_conv(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q), _dev(g, "g"),
                              _dev(beta, "beta"), _dev(conv, "conv"), _dt(conv), conv_rs,
                              _dev(a, "a"), _dev(b, "b", a.dtype), _dt(a), a_rs, b_rs,
@@ -370,7 +381,7 @@ def rmsnorm_gated(x, z, w, *, eps: float = 1e-6, sigmoid: bool = False,
     if w.dim() != 1 or w.shape[0] != dv or not w.is_contiguous():
         raise GdnError(-3, f"w: need contiguous [{dv}]")
     if out is None:
-        out = torch.empty((T, hv, dv), dtype=out_dtype or x.dtype, device=x.device)
+        out = _new((T, hv, dv), out_dtype or x.dtype, x.device, stream)
     if not out.is_contiguous() or tuple(out.shape) != (T, hv, dv):
         raise GdnError(-3, "out: need contiguous [T, Hv, Dv]")
     _check(lib.gdn_rmsnorm_gated(_dev(out, "out"), _dt(out), _dev(x, "x"), _dt(x),
@@ -388,19 +399,9 @@ def prefill_workspace_size(total_tokens, num_seqs, hk, hv, dk, dv, in_dtype,
                                                  _TORCH_DT[in_dtype], flags)
 
 
-def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
-                   state_idx: Optional[torch.Tensor] = None,
-                   has_initial_state: Optional[torch.Tensor] = None, l2norm: bool = True,
-                   l2_eps: float = 1e-6, out: Optional[torch.Tensor] = None, out_dtype=None,
-                   sequential: bool = False, workspace: Optional[torch.Tensor] = None,
-                   check_slots: bool = False, stream=None) -> torch.Tensor:
-    """Varlen prefill over sequences packed back to back (cu_seqlens [N+1] int32).
-
-    q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; g, beta: [T, Hv] f32; state_pool
-    [slots, Hv, Dv, Dk] f32, float16 or bfloat16 (initial states read, final
-    states written).  check_slots: validate cu_seqlens and state_idx first
-    (GDN_CHECK_SLOTS: reads them back and waits on the stream)."""
-    lib = load_library()
+def _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale, state_idx,
+                  has_initial_state, l2norm, l2_eps, out, out_dtype, sequential, check_slots,
+                  stream):
     if state_pool.dim() != 4 or not state_pool.is_contiguous():
         raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
     slots, hv, dv, dk = state_pool.shape
@@ -415,22 +416,41 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise GdnError(-2, "q, k, v must share a dtype")
     if out is None:
-        out = torch.empty((T, hv, dv), dtype=out_dtype or q.dtype, device=q.device)
+        out = _new((T, hv, dv), out_dtype or q.dtype, q.device, stream)
     if not out.is_contiguous() or tuple(out.shape) != (T, hv, dv):
         raise GdnError(-3, "out: need contiguous [T, Hv, Dv]")
     flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_PREFILL_SEQUENTIAL if sequential else 0) |
              (GDN_CHECK_SLOTS if check_slots else 0) | _state_flags(state_pool))
-    ws_need = lib.gdn_prefill_varlen_workspace_size(T, N, hk, hv, dk, dv, _dt(q), flags)
+    args = [_dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
+            q_rs, k_rs, v_rs, _dev(g, "g", torch.float32), g_rs,
+            _dev(beta, "beta", torch.float32), b_rs, _dev(state_pool, "state_pool"), slots,
+            _dev(state_idx, "state_idx", torch.int32),
+            _dev(has_initial_state, "has_initial_state", torch.int8),
+            _dev(cu_seqlens, "cu_seqlens", torch.int32), N, T, hk, hv, dk, dv, float(scale),
+            float(l2_eps), flags]
+    return out, args, (T, N, hk, hv, dk, dv, _dt(q), flags)
+
+
+def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
+                   state_idx: Optional[torch.Tensor] = None,
+                   has_initial_state: Optional[torch.Tensor] = None, l2norm: bool = True,
+                   l2_eps: float = 1e-6, out: Optional[torch.Tensor] = None, out_dtype=None,
+                   sequential: bool = False, workspace: Optional[torch.Tensor] = None,
+                   check_slots: bool = False, stream=None) -> torch.Tensor:
+    """Varlen prefill over sequences packed back to back (cu_seqlens [N+1] int32).
+
+    q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; g, beta: [T, Hv] f32; state_pool
+    [slots, Hv, Dv, Dk] f32, float16 or bfloat16 (initial states read, final
+    states written).  check_slots: validate cu_seqlens and state_idx first
+    (GDN_CHECK_SLOTS: reads them back and waits on the stream)."""
+    lib = load_library()
+    out, args, ws_key = _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale,
+                                      state_idx, has_initial_state, l2norm, l2_eps, out,
+                                      out_dtype, sequential, check_slots, stream)
+    ws_need = lib.gdn_prefill_varlen_workspace_size(*ws_key)
     if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=q.device)
+        workspace = _new((ws_need,), torch.uint8, q.device, stream)
     ws_ptr = _dev(workspace, "workspace") if ws_need else None
     ws_bytes = workspace.numel() * workspace.element_size() if ws_need else 0
-    _check(lib.gdn_prefill_varlen(
-        _dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
-        q_rs, k_rs, v_rs, _dev(g, "g", torch.float32), g_rs, _dev(beta, "beta", torch.float32),
-        b_rs, _dev(state_pool, "state_pool"), slots,
-        _dev(state_idx, "state_idx", torch.int32),
-        _dev(has_initial_state, "has_initial_state", torch.int8),
-        _dev(cu_seqlens, "cu_seqlens", torch.int32), N, T, hk, hv, dk, dv, float(scale),
-        float(l2_eps), flags, ws_ptr, ws_bytes, _stream(stream)))
+    _check(lib.gdn_prefill_varlen(*args, ws_ptr, ws_bytes, _stream(stream)))
     return out

@@ -31,7 +31,7 @@ def announce(msg):
 
 
 def tol(xd, od):
-    return H.OUT_TOL_F32 if (xd == W.F32 and od == W.F32) else H.OUT_TOL_HALF
+    return H.tier_tol(xd, od)
 
 
 def stored(vals, sdt):

@@ -37,7 +37,7 @@ def z_view(norm, rows, hv, dv, dev):
 
 
 def tol(in_dt, out_dt):
-    return H.OUT_TOL_F32 if (in_dt == W.F32 and out_dt == W.F32) else H.OUT_TOL_HALF
+    return H.tier_tol(in_dt, out_dt)
 
 
 NORM_CASES = [

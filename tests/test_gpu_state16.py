@@ -117,15 +117,11 @@ def test_prefill_state16(dev, spec, state_dt, sequential):
 
 
 @pytest.mark.parametrize("state_dt", STATE_DTS, ids=SDT_ID)
-def test_prefill_varlen_gqa3_state16_sampled_heads(dev, state_dt):
-    announce(f"prefill varlen 8 seqs T=32768 Hk8 Hv24 fp16, {W.DTYPE_NAMES[state_dt]} state")
+def test_prefill_varlen_gqa3_state16_all_heads(dev, state_dt):
+    announce(f"prefill varlen 8 seqs T=32768 Hk8 Hv24 fp16, {W.DTYPE_NAMES[state_dt]} state, "
+             f"every head")
     case = W.prefill_varlen_gqa3()
     bits, pool = stored_pool(case, state_dt, dev)
     res = H.run_prefill(case, dev, pool=pool)
-    heads = [5, 23]
-    mask = np.zeros(case.hv, np.uint8)
-    mask[heads] = 1
-    want_out, want_state = oracle.prefill_case(case, head_mask=mask, pool=bits,
-                                               state_dt=state_dt)
-    r_out, r_st = H.check_prefill(case, res, want_out, want_state, heads=heads)
-    print(f"  out rel-L1 {r_out:.3e}  state rel-L1 {r_st:.3e}", flush=True)
+    want_out, want_state = oracle.prefill_case(case, pool=bits, state_dt=state_dt)
+    H.check_prefill(case, res, want_out, want_state, verbose=True)
