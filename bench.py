@@ -10,11 +10,14 @@ value = algorithmic bytes per step / time per step, in GB/s.
 
 Second leg (same JSON line, "prefill"): gdn_gate + gdn_prefill_varlen over 8
 sequences with lengths U(1,8192) summing to 32768 tokens (Hk=8, Hv=24, D=128,
-fp16, initial states from a 64-slot pool), reported in tokens/s.
+fp16, initial states from a 64-slot pool), reported in tokens/s; and
+("prefill_t4096") the same over one sequence of 4096 tokens (Hk=16, Hv=32,
+bf16, zero initial state).
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
-starts.  The CPU oracle is timed on a bounded sample on the host as a
-baseline (not a target).
+starts.  The CPU oracle is timed on the host's cores (a thread per
+independent (sequence, v-head) unit, whole workloads) as a baseline, not a
+target.
 """
 from __future__ import annotations
 
@@ -87,15 +90,17 @@ def measured_traffic():
         return None
 
 
-def prefill_bytes(T, N, hk, hv, dk, dv, in_bytes, out_bytes):
+def prefill_bytes(T, N, hk, hv, dk, dv, in_bytes, out_bytes, n_init=None):
     """Algorithmic HBM bytes of gate + varlen prefill: q/k/v read once, out
     written once, alpha read and g written by the gate, g and beta read by the
-    recurrence, each sequence's state read and written once."""
+    recurrence, the initial state of each of the n_init sequences that have
+    one read once and every final state written once."""
+    n_init = N if n_init is None else n_init
     qkv = T * (2 * hk * dk + hv * dv) * in_bytes
     out = T * hv * dv * out_bytes
     gate = T * hv * 4 * 2          # alpha read, g written
     gb = T * hv * 4 * 2            # g and beta read
-    state = 2 * N * hv * dv * dk * 4
+    state = (n_init + N) * hv * dv * dk * 4
     return qkv + out + gate + gb + state
 
 
@@ -103,6 +108,17 @@ def prefill_flops(T, hv, dk, dv, C=64):
     """Flops of the chunked form per (token, v-head) at chunk size C:
     2 [C (3 Dk + 2 Dv) + 3 Dk Dv + C^2 / 6]."""
     return 2.0 * T * hv * (C * (3 * dk + 2 * dv) + 3 * dk * dv + C * C / 6.0)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -115,6 +131,8 @@ def main():
                     help="wall-clock budget of each CPU-oracle baseline leg")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-t4096", action="store_true",
+                    help="skip the single-sequence T=4096 prefill leg")
     ap.add_argument("--no-state16", action="store_true",
                     help="skip the decode leg with a bf16 state pool")
     ap.add_argument("--no-norm", action="store_true",
@@ -125,7 +143,15 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale factor for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--only", default="",
+                    help="comma list of legs to time (profiling runs): decode, decode_bf16, "
+                         "decode_norm, decode_b1024, conv_update, prefill, t4096, conv_fwd, "
+                         "rmsnorm, cpu; default all")
     args = ap.parse_args()
+    only = {x for x in args.only.split(",") if x}
+
+    def want(leg):
+        return not only or leg in only
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.exit("bench.py: one GPU only (the decode and prefill kernels "
                  "shard by sequence with no exchange); run with --gpus 1")
@@ -166,27 +192,37 @@ def main():
     log(f"decode setup {time.time() - t_setup:.1f}s")
 
     def timed(step, warmup, steps):
-        """Wall seconds over `steps` launches after `warmup`, and each launch's
-        duration (ms) from HIP events recorded on the launch stream."""
+        """Wall seconds over `steps` launches after `warmup` (the timed region:
+        nothing but the launches between two synchronisations), then each
+        launch's duration (ms) from HIP events recorded on the launch stream
+        around `steps` further launches.  The events are kept out of the wall
+        region because their markers add a gap between launches."""
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
-            ev[i][0].record(stream)
             step(warmup + i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            step(warmup + steps + i)
             ev[i][1].record(stream)
         torch.cuda.synchronize()
-        return time.perf_counter() - t0, np.array([a.elapsed_time(b) for a, b in ev])
+        return wall, np.array([a.elapsed_time(b) for a, b in ev])
 
     def decode_step(i):
         gdn.decode(qb, kb, vb, alpha, dt_bias, ssm_a, beta, pool, subsets[i % 4],
                    scale=case.scale, out=out, stream=stream)
 
-    wall, kernel_ms = timed(decode_step, args.warmup, args.steps)
     step_bytes = decode_bytes(B, hk, hv, dk, dv, 2, 2)
+    if want("decode"):
+        wall, kernel_ms = timed(decode_step, args.warmup, args.steps)
+    else:   # a profiling run of other legs only: the headline is not measured
+        wall, kernel_ms = float("nan"), np.array([float("nan")])
     ms_per_step = wall * 1e3 / args.steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     kavg = float(kernel_ms.mean())
@@ -227,7 +263,7 @@ def main():
     }
 
     # ---------------- decode with the pool stored as bf16 ----------------
-    if not args.no_state16:
+    if want("decode_bf16") and not args.no_state16:
         pool16 = to_dev(W.encode(case.pool, W.BF16).view(np.int16)).view(torch.bfloat16)
 
         def decode16_step(i):
@@ -254,7 +290,7 @@ def main():
             f"{bytes16 / (kavg16 * 1e-3) / 1e9:.0f} GB/s")
 
     # ---------------- decode with the gated RMSNorm fused ----------------
-    if not args.no_norm:
+    if want("decode_norm") and not args.no_norm:
         nrm = W.norm_inputs(202, B, hv, dv, W.BF16)
         zb = to_dev(nrm.z.buf.view(np.int16)).view(torch.bfloat16).view(B, hv, dv)
         wb = to_dev(nrm.w.view(np.int16)).view(torch.bfloat16)
@@ -280,7 +316,7 @@ def main():
         log(f"decode + gated norm: kernel avg {kavg_n * 1e3:.1f} us")
 
     # ---------------- large decode from row-strided packed input ----------------
-    if not args.no_large:
+    if want("decode_b1024") and not args.no_large:
         big = W.decode_packed_b1024(with_pool=False)
         B5, hk5, hv5, dk5, dv5 = big.batch, big.hk, big.hv, big.dk, big.dv
         slots5 = 4096
@@ -324,7 +360,7 @@ def main():
         del pool5, pbuf, q5, k5, v5
 
     # ---------------- conv1d update at the decode batch ----------------
-    if not args.no_conv:
+    if want("conv_update") and not args.no_conv:
         C, K = 2 * hk * dk + hv * dv, 4
         crng = np.random.default_rng([202, 0xC0])
         ux = to_dev(W.encode(crng.normal(size=(B, C)).astype(np.float32), W.BF16).view(np.int16)
@@ -374,54 +410,90 @@ def main():
                                state_idx=pidx, has_initial_state=phi, out=pout,
                                workspace=ws, stream=stream)
 
-        for _ in range(8):
-            prefill_step()
-        torch.cuda.synchronize()
-        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.prefill_steps)]
-        t0 = time.perf_counter()
-        for i in range(args.prefill_steps):
-            pev[i][0].record(stream)
-            prefill_step()
-            pev[i][1].record(stream)
-        torch.cuda.synchronize()
-        pwall = time.perf_counter() - t0
-        pms = np.array([a.elapsed_time(b) for a, b in pev])
-        p_ms_step = pwall * 1e3 / args.prefill_steps
-        pbytes = prefill_bytes(T, N, pre.hk, pre.hv, pre.dk, pre.dv, 2, 2)
-        pflops = prefill_flops(T, pre.hv, pre.dk, pre.dv)
-        pavg = float(pms.mean())
-        result["prefill"] = {
-            "workload": "varlen prefill, 8 sequences, lengths U(1,8192) summing to 32768, "
-                        "Hk=8, Hv=24 (GQA 3), D=128, fp16 q/k/v/out, fp32 states from a "
-                        "64-slot pool; gate + recurrence",
-            "lengths": pre.meta["lengths"],
-            "tokens_per_s": round(T / (p_ms_step * 1e-3), 1),
-            "ms_per_step": round(p_ms_step, 4),
-            "kernel_avg_ms": round(pavg, 4),
-            "achieved_GBs": round(pbytes / (pavg * 1e-3) / 1e9, 1),
-            "hbm_frac": round(pbytes / (pavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "chunked_flops_per_step": pflops,
-            "mfma_frac_algorithmic": round(pflops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "path": "chunked" if ws_n > 0 else "token-sequential",
-        }
-        if ws_n > 0:
-            # the call leaves its per-call metadata at the front of the workspace:
-            # int32 cs[N+1], order[N], ocs[N+1], then the split rank it chose
-            words = ws[:4 * (3 * N + 3)].view(torch.int32).cpu().numpy()
-            k = int(words[3 * N + 2])
-            order = [int(x) for x in words[N + 1:2 * N + 1]]
-            result["prefill"]["schedule"] = {
-                "split_rank": k,
-                "walked_early": [pre.meta["lengths"][s] for s in order[:k]],
-                "note": "the records of the k longest sequences are formed first and their "
-                        "walks start at once; the other sequences' records and walks run "
-                        "beside them on a second stream",
+        if want("prefill"):
+            pwall, pms = timed(lambda i: prefill_step(), 8, args.prefill_steps)
+            p_ms_step = pwall * 1e3 / args.prefill_steps
+            pbytes = prefill_bytes(T, N, pre.hk, pre.hv, pre.dk, pre.dv, 2, 2,
+                                   int(pre.has_init.sum()))
+            pflops = prefill_flops(T, pre.hv, pre.dk, pre.dv)
+            pavg = float(pms.mean())
+            result["prefill"] = {
+                "workload": "varlen prefill, 8 sequences, lengths U(1,8192) summing to 32768, "
+                            "Hk=8, Hv=24 (GQA 3), D=128, fp16 q/k/v/out, fp32 states from a "
+                            "64-slot pool; gate + recurrence",
+                "lengths": pre.meta["lengths"],
+                "tokens_per_s": round(T / (p_ms_step * 1e-3), 1),
+                "ms_per_step": round(p_ms_step, 4),
+                "kernel_avg_ms": round(pavg, 4),
+                "achieved_GBs": round(pbytes / (pavg * 1e-3) / 1e9, 1),
+                "hbm_frac": round(pbytes / (pavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "chunked_flops_per_step": pflops,
+                "mfma_frac_algorithmic": round(pflops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "path": "chunked" if ws_n > 0 else "token-sequential",
             }
-        log(f"prefill: {p_ms_step:.3f} ms/step -> {T / (p_ms_step * 1e-3) / 1e6:.2f} M tokens/s")
+            if ws_n > 0:
+                # the call leaves its per-call metadata at the front of the workspace:
+                # int32 cs[N+1], order[N], ocs[N+1], then the split rank it chose
+                words = ws[:4 * (3 * N + 3)].view(torch.int32).cpu().numpy()
+                k = int(words[3 * N + 2])
+                order = [int(x) for x in words[N + 1:2 * N + 1]]
+                result["prefill"]["schedule"] = {
+                    "split_rank": k,
+                    "walked_early": [pre.meta["lengths"][s] for s in order[:k]],
+                    "note": "the records of the k longest sequences are formed first and their "
+                            "walks start at once; the other sequences' records and walks run "
+                            "beside them on a second stream",
+                }
+            log(f"prefill: {p_ms_step:.3f} ms/step -> {T / (p_ms_step * 1e-3) / 1e6:.2f} M tokens/s")
+
+        # the single long sequence: T=4096, Hk=16, Hv=32, bf16, zero initial state
+        if want("t4096") and not args.no_t4096:
+            p3 = W.prefill_t4096()
+            T3 = p3.total_tokens
+            q3 = to_dev(p3.q.buf.view(np.int16)).view(torch.bfloat16).view(T3, p3.hk, p3.dk)
+            k3 = to_dev(p3.k.buf.view(np.int16)).view(torch.bfloat16).view(T3, p3.hk, p3.dk)
+            v3 = to_dev(p3.v.buf.view(np.int16)).view(torch.bfloat16).view(T3, p3.hv, p3.dv)
+            a3, dt3, sa3, b3 = (to_dev(p3.alpha), to_dev(p3.dt_bias), to_dev(p3.ssm_a),
+                                to_dev(p3.beta))
+            pool3 = to_dev(p3.pool)
+            cu3, idx3, hi3 = to_dev(p3.cu_seqlens), to_dev(p3.idx), to_dev(p3.has_init)
+            out3 = torch.empty((T3, p3.hv, p3.dv), dtype=torch.bfloat16, device=dev)
+            g3 = torch.empty((T3, p3.hv), dtype=torch.float32, device=dev)
+            ws3_n = gdn.prefill_workspace_size(T3, 1, p3.hk, p3.hv, p3.dk, p3.dv,
+                                               torch.bfloat16)
+            ws3 = torch.empty(max(ws3_n, 1), dtype=torch.uint8, device=dev)
+
+            def t4096_step(i):
+                gdn.gate(a3, dt3, sa3, out=g3, stream=stream)
+                gdn.prefill_varlen(q3, k3, v3, g3, b3, pool3, cu3, scale=p3.scale,
+                                   state_idx=idx3, has_initial_state=hi3, out=out3,
+                                   workspace=ws3, stream=stream)
+
+            w3, k3ms = timed(t4096_step, 8, args.prefill_steps)
+            ms3 = w3 * 1e3 / args.prefill_steps
+            avg3 = float(k3ms.mean())
+            bytes3 = prefill_bytes(T3, 1, p3.hk, p3.hv, p3.dk, p3.dv, 2, 2, 0)
+            flops3 = prefill_flops(T3, p3.hv, p3.dk, p3.dv)
+            result["prefill_t4096"] = {
+                "workload": "single-sequence prefill T=4096, Hk=16, Hv=32, D=128, bf16 q/k/v/out, "
+                            "zero initial state (slot never read), fp32 final state; "
+                            "gate + recurrence",
+                "tokens_per_s": round(T3 / (ms3 * 1e-3), 1),
+                "ms_per_step": round(ms3, 4),
+                "kernel_avg_ms": round(avg3, 4),
+                "algorithmic_bytes_per_step": bytes3,
+                "achieved_GBs": round(bytes3 / (avg3 * 1e-3) / 1e9, 1),
+                "hbm_frac": round(bytes3 / (avg3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "chunked_flops_per_step": flops3,
+                "mfma_frac_algorithmic": round(flops3 / (avg3 * 1e-3) / 1e12 /
+                                               MFMA_BF16_PEAK_TFLOPS, 4),
+                "path": "chunked" if ws3_n > 0 else "token-sequential",
+            }
+            log(f"prefill T=4096: {ms3:.3f} ms/step -> {T3 / (ms3 * 1e-3) / 1e6:.2f} M tokens/s")
+            del q3, k3, v3, out3, ws3, pool3
 
         # the causal conv1d before the front-end, over the same tokens
-        if not args.no_conv:
+        if want("conv_fwd") and not args.no_conv:
             C, K = 2 * pre.hk * pre.dk + pre.hv * pre.dv, 4
             crng = np.random.default_rng([404, 0xC0])
             cx = to_dev(W.encode(crng.normal(size=(T, C)).astype(np.float32), W.F16))
@@ -436,7 +508,7 @@ def main():
             cwall, ck = timed(conv_step, 3, args.prefill_steps)
             cbytes = 2 * T * C * 2 + 2 * N * C * (K - 1) * 2 + C * K * 2
             cavg = float(ck.mean())
-            result["prefill"]["conv1d_fwd"] = {
+            result.setdefault("prefill", {})["conv1d_fwd"] = {
                 "workload": f"depthwise causal conv1d (K=4, silu) over the 32768 packed tokens, "
                             f"{C} fp16 channels (q|k|v), fp16 state from the 64-slot cache",
                 "kernel_avg_us": round(cavg * 1e3, 2),
@@ -448,7 +520,7 @@ def main():
             del cx, cout
 
         # the gated RMSNorm over the prefill output (a separate HBM pass)
-        if not args.no_norm:
+        if want("rmsnorm") and not args.no_norm:
             pn = W.norm_inputs(404, T, pre.hv, pre.dv, W.F16)
             pz = to_dev(pn.z.buf).view(T, pre.hv, pre.dv)
             pw = to_dev(pn.w)
@@ -460,7 +532,7 @@ def main():
             nwall, nk = timed(norm_step, 3, args.prefill_steps)
             nbytes = 3 * T * pre.hv * pre.dv * 2 + pre.dv * 2
             navg = float(nk.mean())
-            result["prefill"]["rmsnorm_gated"] = {
+            result.setdefault("prefill", {})["rmsnorm_gated"] = {
                 "workload": "gated RMSNorm (silu) over the [32768, 24, 128] fp16 prefill output "
                             "with an fp16 gate and weight",
                 "kernel_avg_us": round(navg * 1e3, 2),
@@ -471,9 +543,13 @@ def main():
             log(f"prefill gated norm: kernel avg {navg * 1e3:.1f} us")
 
     # ---------------- CPU oracle baseline ----------------
-    if not args.no_cpu:
+    if want("cpu") and not args.no_cpu:
         import oracle
-        ncores = 1
+        nthr = oracle.default_threads()
+        oracle.set_threads(nthr)
+        model, host_cpus = cpu_model(), os.cpu_count()
+        where = (f"{nthr} threads over independent (sequence, v-head) units on {model} "
+                 f"({host_cpus} logical CPUs on the host)")
         t0 = time.perf_counter()
         reps = 0
         while True:
@@ -484,45 +560,34 @@ def main():
         cpu_t = time.perf_counter() - t0
         cpu_gbs = step_bytes * reps / cpu_t / 1e9
         result["cpu_baseline"] = {
-            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": ncores, "kind": "oracle",
-            "sample": f"{reps} full decode step(s) of the B=256 workload (gate + step in f64, "
-                      f"single thread) in {cpu_t:.1f} s",
+            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{reps} whole decode step(s) of the B=256 workload (gate + step in f64) "
+                      f"in {cpu_t:.1f} s; {where}",
+            "cpu_model": model, "host_cpus": host_cpus,
         }
-        log(f"cpu oracle decode: {cpu_gbs:.3f} GB/s over {reps} step(s)")
-        if not args.no_prefill:
-            # the first 2048 tokens of the longest sequence, one v-head
-            s = int(np.argmax(pre.meta["lengths"]))
-            a0, a1 = int(pre.cu_seqlens[s]), int(pre.cu_seqlens[s]) + 2048
-            mask = np.zeros(pre.hv, np.uint8)
-            mask[0] = 1
-            sub = W.PrefillCase(
-                name="cpu-sample", total_tokens=a1 - a0, num_seqs=1, hk=pre.hk, hv=pre.hv,
-                dk=pre.dk, dv=pre.dv, in_dtype=pre.in_dtype, out_dtype=pre.out_dtype,
-                q=W.View(np.ascontiguousarray(pre.q.buf[a0:a1]), 0, pre.q.row_stride, W.F16),
-                k=W.View(np.ascontiguousarray(pre.k.buf[a0:a1]), 0, pre.k.row_stride, W.F16),
-                v=W.View(np.ascontiguousarray(pre.v.buf[a0:a1]), 0, pre.v.row_stride, W.F16),
-                alpha=np.ascontiguousarray(pre.alpha[a0:a1]), dt_bias=pre.dt_bias,
-                ssm_a=pre.ssm_a, beta=np.ascontiguousarray(pre.beta[a0:a1]),
-                cu_seqlens=np.array([0, a1 - a0], np.int32), pool=pre.pool,
-                idx=pre.idx[s:s + 1].copy(), has_init=np.ones(1, np.int8), scale=pre.scale)
-            # one v-head at a time until about half the decode sample's time
+        log(f"cpu oracle decode: {cpu_gbs:.3f} GB/s over {reps} step(s), {nthr} threads")
+        if "prefill" in result:
             t0 = time.perf_counter()
-            heads = 0
-            while heads < pre.hv:
-                mask[:] = 0
-                mask[heads] = 1
-                oracle.prefill_case(sub, head_mask=mask)
-                heads += 1
-                if time.perf_counter() - t0 >= args.cpu_seconds / 2:
-                    break
+            oracle.prefill_case(pre)
             pt = time.perf_counter() - t0
-            # heads x 2048 tokens of one v-head each = heads x 2048 / Hv whole-layer tokens
             result["prefill"]["cpu_baseline"] = {
-                "value": round(heads * (a1 - a0) / pre.hv / pt, 2), "unit": "tokens/s",
-                "cores": 1, "kind": "oracle",
-                "sample": f"{heads} of {pre.hv} v-heads over {a1 - a0} tokens of sequence {s} "
-                          f"({pt:.1f} s, single thread), scaled to all heads",
+                "value": round(pre.total_tokens / pt, 2), "unit": "tokens/s", "cores": nthr,
+                "kind": "oracle",
+                "sample": f"the whole varlen workload ({pre.total_tokens} tokens, all "
+                          f"{pre.hv} v-heads, gate + recurrence in f64) in {pt:.1f} s; {where}",
             }
+            log(f"cpu oracle prefill: {pre.total_tokens / pt:.1f} tokens/s")
+            if "prefill_t4096" in result:
+                p3 = W.prefill_t4096()
+                t0 = time.perf_counter()
+                oracle.prefill_case(p3)
+                pt3 = time.perf_counter() - t0
+                result["prefill_t4096"]["cpu_baseline"] = {
+                    "value": round(p3.total_tokens / pt3, 2), "unit": "tokens/s",
+                    "cores": nthr, "kind": "oracle",
+                    "sample": f"the whole T=4096 workload (all {p3.hv} v-heads) in "
+                              f"{pt3:.1f} s; {where}",
+                }
 
     print(json.dumps(result), flush=True)
 
