@@ -369,6 +369,39 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
                        int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * gdn_prefill_varlen_noalloc -- gdn_prefill_varlen with no workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes
+ * every other argument of gdn_prefill_varlen with the same meaning, layout
+ * and errors, runs the same kernels, and allocates nothing: the chunked path's
+ * per-call records live in a fixed scratch array of
+ * GDN_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends (its address is looked up on the first call on a
+ * device, with that device current).
+ *   Limit: sizes whose gdn_prefill_varlen_workspace_size exceeds
+ *   GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_SHAPE and enqueue nothing (64 MiB
+ *   holds e.g. one 4096-token sequence at hv = 32, dv = 128, or 2600
+ *   (64-token chunk, v-head) records in all).
+ *   Sharing: every call on a device uses that device's one array, and the
+ *   whole call stays on `stream` (no second stream); calls that overlap on
+ *   one device -- on different streams or host threads, or graph replays
+ *   running concurrently -- race on it and give undefined results.  Calls
+ *   ordered on one stream are safe; each call rewrites what it reads.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int gdn_prefill_varlen_noalloc(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                               const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                               int64_t k_row_stride, int64_t v_row_stride, const float* g,
+                               int64_t g_row_stride, const float* beta,
+                               int64_t beta_row_stride, void* state_pool, int64_t num_slots,
+                               const int32_t* state_idx, const int8_t* has_initial_state,
+                               const int32_t* cu_seqlens, int64_t num_seqs,
+                               int64_t total_tokens, int64_t hk, int64_t hv, int64_t dk,
+                               int64_t dv, float scale, float l2_eps, uint32_t flags,
+                               hipStream_t stream);
+
 /* Message for the last error returned on this thread ("" if none). */
 const char* gdn_last_error(void);
 

@@ -7,6 +7,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/gdn.h"
@@ -494,16 +495,21 @@ size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs,
   return gdn::chunked_workspace_bytes(total_tokens, num_seqs, (int)hv, (int)dk, (int)dv);
 }
 
-int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
-                       gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
-                       int64_t v_row_stride, const float* g, int64_t g_row_stride,
-                       const float* beta, int64_t beta_row_stride, void* state_pool,
-                       int64_t num_slots, const int32_t* state_idx,
-                       const int8_t* has_initial_state, const int32_t* cu_seqlens,
-                       int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
-                       int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* op = "gdn_prefill_varlen";
+}  // extern "C"
+
+namespace {
+
+// gdn_prefill_varlen and its allocation-free variant (which passes the
+// library's per-device scratch as the workspace and keeps the call on one
+// stream).
+int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, const void* k,
+                 const void* v, gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+                 int64_t v_row_stride, const float* g, int64_t g_row_stride, const float* beta,
+                 int64_t beta_row_stride, void* state_pool, int64_t num_slots,
+                 const int32_t* state_idx, const int8_t* has_initial_state,
+                 const int32_t* cu_seqlens, int64_t num_seqs, int64_t total_tokens, int64_t hk,
+                 int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream, bool no_split) {
   int rc;
   if (num_seqs < 0 || total_tokens < 0 || num_slots < 0)
     return fail(GDN_ERR_SHAPE, "%s: negative size", op);
@@ -554,6 +560,7 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
   a.total_tokens = total_tokens;
   a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
   a.scale = scale; a.l2_eps = l2_eps; a.l2norm = (flags & GDN_L2NORM_QK) ? 1 : 0;
+  a.no_split = no_split ? 1 : 0;
   if (use_chunked(hk, hv, dk, dv, in_dt, out_dt, flags) && total_tokens > 0 &&
       gdn::chunked_layout_ok(q, k, v, q_row_stride, k_row_stride, v_row_stride)) {
     const size_t need = gdn::chunked_workspace_bytes(total_tokens, num_seqs, (int)hv, (int)dk,
@@ -566,6 +573,85 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
     return hip_status(op, gdn::launch_prefill_chunked(a, workspace, workspace_bytes, stream));
   }
   return hip_status(op, gdn::launch_prefill_sequential(a, stream));
+}
+
+
+// Scratch of gdn_prefill_varlen_noalloc: one copy of this array per device,
+// held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's scratch address (resolved on the first call on that
+// device, with it current), or nullptr with the error message set.
+void* device_scratch(const char* op) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    fail(GDN_ERR_HIP, "%s: no current device (or device index %d too large)", op, dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(GDN_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", op, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
+                       gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+                       int64_t v_row_stride, const float* g, int64_t g_row_stride,
+                       const float* beta, int64_t beta_row_stride, void* state_pool,
+                       int64_t num_slots, const int32_t* state_idx,
+                       const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                       int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                       int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return prefill_impl("gdn_prefill_varlen", out, out_dt, q, k, v, in_dt, q_row_stride,
+                      k_row_stride, v_row_stride, g, g_row_stride, beta, beta_row_stride,
+                      state_pool, num_slots, state_idx, has_initial_state, cu_seqlens, num_seqs,
+                      total_tokens, hk, hv, dk, dv, scale, l2_eps, flags, workspace,
+                      workspace_bytes, stream, false);
+}
+
+int gdn_prefill_varlen_noalloc(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                               const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                               int64_t k_row_stride, int64_t v_row_stride, const float* g,
+                               int64_t g_row_stride, const float* beta,
+                               int64_t beta_row_stride, void* state_pool, int64_t num_slots,
+                               const int32_t* state_idx, const int8_t* has_initial_state,
+                               const int32_t* cu_seqlens, int64_t num_seqs,
+                               int64_t total_tokens, int64_t hk, int64_t hv, int64_t dk,
+                               int64_t dv, float scale, float l2_eps, uint32_t flags,
+                               hipStream_t stream) {
+  const char* op = "gdn_prefill_varlen_noalloc";
+  const size_t need = gdn_prefill_varlen_workspace_size(total_tokens, num_seqs, hk, hv, dk, dv,
+                                                        in_dt, flags);
+  if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+    return fail(GDN_ERR_SHAPE,
+                "%s: these sizes need %zu bytes of scratch, more than the %zu this entry "
+                "point holds per device; use gdn_prefill_varlen with a workspace",
+                op, need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0 && !(ws = device_scratch(op))) return GDN_ERR_HIP;
+  return prefill_impl(op, out, out_dt, q, k, v, in_dt, q_row_stride, k_row_stride,
+                      v_row_stride, g, g_row_stride, beta, beta_row_stride, state_pool,
+                      num_slots, state_idx, has_initial_state, cu_seqlens, num_seqs,
+                      total_tokens, hk, hv, dk, dv, scale, l2_eps, flags, ws,
+                      ws ? (size_t)GDN_NOALLOC_SCRATCH_BYTES : 0, stream, true);
 }
 
 }  // extern "C"

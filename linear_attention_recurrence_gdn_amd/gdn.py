@@ -33,7 +33,8 @@ _TORCH_DT = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN
 
 EXPORTS = ("gdn_conv1d_fwd", "gdn_conv1d_update", "gdn_gate", "gdn_gate_beta", "gdn_post_conv", "gdn_decode", "gdn_decode_gated_norm",
            "gdn_rmsnorm_gated",
-           "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_last_error")
+           "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_noalloc",
+           "gdn_last_error")
 
 
 class GdnError(RuntimeError):
@@ -86,6 +87,10 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_prefill_varlen.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp,
                                        i64, vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                        f32, f32, u32, vp, sz, vp]
+    lib.gdn_prefill_varlen_noalloc.restype = i32
+    lib.gdn_prefill_varlen_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp,
+                                               i64, vp, i64, vp, i64, vp, vp, vp, i64, i64,
+                                               i64, i64, i64, i64, f32, f32, u32, vp]
     _lib = lib
     return lib
 
@@ -453,4 +458,25 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
     ws_ptr = _dev(workspace, "workspace") if ws_need else None
     ws_bytes = workspace.numel() * workspace.element_size() if ws_need else 0
     _check(lib.gdn_prefill_varlen(*args, ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
+
+
+def prefill_varlen_noalloc(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
+                           state_idx: Optional[torch.Tensor] = None,
+                           has_initial_state: Optional[torch.Tensor] = None,
+                           l2norm: bool = True, l2_eps: float = 1e-6,
+                           out: Optional[torch.Tensor] = None, out_dtype=None,
+                           sequential: bool = False, check_slots: bool = False,
+                           stream=None) -> torch.Tensor:
+    """prefill_varlen through gdn_prefill_varlen_noalloc: no workspace; the
+    library's fixed per-device scratch holds the per-call records (calls that
+    overlap on one device race on it).  Pass `out` to allocate nothing here."""
+    lib = load_library()
+    out, args, _ = _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale, state_idx,
+                                 has_initial_state, l2norm, l2_eps, out, out_dtype, sequential,
+                                 check_slots, stream)
+    _check(lib.gdn_prefill_varlen_noalloc(*args, _stream(stream)))
     return out

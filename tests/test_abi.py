@@ -227,3 +227,22 @@ def test_conv1d_argument_errors():
     assert cu(batch=2048, k=1) == -1 and "null pointer" in _err(lib)   # width 1: no state
     assert cu() == -1 and _err(lib).startswith("gdn_conv1d_update:")
     assert cu(batch=0) == 0
+
+
+def test_prefill_noalloc_refuses_sizes_beyond_its_scratch():
+    """The allocation-free prefill checks its fixed scratch against the call's
+    sizes before anything else (host only: nothing is enqueued)."""
+    lib = pkg.load_library()
+    T, hk, hv, dk, dv = 16384, 2, 16, 128, 128
+    assert lib.gdn_prefill_varlen_workspace_size(T, 1, hk, hv, dk, dv, 2, 1) > B.NOALLOC_SCRATCH_BYTES
+    rc = lib.gdn_prefill_varlen_noalloc(None, 2, None, None, None, 2, hk * dk, hk * dk, hv * dv,
+                                        None, hv, None, hv, None, 1, None, None, None, 1, T, hk,
+                                        hv, dk, dv, 0.088, 1e-6, 1, None)
+    assert rc == -3 and "scratch" in _err(lib)
+    assert _err(lib).startswith("gdn_prefill_varlen_noalloc:")
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GDN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
