@@ -110,6 +110,28 @@ def prefill_flops(T, hv, dk, dv, C=64):
     return 2.0 * T * hv * (C * (3 * dk + 2 * dv) + 3 * dk * dv + C * C / 6.0)
 
 
+def schedule_of(ws, N, lengths):
+    """The schedule a chunked prefill call chose, from the per-call metadata it
+    leaves at the front of its workspace: int32 cs[N+1], order[N], ocs[N+1],
+    then the split rank k, the number of split sequences ks, their segment
+    count S and segment lengths (chunks)."""
+    import torch
+    words = ws[:4 * (3 * N + 7)].view(torch.int32).cpu().numpy()
+    k, ks, S = (int(x) for x in words[3 * N + 2:3 * N + 5])
+    order = [int(x) for x in words[N + 1:2 * N + 1]]
+    return {
+        "split_rank": k,
+        "walked_early": [lengths[s] for s in order[:k]],
+        "split_sequences": [lengths[s] for s in order[:ks]],
+        "segments": S if ks else 1,
+        "note": "the records of the k longest sequences are formed first and their walks "
+                "start at once, the other sequences' records and walks beside them on a second "
+                "stream; each split sequence is walked in S segments: first its segment-0 "
+                "state and each middle segment's local state and transition, then every "
+                "segment with outputs from its exact entry state",
+    }
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -432,18 +454,7 @@ def main():
                 "path": "chunked" if ws_n > 0 else "token-sequential",
             }
             if ws_n > 0:
-                # the call leaves its per-call metadata at the front of the workspace:
-                # int32 cs[N+1], order[N], ocs[N+1], then the split rank it chose
-                words = ws[:4 * (3 * N + 3)].view(torch.int32).cpu().numpy()
-                k = int(words[3 * N + 2])
-                order = [int(x) for x in words[N + 1:2 * N + 1]]
-                result["prefill"]["schedule"] = {
-                    "split_rank": k,
-                    "walked_early": [pre.meta["lengths"][s] for s in order[:k]],
-                    "note": "the records of the k longest sequences are formed first and their "
-                            "walks start at once; the other sequences' records and walks run "
-                            "beside them on a second stream",
-                }
+                result["prefill"]["schedule"] = schedule_of(ws, N, pre.meta["lengths"])
             log(f"prefill: {p_ms_step:.3f} ms/step -> {T / (p_ms_step * 1e-3) / 1e6:.2f} M tokens/s")
 
         # the single long sequence: T=4096, Hk=16, Hv=32, bf16, zero initial state
@@ -488,6 +499,7 @@ def main():
                 "mfma_frac_algorithmic": round(flops3 / (avg3 * 1e-3) / 1e12 /
                                                MFMA_BF16_PEAK_TFLOPS, 4),
                 "path": "chunked" if ws3_n > 0 else "token-sequential",
+                "schedule": schedule_of(ws3, 1, [T3]) if ws3_n > 0 else None,
             }
             log(f"prefill T=4096: {ms3:.3f} ms/step -> {T3 / (ms3 * 1e-3) / 1e6:.2f} M tokens/s")
             del q3, k3, v3, out3, ws3, pool3

@@ -380,16 +380,15 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
  * until the process ends (its address is looked up on the first call on a
  * device, with that device current).
  *   Limit: sizes whose gdn_prefill_varlen_workspace_size exceeds
- *   GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_SHAPE and enqueue nothing (64 MiB
- *   holds e.g. one 4096-token sequence at hv = 32, dv = 128, or 2600
- *   (64-token chunk, v-head) records in all).
+ *   GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_SHAPE and enqueue nothing (128
+ *   MiB holds e.g. one 8192-token sequence at hv = 32, dv = 128).
  *   Sharing: every call on a device uses that device's one array, and the
  *   whole call stays on `stream` (no second stream); calls that overlap on
  *   one device -- on different streams or host threads, or graph replays
  *   running concurrently -- race on it and give undefined results.  Calls
  *   ordered on one stream are safe; each call rewrites what it reads.
  */
-#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 int gdn_prefill_varlen_noalloc(void* out, gdn_dtype out_dt, const void* q, const void* k,
                                const void* v, gdn_dtype in_dt, int64_t q_row_stride,

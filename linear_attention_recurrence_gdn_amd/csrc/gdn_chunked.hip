@@ -125,12 +125,45 @@ __device__ __forceinline__ void chunk_bounds(const PrefillArgs& a, int64_t s, in
 //   ocs[r]   number of chunks of the sequences ranked before r;
 //   info[0]  split rank k: ranks [0, k) (the longest sequences) are walked as
 //            soon as their own records exist, while the records and walks of
-//            the other ranks proceed beside them on the remaining CUs.
+//            the other ranks proceed beside them on the remaining CUs;
+//   info[1]  ks: ranks [0, ks) are split into info[2] = S segments each, of
+//            info[3 + r] chunks (the last one may be shorter);
 // The walk starts the longest sequences first, since the longest one bounds
 // the whole prefill.
+//
+// Segments.  Over a run of tokens the state maps affinely, S_out = S_in M +
+// S_loc, where M = prod_t decay_t (I - beta_t k_t k_t^T) (Dk x Dk) is the walk
+// of the identity with v = 0 and S_loc the walk from zero.  A split sequence is
+// walked in two phases: A) the state alone (no outputs) over segment 0 from
+// the real initial state, giving S_in of segment 1, and for each middle
+// segment j its S_loc and M, all at once; B) every segment j with its outputs,
+// from its exact entry state S_in(1) M_1 ... + (folded in a prologue:
+// S <- S M_i + S_loc,i for i = 1 .. j - 1).  The chain of chunk steps of a
+// sequence of C chunks shrinks from C to about (3/4 + 1) C / S, for about
+// (3/4 (2 S - 3) + S) C / S workgroup steps in all instead of C.
 // ---------------------------------------------------------------------------
 constexpr int kOrderMax = 1024;
-constexpr int kSplitMax = 8;  // most ranks the early walk may take
+constexpr int kSplitMax = 8;   // most ranks the early walk may take
+constexpr int kSegRanks = 2;   // most ranks (the longest) a call splits into segments
+constexpr int kSegMax = 5;     // most segments per split rank
+constexpr int kInfoWords = 3 + kSegRanks;
+
+// How far a call of these sizes may split: S segments need at least 2 S
+// chunks, so at most (chunks + 1) / 2 segments and total_tokens / 256 + 1
+// split ranks.  The workspace holds 2 (S - 1) f32 states per split rank and
+// v-head: the initial state, the entry state of segment 1, and S_loc and M^T
+// of each middle segment.
+struct SegBounds {
+  int ranks, smax;
+  int slots() const { return ranks > 0 ? 2 * (smax - 1) : 0; }
+};
+inline SegBounds seg_bounds(int64_t total_tokens, int64_t num_seqs) {
+  const int64_t chunks = (total_tokens + CK - 1) / CK;
+  const int smax = (int)std::min<int64_t>(kSegMax, (chunks + 1) / 2);
+  const int ranks = (int)std::min<int64_t>({(int64_t)kSegRanks, num_seqs, total_tokens / (4 * CK) + 1});
+  if (smax < 2 || num_seqs > kOrderMax) return {0, 1};
+  return {ranks, smax};
+}
 
 struct MetaPtrs {
   int32_t *cs, *order, *ocs, *info;
@@ -138,7 +171,7 @@ struct MetaPtrs {
 
 __host__ __device__ inline MetaPtrs meta_ptrs(void* ws, int64_t n) {
   int32_t* p = static_cast<int32_t*>(ws);
-  return {p, p + n + 1, p + 2 * n + 1, p + 3 * n + 2};
+  return {p, p + n + 1, p + 2 * n + 1, p + 3 * n + 2};  // info: kInfoWords words
 }
 
 // block-wide inclusive scan of one value per thread (256 threads)
@@ -156,37 +189,83 @@ __device__ __forceinline__ int32_t block_scan256(int32_t v, int32_t* part) {
   return r;
 }
 
-// The split rank from a cost model in units of one chunk step of one walk
-// workgroup (measured: a walk step costs about as much as the prep of one
-// (chunk, v-head) record on one CU):
-//   together:  all records on all CUs, then the walks;
-//   split k:   the records of ranks [0, k) on all CUs, then their walks on
-//              k hv ntiles CUs, beside the other records and walks on the
-//              remaining F CUs.
-// A walk phase takes max(longest sequence, its work / CUs).
-__device__ int split_rank(const int32_t* ocs, int n, int hv, int ntiles, int ncu, int kmax) {
-  const double C = ocs[n], H = hv, NT = ntiles, NC = ncu;
-  const double c0 = ocs[1] - ocs[0];
-  double best = C * H / NC + fmax(c0, C * H * NT / NC);
-  int kbest = 0;
-  for (int k = 1; k <= kmax && k < n; ++k) {
-    const double F = NC - (double)k * H * NT;
-    if (F < NC / 2) break;
-    const double CL = ocs[k], ck = ocs[k + 1] - ocs[k];
-    const double head = CL * H / NC;
-    const double tl = head + c0;
-    const double tr = head + (C - CL) * H / F + fmax(ck, (C - CL) * H * NT / F);
-    const double t = fmax(tl, tr) + 4.0;  // the second stream's launches and joins
-    if (t < best) {
-      best = t;
-      kbest = k;
+// The schedule of a call, from a cost model in units of one chunk step of one
+// walk workgroup (measured on MI355X: a walk step takes about 2.4 us, the
+// prep of one (chunk, v-head) record on one CU about as long, a step that
+// updates the state alone about 0.9 of a full one, and folding one middle
+// segment's transition into a segment's entry state about one step).  W
+// workgroups walk one sequence (or segment, or one middle segment's M);
+// workgroups of a phase beyond the CUs it has wait for a second round.
+// Chooses
+//   k   the split rank (0: everything in one order; the host passes kmax = 0
+//       when it will not use a second stream),
+//   ks  the longest ranks split into S segments each (ks <= k when k > 0, so
+//       a split sequence's two phases stay in one stream order).
+// Ranks are sorted by length, so the longest unsplit rank is rank ks.
+struct Plan {
+  int k, ks, S;
+};
+
+constexpr double kStateStep = 0.9;  // a state-only walk step against a full one
+constexpr double kFoldStep = 1.0;   // folding one transition into an entry state
+
+// Walks of ranks [0, r1) on `cap` CUs, ranks [0, ks) split S ways.
+__device__ double plan_walks(const int32_t* ocs, int r1, int ks, int S, double W, double cap) {
+  double tA = 0.0, tB = 0.0, work = 0.0;
+  if (ks > 0) {
+    double Lmax = 0.0;
+    for (int r = 0; r < ks; ++r) {
+      const double L = ceil((double)(ocs[r + 1] - ocs[r]) / S);
+      Lmax = fmax(Lmax, L);
+      work += W * S * L;
     }
+    tA = kStateStep * Lmax * ceil(W * ks * (2 * S - 3) / cap);
+    tB = Lmax * ceil(W * ks * S / cap) + kFoldStep * (S - 2);
   }
-  return kbest;
+  const double chain = ks < r1 ? (double)(ocs[ks + 1] - ocs[ks]) : 0.0;
+  work += W * (double)(ocs[r1] - ocs[ks]);
+  return tA + fmax(fmax(tB, chain), work / cap);
+}
+
+// The cost of candidate `c` (k, ks, S), or a huge value when it is not allowed.
+// Candidates: c = (k * 3 + ks) * kSegMax + (S - 1) for k in [0, kSplitMax + 1]
+// (k = kSplitMax + 1 stands for k = n: every rank early).
+constexpr int kPlanCands = (kSplitMax + 2) * 3 * kSegMax;
+static_assert(kPlanCands <= 256 && kSegRanks <= 2, "one plan candidate per metadata thread");
+__device__ double plan_cost(int c, const int32_t* ocs, int n, int hv, double W, double NC,
+                            int kmax, int ksmax, int smax, Plan& p) {
+  const double no = 1e300;
+  int k = c / (3 * kSegMax);
+  const int ks = (c / kSegMax) % 3, S = c % kSegMax + 1;
+  if ((ks == 0) != (S == 1) || S > smax || ks > ksmax || ks > n) return no;
+  for (int r = 0; r < ks; ++r)
+    if (ocs[r + 1] - ocs[r] < 2 * S) return no;
+  const double C = ocs[n], H = hv;
+  const double records = C * H / NC;
+  if (k == kSplitMax + 1) {  // every rank early: one stream order, with a second stream at hand
+    if (kmax == 0 || n > kSplitMax || ks == 0) return no;
+    p = {n, ks, S};
+    return records + plan_walks(ocs, n, ks, S, W, NC) + 2.0;  // the empty second part
+  }
+  if (k == 0) {
+    if (kmax > 0 && ks > 0) return no;  // the second stream's order cannot split
+    p = {0, ks, S};
+    return records + plan_walks(ocs, n, ks, S, W, NC);
+  }
+  if (k > kmax || k >= n || ks > k) return no;
+  const double wgs = fmax(W * ks * (2 * S - 3), W * (ks * S + (k - ks)));
+  if (wgs > NC / 2) return no;
+  const double F = NC - wgs, CL = ocs[k];
+  const double head = CL * H / NC;
+  const double t1 = head + plan_walks(ocs, k, ks, S, W, NC / 2);
+  const double t2 = head + (C - CL) * H / F + fmax((double)(ocs[k + 1] - ocs[k]), (C - CL) * W / F);
+  p = {k, ks, S};
+  return fmax(t1, t2) + 4.0;  // the second stream's launches and joins
 }
 
 __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs m, int ntiles,
-                                                         int ncu, int kmax) {
+                                                         int ncu, int kmax, int ksmax,
+                                                         int smax) {
   __shared__ int32_t part[256];
   // Up to kOrderMax sequences the three tables are built in LDS and copied
   // out once at the end (no global round trips between the steps).
@@ -245,8 +324,32 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
     __syncthreads();
   }
   __syncthreads();
+  // the plan: one candidate per thread, then the cheapest (ties: the lowest index)
+  __shared__ double cost[256];
+  __shared__ Plan plans[256];
+  {
+    Plan p = {0, 0, 1};
+    double t = 1e300;
+    if (small && threadIdx.x < kPlanCands)
+      t = plan_cost(threadIdx.x, ocs, n, a.hv, (double)a.hv * ntiles, ncu, kmax, ksmax, smax, p);
+    cost[threadIdx.x] = t;
+    plans[threadIdx.x] = p;
+  }
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < (unsigned)off && cost[threadIdx.x + off] < cost[threadIdx.x]) {
+      cost[threadIdx.x] = cost[threadIdx.x + off];
+      plans[threadIdx.x] = plans[threadIdx.x + off];
+    }
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
-    m.info[0] = small ? split_rank(ocs, n, a.hv, ntiles, ncu, kmax) : 0;
+    const Plan p = cost[0] < 1e299 ? plans[0] : Plan{0, 0, 1};
+    m.info[0] = p.k;
+    m.info[1] = p.ks;
+    m.info[2] = p.S;
+    for (int r = 0; r < kSegRanks; ++r)
+      m.info[3 + r] = r < p.ks ? (ocs[r + 1] - ocs[r] + p.S - 1) / p.S : 0;
   }
   if (small) {
     for (int i = threadIdx.x; i <= n; i += 256) {
@@ -737,6 +840,7 @@ struct WalkCtx {
   const char* recs;
   int64_t t_begin, t_end;
   int c0, h, hk, dv0;
+  int v_on;  // 0: v reads as zeros (the identity's walk)
 };
 
 __device__ __forceinline__ int chunk_len(const WalkCtx& c, int ch) {
@@ -804,8 +908,9 @@ __device__ __forceinline__ void stage_offsets(StageOffsets<NW, NB>& o, const Pre
 // high/low and P, 3 = the V columns and the factors.  The q/k/v rows go
 // through buffer resources that end at the chunk's last token, so rows past
 // the end of the sequence arrive as zeros.  The walk spreads the parts over
-// a chunk step so the CU's load path works while the wave computes.
-template <int NW, int NB, int PART>
+// a chunk step so the CU's load path works while the wave computes.  A walk
+// without outputs (OUTS false) loads neither Q nor P.
+template <int NW, int NB, int PART, bool OUTS>
 __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx& c, int ch,
                                                int w, int lane, const StageOffsets<NW, NB>& o) {
   using SO = StageOffsets<NW, NB>;
@@ -820,6 +925,7 @@ __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx
 #pragma unroll
     for (int i = 0; i < SO::NKQ; ++i) dma16_buf(kr, o.k[i], B.K + 512 * (NW * i + w));
   } else if constexpr (PART == 1) {
+    if constexpr (!OUTS) return;
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(static_cast<const uint16_t*>(a.q) + tb * a.q_rs +
                               (int64_t)c.hk * DKC),
@@ -834,13 +940,13 @@ __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx
       const int u = NW * i + w;
       dma16_buf(rr, REC_TH + o.tp[i], B.Th + 512 * u);
       dma16_buf(rr, REC_TL + o.tp[i], B.Tl + 512 * u);
-      dma16_buf(rr, REC_P + o.tp[i], B.P + 512 * u);
+      if constexpr (OUTS) dma16_buf(rr, REC_P + o.tp[i], B.P + 512 * u);
     }
   } else {
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(static_cast<const uint16_t*>(a.v) + tb * a.v_rs +
                               (int64_t)c.h * a.dv),
-        0, (int)(L * a.v_rs * 2), kBufferFlags);
+        0, c.v_on ? (int)(L * a.v_rs * 2) : 0, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < SO::NVL; ++i) dma16_buf(vr, o.v[i], B.V + 512 * (NW * i + w));
     if (w == 0) dma16(chunk_rec(c, ch) + REC_F + 16 * lane, B.F);
@@ -848,13 +954,13 @@ __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx
 }
 
 // All loads of chunk `ch` into B.
-template <int NW, int NB>
+template <int NW, int NB, bool OUTS>
 __device__ __forceinline__ void stage_dma(WalkBuf<NW, NB>& B, const WalkCtx& c, int ch, int w,
                                           int lane, const StageOffsets<NW, NB>& o) {
-  stage_dma_part<NW, NB, 0>(B, c, ch, w, lane, o);
-  stage_dma_part<NW, NB, 1>(B, c, ch, w, lane, o);
-  stage_dma_part<NW, NB, 2>(B, c, ch, w, lane, o);
-  stage_dma_part<NW, NB, 3>(B, c, ch, w, lane, o);
+  stage_dma_part<NW, NB, 0, OUTS>(B, c, ch, w, lane, o);
+  stage_dma_part<NW, NB, 1, OUTS>(B, c, ch, w, lane, o);
+  stage_dma_part<NW, NB, 2, OUTS>(B, c, ch, w, lane, o);
+  stage_dma_part<NW, NB, 3, OUTS>(B, c, ch, w, lane, o);
 }
 
 // Waits for this wave's outstanding global accesses (the chunk loads above)
@@ -909,12 +1015,23 @@ __device__ __forceinline__ void pack_split(const f32x4& t0, const f32x4& t1,
   lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), x8);
 }
 
+// What a walk workgroup does (see the segment notes at the metadata):
+enum WalkKind {
+  kFullWalk = 0,  // a sequence or one of its segments, with outputs
+  kWalkA0 = 1,    // segment 0 of a split sequence, state only: S_in of segment 1
+  kWalkLoc = 2,   // a middle segment from zero, state only: its S_loc
+  kWalkTrn = 3    // a middle segment from the identity with v = 0 (Dk rows): its M
+};
+
 // Outputs leave through a buffer resource whose range ends at the chunk's last
 // row: stores of rows past the end of the sequence (and of a block past dv)
 // fall outside it and are dropped by the hardware, with no branch per row.
-template <int TIN, int TOUT, int NW, int NB, int MINB>
+// OUTS: the walk forms outputs (full walks); else it updates the state alone
+// (the first phase of split sequences) and never loads Q or P.
+template <int TIN, int TOUT, int NW, int NB, int MINB, bool OUTS>
 __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
-    PrefillArgs a, MetaPtrs m, const char* recs, int ntiles, int max_chunks, int part) {
+    PrefillArgs a, MetaPtrs m, const char* recs, float* segws, int seg_slots, int ntiles,
+    int max_chunks, int part) {
   constexpr int NTH = 64 * NW;
   constexpr int VC = WalkBuf<NW, NB>::VC;
   // the two chunk buffers are dynamic LDS: the static size would make the
@@ -935,23 +1052,53 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   // XCD-aware mapping.  Workgroups are dealt round-robin to the 8 XCDs, each
   // with its own L2; the tiles of one v-head re-read the same per-chunk
   // records, and the v-heads of one GQA group the same q/k rows, so a unit
-  // (sequence, q/k head) keeps all ratio * ntiles of its workgroups on one
+  // (walk item, q/k head) keeps all ratio * ntiles of its workgroups on one
   // XCD: block b -> xcd = b % 8, unit = (b / 8) / per_unit * 8 + xcd.
   const int ratio = a.hv / a.hk;
   const int per_unit = ratio * ntiles;
   const int xcd = blockIdx.x % kXcds;
   const int rblk = blockIdx.x / kXcds;
   const int unit = (rblk / per_unit) * kXcds + xcd;
-  // this launch part's ranks: 0 = [0, k), 1 = [k, n), 2 = all
+  const int item = unit / a.hk;
   const int n = (int)a.num_seqs;
-  const int ksplit = part == 2 ? 0 : m.info[0];
-  const int rbeg = part == 1 ? ksplit : 0, rend = part == 0 ? ksplit : n;
-  const int s_rank = rbeg + unit / a.hk;
-  if (s_rank >= rend) return;
+  const int ksplit = m.info[0], ks = m.info[1], nseg_split = m.info[2];
+  // this launch's walk items
+  int rank, seg, nseg, kind;
+  if constexpr (!OUTS) {
+    // phase A of the split ranks [0, ks): per rank 2 S - 3 items: segment 0,
+    // then (S_loc, M) of each middle segment 1 .. S - 2
+    const int per = 2 * nseg_split - 3;
+    if (ks == 0 || per <= 0) return;
+    rank = item / per;
+    if (rank >= ks) return;
+    const int li = item % per;
+    seg = li == 0 ? 0 : 1 + (li - 1) / 2;
+    kind = li == 0 ? kWalkA0 : ((li - 1) & 1) ? kWalkTrn : kWalkLoc;
+    nseg = nseg_split;
+  } else {
+    // ranks of this launch part: 0 = [0, k), 1 = [k, n), 2 = all; the split
+    // ranks among them (always the first) have one item per segment
+    const int r0 = part == 1 ? ksplit : 0, r1 = part == 0 ? ksplit : n;
+    const int nsplit = max(0, min(ks, r1) - r0);
+    if (item < nsplit * nseg_split) {
+      rank = r0 + item / nseg_split;
+      seg = item % nseg_split;
+      nseg = nseg_split;
+    } else {
+      rank = r0 + nsplit + (item - nsplit * nseg_split);
+      seg = 0;
+      nseg = 1;
+    }
+    if (rank >= r1) return;
+    kind = kFullWalk;
+  }
+  // state rows of this walk: dv, or Dk for the identity's walk
+  const int rows = kind == kWalkTrn ? DKC : a.dv;
   const int j0 = rblk % per_unit;
   const int tile = j0 % ntiles;
+  if (tile * VC >= rows) return;
   const int h = (unit % a.hk) * ratio + j0 / ntiles;
-  const int s = m.order[s_rank];
+  const int s = m.order[rank];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = lane >> 4, cl = lane & 15;
@@ -959,26 +1106,35 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   WalkCtx c;
   c.a = &a;
   c.recs = recs;
-  chunk_bounds(a, s, c.t_begin, c.t_end);
-  c.c0 = m.cs[s];
+  int64_t seq_t0, seq_t1;
+  chunk_bounds(a, s, seq_t0, seq_t1);
+  // a well-formed cu_seqlens gives cs[s] + chunks <= max_chunks; a malformed
+  // one (overlapping ranges) must still never index past the workspace
+  const int nch_seq =
+      max(0, min((int)((seq_t1 - seq_t0 + CK - 1) / CK), max_chunks - m.cs[s]));
+  const int seg_len = nseg > 1 ? m.info[3 + rank] : nch_seq;
+  const int ch0 = min(seg * seg_len, nch_seq);
+  const int nch = min(seg_len, nch_seq - ch0);
+  c.t_begin = seq_t0 + (int64_t)ch0 * CK;
+  c.t_end = min(seq_t1, seq_t0 + (int64_t)(ch0 + nch) * CK);
+  c.c0 = m.cs[s] + ch0;
   c.h = h;
   c.hk = h / ratio;
   c.dv0 = tile * VC;
+  c.v_on = kind == kWalkTrn ? 0 : 1;
   // this wave's blocks: state rows dvw + 16 nb .. +15
   const int dvw = c.dv0 + 16 * NB * w;
-  // a well-formed cu_seqlens gives c0 + nch <= max_chunks; a malformed one
-  // (overlapping ranges) must still never index past the workspace
-  const int nch =
-      max(0, min((int)((c.t_end - c.t_begin + CK - 1) / CK), max_chunks - c.c0));
   const int64_t slot = a.idx ? (int64_t)a.idx[s] : (int64_t)s;
   const int64_t out_rs = (int64_t)a.hv * a.dv;
 
   if (slot < 0 || slot >= a.num_slots) {
     // caller error: NaN outputs for these rows, no state access
-    for (int64_t t = c.t_begin + tid / VC; t < c.t_end; t += NTH / VC) {
-      const int col = c.dv0 + tid % VC;
-      if (col < a.dv) store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + col,
-                             __builtin_nanf(""));
+    if constexpr (OUTS) {
+      for (int64_t t = c.t_begin + tid / VC; t < c.t_end; t += NTH / VC) {
+        const int col = c.dv0 + tid % VC;
+        if (col < a.dv) store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + col,
+                               __builtin_nanf(""));
+      }
     }
     return;
   }
@@ -987,30 +1143,162 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   using Ot = typename OutT<TOUT>::type;
   Ot* out = static_cast<Ot*>(a.out) + (int64_t)h * a.dv + dvw;  // this wave's column 0
 
+  // The split sequence's workspace states: slot 0 its initial state, 1 the
+  // entry state of segment 1, 2 i and 2 i + 1 the S_loc and M^T of middle
+  // segment i.  One state is ntiles tiles of VC rows x Dk f32, each kept in the
+  // walk's register layout (16 bytes per lane and tile, a wave's lanes
+  // contiguous); M^T alone is a plain [Dk][Dk] row-major matrix.
+  constexpr int kTileFloats = NB * 8 * NW * 64 * 4;
+  const size_t slot_floats = (size_t)ntiles * kTileFloats;
+  auto ws_state = [&](int sl) {
+    return segws + ((size_t)(rank * a.hv + h) * seg_slots + sl) * slot_floats;
+  };
+  auto tile_off = [&](int nb, int kb) { return (((nb * 8 + kb) * NW + w) * 64 + lane) * 4; };
+
   // St[nb][kb], element r: S[dvw + 16 nb + cl][blk_row(kb, 4g + r)]
   f32x4 St[NB][8];
+  auto ld_tiles = [&](const float* p) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const bool ld = init && dvw + 16 * nb < a.dv;
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      const float4 v = ld ? state_load4_rt(a.state_dt, a.pool, Sg + 16 * nb * DKC + blk_row(kb, 4 * g))
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      St[nb][kb] = (f32x4){v.x, v.y, v.z, v.w};
-    }
-  }
-  auto store_state = [&]() {
+      for (int kb = 0; kb < 8; ++kb)
+        St[nb][kb] = *reinterpret_cast<const f32x4*>(p + tile * kTileFloats + tile_off(nb, kb));
+  };
+  auto st_tiles = [&](float* p) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        *reinterpret_cast<f32x4*>(p + tile * kTileFloats + tile_off(nb, kb)) = St[nb][kb];
+  };
+  const bool from_pool = kind == kWalkA0 || (kind == kFullWalk && nseg == 1);
+  if (from_pool || kind == kWalkLoc || (kind == kFullWalk && seg == 0)) {
+    // the real initial state (from the pool, or as segment 0 of a split
+    // sequence from the copy its phase-A walk kept: the last segment may
+    // already be overwriting the pool slot), or zeros
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (dvw + 16 * nb < a.dv) {
+      const bool ld = init && kind != kWalkLoc && dvw + 16 * nb < rows;
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-          state_store4_rt(a.state_dt, a.pool, Sg + 16 * nb * DKC + blk_row(kb, 4 * g),
-                          make_float4(St[nb][kb][0], St[nb][kb][1], St[nb][kb][2], St[nb][kb][3]));
+      for (int kb = 0; kb < 8; ++kb) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ld && from_pool) {
+          v = state_load4_rt(a.state_dt, a.pool, Sg + 16 * nb * DKC + blk_row(kb, 4 * g));
+        } else if (ld) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(ws_state(0) + tile * kTileFloats +
+                                                          tile_off(nb, kb));
+          v = make_float4(t[0], t[1], t[2], t[3]);
+        }
+        St[nb][kb] = (f32x4){v.x, v.y, v.z, v.w};
       }
     }
+    if (kind == kWalkA0 && init) st_tiles(ws_state(0));
+  } else if (kind == kWalkTrn) {
+    // the identity: S[row][key] = 1 where key == row
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          St[nb][kb][r] = blk_row(kb, 4 * g + r) == dvw + 16 * nb + cl ? 1.0f : 0.0f;
+  } else {
+    ld_tiles(ws_state(1));  // segment j >= 1 starts from the entry state of segment 1 ...
+  }
+  auto store_state = [&]() {
+    if (kind == kFullWalk) {
+      if (seg != nseg - 1) return;  // only the last segment's final state is kept
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (dvw + 16 * nb < a.dv) {
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb)
+            state_store4_rt(a.state_dt, a.pool, Sg + 16 * nb * DKC + blk_row(kb, 4 * g),
+                            make_float4(St[nb][kb][0], St[nb][kb][1], St[nb][kb][2],
+                                        St[nb][kb][3]));
+        }
+      }
+    } else if (kind == kWalkTrn) {
+      // M^T[key][row] = S[row][key]: a plain row-major [Dk][Dk] matrix
+      float* mt = ws_state(2 * seg + 1);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            mt[blk_row(kb, 4 * g + r) * DKC + dvw + 16 * nb + cl] = St[nb][kb][r];
+    } else {
+      st_tiles(ws_state(kind == kWalkA0 ? 1 : 2 * seg));
+    }
   };
-  if (nch == 0) {  // empty sequence: the state passes through (or is zeroed)
+
+  // Per-lane LDS offsets (elements).  Every operand row of token block b is
+  // blk_row(b, m) = 32 (b / 2) + 4 (b % 2) + rm with rm = 8 (m / 4) + m % 4, and
+  // the swizzles depend on rm only, so each read is a per-lane base (one per
+  // k-step) plus a compile-time offset for the block.
+  const int rmA = 8 * (cl >> 2) + (cl & 3);  // A-operand row within a block pair
+  const int sK = kq_swz(rmA);                  // the swizzles of those rows (any block)
+  const int sT = tp_swz(rmA);
+  int kqb[4], tpb[2], trb[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) kqb[jj] = rmA * DKC + 8 * ((4 * jj + g) ^ sK);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) tpb[j] = rmA * CK + 8 * ((4 * j + g) ^ sT);
+
+  if (kind == kFullWalk && seg > 0) {
+    // ... and folds in middle segments 1 .. seg - 1: S <- S M_i + S_loc,i, as
+    // St <- M_i^T St + S_loc,i^T.  M_i^T is staged in LDS as 16-bit high / low
+    // parts with K's row layout and swizzle (Dk rows, 8 row blocks), and each
+    // product is the X = K St product with M_i^T in K's place.
+    uint16_t* mh = reinterpret_cast<uint16_t*>(walk_lds);
+    uint16_t* ml = mh + DKC * DKC;
+    for (int i = 1; i < seg; ++i) {
+      const float* mt = ws_state(2 * i + 1);
+      for (int u = tid; u < DKC * 16; u += NTH) {
+        const int row = u >> 4, c8 = u & 15;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(mt + row * DKC + 8 * c8);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(mt + row * DKC + 8 * c8 + 4);
+        x8 hi, lo;
+        pack_split<TIN>(x0, x1, hi, lo);
+        const int off = row * DKC + 8 * (c8 ^ kq_swz(row));
+        *reinterpret_cast<x8*>(mh + off) = hi;
+        *reinterpret_cast<x8*>(ml + off) = lo;
+      }
+      lds_barrier();
+      f32x4 Sn[NB][8];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) Sn[nb][kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          x8 sh, sl;
+          pack_split<TIN>(St[nb][2 * jj], St[nb][2 * jj + 1], sh, sl);
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            const int rb = 32 * (kb >> 1) + 4 * (kb & 1);
+            const x8 ah = *reinterpret_cast<const x8*>(mh + kqb[jj] + rb * DKC);
+            const x8 al = *reinterpret_cast<const x8*>(ml + kqb[jj] + rb * DKC);
+            Sn[nb][kb] = M::mma(ah, sh, Sn[nb][kb]);
+            Sn[nb][kb] = M::mma(ah, sl, Sn[nb][kb]);
+            Sn[nb][kb] = M::mma(al, sh, Sn[nb][kb]);
+          }
+        }
+      }
+      const float* sloc = ws_state(2 * i);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+          St[nb][kb] = Sn[nb][kb] +
+                       *reinterpret_cast<const f32x4*>(sloc + tile * kTileFloats + tile_off(nb, kb));
+      lds_barrier();  // every wave is done with M_i^T before it is overwritten
+    }
+  }
+  if (nch == 0) {  // no tokens in this walk: the state passes through (or is zeroed)
     store_state();
     return;
   }
@@ -1025,21 +1313,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     for (int i = tid; i < n16; i += NTH) z[i] = (u32x4){0u, 0u, 0u, 0u};
   }
   lds_barrier();
-  stage_dma<NW, NB>(sb[0], c, 0, w, lane, so);
+  stage_dma<NW, NB, OUTS>(sb[0], c, 0, w, lane, so);
   stage_sync();
 
-  // Per-lane LDS offsets (elements).  Every operand row of token block b is
-  // blk_row(b, m) = 32 (b / 2) + 4 (b % 2) + rm with rm = 8 (m / 4) + m % 4, and
-  // the swizzles depend on rm only, so each read is a per-lane base (one per
-  // k-step) plus a compile-time offset for the block.
-  const int rmA = 8 * (cl >> 2) + (cl & 3);  // A-operand row within a block pair
-  const int sK = kq_swz(rmA);                  // the swizzles of those rows (any block)
-  const int sT = tp_swz(rmA);
-  int kqb[4], tpb[2], trb[4];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) kqb[jj] = rmA * DKC + 8 * ((4 * jj + g) ^ sK);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) tpb[j] = rmA * CK + 8 * ((4 * j + g) ^ sT);
   {
     // transposing reads: this lane supplies row 32 j + 8 g + 4 h + e, chunk
     // 4 (kb / 2) + q (+ 4 elements when kb is odd); the row swizzle is kq_swz(8 g + e)
@@ -1070,7 +1346,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
   // leave during the next step (or after the last one), so the wait for the
   // next chunk's loads at the end of a step does not also wait for the stores.
   auto store_rows = [&](const WalkBuf<NW, NB>* __restrict__ buf, int chp) {
-    if constexpr (TOUT != kF32) {
+    if constexpr (OUTS && TOUT != kF32) {
       const int64_t tbp = c.t_begin + (int64_t)chp * CK;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           out + tbp * out_rs, 0, chunk_len(c, chp) * out_row, kBufferFlags);
@@ -1116,7 +1392,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       for (int b = 0; b < 4; ++b) {
         const int rb = 32 * (b >> 1) + 4 * (b & 1);
         kd[b] = *reinterpret_cast<const x8*>(sm.K + kqb[jj] + rb * DKC);
-        qd[b] = *reinterpret_cast<const x8*>(sm.Q + kqb[jj] + rb * DKC);
+        if constexpr (OUTS) qd[b] = *reinterpret_cast<const x8*>(sm.Q + kqb[jj] + rb * DKC);
       }
     };
     read_kq(kf[0], qf[0], 0);
@@ -1140,8 +1416,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     for (int jj = 0; jj < 4; ++jj) {
       if (jj < 3) read_kq(kf[(jj + 1) & 1], qf[(jj + 1) & 1], jj + 1);
       if (more && jj == 1) {
-        stage_dma_part<NW, NB, 0>(*nxt, c, ch + 1, w, lane, so);
-        stage_dma_part<NW, NB, 1>(*nxt, c, ch + 1, w, lane, so);
+        stage_dma_part<NW, NB, 0, OUTS>(*nxt, c, ch + 1, w, lane, so);
+        stage_dma_part<NW, NB, 1, OUTS>(*nxt, c, ch + 1, w, lane, so);
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -1150,9 +1426,9 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           X[nb][b] = M::mma(kf[jj & 1][b], sh, X[nb][b]);
-          QS[nb][b] = M::mma(qf[jj & 1][b], sh, QS[nb][b]);
+          if constexpr (OUTS) QS[nb][b] = M::mma(qf[jj & 1][b], sh, QS[nb][b]);
           X[nb][b] = M::mma(kf[jj & 1][b], sl, X[nb][b]);
-          QS[nb][b] = M::mma(qf[jj & 1][b], sl, QS[nb][b]);
+          if constexpr (OUTS) QS[nb][b] = M::mma(qf[jj & 1][b], sl, QS[nb][b]);
         }
       }
     }
@@ -1190,7 +1466,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
-    if (more) stage_dma_part<NW, NB, 2>(*nxt, c, ch + 1, w, lane, so);
+    if (more) stage_dma_part<NW, NB, 2, OUTS>(*nxt, c, ch + 1, w, lane, so);
     // ---- U = T_b Z (lower triangular in token blocks) ----
     f32x4 U[NB][4];
 #pragma unroll
@@ -1213,9 +1489,12 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int rb = 32 * (b >> 1) + 4 * (b & 1);
+      if constexpr (OUTS) {
 #pragma unroll
-      for (int j = 0; j <= (b >> 1); ++j) pff[b][j] = *reinterpret_cast<const x8*>(sm.P + tpb[j] + rb * CK);
-      fo4[b] = *reinterpret_cast<const float4*>(sm.F + CK + fb + rb);
+        for (int j = 0; j <= (b >> 1); ++j)
+          pff[b][j] = *reinterpret_cast<const x8*>(sm.P + tpb[j] + rb * CK);
+        fo4[b] = *reinterpret_cast<const float4*>(sm.F + CK + fb + rb);
+      }
     }
     x8 Uh[NB][2], Ul[NB][2], Wh[NB][2], Wl[NB][2];
 #pragma unroll
@@ -1227,18 +1506,18 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
         const f32x4& u1 = U[nb][2 * j + 1];
         const f32x4 w0 = {fw[0].x * u0[0], fw[0].y * u0[1], fw[0].z * u0[2], fw[0].w * u0[3]};
         const f32x4 w1 = {fw[1].x * u1[0], fw[1].y * u1[1], fw[1].z * u1[2], fw[1].w * u1[3]};
-        if constexpr (kFullOut)
+        if constexpr (OUTS && kFullOut)
           pack_split<TIN>(u0, u1, Uh[nb][j], Ul[nb][j]);
-        else
+        else if constexpr (OUTS)
           pack_hi<TIN>(u0, u1, Uh[nb][j]);
         pack_split<TIN>(w0, w1, Wh[nb][j], Wl[nb][j]);
       }
     }
 
-    if (more) stage_dma_part<NW, NB, 3>(*nxt, c, ch + 1, w, lane, so);
+    if (more) stage_dma_part<NW, NB, 3, OUTS>(*nxt, c, ch + 1, w, lane, so);
     // ---- O = diag(fo) QS + P U, stored ----
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < (OUTS ? 4 : 0); ++b) {
       const int rb = 32 * (b >> 1) + 4 * (b & 1);
       const float4 fo = fo4[b];
       f32x4 o[NB];
@@ -1322,9 +1601,20 @@ int64_t max_chunks(int64_t total_tokens, int64_t num_seqs) {
   return (total_tokens + CK - 1) / CK + num_seqs;
 }
 
-size_t meta_bytes(int64_t num_seqs) { return (size_t)((3 * num_seqs + 6) * 4 + 255) / 256 * 256; }
+size_t meta_bytes(int64_t num_seqs) {
+  return (size_t)((3 * num_seqs + 2 + kInfoWords) * 4 + 255) / 256 * 256;
+}
 
-int walk_tiles(int dv) { return (dv + WALK_BV - 1) / WALK_BV; }
+// workgroups per walk of one v-head: enough for dv state rows, and for the Dk
+// rows of a middle segment's transition walk
+int walk_tiles(int dv) { return (std::max(dv, DKC) + WALK_BV - 1) / WALK_BV; }
+
+// the split sequences' states (per split rank and v-head, each walk_tiles
+// tiles of WALK_BV rows x Dk f32)
+size_t seg_bytes(int64_t total_tokens, int64_t num_seqs, int hv, int dv) {
+  const SegBounds b = seg_bounds(total_tokens, num_seqs);
+  return (size_t)b.ranks * hv * b.slots() * walk_tiles(dv) * WALK_BV * DKC * sizeof(float);
+}
 
 
 // Per device: the CU count, and a second stream with two events for the split
@@ -1359,11 +1649,16 @@ SplitRes* split_res(int dev) {
 
 template <int TIN>
 hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) {
+  // workspace: metadata, the split sequences' states, the per-chunk records
   const MetaPtrs m = meta_ptrs(ws, a.num_seqs);
-  char* recs = static_cast<char*>(ws) + meta_bytes(a.num_seqs);
+  float* segws = reinterpret_cast<float*>(static_cast<char*>(ws) + meta_bytes(a.num_seqs));
+  char* recs = reinterpret_cast<char*>(segws) + seg_bytes(a.total_tokens, a.num_seqs, a.hv, a.dv);
   const int64_t mc = max_chunks(a.total_tokens, a.num_seqs);
   const int ntiles = walk_tiles(a.dv);
   const int per_seq_wgs = a.hv * ntiles;
+  // the longest ranks may be split into segments (needs the ranking by length)
+  const SegBounds sb = seg_bounds(a.total_tokens, a.num_seqs);
+  const int ksmax = sb.ranks, smax = sb.smax;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
   // The split schedule needs its second stream on the caller's stream's
@@ -1387,7 +1682,8 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
                                    (int64_t)(ncu / 2 / per_seq_wgs)});
   if (kmax == 0) lock.unlock();
 
-  hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, m, ntiles, ncu, kmax);
+  hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, m, ntiles, ncu, kmax,
+                     ksmax, smax);
 
   const int64_t prep_units = mc * a.hk;
   if (prep_units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
@@ -1398,14 +1694,18 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   };
   const int ratio = a.hv / a.hk;
   const size_t lds = 2 * sizeof(WalkBuf<WALK_NW, WALK_NB>);
-  auto walk_blocks = [&](int64_t ranks) {
-    return (ranks * a.hk + kXcds - 1) / kXcds * kXcds * ratio * ntiles;
+  // walk items of a launch: at most one per rank, plus S - 1 more for each
+  // split rank (phase B), or 2 S - 3 per split rank (phase A)
+  auto walk_blocks = [&](int64_t items) {
+    return (items * a.hk + kXcds - 1) / kXcds * kXcds * ratio * ntiles;
   };
-  if (walk_blocks(a.num_seqs) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t seg_items = (int64_t)ksmax * (smax - 1);
+  const int64_t a_items = (int64_t)ksmax * (2 * smax - 3);
+  if (walk_blocks(a.num_seqs + seg_items) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   // the dynamic-LDS limit is raised once per device and kernel: one mask per
-  // output type, since the two walk kernels are distinct functions
-  static std::atomic<uint64_t> raised_f32{0}, raised_16{0};
-  auto walk = [&](int part, int64_t ranks, hipStream_t st) -> hipError_t {
+  // kernel (outputs f32 / 16-bit, and the state-only walk)
+  static std::atomic<uint64_t> raised_f32{0}, raised_16{0}, raised_st{0};
+  auto walk = [&](int part, int64_t items, hipStream_t st, bool outs) -> hipError_t {
     auto go = [&](auto kern, std::atomic<uint64_t>& raised) -> hipError_t {
       const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
       if (!bit || !(raised.load(std::memory_order_acquire) & bit)) {
@@ -1415,34 +1715,43 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
         if (e != hipSuccess) return e;
         raised.fetch_or(bit, std::memory_order_acq_rel);
       }
-      hipLaunchKernelGGL(kern, dim3((unsigned)walk_blocks(ranks)), dim3(64 * WALK_NW), lds, st,
-                         a, m, (const char*)recs, ntiles, (int)mc, part);
+      hipLaunchKernelGGL(kern, dim3((unsigned)walk_blocks(items)), dim3(64 * WALK_NW), lds, st,
+                         a, m, (const char*)recs, segws, sb.slots(), ntiles, (int)mc, part);
       return hipSuccess;
     };
+    if (!outs)
+      return go(chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB, false>, raised_st);
     return a.out_dt == kF32
-               ? go(chunk_state_kernel<TIN, kF32, WALK_NW, WALK_NB, WALK_MINB>, raised_f32)
-               : go(chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB>, raised_16);
+               ? go(chunk_state_kernel<TIN, kF32, WALK_NW, WALK_NB, WALK_MINB, true>, raised_f32)
+               : go(chunk_state_kernel<TIN, TIN, WALK_NW, WALK_NB, WALK_MINB, true>, raised_16);
   };
 
   hipError_t e;
   if (kmax == 0) {
+    // one stream: all records, the first phase of the split ranks (if the
+    // device chose any), then every walk with outputs
     prep(2, stream);
-    if ((e = walk(2, a.num_seqs, stream)) != hipSuccess) return e;
+    if (a_items > 0 && (e = walk(0, a_items, stream, false)) != hipSuccess) return e;
+    if ((e = walk(2, a.num_seqs + seg_items, stream, true)) != hipSuccess) return e;
     return hipGetLastError();
   }
   // Split schedule (the rank k is chosen on the device; k = 0 leaves parts 0
   // empty and runs everything as part 1):
-  //   caller's stream: meta, records of ranks [0, k), their walks
+  //   caller's stream: meta, records of ranks [0, k), the first phase of the
+  //                    split ranks among them, their walks
   //   second stream:   (after those records) the other records, their walks
   // and the caller's stream then waits for the second.  The early walks are
   // queued right behind their records on the caller's stream, so they take
   // their CUs before the other records fill the device.
   prep(0, stream);
   if ((e = hipEventRecord(sr->records_early, stream)) != hipSuccess) return e;
-  if ((e = walk(0, kmax, stream)) != hipSuccess) return e;
+  if (a_items > 0 && (e = walk(0, a_items, stream, false)) != hipSuccess) return e;
+  // the early part: at most kmax ranks, or all of them when there are few
+  const int64_t early = a.num_seqs <= kSplitMax ? a.num_seqs : kmax;
+  if ((e = walk(0, early + seg_items, stream, true)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(sr->aux, sr->records_early, 0)) != hipSuccess) return e;
   prep(1, sr->aux);
-  if ((e = walk(1, a.num_seqs, sr->aux)) != hipSuccess) return e;
+  if ((e = walk(1, a.num_seqs, sr->aux, true)) != hipSuccess) return e;
   if ((e = hipEventRecord(sr->rest_done, sr->aux)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(stream, sr->rest_done, 0)) != hipSuccess) return e;
   return hipGetLastError();
@@ -1467,8 +1776,9 @@ bool chunked_layout_ok(const void* q, const void* k, const void* v, int64_t q_rs
 }
 
 size_t chunked_workspace_bytes(int64_t total_tokens, int64_t num_seqs, int hv, int dk, int dv) {
-  (void)dk; (void)dv;
-  return meta_bytes(num_seqs) + (size_t)max_chunks(total_tokens, num_seqs) * (size_t)hv * REC_BYTES;
+  (void)dk;
+  return meta_bytes(num_seqs) + seg_bytes(total_tokens, num_seqs, hv, dv) +
+         (size_t)max_chunks(total_tokens, num_seqs) * (size_t)hv * REC_BYTES;
 }
 
 hipError_t launch_prefill_chunked(const PrefillArgs& a, void* ws, size_t ws_bytes,

@@ -461,7 +461,7 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
     return out
 
 
-NOALLOC_SCRATCH_BYTES = 64 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
+NOALLOC_SCRATCH_BYTES = 128 << 20   # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 
 
 def prefill_varlen_noalloc(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,

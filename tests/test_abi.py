@@ -233,7 +233,7 @@ def test_prefill_noalloc_refuses_sizes_beyond_its_scratch():
     """The allocation-free prefill checks its fixed scratch against the call's
     sizes before anything else (host only: nothing is enqueued)."""
     lib = pkg.load_library()
-    T, hk, hv, dk, dv = 16384, 2, 16, 128, 128
+    T, hk, hv, dk, dv = 32768, 2, 16, 128, 128
     assert lib.gdn_prefill_varlen_workspace_size(T, 1, hk, hv, dk, dv, 2, 1) > B.NOALLOC_SCRATCH_BYTES
     rc = lib.gdn_prefill_varlen_noalloc(None, 2, None, None, None, 2, hk * dk, hk * dk, hv * dv,
                                         None, hv, None, hv, None, 1, None, None, None, 1, T, hk,

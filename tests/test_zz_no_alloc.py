@@ -79,7 +79,7 @@ def test_noalloc_t4096_then_small(dev):
 
 def test_noalloc_refuses_sizes_beyond_the_scratch(dev):
     announce("prefill noalloc: a size beyond the scratch returns GDN_ERR_SHAPE, enqueues nothing")
-    T, hk, hv, dk, dv = 16384, 2, 16, 128, 128
+    T, hk, hv, dk, dv = 32768, 2, 16, 128, 128
     need = gdn.prefill_workspace_size(T, 1, hk, hv, dk, dv, torch.bfloat16)
     assert need > gdn.gdn.NOALLOC_SCRATCH_BYTES
     q = torch.zeros((T, hk, dk), dtype=torch.bfloat16, device=dev)
