@@ -425,12 +425,13 @@ def main():
         g = torch.empty((T, pre.hv), dtype=torch.float32, device=dev)
         ws_n = gdn.prefill_workspace_size(T, N, pre.hk, pre.hv, pre.dk, pre.dv, torch.float16)
         ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+        aux = torch.cuda.Stream()   # the second stream of the split schedule
 
         def prefill_step():
             gdn.gate(pa, pdt, pssm, out=g, stream=stream)
             gdn.prefill_varlen(qp, kp, vp, g, pbeta, ppool, pcu, scale=pre.scale,
                                state_idx=pidx, has_initial_state=phi, out=pout,
-                               workspace=ws, stream=stream)
+                               workspace=ws, stream=stream, aux_stream=aux)
 
         if want("prefill"):
             pwall, pms = timed(lambda i: prefill_step(), 8, args.prefill_steps)
@@ -478,7 +479,7 @@ def main():
                 gdn.gate(a3, dt3, sa3, out=g3, stream=stream)
                 gdn.prefill_varlen(q3, k3, v3, g3, b3, pool3, cu3, scale=p3.scale,
                                    state_idx=idx3, has_initial_state=hi3, out=out3,
-                                   workspace=ws3, stream=stream)
+                                   workspace=ws3, stream=stream, aux_stream=aux)
 
             w3, k3ms = timed(t4096_step, 8, args.prefill_steps)
             ms3 = w3 * 1e3 / args.prefill_steps

@@ -70,7 +70,7 @@ enum {
   GDN_STATE_F16 = 1u << 3,           /* state pool stored as IEEE binary16 */
   GDN_STATE_BF16 = 1u << 4,          /* state pool stored as bfloat16 */
   GDN_NORM_SIGMOID = 1u << 5,        /* gated norm: sigmoid gate instead of silu */
-  GDN_BETA_RAW = 1u << 6,            /* decode: beta is the raw projection b */
+  /* 1u << 6 is not used */
   GDN_BETA_ROUNDED = 1u << 7,        /* gate_beta/post_conv: round sigmoid(b) to b's dtype */
   GDN_CONV_SILU = 1u << 8            /* conv1d: silu activation (else identity) */
 };
@@ -219,11 +219,8 @@ int gdn_post_conv(void* q_out, void* k_out, void* v_out, gdn_dtype out_dt, float
  *              into the same buffer with the same row stride.
  *   alpha      [batch, hv] in alpha_dt, row stride alpha_row_stride.
  *   dt_bias, ssm_a  [hv] f32.   beta [batch, hv] f32 (post-sigmoid),
- *              row stride beta_row_stride; with GDN_BETA_RAW it is instead
- *              the raw projection b in alpha_dt (e.g. the b columns of the
- *              merged b|a row that alpha also points into) and the step uses
- *              sigmoid(b) computed in f32 and rounded through alpha_dt
- *              (vllm.cpp PackedDecodeReference).
+ *              row stride beta_row_stride (gdn_decode_packed takes the raw
+ *              projection b instead).
  *   state_pool [num_slots, hv, dv, dk] f32 (or binary16 / bfloat16 with
  *              GDN_STATE_F16 / GDN_STATE_BF16), read and written in place.
  *   state_idx  [batch] int32: row b uses slot state_idx[b].  A negative
@@ -233,19 +230,39 @@ int gdn_post_conv(void* q_out, void* k_out, void* v_out, gdn_dtype out_dt, float
  *              touched.  Two rows naming the same slot race (undefined).
  *   scale      > 0 and finite (usually 1/sqrt(dk)).
  *   flags      GDN_L2NORM_QK to normalise q and k with l2_eps; GDN_CHECK_SLOTS
- *              to validate state_idx first (negative entries allowed);
- *              GDN_BETA_RAW (see beta); at most one of GDN_STATE_F16,
- *              GDN_STATE_BF16.
+ *              to validate state_idx first (negative entries allowed); at most
+ *              one of GDN_STATE_F16, GDN_STATE_BF16.
  * batch == 0 enqueues nothing and returns GDN_OK.
  */
 int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
                gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
                int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-               const void* beta, int64_t beta_row_stride, void* state_pool,
+               const float* beta, int64_t beta_row_stride, void* state_pool,
                int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
                uint32_t flags, hipStream_t stream);
+
+/*
+ * gdn_decode_packed -- gdn_decode from the raw gate projections a and b, as
+ * the packed decode op takes them (vllm.cpp test_ops_gdn.cpp,
+ * PackedDecodeReference and the packed in_proj_ba case): the step uses
+ * g = softplus(a + dt_bias) * ssm_a and beta = sigmoid(b), the sigmoid
+ * computed in f32 and rounded through ab_dt.
+ *   a_raw, b_raw  [batch, hv] in ab_dt (f32, f16 or bf16) with their own row
+ *              strides (>= hv): e.g. the a and b column views of one merged
+ *              b|a projection row.
+ *   every other argument as for gdn_decode (q, k, v may be views into the
+ *   conv output row: q | k | v with its row stride).
+ */
+int gdn_decode_packed(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
+                      gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+                      int64_t v_row_stride, const void* a_raw, const void* b_raw,
+                      gdn_dtype ab_dt, int64_t a_row_stride, int64_t b_row_stride,
+                      const float* dt_bias, const float* ssm_a, void* state_pool,
+                      int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
+                      int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
+                      uint32_t flags, hipStream_t stream);
 
 /*
  * gdn_decode_gated_norm -- gdn_decode followed, in the same kernel, by the
@@ -272,7 +289,7 @@ int gdn_decode_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void
                           const void* v, gdn_dtype in_dt, int64_t q_row_stride,
                           int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
                           gdn_dtype alpha_dt, int64_t alpha_row_stride, const float* dt_bias,
-                          const float* ssm_a, const void* beta, int64_t beta_row_stride,
+                          const float* ssm_a, const float* beta, int64_t beta_row_stride,
                           void* state_pool, int64_t num_slots, const int32_t* state_idx,
                           int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
                           float scale, float l2_eps, const void* norm_z,
@@ -307,11 +324,13 @@ int gdn_rmsnorm_gated(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt
 
 /*
  * gdn_prefill_varlen_workspace_size -- bytes of device workspace that
- * gdn_prefill_varlen needs for these sizes and flags (0 if none).  The
- * chunked path (bf16/fp16 inputs, dk = 128, dv a multiple of 16) keeps one
- * 25,600-byte record per (64-token chunk, v-head): about
- * (total_tokens / 64 + num_seqs) * hv * 25,600 bytes plus about 12 bytes per
- * sequence; the token-sequential path needs none.  Whether a call takes the
+ * gdn_prefill_varlen (and gdn_prefill_varlen_aux) needs for these sizes and
+ * flags (0 if none).  The chunked path (bf16/fp16 inputs, dk = 128, dv a
+ * multiple of 16) keeps one 25,600-byte record per (64-token chunk, v-head):
+ * about (total_tokens / 64 + num_seqs) * hv * 25,600 bytes, plus about 12
+ * bytes per sequence, plus for the (at most two) longest sequences it may
+ * split into segments up to 8 f32 states of dv x dk per v-head (fewer when
+ * total_tokens is small); the token-sequential path needs none.  Whether a call takes the
  * chunked path also depends on its pointers (16-byte aligned q/k/v rows,
  * strides multiples of 8 elements): with a smaller workspace it fails rather
  * than falling back.
@@ -351,13 +370,10 @@ size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs,
  *                forces the token-sequential kernel instead of the chunked
  *                one; at most one of GDN_STATE_F16, GDN_STATE_BF16.
  * num_seqs == 0 enqueues nothing and returns GDN_OK.
- * Streams: everything is ordered on `stream`.  When the lengths are skewed
- * the chunked path may run part of the work on a second stream the library
- * owns (one per device, created on first use and kept for the life of the
- * process, default priority), forked from and joined back into `stream`
- * with events, so later work on `stream` still sees every result.  It does
- * not do so while `stream` is being captured or when `stream` belongs to
- * another device than the current one.
+ * Streams: every kernel runs on `stream` (gdn_prefill_varlen_aux may also
+ * use a second stream the caller passes).  The library owns no stream and
+ * holds no lock across launches; calls on different streams run
+ * concurrently, each in its own workspace.
  */
 int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k,
                        const void* v, gdn_dtype in_dt, int64_t q_row_stride,
@@ -368,6 +384,30 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
                        int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
                        int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdn_prefill_varlen_aux -- gdn_prefill_varlen with a second stream of the
+ * caller's, aux_stream, for the split schedule: when the lengths are skewed,
+ * the records and walks of the shorter sequences run on aux_stream beside the
+ * longest sequences' walks on `stream`, forked from and joined back into
+ * `stream` with two events (created per host thread and device on first use
+ * and kept for the life of the process), so later work on `stream` sees
+ * every result and `aux_stream` is left with no pending dependency on this
+ * call's later work.  aux_stream must be on the same device as `stream`;
+ * NULL, equal to `stream`, on another device, or while `stream` is being
+ * captured, the call runs on `stream` alone exactly as gdn_prefill_varlen.
+ * Two calls that share aux_stream are serialised on it.
+ */
+int gdn_prefill_varlen_aux(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                           const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                           int64_t k_row_stride, int64_t v_row_stride, const float* g,
+                           int64_t g_row_stride, const float* beta, int64_t beta_row_stride,
+                           void* state_pool, int64_t num_slots, const int32_t* state_idx,
+                           const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                           int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                           int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipStream_t aux_stream);
 
 /*
  * gdn_prefill_varlen_noalloc -- gdn_prefill_varlen with no workspace argument,
@@ -383,10 +423,10 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
  *   GDN_NOALLOC_SCRATCH_BYTES return GDN_ERR_SHAPE and enqueue nothing (128
  *   MiB holds e.g. one 8192-token sequence at hv = 32, dv = 128).
  *   Sharing: every call on a device uses that device's one array, and the
- *   whole call stays on `stream` (no second stream); calls that overlap on
- *   one device -- on different streams or host threads, or graph replays
- *   running concurrently -- race on it and give undefined results.  Calls
- *   ordered on one stream are safe; each call rewrites what it reads.
+ *   whole call stays on `stream`; calls that overlap on one device -- on
+ *   different streams or host threads, or graph replays running
+ *   concurrently -- race on it and give undefined results.  Calls ordered on
+ *   one stream are safe; each call rewrites what it reads.
  */
 #define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 

@@ -263,7 +263,7 @@ int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, cons
                 const void* v, gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                 int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
                 int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-                const void* beta, int64_t beta_row_stride, void* state_pool,
+                const void* beta, bool beta_raw, int64_t beta_row_stride, void* state_pool,
                 int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                 int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
                 const NormIn* norm, uint32_t flags, hipStream_t stream) {
@@ -276,7 +276,7 @@ int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, cons
   if (out_dt != GDN_F32 && out_dt != in_dt)
     return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
   const uint32_t known = GDN_L2NORM_QK | GDN_CHECK_SLOTS | GDN_STATE_F16 | GDN_STATE_BF16 |
-                         GDN_BETA_RAW | (norm ? (uint32_t)GDN_NORM_SIGMOID : 0u);
+                         (norm ? (uint32_t)GDN_NORM_SIGMOID : 0u);
   if (flags & ~known) return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
   if (norm) {
     if (!(norm->eps >= 0.0f) || !isfinite(norm->eps))
@@ -304,7 +304,7 @@ int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, cons
     return fail(GDN_ERR_SHAPE, "%s: v/alpha/beta row stride below its row width", op);
   if (!aligned(state_pool, 16)) return fail(GDN_ERR_ARG, "%s: state pool must be 16-byte aligned", op);
   if (!aligned(alpha, (size_t)elem_bytes(alpha_dt)) ||
-      !aligned(beta, (flags & GDN_BETA_RAW) ? (size_t)elem_bytes(alpha_dt) : 4))
+      !aligned(beta, beta_raw ? (size_t)elem_bytes(alpha_dt) : 4))
     return fail(GDN_ERR_ARG, "%s: alpha/beta must be aligned to their element size", op);
   if (batch * hv > ((int64_t)1 << 40)) return fail(GDN_ERR_SHAPE, "%s: batch*hv too large", op);
   if (flags & GDN_CHECK_SLOTS) {
@@ -318,7 +318,7 @@ int decode_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, cons
   a.qk_vec = qk_vector_ok(q, k, in_dt, q_row_stride, k_row_stride) ? 1 : 0;
   a.alpha = alpha; a.alpha_dt = alpha_dt; a.alpha_rs = alpha_row_stride;
   a.dt_bias = dt_bias; a.ssm_a = ssm_a; a.beta = beta; a.beta_rs = beta_row_stride;
-  a.beta_raw = (flags & GDN_BETA_RAW) ? 1 : 0;
+  a.beta_raw = beta_raw ? 1 : 0;
   a.pool = state_pool; a.state_dt = state_dt; a.num_slots = num_slots; a.idx = state_idx;
   a.batch = batch;
   a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
@@ -338,21 +338,35 @@ int gdn_decode(void* out, gdn_dtype out_dt, const void* q, const void* k, const 
                gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                int64_t v_row_stride, const void* alpha, gdn_dtype alpha_dt,
                int64_t alpha_row_stride, const float* dt_bias, const float* ssm_a,
-               const void* beta, int64_t beta_row_stride, void* state_pool,
+               const float* beta, int64_t beta_row_stride, void* state_pool,
                int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
                int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
                hipStream_t stream) {
   return decode_impl("gdn_decode", out, out_dt, q, k, v, in_dt, q_row_stride, k_row_stride,
                      v_row_stride, alpha, alpha_dt, alpha_row_stride, dt_bias, ssm_a, beta,
-                     beta_row_stride, state_pool, num_slots, state_idx, batch, hk, hv, dk, dv,
-                     scale, l2_eps, nullptr, flags, stream);
+                     false, beta_row_stride, state_pool, num_slots, state_idx, batch, hk, hv,
+                     dk, dv, scale, l2_eps, nullptr, flags, stream);
+}
+
+int gdn_decode_packed(void* out, gdn_dtype out_dt, const void* q, const void* k, const void* v,
+                      gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
+                      int64_t v_row_stride, const void* a_raw, const void* b_raw,
+                      gdn_dtype ab_dt, int64_t a_row_stride, int64_t b_row_stride,
+                      const float* dt_bias, const float* ssm_a, void* state_pool,
+                      int64_t num_slots, const int32_t* state_idx, int64_t batch, int64_t hk,
+                      int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps,
+                      uint32_t flags, hipStream_t stream) {
+  return decode_impl("gdn_decode_packed", out, out_dt, q, k, v, in_dt, q_row_stride,
+                     k_row_stride, v_row_stride, a_raw, ab_dt, a_row_stride, dt_bias, ssm_a,
+                     b_raw, true, b_row_stride, state_pool, num_slots, state_idx, batch, hk, hv,
+                     dk, dv, scale, l2_eps, nullptr, flags, stream);
 }
 
 int gdn_decode_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void* k,
                           const void* v, gdn_dtype in_dt, int64_t q_row_stride,
                           int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
                           gdn_dtype alpha_dt, int64_t alpha_row_stride, const float* dt_bias,
-                          const float* ssm_a, const void* beta, int64_t beta_row_stride,
+                          const float* ssm_a, const float* beta, int64_t beta_row_stride,
                           void* state_pool, int64_t num_slots, const int32_t* state_idx,
                           int64_t batch, int64_t hk, int64_t hv, int64_t dk, int64_t dv,
                           float scale, float l2_eps, const void* norm_z,
@@ -361,8 +375,8 @@ int gdn_decode_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void
   const NormIn n{norm_z, norm_z_row_stride, norm_w, norm_eps};
   return decode_impl("gdn_decode_gated_norm", out, out_dt, q, k, v, in_dt, q_row_stride,
                      k_row_stride, v_row_stride, alpha, alpha_dt, alpha_row_stride, dt_bias,
-                     ssm_a, beta, beta_row_stride, state_pool, num_slots, state_idx, batch, hk,
-                     hv, dk, dv, scale, l2_eps, &n, flags, stream);
+                     ssm_a, beta, false, beta_row_stride, state_pool, num_slots, state_idx,
+                     batch, hk, hv, dk, dv, scale, l2_eps, &n, flags, stream);
 }
 
 int gdn_rmsnorm_gated(void* out, gdn_dtype out_dt, const void* x, gdn_dtype x_dt,
@@ -499,9 +513,10 @@ size_t gdn_prefill_varlen_workspace_size(int64_t total_tokens, int64_t num_seqs,
 
 namespace {
 
-// gdn_prefill_varlen and its allocation-free variant (which passes the
-// library's per-device scratch as the workspace and keeps the call on one
-// stream).
+// gdn_prefill_varlen, its variant with the caller's second stream (aux, for
+// the split schedule; null: the caller's stream alone) and its
+// allocation-free variant (which passes the library's per-device scratch as
+// the workspace).
 int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, const void* k,
                  const void* v, gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
                  int64_t v_row_stride, const float* g, int64_t g_row_stride, const float* beta,
@@ -509,7 +524,7 @@ int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, con
                  const int32_t* state_idx, const int8_t* has_initial_state,
                  const int32_t* cu_seqlens, int64_t num_seqs, int64_t total_tokens, int64_t hk,
                  int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream, bool no_split) {
+                 void* workspace, size_t workspace_bytes, hipStream_t stream, hipStream_t aux) {
   int rc;
   if (num_seqs < 0 || total_tokens < 0 || num_slots < 0)
     return fail(GDN_ERR_SHAPE, "%s: negative size", op);
@@ -560,7 +575,6 @@ int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, con
   a.total_tokens = total_tokens;
   a.hk = (int)hk; a.hv = (int)hv; a.dk = (int)dk; a.dv = (int)dv;
   a.scale = scale; a.l2_eps = l2_eps; a.l2norm = (flags & GDN_L2NORM_QK) ? 1 : 0;
-  a.no_split = no_split ? 1 : 0;
   if (use_chunked(hk, hv, dk, dv, in_dt, out_dt, flags) && total_tokens > 0 &&
       gdn::chunked_layout_ok(q, k, v, q_row_stride, k_row_stride, v_row_stride)) {
     const size_t need = gdn::chunked_workspace_bytes(total_tokens, num_seqs, (int)hv, (int)dk,
@@ -570,7 +584,7 @@ int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, con
                   workspace_bytes);
     if (need > 0 && !aligned(workspace, 256))
       return fail(GDN_ERR_ARG, "%s: workspace must be 256-byte aligned", op);
-    return hip_status(op, gdn::launch_prefill_chunked(a, workspace, workspace_bytes, stream));
+    return hip_status(op, gdn::launch_prefill_chunked(a, workspace, workspace_bytes, stream, aux));
   }
   return hip_status(op, gdn::launch_prefill_sequential(a, stream));
 }
@@ -624,7 +638,24 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
                       k_row_stride, v_row_stride, g, g_row_stride, beta, beta_row_stride,
                       state_pool, num_slots, state_idx, has_initial_state, cu_seqlens, num_seqs,
                       total_tokens, hk, hv, dk, dv, scale, l2_eps, flags, workspace,
-                      workspace_bytes, stream, false);
+                      workspace_bytes, stream, nullptr);
+}
+
+int gdn_prefill_varlen_aux(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                           const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                           int64_t k_row_stride, int64_t v_row_stride, const float* g,
+                           int64_t g_row_stride, const float* beta, int64_t beta_row_stride,
+                           void* state_pool, int64_t num_slots, const int32_t* state_idx,
+                           const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                           int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                           int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipStream_t aux_stream) {
+  return prefill_impl("gdn_prefill_varlen_aux", out, out_dt, q, k, v, in_dt, q_row_stride,
+                      k_row_stride, v_row_stride, g, g_row_stride, beta, beta_row_stride,
+                      state_pool, num_slots, state_idx, has_initial_state, cu_seqlens, num_seqs,
+                      total_tokens, hk, hv, dk, dv, scale, l2_eps, flags, workspace,
+                      workspace_bytes, stream, aux_stream);
 }
 
 int gdn_prefill_varlen_noalloc(void* out, gdn_dtype out_dt, const void* q, const void* k,
@@ -651,7 +682,7 @@ int gdn_prefill_varlen_noalloc(void* out, gdn_dtype out_dt, const void* q, const
                       v_row_stride, g, g_row_stride, beta, beta_row_stride, state_pool,
                       num_slots, state_idx, has_initial_state, cu_seqlens, num_seqs,
                       total_tokens, hk, hv, dk, dv, scale, l2_eps, flags, ws,
-                      ws ? (size_t)GDN_NOALLOC_SCRATCH_BYTES : 0, stream, true);
+                      ws ? (size_t)GDN_NOALLOC_SCRATCH_BYTES : 0, stream, nullptr);
 }
 
 }  // extern "C"

@@ -41,7 +41,6 @@
 // when a head's gate is thousands per chunk.
 #include <algorithm>
 #include <atomic>
-#include <mutex>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -1617,38 +1616,44 @@ size_t seg_bytes(int64_t total_tokens, int64_t num_seqs, int hv, int dv) {
 }
 
 
-// Per device: the CU count, and a second stream with two events for the split
-// schedule (created on first use, kept for the life of the process).
-struct SplitRes {
-  bool tried = false, ok = false;
-  int ncu = 0;
-  hipStream_t aux = nullptr;
-  hipEvent_t records_early = nullptr, rest_done = nullptr;
-};
 constexpr int kMaxDevices = 64;
-SplitRes g_split[kMaxDevices];
-std::mutex g_split_mu;
 
-// Returns the device's resources, or nullptr when the split schedule is unavailable.
-SplitRes* split_res(int dev) {
-  if (dev < 0 || dev >= kMaxDevices) return nullptr;
-  SplitRes& r = g_split[dev];
-  if (!r.tried) {
-    r.tried = true;
-    int ncu = 0;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        ncu <= 0)
-      return nullptr;
-    r.ncu = ncu;
-    r.ok = hipStreamCreateWithFlags(&r.aux, hipStreamNonBlocking) == hipSuccess &&
-           hipEventCreateWithFlags(&r.records_early, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&r.rest_done, hipEventDisableTiming) == hipSuccess;
+// The CU count of a device (asked once; racing first calls store the same value).
+int device_cus(int dev) {
+  static std::atomic<int> cus[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return 256;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return r.ok ? &r : nullptr;
+  return n;
+}
+
+// The fork and join events of the split schedule: two per host thread and
+// device, created on the thread's first split call on that device and kept
+// for the life of the process (a wait takes the event as it was recorded when
+// the wait was enqueued, so later calls on the thread may record it again).
+struct SplitEvents {
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+thread_local SplitEvents t_split_events[kMaxDevices];
+
+const SplitEvents* split_events(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  SplitEvents& e = t_split_events[dev];
+  if (!e.fork && hipEventCreateWithFlags(&e.fork, hipEventDisableTiming) != hipSuccess)
+    e.fork = nullptr;
+  if (!e.join && hipEventCreateWithFlags(&e.join, hipEventDisableTiming) != hipSuccess)
+    e.join = nullptr;
+  return e.fork && e.join ? &e : nullptr;
 }
 
 template <int TIN>
-hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) {
+hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream,
+                            hipStream_t aux) {
   // workspace: metadata, the split sequences' states, the per-chunk records
   const MetaPtrs m = meta_ptrs(ws, a.num_seqs);
   float* segws = reinterpret_cast<float*>(static_cast<char*>(ws) + meta_bytes(a.num_seqs));
@@ -1661,26 +1666,27 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   const int ksmax = sb.ranks, smax = sb.smax;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-  // The split schedule needs its second stream on the caller's stream's
-  // device (the current one), and is not used while the caller's stream is
-  // being captured; the early walk may take at most half of the CUs, so the
-  // records of the other ranks always have room.
-  bool can_split = !a.no_split && a.num_seqs >= 2 && a.num_seqs <= kOrderMax;
+  // The split schedule runs part of the call on the caller's second stream
+  // `aux`, which must be on the caller's stream's device (the current one);
+  // it is not used while the caller's stream is being captured.  The early
+  // walk may take at most half of the CUs, so the records of the other ranks
+  // always have room.
+  bool can_split = aux != nullptr && aux != stream && a.num_seqs >= 2 &&
+                   a.num_seqs <= kOrderMax;
   if (can_split) {
-    hipDevice_t sdev = -1;
+    hipDevice_t sdev = -1, adev = -1;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     can_split = hipStreamGetDevice(stream, &sdev) == hipSuccess && sdev == dev &&
+                hipStreamGetDevice(aux, &adev) == hipSuccess && adev == dev &&
                 hipStreamIsCapturing(stream, &cap) == hipSuccess &&
                 cap == hipStreamCaptureStatusNone;
   }
-  std::unique_lock<std::mutex> lock(g_split_mu);
-  SplitRes* sr = split_res(dev);
-  int ncu = sr ? sr->ncu : 256;
+  const int ncu = device_cus(dev);
+  const SplitEvents* ev = can_split ? split_events(dev) : nullptr;
   int kmax = 0;
-  if (sr && can_split)
+  if (ev)
     kmax = (int)std::min<int64_t>({(int64_t)kSplitMax, a.num_seqs - 1,
                                    (int64_t)(ncu / 2 / per_seq_wgs)});
-  if (kmax == 0) lock.unlock();
 
   hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, m, ntiles, ncu, kmax,
                      ksmax, smax);
@@ -1739,21 +1745,21 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream) 
   // empty and runs everything as part 1):
   //   caller's stream: meta, records of ranks [0, k), the first phase of the
   //                    split ranks among them, their walks
-  //   second stream:   (after those records) the other records, their walks
+  //   aux stream:      (after those records) the other records, their walks
   // and the caller's stream then waits for the second.  The early walks are
   // queued right behind their records on the caller's stream, so they take
   // their CUs before the other records fill the device.
   prep(0, stream);
-  if ((e = hipEventRecord(sr->records_early, stream)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ev->fork, stream)) != hipSuccess) return e;
   if (a_items > 0 && (e = walk(0, a_items, stream, false)) != hipSuccess) return e;
   // the early part: at most kmax ranks, or all of them when there are few
   const int64_t early = a.num_seqs <= kSplitMax ? a.num_seqs : kmax;
   if ((e = walk(0, early + seg_items, stream, true)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(sr->aux, sr->records_early, 0)) != hipSuccess) return e;
-  prep(1, sr->aux);
-  if ((e = walk(1, a.num_seqs, sr->aux, true)) != hipSuccess) return e;
-  if ((e = hipEventRecord(sr->rest_done, sr->aux)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(stream, sr->rest_done, 0)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(aux, ev->fork, 0)) != hipSuccess) return e;
+  prep(1, aux);
+  if ((e = walk(1, a.num_seqs, aux, true)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ev->join, aux)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(stream, ev->join, 0)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
@@ -1782,13 +1788,13 @@ size_t chunked_workspace_bytes(int64_t total_tokens, int64_t num_seqs, int hv, i
 }
 
 hipError_t launch_prefill_chunked(const PrefillArgs& a, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, hipStream_t aux) {
   if (ws_bytes < chunked_workspace_bytes(a.total_tokens, a.num_seqs, a.hv, a.dk, a.dv))
     return hipErrorInvalidValue;
   if (a.num_seqs >= (1 << 30) || max_chunks(a.total_tokens, a.num_seqs) >= (1 << 30))
     return hipErrorInvalidValue;
-  if (a.in_dt == kBF16) return launch_chunked_t<kBF16>(a, ws, stream);
-  if (a.in_dt == kF16) return launch_chunked_t<kF16>(a, ws, stream);
+  if (a.in_dt == kBF16) return launch_chunked_t<kBF16>(a, ws, stream, aux);
+  if (a.in_dt == kF16) return launch_chunked_t<kF16>(a, ws, stream, aux);
   return hipErrorInvalidValue;
 }
 

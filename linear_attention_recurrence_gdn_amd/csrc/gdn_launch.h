@@ -135,7 +135,6 @@ struct PrefillArgs {
   int hk, hv, dk, dv;
   float scale, l2_eps;
   int l2norm;
-  int no_split;   // keep the whole chunked call on `stream` (no second stream)
 };
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
@@ -157,7 +156,8 @@ bool chunked_supported(int in_dt, int out_dt, int64_t hv, int dk, int dv);
 bool chunked_layout_ok(const void* q, const void* k, const void* v, int64_t q_rs, int64_t k_rs,
                        int64_t v_rs);
 size_t chunked_workspace_bytes(int64_t total_tokens, int64_t num_seqs, int hv, int dk, int dv);
+// `aux` (may be null): the caller's second stream for the split schedule.
 hipError_t launch_prefill_chunked(const PrefillArgs& a, void* ws, size_t ws_bytes,
-                                  hipStream_t stream);
+                                  hipStream_t stream, hipStream_t aux);
 
 }  // namespace gdn

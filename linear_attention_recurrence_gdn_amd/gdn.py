@@ -24,17 +24,17 @@ GDN_PREFILL_SEQUENTIAL = 1 << 2
 GDN_STATE_F16 = 1 << 3
 GDN_STATE_BF16 = 1 << 4
 GDN_NORM_SIGMOID = 1 << 5
-GDN_BETA_RAW = 1 << 6
 GDN_BETA_ROUNDED = 1 << 7
 GDN_CONV_SILU = 1 << 8
 _STATE_FLAGS = {torch.float32: 0, torch.float16: GDN_STATE_F16, torch.bfloat16: GDN_STATE_BF16}
 
 _TORCH_DT = {torch.float32: GDN_F32, torch.float16: GDN_F16, torch.bfloat16: GDN_BF16}
 
-EXPORTS = ("gdn_conv1d_fwd", "gdn_conv1d_update", "gdn_gate", "gdn_gate_beta", "gdn_post_conv", "gdn_decode", "gdn_decode_gated_norm",
+EXPORTS = ("gdn_conv1d_fwd", "gdn_conv1d_update", "gdn_gate", "gdn_gate_beta", "gdn_post_conv",
+           "gdn_decode", "gdn_decode_packed", "gdn_decode_gated_norm",
            "gdn_rmsnorm_gated",
-           "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_noalloc",
-           "gdn_last_error")
+           "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_aux",
+           "gdn_prefill_varlen_noalloc", "gdn_last_error")
 
 
 class GdnError(RuntimeError):
@@ -63,6 +63,10 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_decode.restype = i32
     lib.gdn_decode.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i32, i64, vp, vp,
                                vp, i64, vp, i64, vp, i64, i64, i64, i64, i64, f32, f32, u32, vp]
+    lib.gdn_decode_packed.restype = i32
+    lib.gdn_decode_packed.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, vp, i32,
+                                      i64, i64, vp, vp, vp, i64, vp, i64, i64, i64, i64, i64,
+                                      f32, f32, u32, vp]
     lib.gdn_conv1d_fwd.restype = i32
     lib.gdn_conv1d_fwd.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp, i64, i64, vp, vp, vp, i64,
                                    i64, i64, i64, u32, vp]
@@ -87,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_prefill_varlen.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp, i64, vp,
                                        i64, vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                        f32, f32, u32, vp, sz, vp]
+    lib.gdn_prefill_varlen_aux.restype = i32
+    lib.gdn_prefill_varlen_aux.argtypes = lib.gdn_prefill_varlen.argtypes + [vp]
     lib.gdn_prefill_varlen_noalloc.restype = i32
     lib.gdn_prefill_varlen_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp,
                                                i64, vp, i64, vp, i64, vp, vp, vp, i64, i64,
@@ -187,9 +193,9 @@ def decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scale
     state_pool [slots, Hv, Dv, Dk] contiguous, f32 or 16-bit storage (float16 /
     bfloat16: widened to f32 for the step, the new state rounded on store);
     state_idx [B] int32.  check_slots: validate state_idx first (GDN_CHECK_SLOTS:
-    reads it back and waits on the stream; not capturable).  beta_raw: beta is
-    the raw projection b in alpha's dtype (GDN_BETA_RAW: sigmoid(b) rounded
-    through that dtype)."""
+    reads it back and waits on the stream; not capturable).  beta_raw: alpha
+    and beta are the raw projections a and b in one dtype (gdn_decode_packed:
+    beta = sigmoid(b) rounded through that dtype)."""
     return _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, scale=scale,
                    l2norm=l2norm, l2_eps=l2_eps, out=out, out_dtype=out_dtype,
                    check_slots=check_slots, beta_raw=beta_raw, stream=stream, norm=None)
@@ -234,14 +240,23 @@ def _decode(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, state_idx, *, scal
     if not out.is_contiguous() or tuple(out.shape) != (B, hv, dv):
         raise GdnError(-3, "out: need contiguous [B, Hv, Dv]")
     flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_CHECK_SLOTS if check_slots else 0) |
-             (GDN_BETA_RAW if beta_raw else 0) | _state_flags(state_pool))
-    args = [_dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
-            q_rs, k_rs, v_rs, _dev(alpha, "alpha"), _dt(alpha), a_rs,
-            _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
-            _dev(beta, "beta", alpha.dtype if beta_raw else torch.float32), b_rs,
-            _dev(state_pool, "state_pool"),
-            slots, _dev(state_idx, "state_idx", torch.int32), B, hk, hv, dk, dv, float(scale),
-            float(l2_eps)]
+             _state_flags(state_pool))
+    head = [_dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
+            q_rs, k_rs, v_rs]
+    tail = [_dev(state_pool, "state_pool"), slots, _dev(state_idx, "state_idx", torch.int32),
+            B, hk, hv, dk, dv, float(scale), float(l2_eps)]
+    if beta_raw:
+        if norm is not None:
+            raise GdnError(-1, "the fused norm takes post-sigmoid beta")
+        _check(lib.gdn_decode_packed(*head, _dev(alpha, "a"), _dev(beta, "b", alpha.dtype),
+                                     _dt(alpha), a_rs, b_rs,
+                                     _dev(dt_bias, "dt_bias", torch.float32),
+                                     _dev(ssm_a, "ssm_a", torch.float32), *tail, flags,
+                                     _stream(stream)))
+        return out
+    args = head + [_dev(alpha, "alpha"), _dt(alpha), a_rs,
+                   _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
+                   _dev(beta, "beta", torch.float32), b_rs] + tail
     if norm is None:
         _check(lib.gdn_decode(*args, flags, _stream(stream)))
         return out
@@ -441,13 +456,15 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
                    has_initial_state: Optional[torch.Tensor] = None, l2norm: bool = True,
                    l2_eps: float = 1e-6, out: Optional[torch.Tensor] = None, out_dtype=None,
                    sequential: bool = False, workspace: Optional[torch.Tensor] = None,
-                   check_slots: bool = False, stream=None) -> torch.Tensor:
+                   check_slots: bool = False, stream=None, aux_stream=None) -> torch.Tensor:
     """Varlen prefill over sequences packed back to back (cu_seqlens [N+1] int32).
 
     q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; g, beta: [T, Hv] f32; state_pool
     [slots, Hv, Dv, Dk] f32, float16 or bfloat16 (initial states read, final
     states written).  check_slots: validate cu_seqlens and state_idx first
-    (GDN_CHECK_SLOTS: reads them back and waits on the stream)."""
+    (GDN_CHECK_SLOTS: reads them back and waits on the stream).  aux_stream:
+    a second stream of the caller's for the split schedule
+    (gdn_prefill_varlen_aux); without it the call runs on `stream` alone."""
     lib = load_library()
     out, args, ws_key = _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale,
                                       state_idx, has_initial_state, l2norm, l2_eps, out,
@@ -457,7 +474,11 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
         workspace = _new((ws_need,), torch.uint8, q.device, stream)
     ws_ptr = _dev(workspace, "workspace") if ws_need else None
     ws_bytes = workspace.numel() * workspace.element_size() if ws_need else 0
-    _check(lib.gdn_prefill_varlen(*args, ws_ptr, ws_bytes, _stream(stream)))
+    if aux_stream is not None:
+        _check(lib.gdn_prefill_varlen_aux(*args, ws_ptr, ws_bytes, _stream(stream),
+                                          aux_stream.cuda_stream))
+    else:
+        _check(lib.gdn_prefill_varlen(*args, ws_ptr, ws_bytes, _stream(stream)))
     return out
 
 

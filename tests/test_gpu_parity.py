@@ -330,10 +330,10 @@ def test_prefill_varlen_gqa3_all_heads(dev):
 def test_prefill_skewed_batch_split_schedule(dev):
     """One 8192-token sequence beside seven of 2048 (GQA 3, fp16): the longest
     sequence bounds the call, so the chunked path walks it as soon as its own
-    records exist while the others' records and walks run beside it on a
-    second stream.  The split rank is read back from the metadata the call
-    leaves in the workspace (int32 words cs[n+1], order[n], ocs[n+1], then
-    the split rank)."""
+    records exist while the others' records and walks run beside it on the
+    caller's second stream (gdn_prefill_varlen_aux).  The split rank is read
+    back from the metadata the call leaves in the workspace (int32 words
+    cs[n+1], order[n], ocs[n+1], then the split rank)."""
     announce("prefill skewed batch [8192, 7 x 2048] Hk8 Hv24 fp16: split schedule, every head")
     lengths = [8192] + [2048] * 7
     case = W.make_prefill_case("skew", 4242, lengths=lengths, hk=8, hv=24, dk=128, dv=128,
@@ -347,9 +347,10 @@ def test_prefill_skewed_batch_split_schedule(dev):
     pool0 = pool.clone()
     ws_n = gdn.prefill_workspace_size(T, N, case.hk, case.hv, case.dk, case.dv, torch.float16)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    aux = torch.cuda.Stream()
     out = gdn.prefill_varlen(q, k, v, g, t(case.beta), pool, t(case.cu_seqlens),
                              scale=case.scale, state_idx=t(case.idx),
-                             has_initial_state=t(case.has_init), workspace=ws)
+                             has_initial_state=t(case.has_init), workspace=ws, aux_stream=aux)
     torch.cuda.synchronize()
     words = ws[:4 * (3 * N + 5)].view(torch.int32).cpu().numpy()
     split_rank, split_seqs, segments = (int(x) for x in words[3 * N + 2:3 * N + 5])
@@ -522,3 +523,59 @@ def test_prefill_on_a_side_stream_then_reallocate(dev):
     want_out, want_state = oracle.prefill_case(case)
     res = H.PrefillResult(H.out_to_f64(out), pool, None, True)
     H.check_prefill(case, res, want_out, want_state)
+
+
+def test_prefill_calls_on_two_streams_run_concurrently(dev):
+    """Two prefill calls on two streams, each with its own second stream for
+    the split schedule, enqueued back to back with no synchronisation between
+    them: outputs and final states byte-equal to the same calls run one after
+    the other (the library shares no stream, event or lock between calls)."""
+    announce("prefill: two calls on two streams concurrently vs one after the other")
+    cases = [W.make_prefill_case("c2a", 6071, lengths=[3000, 200, 700, 50], hk=2, hv=6, dk=128,
+                                 dv=128, in_dtype=W.BF16, out_dtype=W.BF16, slots=6),
+             W.make_prefill_case("c2b", 6072, lengths=[90, 2500, 1300], hk=1, hv=3, dk=128,
+                                 dv=128, in_dtype=W.F16, out_dtype=W.F16, slots=5)]
+    t = lambda a: torch.from_numpy(a).to(dev)
+    inputs = []
+    for case in cases:
+        _, q, k, v = H.upload_views(case, dev, case.total_tokens)
+        g = gdn.gate(t(case.alpha), t(case.dt_bias), t(case.ssm_a))
+        ws = torch.empty(gdn.prefill_workspace_size(case.total_tokens, case.num_seqs, case.hk,
+                                                    case.hv, case.dk, case.dv,
+                                                    H.TORCH_OF[case.in_dtype]),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty((case.total_tokens, case.hv, case.dv),
+                          dtype=H.TORCH_OF[case.out_dtype], device=dev)
+        inputs.append((case, q, k, v, g, t(case.beta), t(case.cu_seqlens), t(case.idx),
+                       t(case.pool), ws, out))
+    torch.cuda.synchronize()
+
+    def call(inp, pool, stream, aux):
+        case, q, k, v, g, beta, cu, idx, _, ws, out = inp
+        gdn.prefill_varlen(q, k, v, g, beta, pool, cu, scale=case.scale, state_idx=idx,
+                           out=out, workspace=ws, stream=stream, aux_stream=aux)
+
+    # one after the other on the current stream (each with a second stream)
+    seq = []
+    for inp in inputs:
+        pool = inp[8].clone()
+        call(inp, pool, torch.cuda.current_stream(), torch.cuda.Stream())
+        torch.cuda.synchronize()
+        seq.append((inp[10].clone(), pool))
+    # concurrently
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    pools = [inp[8].clone() for inp in inputs]
+    for inp in inputs:
+        inp[10].zero_()
+    torch.cuda.synchronize()
+    for i, inp in enumerate(inputs):
+        streams[2 * i].wait_stream(torch.cuda.current_stream())
+        call(inp, pools[i], streams[2 * i], streams[2 * i + 1])
+    torch.cuda.synchronize()
+    for i, inp in enumerate(inputs):
+        assert H.bytes_equal(inp[10], seq[i][0]), f"call {i}: outputs differ"
+        assert H.bytes_equal(pools[i], seq[i][1]), f"call {i}: states differ"
+    for i, inp in enumerate(inputs):
+        want_out, want_state = oracle.prefill_case(inp[0])
+        H.check_prefill(inp[0], H.PrefillResult(H.out_to_f64(seq[i][0]), seq[i][1], None, True),
+                        want_out, want_state)
