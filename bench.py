@@ -91,17 +91,16 @@ def measured_traffic():
 
 
 def prefill_bytes(T, N, hk, hv, dk, dv, in_bytes, out_bytes, n_init=None):
-    """Algorithmic HBM bytes of gate + varlen prefill: q/k/v read once, out
-    written once, alpha read and g written by the gate, g and beta read by the
-    recurrence, the initial state of each of the n_init sequences that have
-    one read once and every final state written once."""
+    """Algorithmic HBM bytes of the varlen prefill with the gate fused: q/k/v
+    read once, out written once, alpha (f32) and beta read once per (token,
+    v-head), the initial state of each of the n_init sequences that have one
+    read once and every final state written once."""
     n_init = N if n_init is None else n_init
     qkv = T * (2 * hk * dk + hv * dv) * in_bytes
     out = T * hv * dv * out_bytes
-    gate = T * hv * 4 * 2          # alpha read, g written
-    gb = T * hv * 4 * 2            # g and beta read
+    gate = T * hv * 4 * 2          # alpha and beta read
     state = (n_init + N) * hv * dv * dk * 4
-    return qkv + out + gate + gb + state
+    return qkv + out + gate + state
 
 
 def prefill_flops(T, hv, dk, dv, C=64):
@@ -422,16 +421,14 @@ def main():
         ppool = to_dev(pre.pool)
         pcu, pidx, phi = to_dev(pre.cu_seqlens), to_dev(pre.idx), to_dev(pre.has_init)
         pout = torch.empty((T, pre.hv, pre.dv), dtype=torch.float16, device=dev)
-        g = torch.empty((T, pre.hv), dtype=torch.float32, device=dev)
         ws_n = gdn.prefill_workspace_size(T, N, pre.hk, pre.hv, pre.dk, pre.dv, torch.float16)
         ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
         aux = torch.cuda.Stream()   # the second stream of the split schedule
 
         def prefill_step():
-            gdn.gate(pa, pdt, pssm, out=g, stream=stream)
-            gdn.prefill_varlen(qp, kp, vp, g, pbeta, ppool, pcu, scale=pre.scale,
-                               state_idx=pidx, has_initial_state=phi, out=pout,
-                               workspace=ws, stream=stream, aux_stream=aux)
+            gdn.prefill_varlen_gated(qp, kp, vp, pa, pdt, pssm, pbeta, ppool, pcu,
+                                     scale=pre.scale, state_idx=pidx, has_initial_state=phi,
+                                     out=pout, workspace=ws, stream=stream, aux_stream=aux)
 
         if want("prefill"):
             pwall, pms = timed(lambda i: prefill_step(), 8, args.prefill_steps)
@@ -443,7 +440,8 @@ def main():
             result["prefill"] = {
                 "workload": "varlen prefill, 8 sequences, lengths U(1,8192) summing to 32768, "
                             "Hk=8, Hv=24 (GQA 3), D=128, fp16 q/k/v/out, fp32 states from a "
-                            "64-slot pool; gate + recurrence",
+                            "64-slot pool; gate fused into the recurrence "
+                            "(gdn_prefill_varlen_gated)",
                 "lengths": pre.meta["lengths"],
                 "tokens_per_s": round(T / (p_ms_step * 1e-3), 1),
                 "ms_per_step": round(p_ms_step, 4),
@@ -470,16 +468,15 @@ def main():
             pool3 = to_dev(p3.pool)
             cu3, idx3, hi3 = to_dev(p3.cu_seqlens), to_dev(p3.idx), to_dev(p3.has_init)
             out3 = torch.empty((T3, p3.hv, p3.dv), dtype=torch.bfloat16, device=dev)
-            g3 = torch.empty((T3, p3.hv), dtype=torch.float32, device=dev)
             ws3_n = gdn.prefill_workspace_size(T3, 1, p3.hk, p3.hv, p3.dk, p3.dv,
                                                torch.bfloat16)
             ws3 = torch.empty(max(ws3_n, 1), dtype=torch.uint8, device=dev)
 
             def t4096_step(i):
-                gdn.gate(a3, dt3, sa3, out=g3, stream=stream)
-                gdn.prefill_varlen(q3, k3, v3, g3, b3, pool3, cu3, scale=p3.scale,
-                                   state_idx=idx3, has_initial_state=hi3, out=out3,
-                                   workspace=ws3, stream=stream, aux_stream=aux)
+                gdn.prefill_varlen_gated(q3, k3, v3, a3, dt3, sa3, b3, pool3, cu3,
+                                         scale=p3.scale, state_idx=idx3, has_initial_state=hi3,
+                                         out=out3, workspace=ws3, stream=stream,
+                                         aux_stream=aux)
 
             w3, k3ms = timed(t4096_step, 8, args.prefill_steps)
             ms3 = w3 * 1e3 / args.prefill_steps
@@ -489,7 +486,7 @@ def main():
             result["prefill_t4096"] = {
                 "workload": "single-sequence prefill T=4096, Hk=16, Hv=32, D=128, bf16 q/k/v/out, "
                             "zero initial state (slot never read), fp32 final state; "
-                            "gate + recurrence",
+                            "gate fused into the recurrence (gdn_prefill_varlen_gated)",
                 "tokens_per_s": round(T3 / (ms3 * 1e-3), 1),
                 "ms_per_step": round(ms3, 4),
                 "kernel_avg_ms": round(avg3, 4),

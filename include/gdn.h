@@ -71,7 +71,7 @@ enum {
   GDN_STATE_BF16 = 1u << 4,          /* state pool stored as bfloat16 */
   GDN_NORM_SIGMOID = 1u << 5,        /* gated norm: sigmoid gate instead of silu */
   /* 1u << 6 is not used */
-  GDN_BETA_ROUNDED = 1u << 7,        /* gate_beta/post_conv: round sigmoid(b) to b's dtype */
+  GDN_BETA_ROUNDED = 1u << 7,        /* gate_beta/post_conv/prefill_packed: round sigmoid(b) to b's dtype */
   GDN_CONV_SILU = 1u << 8            /* conv1d: silu activation (else identity) */
 };
 /*
@@ -408,6 +408,59 @@ int gdn_prefill_varlen_aux(void* out, gdn_dtype out_dt, const void* q, const voi
                            int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
                            void* workspace, size_t workspace_bytes, hipStream_t stream,
                            hipStream_t aux_stream);
+
+/*
+ * gdn_prefill_varlen_gated -- gdn_prefill_varlen_aux with the gate fused, as
+ * gdn_decode fuses it: no g array; the kernels form
+ * g = softplus(alpha + dt_bias) * ssm_a for each (token, v-head) with the
+ * arithmetic of gdn_gate, so the result is bit-identical to gdn_gate followed
+ * by gdn_prefill_varlen_aux (Winery-Strata elementwise_parity.cpp, the
+ * gdn_gate block; vllm.cpp test_ops_gdn.cpp, GdnPrefill's inputs).
+ *   alpha      [total_tokens, hv] in alpha_dt (f32, f16 or bf16), row stride
+ *              alpha_row_stride (>= hv).   dt_bias, ssm_a  [hv] f32.
+ *   beta       [total_tokens, hv] f32 post-sigmoid, row stride beta_row_stride.
+ *   every other argument as for gdn_prefill_varlen_aux (aux_stream may be
+ *   NULL), the same workspace size.
+ */
+int gdn_prefill_varlen_gated(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                             const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                             int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
+                             gdn_dtype alpha_dt, int64_t alpha_row_stride, const float* dt_bias,
+                             const float* ssm_a, const float* beta, int64_t beta_row_stride,
+                             void* state_pool, int64_t num_slots, const int32_t* state_idx,
+                             const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                             int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                             int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             hipStream_t aux_stream);
+
+/*
+ * gdn_prefill_varlen_packed -- the prefill fed by the front-end's raw
+ * projections (vllm.cpp test_ops_gdn.cpp, "gdn_post_conv fused == composed"
+ * and the packed in_proj_ba case): q, k, v may be views into the conv output
+ * rows (q | k | v with its row stride; normalised in the kernels with
+ * GDN_L2NORM_QK), and g and beta are formed per (token, v-head) from the raw
+ * a and b: g = softplus(a + dt_bias) * ssm_a, beta = sigmoid(b) in f32, with
+ * GDN_BETA_ROUNDED rounded through ab_dt -- bit-identical to gdn_gate_beta
+ * (same flag) followed by gdn_prefill_varlen_aux.  Nothing but the outputs
+ * and final states is written: no q, k, v, g or beta array is formed.
+ *   a_raw, b_raw  [total_tokens, hv] in ab_dt with their own row strides
+ *              (>= hv): e.g. the a and b column views of one merged b|a row.
+ *   dt_bias, ssm_a  [hv] f32.
+ *   flags      as gdn_prefill_varlen, plus GDN_BETA_ROUNDED.
+ *   every other argument as for gdn_prefill_varlen_aux.
+ */
+int gdn_prefill_varlen_packed(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                              const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                              int64_t k_row_stride, int64_t v_row_stride, const void* a_raw,
+                              const void* b_raw, gdn_dtype ab_dt, int64_t a_row_stride,
+                              int64_t b_row_stride, const float* dt_bias, const float* ssm_a,
+                              void* state_pool, int64_t num_slots, const int32_t* state_idx,
+                              const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                              int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                              int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              hipStream_t aux_stream);
 
 /*
  * gdn_prefill_varlen_noalloc -- gdn_prefill_varlen with no workspace argument,

@@ -517,10 +517,25 @@ namespace {
 // the split schedule; null: the caller's stream alone) and its
 // allocation-free variant (which passes the library's per-device scratch as
 // the workspace).
+// Where a prefill takes g and beta from: g materialised (f32), or formed in
+// the kernels from alpha (alpha_dt) with dt_bias and ssm_a; beta as f32
+// post-sigmoid values, or (beta_raw) the raw b in alpha_dt.
+struct GateIn {
+  const float* g;
+  int64_t g_rs;
+  const void* alpha;
+  gdn_dtype alpha_dt;
+  int64_t alpha_rs;
+  const float* dt_bias;
+  const float* ssm_a;
+  const void* beta;
+  int64_t beta_rs;
+  bool beta_raw;
+};
+
 int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, const void* k,
                  const void* v, gdn_dtype in_dt, int64_t q_row_stride, int64_t k_row_stride,
-                 int64_t v_row_stride, const float* g, int64_t g_row_stride, const float* beta,
-                 int64_t beta_row_stride, void* state_pool, int64_t num_slots,
+                 int64_t v_row_stride, const GateIn& gt, void* state_pool, int64_t num_slots,
                  const int32_t* state_idx, const int8_t* has_initial_state,
                  const int32_t* cu_seqlens, int64_t num_seqs, int64_t total_tokens, int64_t hk,
                  int64_t hv, int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
@@ -534,8 +549,10 @@ int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, con
   if (out_dt != GDN_F32 && out_dt != in_dt)
     return fail(GDN_ERR_DTYPE, "%s: out dtype must be f32 or the input dtype", op);
   if (flags & ~(uint32_t)(GDN_L2NORM_QK | GDN_CHECK_SLOTS | GDN_PREFILL_SEQUENTIAL |
-                          GDN_STATE_F16 | GDN_STATE_BF16))
+                          GDN_STATE_F16 | GDN_STATE_BF16 |
+                          (gt.beta_raw ? (uint32_t)GDN_BETA_ROUNDED : 0u)))
     return fail(GDN_ERR_ARG, "%s: unknown flags 0x%x", op, flags);
+  if (gt.alpha && !valid_dt(gt.alpha_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
   const int state_dt = state_dtype(flags);
   if (state_dt < 0) return fail(GDN_ERR_DTYPE, "%s: GDN_STATE_F16 and GDN_STATE_BF16 both set", op);
   if (num_seqs == 0) return ok();
@@ -545,10 +562,14 @@ int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, con
                 (long long)num_slots);
   if (!aligned(state_pool, 16)) return fail(GDN_ERR_ARG, "%s: state pool must be 16-byte aligned", op);
   if (total_tokens > 0) {
-    if (!out || !q || !k || !v || !g || !beta) return fail(GDN_ERR_ARG, "%s: null pointer", op);
+    if (!out || !q || !k || !v || !gt.beta || (gt.alpha ? !gt.dt_bias || !gt.ssm_a : !gt.g))
+      return fail(GDN_ERR_ARG, "%s: null pointer", op);
     if ((rc = check_qk(op, q, k, in_dt, q_row_stride, k_row_stride, hk, dk))) return rc;
-    if (v_row_stride < hv * dv || g_row_stride < hv || beta_row_stride < hv)
-      return fail(GDN_ERR_SHAPE, "%s: v/g/beta row stride below its row width", op);
+    if (v_row_stride < hv * dv || (gt.alpha ? gt.alpha_rs : gt.g_rs) < hv || gt.beta_rs < hv)
+      return fail(GDN_ERR_SHAPE, "%s: v/gate/beta row stride below its row width", op);
+    const size_t ab = gt.alpha ? (size_t)elem_bytes(gt.alpha_dt) : 4;
+    if ((gt.alpha && !aligned(gt.alpha, ab)) || !aligned(gt.beta, gt.beta_raw ? ab : 4))
+      return fail(GDN_ERR_ARG, "%s: gate inputs must be aligned to their element size", op);
   }
   if (flags & GDN_CHECK_SLOTS) {
     std::vector<int32_t> h;
@@ -569,7 +590,10 @@ int prefill_impl(const char* op, void* out, gdn_dtype out_dt, const void* q, con
   a.out = out; a.out_dt = out_dt; a.q = q; a.k = k; a.v = v; a.in_dt = in_dt;
   a.q_rs = q_row_stride; a.k_rs = k_row_stride; a.v_rs = v_row_stride;
   a.qk_vec = qk_vector_ok(q, k, in_dt, q_row_stride, k_row_stride) ? 1 : 0;
-  a.g = g; a.g_rs = g_row_stride; a.beta = beta; a.beta_rs = beta_row_stride;
+  a.g = gt.g; a.g_rs = gt.g_rs; a.beta = gt.beta; a.beta_rs = gt.beta_rs;
+  a.alpha = gt.alpha; a.alpha_dt = gt.alpha_dt; a.alpha_rs = gt.alpha_rs;
+  a.dt_bias = gt.dt_bias; a.ssm_a = gt.ssm_a; a.beta_raw = gt.beta_raw ? 1 : 0;
+  a.round_beta = (flags & GDN_BETA_ROUNDED) ? 1 : 0;
   a.pool = state_pool; a.state_dt = state_dt; a.num_slots = num_slots; a.idx = state_idx;
   a.has_init = has_initial_state; a.cu = cu_seqlens; a.num_seqs = num_seqs;
   a.total_tokens = total_tokens;
@@ -634,11 +658,12 @@ int gdn_prefill_varlen(void* out, gdn_dtype out_dt, const void* q, const void* k
                        int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
                        int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const GateIn gt{g, g_row_stride, nullptr, GDN_F32, 0, nullptr, nullptr, beta, beta_row_stride,
+                  false};
   return prefill_impl("gdn_prefill_varlen", out, out_dt, q, k, v, in_dt, q_row_stride,
-                      k_row_stride, v_row_stride, g, g_row_stride, beta, beta_row_stride,
-                      state_pool, num_slots, state_idx, has_initial_state, cu_seqlens, num_seqs,
-                      total_tokens, hk, hv, dk, dv, scale, l2_eps, flags, workspace,
-                      workspace_bytes, stream, nullptr);
+                      k_row_stride, v_row_stride, gt, state_pool, num_slots, state_idx,
+                      has_initial_state, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv,
+                      scale, l2_eps, flags, workspace, workspace_bytes, stream, nullptr);
 }
 
 int gdn_prefill_varlen_aux(void* out, gdn_dtype out_dt, const void* q, const void* k,
@@ -651,11 +676,50 @@ int gdn_prefill_varlen_aux(void* out, gdn_dtype out_dt, const void* q, const voi
                            int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
                            void* workspace, size_t workspace_bytes, hipStream_t stream,
                            hipStream_t aux_stream) {
+  const GateIn gt{g, g_row_stride, nullptr, GDN_F32, 0, nullptr, nullptr, beta, beta_row_stride,
+                  false};
   return prefill_impl("gdn_prefill_varlen_aux", out, out_dt, q, k, v, in_dt, q_row_stride,
-                      k_row_stride, v_row_stride, g, g_row_stride, beta, beta_row_stride,
-                      state_pool, num_slots, state_idx, has_initial_state, cu_seqlens, num_seqs,
-                      total_tokens, hk, hv, dk, dv, scale, l2_eps, flags, workspace,
-                      workspace_bytes, stream, aux_stream);
+                      k_row_stride, v_row_stride, gt, state_pool, num_slots, state_idx,
+                      has_initial_state, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv,
+                      scale, l2_eps, flags, workspace, workspace_bytes, stream, aux_stream);
+}
+
+int gdn_prefill_varlen_gated(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                             const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                             int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
+                             gdn_dtype alpha_dt, int64_t alpha_row_stride, const float* dt_bias,
+                             const float* ssm_a, const float* beta, int64_t beta_row_stride,
+                             void* state_pool, int64_t num_slots, const int32_t* state_idx,
+                             const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                             int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                             int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             hipStream_t aux_stream) {
+  const GateIn gt{nullptr, 0, alpha, alpha_dt, alpha_row_stride, dt_bias, ssm_a, beta,
+                  beta_row_stride, false};
+  return prefill_impl("gdn_prefill_varlen_gated", out, out_dt, q, k, v, in_dt, q_row_stride,
+                      k_row_stride, v_row_stride, gt, state_pool, num_slots, state_idx,
+                      has_initial_state, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv,
+                      scale, l2_eps, flags, workspace, workspace_bytes, stream, aux_stream);
+}
+
+int gdn_prefill_varlen_packed(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                              const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                              int64_t k_row_stride, int64_t v_row_stride, const void* a_raw,
+                              const void* b_raw, gdn_dtype ab_dt, int64_t a_row_stride,
+                              int64_t b_row_stride, const float* dt_bias, const float* ssm_a,
+                              void* state_pool, int64_t num_slots, const int32_t* state_idx,
+                              const int8_t* has_initial_state, const int32_t* cu_seqlens,
+                              int64_t num_seqs, int64_t total_tokens, int64_t hk, int64_t hv,
+                              int64_t dk, int64_t dv, float scale, float l2_eps, uint32_t flags,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              hipStream_t aux_stream) {
+  const GateIn gt{nullptr, 0, a_raw, ab_dt, a_row_stride, dt_bias, ssm_a, b_raw, b_row_stride,
+                  true};
+  return prefill_impl("gdn_prefill_varlen_packed", out, out_dt, q, k, v, in_dt, q_row_stride,
+                      k_row_stride, v_row_stride, gt, state_pool, num_slots, state_idx,
+                      has_initial_state, cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv,
+                      scale, l2_eps, flags, workspace, workspace_bytes, stream, aux_stream);
 }
 
 int gdn_prefill_varlen_noalloc(void* out, gdn_dtype out_dt, const void* q, const void* k,
@@ -678,11 +742,12 @@ int gdn_prefill_varlen_noalloc(void* out, gdn_dtype out_dt, const void* q, const
                 op, need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
   if (need > 0 && !(ws = device_scratch(op))) return GDN_ERR_HIP;
+  const GateIn gt{g, g_row_stride, nullptr, GDN_F32, 0, nullptr, nullptr, beta, beta_row_stride,
+                  false};
   return prefill_impl(op, out, out_dt, q, k, v, in_dt, q_row_stride, k_row_stride,
-                      v_row_stride, g, g_row_stride, beta, beta_row_stride, state_pool,
-                      num_slots, state_idx, has_initial_state, cu_seqlens, num_seqs,
-                      total_tokens, hk, hv, dk, dv, scale, l2_eps, flags, ws,
-                      ws ? (size_t)GDN_NOALLOC_SCRATCH_BYTES : 0, stream, nullptr);
+                      v_row_stride, gt, state_pool, num_slots, state_idx, has_initial_state,
+                      cu_seqlens, num_seqs, total_tokens, hk, hv, dk, dv, scale, l2_eps, flags,
+                      ws, ws ? (size_t)GDN_NOALLOC_SCRATCH_BYTES : 0, stream, nullptr);
 }
 
 }  // extern "C"

@@ -44,6 +44,7 @@
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
+#include "gdn_prefill_gate.h"
 
 namespace gdn {
 namespace {
@@ -477,10 +478,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     const int jh = kPrepHeads * q + w;
     gv = 0.0f;
     bv = 0.0f;
-    if (jh < ratio && lane < L) {
-      gv = a.g[(tb + lane) * a.g_rs + hk * ratio + jh];
-      bv = a.beta[(tb + lane) * a.beta_rs + hk * ratio + jh];
-    }
+    if (jh < ratio && lane < L) token_gate(a, tb + lane, hk * ratio + jh, gv, bv);
   };
   load_gb(0);
 

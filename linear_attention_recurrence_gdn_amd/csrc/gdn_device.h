@@ -321,4 +321,11 @@ __device__ __forceinline__ float beta_from_raw(float b, bool round) {
   else return s;
 }
 
+// beta from the raw b, the storage format chosen at run time
+__device__ __forceinline__ float beta_from_raw_rt(float b, int dt, bool round) {
+  return dt == kBF16 ? beta_from_raw<kBF16>(b, round)
+         : dt == kF16 ? beta_from_raw<kF16>(b, round)
+                      : beta_from_raw<kF32>(b, round);
+}
+
 }  // namespace gdn

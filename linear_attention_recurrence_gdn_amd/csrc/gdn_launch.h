@@ -120,10 +120,19 @@ struct PrefillArgs {
   int in_dt;
   int64_t q_rs, k_rs, v_rs;
   int qk_vec;
-  const float* g;
+  const float* g;       // [T, hv] f32, or null: formed from alpha below
   int64_t g_rs;
-  const float* beta;
+  const void* beta;     // [T, hv] f32 post-sigmoid, or (beta_raw) the raw b in alpha_dt
   int64_t beta_rs;
+  // the gate fused (alpha != null): g = softplus(alpha + dt_bias) * ssm_a per
+  // (token, v-head), exactly as gate_kernel forms it
+  const void* alpha;
+  int alpha_dt;
+  int64_t alpha_rs;
+  const float* dt_bias;
+  const float* ssm_a;
+  int beta_raw;         // beta = sigmoid(b) of the raw b (in alpha_dt) ...
+  int round_beta;       // ... rounded through alpha_dt
   void* pool;     // [slots, hv, dv, dk] in state_dt
   int state_dt;
   int64_t num_slots;

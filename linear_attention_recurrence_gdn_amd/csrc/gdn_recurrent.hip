@@ -28,6 +28,7 @@
 //   - waves are independent: no LDS and no barriers.
 #include "gdn_device.h"
 #include "gdn_launch.h"
+#include "gdn_prefill_gate.h"
 
 namespace gdn {
 
@@ -315,8 +316,7 @@ __device__ __forceinline__ TokenRaw<TIN> load_token(const PrefillArgs& a, int64_
   in.q = load_raw4<TIN>(a.q, t * a.q_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
   in.k = load_raw4<TIN>(a.k, t * a.k_rs + (int64_t)hk * DK + col, a.qk_vec != 0);
   in.v = load_raw1<TIN>(a.v, t * a.v_rs + (int64_t)h * a.dv + vrow);
-  in.g = a.g[t * a.g_rs + h];
-  in.beta = a.beta[t * a.beta_rs + h];
+  token_gate(a, t, h, in.g, in.beta);
   return in;
 }
 

@@ -34,7 +34,8 @@ EXPORTS = ("gdn_conv1d_fwd", "gdn_conv1d_update", "gdn_gate", "gdn_gate_beta", "
            "gdn_decode", "gdn_decode_packed", "gdn_decode_gated_norm",
            "gdn_rmsnorm_gated",
            "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_aux",
-           "gdn_prefill_varlen_noalloc", "gdn_last_error")
+           "gdn_prefill_varlen_gated", "gdn_prefill_varlen_packed", "gdn_prefill_varlen_noalloc",
+           "gdn_last_error")
 
 
 class GdnError(RuntimeError):
@@ -93,6 +94,12 @@ def load_library(path: str = LIB_PATH):
                                        f32, f32, u32, vp, sz, vp]
     lib.gdn_prefill_varlen_aux.restype = i32
     lib.gdn_prefill_varlen_aux.argtypes = lib.gdn_prefill_varlen.argtypes + [vp]
+    pre = [vp, i32, vp, vp, vp, i32, i64, i64, i64]
+    post = [vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, u32, vp, sz, vp, vp]
+    lib.gdn_prefill_varlen_gated.restype = i32
+    lib.gdn_prefill_varlen_gated.argtypes = pre + [vp, i32, i64, vp, vp, vp, i64] + post
+    lib.gdn_prefill_varlen_packed.restype = i32
+    lib.gdn_prefill_varlen_packed.argtypes = pre + [vp, vp, i32, i64, i64, vp, vp] + post
     lib.gdn_prefill_varlen_noalloc.restype = i32
     lib.gdn_prefill_varlen_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64, i64, vp,
                                                i64, vp, i64, vp, i64, vp, vp, vp, i64, i64,
@@ -419,9 +426,10 @@ def prefill_workspace_size(total_tokens, num_seqs, hk, hv, dk, dv, in_dtype,
                                                  _TORCH_DT[in_dtype], flags)
 
 
-def _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale, state_idx,
-                  has_initial_state, l2norm, l2_eps, out, out_dtype, sequential, check_slots,
-                  stream):
+def _prefill_common(q, k, v, state_pool, cu_seqlens, scale, state_idx, has_initial_state,
+                    l2norm, l2_eps, out, out_dtype, sequential, check_slots, stream,
+                    extra_flags=0):
+    """The arguments before and after the gate inputs of every prefill entry."""
     if state_pool.dim() != 4 or not state_pool.is_contiguous():
         raise GdnError(-3, "state_pool: need contiguous [slots, Hv, Dv, Dk]")
     slots, hv, dv, dk = state_pool.shape
@@ -431,8 +439,6 @@ def _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale, state_idx,
     q_rs = _rows(q, "q", hk, dk)
     k_rs = _rows(k, "k", hk, dk)
     v_rs = _rows(v, "v", hv, dv)
-    g_rs = _rows2(g, "g", hv)
-    b_rs = _rows2(beta, "beta", hv)
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise GdnError(-2, "q, k, v must share a dtype")
     if out is None:
@@ -440,15 +446,24 @@ def _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale, state_idx,
     if not out.is_contiguous() or tuple(out.shape) != (T, hv, dv):
         raise GdnError(-3, "out: need contiguous [T, Hv, Dv]")
     flags = ((GDN_L2NORM_QK if l2norm else 0) | (GDN_PREFILL_SEQUENTIAL if sequential else 0) |
-             (GDN_CHECK_SLOTS if check_slots else 0) | _state_flags(state_pool))
-    args = [_dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
-            q_rs, k_rs, v_rs, _dev(g, "g", torch.float32), g_rs,
-            _dev(beta, "beta", torch.float32), b_rs, _dev(state_pool, "state_pool"), slots,
+             (GDN_CHECK_SLOTS if check_slots else 0) | _state_flags(state_pool) | extra_flags)
+    head = [_dev(out, "out"), _dt(out), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dt(q),
+            q_rs, k_rs, v_rs]
+    tail = [_dev(state_pool, "state_pool"), slots,
             _dev(state_idx, "state_idx", torch.int32),
             _dev(has_initial_state, "has_initial_state", torch.int8),
             _dev(cu_seqlens, "cu_seqlens", torch.int32), N, T, hk, hv, dk, dv, float(scale),
             float(l2_eps), flags]
-    return out, args, (T, N, hk, hv, dk, dv, _dt(q), flags)
+    return out, head, tail, (T, N, hk, hv, dk, dv, _dt(q), flags)
+
+
+def _workspace(lib, ws_key, workspace, device, stream):
+    ws_need = lib.gdn_prefill_varlen_workspace_size(*ws_key)
+    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
+        workspace = _new((ws_need,), torch.uint8, device, stream)
+    ws_ptr = _dev(workspace, "workspace") if ws_need else None
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_need else 0
+    return ws_ptr, ws_bytes
 
 
 def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
@@ -466,19 +481,68 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
     a second stream of the caller's for the split schedule
     (gdn_prefill_varlen_aux); without it the call runs on `stream` alone."""
     lib = load_library()
-    out, args, ws_key = _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale,
-                                      state_idx, has_initial_state, l2norm, l2_eps, out,
-                                      out_dtype, sequential, check_slots, stream)
-    ws_need = lib.gdn_prefill_varlen_workspace_size(*ws_key)
-    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
-        workspace = _new((ws_need,), torch.uint8, q.device, stream)
-    ws_ptr = _dev(workspace, "workspace") if ws_need else None
-    ws_bytes = workspace.numel() * workspace.element_size() if ws_need else 0
+    out, head, tail, ws_key = _prefill_common(q, k, v, state_pool, cu_seqlens, scale, state_idx,
+                                              has_initial_state, l2norm, l2_eps, out, out_dtype,
+                                              sequential, check_slots, stream)
+    hv = state_pool.shape[1]
+    gate = [_dev(g, "g", torch.float32), _rows2(g, "g", hv), _dev(beta, "beta", torch.float32),
+            _rows2(beta, "beta", hv)]
+    ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
     if aux_stream is not None:
-        _check(lib.gdn_prefill_varlen_aux(*args, ws_ptr, ws_bytes, _stream(stream),
+        _check(lib.gdn_prefill_varlen_aux(*head, *gate, *tail, ws_ptr, ws_bytes, _stream(stream),
                                           aux_stream.cuda_stream))
     else:
-        _check(lib.gdn_prefill_varlen(*args, ws_ptr, ws_bytes, _stream(stream)))
+        _check(lib.gdn_prefill_varlen(*head, *gate, *tail, ws_ptr, ws_bytes, _stream(stream)))
+    return out
+
+
+def prefill_varlen_gated(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, cu_seqlens, *,
+                         scale: float, state_idx=None, has_initial_state=None,
+                         l2norm: bool = True, l2_eps: float = 1e-6, out=None, out_dtype=None,
+                         sequential: bool = False, workspace=None, check_slots: bool = False,
+                         stream=None, aux_stream=None) -> torch.Tensor:
+    """prefill_varlen with the gate fused (gdn_prefill_varlen_gated): alpha
+    [T, Hv] (f32/f16/bf16, rows may be strided), dt_bias and ssm_a [Hv] f32,
+    beta [T, Hv] f32 post-sigmoid; no g array is formed."""
+    lib = load_library()
+    out, head, tail, ws_key = _prefill_common(q, k, v, state_pool, cu_seqlens, scale, state_idx,
+                                              has_initial_state, l2norm, l2_eps, out, out_dtype,
+                                              sequential, check_slots, stream)
+    hv = state_pool.shape[1]
+    gate = [_dev(alpha, "alpha"), _dt(alpha), _rows2(alpha, "alpha", hv),
+            _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
+            _dev(beta, "beta", torch.float32), _rows2(beta, "beta", hv)]
+    ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
+    _check(lib.gdn_prefill_varlen_gated(*head, *gate, *tail, ws_ptr, ws_bytes, _stream(stream),
+                                        aux_stream.cuda_stream if aux_stream is not None
+                                        else None))
+    return out
+
+
+def prefill_varlen_packed(q, k, v, a, b, dt_bias, ssm_a, state_pool, cu_seqlens, *,
+                          scale: float, rounded: bool = False, state_idx=None,
+                          has_initial_state=None, l2norm: bool = True, l2_eps: float = 1e-6,
+                          out=None, out_dtype=None, sequential: bool = False, workspace=None,
+                          check_slots: bool = False, stream=None,
+                          aux_stream=None) -> torch.Tensor:
+    """The prefill fed by the front-end's raw projections
+    (gdn_prefill_varlen_packed): q, k, v may be views into the conv output rows;
+    a, b [T, Hv] raw (one dtype, rows may be strided: column views of one
+    merged b|a row); g and beta = sigmoid(b) (rounded through b's dtype with
+    `rounded`) are formed in the kernels."""
+    lib = load_library()
+    out, head, tail, ws_key = _prefill_common(
+        q, k, v, state_pool, cu_seqlens, scale, state_idx, has_initial_state, l2norm, l2_eps, out,
+        out_dtype, sequential, check_slots, stream, GDN_BETA_ROUNDED if rounded else 0)
+    hv = state_pool.shape[1]
+    if b.shape[0] != a.shape[0]:
+        raise GdnError(-3, f"b: {b.shape[0]} rows, a has {a.shape[0]}")
+    gate = [_dev(a, "a"), _dev(b, "b", a.dtype), _dt(a), _rows2(a, "a", hv), _rows2(b, "b", hv),
+            _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32)]
+    ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
+    _check(lib.gdn_prefill_varlen_packed(*head, *gate, *tail, ws_ptr, ws_bytes, _stream(stream),
+                                         aux_stream.cuda_stream if aux_stream is not None
+                                         else None))
     return out
 
 
@@ -496,8 +560,11 @@ def prefill_varlen_noalloc(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: f
     library's fixed per-device scratch holds the per-call records (calls that
     overlap on one device race on it).  Pass `out` to allocate nothing here."""
     lib = load_library()
-    out, args, _ = _prefill_args(q, k, v, g, beta, state_pool, cu_seqlens, scale, state_idx,
-                                 has_initial_state, l2norm, l2_eps, out, out_dtype, sequential,
-                                 check_slots, stream)
-    _check(lib.gdn_prefill_varlen_noalloc(*args, _stream(stream)))
+    out, head, tail, _ = _prefill_common(q, k, v, state_pool, cu_seqlens, scale, state_idx,
+                                         has_initial_state, l2norm, l2_eps, out, out_dtype,
+                                         sequential, check_slots, stream)
+    hv = state_pool.shape[1]
+    gate = [_dev(g, "g", torch.float32), _rows2(g, "g", hv), _dev(beta, "beta", torch.float32),
+            _rows2(beta, "beta", hv)]
+    _check(lib.gdn_prefill_varlen_noalloc(*head, *gate, *tail, _stream(stream)))
     return out

@@ -189,3 +189,75 @@ def test_prefill_from_conv_rows_and_gate_beta(dev, sequential):
     assert H.rel_l1(got, want_out) <= H.OUT_TOL_HALF
     st = dpool[t(idx.astype(np.int64))].cpu().numpy()
     assert H.rel_l1(st, want_state) <= H.STATE_TOL
+
+
+FUSED_CASES = [
+    # (lengths, hk, hv, in dtype, a/b dtype, out dtype, rounded beta)
+    ([70, 1, 1300, 64], 2, 4, W.BF16, W.BF16, W.BF16, True),
+    ([33, 900], 1, 3, W.F16, W.F16, W.F32, False),
+    ([200, 5, 17], 2, 2, W.BF16, W.F32, W.BF16, False),
+]
+
+
+@pytest.mark.parametrize("sequential", [True, False], ids=["sequential", "default"])
+@pytest.mark.parametrize("spec", FUSED_CASES, ids=lambda s: "L{}-{}-ab{}-{}".format(
+    "_".join(map(str, s[0])), W.DTYPE_NAMES[s[3]], W.DTYPE_NAMES[s[4]],
+    "rounded" if s[6] else "f32beta"))
+def test_prefill_with_the_gate_fused(dev, spec, sequential):
+    """gdn_prefill_varlen_packed (q|k|v straight from padded conv rows, g and
+    beta formed in the kernels from the raw b|a row) and
+    gdn_prefill_varlen_gated (raw alpha, post-sigmoid beta) give the same bits
+    as gdn_gate_beta / gdn_gate followed by gdn_prefill_varlen, and match the
+    oracle."""
+    lengths, hk, hv, dt, abd, outd, rounded = spec
+    announce(f"prefill with the gate fused {spec} sequential={sequential}")
+    dk, dv, pad = 128, 128, 8
+    T = sum(lengths)
+    rng = np.random.default_rng(5252 + T)
+    width = 2 * hk * dk + hv * dv
+    conv = W.nan_fill((T, width + pad), dt)
+    conv[:, :width] = W.encode(rng.normal(size=(T, width)), dt)
+    alpha, dt_bias, ssm_a = W.gate_inputs(rng, T, hv, large_every_third=True,
+                                          head0_offset=0.0, a_log_hi=2.0)
+    ba = W.merged_ba(5252 + T, alpha, abd)
+    slots = len(lengths) + 2
+    pool = W.make_pool(5252, slots, hv, dv, dk, 0.05)
+    idx = rng.permutation(slots)[:len(lengths)].astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    scale = float(np.float32(1.0 / np.sqrt(dk)))
+    t = lambda x: torch.from_numpy(x).to(dev)
+    cd = H.to_dev(conv, dt, dev).reshape(-1)
+    stride = width + pad
+    q = cd.as_strided((T, hk, dk), (stride, dk, 1), 0)
+    k = cd.as_strided((T, hk, dk), (stride, dk, 1), hk * dk)
+    v = cd.as_strided((T, hv, dv), (stride, dv, 1), 2 * hk * dk)
+    _, a, b = ba_views(ba, T, hv, dev)
+    od = H.TORCH_OF[outd]
+    kw = dict(scale=scale, state_idx=t(idx), sequential=sequential, out_dtype=od)
+    # composed: materialised g and beta
+    g, beta = gdn.gate_beta(a, b, t(dt_bias), t(ssm_a), rounded=rounded)
+    pool_c = t(pool)
+    out_c = gdn.prefill_varlen(q, k, v, g, beta, pool_c, t(cu), **kw)
+    # packed: raw a and b
+    pool_p = t(pool)
+    out_p = gdn.prefill_varlen_packed(q, k, v, a, b, t(dt_bias), t(ssm_a), pool_p, t(cu),
+                                      rounded=rounded, **kw)
+    # gated: raw alpha (the a view) with the materialised post-sigmoid beta
+    pool_g = t(pool)
+    out_g = gdn.prefill_varlen_gated(q, k, v, a, t(dt_bias), t(ssm_a), beta, pool_g, t(cu),
+                                     **kw)
+    torch.cuda.synchronize()
+    assert H.bytes_equal(out_p, out_c) and H.bytes_equal(pool_p, pool_c), "packed differs"
+    assert H.bytes_equal(out_g, out_c) and H.bytes_equal(pool_g, pool_c), "gated differs"
+    wg, wb = oracle.gate_beta(ba.buf, ba.a_off, ba.row_stride, ba.buf, ba.b_off, ba.row_stride,
+                              abd, dt_bias, ssm_a, rows=T, hv=hv, round_beta=rounded)
+    want_out, want_state = oracle.prefill_varlen(
+        cu_seqlens=cu, hk=hk, hv=hv, dk=dk, dv=dv, q=conv, q_off=0, q_rs=stride, k=conv,
+        k_off=hk * dk, k_rs=stride, v=conv, v_off=2 * hk * dk, v_rs=stride, in_dt=dt, g=wg,
+        beta=wb.astype(np.float32), pool=pool, idx=idx, has_init=None, scale=scale)
+    got = H.out_to_f64(out_p)
+    assert np.isfinite(got).all()
+    H.check_units(got, want_out, 2, H.tier_tol(dt, outd), "fused-gate prefill output")
+    st = pool_p[t(idx.astype(np.int64))].cpu().numpy()
+    H.check_units(st, want_state, 2, H.STATE_TOL, "fused-gate prefill state")
+    assert H.bytes_equal(cd, H.to_dev(conv, dt, dev).reshape(-1)), "the conv rows were written"
