@@ -167,7 +167,7 @@ def main():
     ap.add_argument("--only", default="",
                     help="comma list of legs to time (profiling runs): decode, decode_bf16, "
                          "decode_norm, decode_b1024, conv_update, prefill, t4096, conv_fwd, "
-                         "rmsnorm, cpu; default all")
+                         "post_conv, rmsnorm, cpu; default all")
     args = ap.parse_args()
     only = {x for x in args.only.split(",") if x}
 
@@ -530,6 +530,34 @@ def main():
             del cx, cout
 
         # the gated RMSNorm over the prefill output (a separate HBM pass)
+        if want("post_conv") and not args.no_conv:
+            # the front-end after the conv, materialising q, k (normalised), v, g and beta
+            # from the conv rows and one merged fp16 b | a row per token
+            C = 2 * pre.hk * pre.dk + pre.hv * pre.dv
+            frng = np.random.default_rng([505, 0xC0])
+            fx = to_dev(W.encode(frng.uniform(-1.5, 1.5, size=(T, C)), W.F16))
+            fba = to_dev(W.encode(frng.uniform(-2, 2, size=(T, 2 * pre.hv)), W.F16))
+            fb, fa = fba[:, :pre.hv], fba[:, pre.hv:]
+
+            def post_conv_step(i):
+                gdn.post_conv(fx, fa, fb, pdt, pssm, hk=pre.hk, dk=pre.dk, dv=pre.dv,
+                              stream=stream)
+
+            _, fk = timed(post_conv_step, 3, args.prefill_steps)
+            fbytes = 2 * T * C * 2 + T * pre.hv * (2 * 2 + 2 * 4)
+            favg = float(fk.mean())
+            result.setdefault("prefill", {})["post_conv"] = {
+                "workload": f"post-conv front-end over the 32768 packed tokens: {C} fp16 "
+                            f"channels in and out (q, k L2-normalised), g and beta in f32 "
+                            f"from a merged fp16 b | a row (two kernels)",
+                "kernel_avg_us": round(favg * 1e3, 2),
+                "algorithmic_bytes": fbytes,
+                "achieved_GBs": round(fbytes / (favg * 1e-3) / 1e9, 1),
+                "hbm_frac": round(fbytes / (favg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            }
+            log(f"prefill post_conv: kernel avg {favg * 1e3:.1f} us")
+            del fx, fba, fa, fb
+
         if want("rmsnorm") and not args.no_norm:
             pn = W.norm_inputs(404, T, pre.hv, pre.dv, W.F16)
             pz = to_dev(pn.z.buf).view(T, pre.hv, pre.dv)

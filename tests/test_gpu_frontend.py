@@ -72,8 +72,15 @@ def test_gate_beta_from_merged_row(dev, dt, rounded):
     (3, 4, 4, 300, 128, W.BF16, W.F32, 5),
     (1, 1, 2, 64, 64, W.F16, W.F16, 0),
     (17, 4, 8, 128, 128, W.F32, W.BF16, 0),
-], ids=lambda s: "T{}-hk{}-hv{}-dk{}-dv{}-{}-{}".format(s[0], s[1], s[2], s[3], s[4],
-                                                        W.DTYPE_NAMES[s[5]], W.DTYPE_NAMES[s[6]]))
+    # 16-byte lanes: a head on 64 lanes, on one lane, ragged v widths
+    (6, 2, 4, 512, 64, W.BF16, W.F16, 0),
+    (9, 3, 3, 8, 24, W.F16, W.F32, 0),
+    (7, 2, 2, 256, 12, W.F32, W.F16, 0),
+    (300, 16, 32, 128, 128, W.BF16, W.BF16, 0),
+    # a row stride that is not a multiple of 16 bytes: one element per lane
+    (4, 16, 32, 128, 128, W.BF16, W.BF16, 5),
+], ids=lambda s: "T{}-hk{}-hv{}-dk{}-dv{}-{}-{}-pad{}".format(
+    s[0], s[1], s[2], s[3], s[4], W.DTYPE_NAMES[s[5]], W.DTYPE_NAMES[s[6]], s[7]))
 def test_post_conv(dev, spec):
     T, hk, hv, dk, dv, cdt, odt, pad = spec
     announce(f"post_conv {spec}")
