@@ -830,6 +830,7 @@ struct WalkBuf {
   uint16_t Th[CK * CK], Tl[CK * CK], P[CK * CK];
   uint16_t V[CK * VC];
   float F[4 * CK];
+  float Fpad[4 * CK];  // where the factor loads of waves other than 0 land (zero bytes)
 };
 
 struct WalkCtx {
@@ -906,14 +907,18 @@ __device__ __forceinline__ void stage_offsets(StageOffsets<NW, NB>& o, const Pre
 // through buffer resources that end at the chunk's last token, so rows past
 // the end of the sequence arrive as zeros.  The walk spreads the parts over
 // a chunk step so the CU's load path works while the wave computes.  A walk
-// without outputs (OUTS false) loads neither Q nor P.
+// without outputs (OUTS false) loads neither Q nor P.  With `on` false every
+// resource is empty: the same instructions run, touch no memory and fill B
+// with zeros, so a step has no branch around them (the step's instructions
+// stay one region for the scheduler).
 template <int NW, int NB, int PART, bool OUTS>
 __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx& c, int ch,
-                                               int w, int lane, const StageOffsets<NW, NB>& o) {
+                                               int w, int lane, const StageOffsets<NW, NB>& o,
+                                               bool on = true) {
   using SO = StageOffsets<NW, NB>;
   const PrefillArgs& a = *c.a;
   const int64_t tb = c.t_begin + (int64_t)ch * CK;
-  const int L = chunk_len(c, ch);
+  const int L = on ? chunk_len(c, ch) : 0;
   if constexpr (PART == 0) {
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + tb * a.k_rs +
@@ -931,7 +936,7 @@ __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx
     for (int i = 0; i < SO::NKQ; ++i) dma16_buf(qr, o.q[i], B.Q + 512 * (NW * i + w));
   } else if constexpr (PART == 2) {
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(chunk_rec(c, ch)), 0, REC_BYTES, kBufferFlags);
+        const_cast<char*>(chunk_rec(c, ch)), 0, on ? REC_BYTES : 0, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < SO::NTP; ++i) {
       const int u = NW * i + w;
@@ -946,7 +951,13 @@ __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx
         0, c.v_on ? (int)(L * a.v_rs * 2) : 0, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < SO::NVL; ++i) dma16_buf(vr, o.v[i], B.V + 512 * (NW * i + w));
-    if (w == 0) dma16(chunk_rec(c, ch) + REC_F + 16 * lane, B.F);
+    // the factors (1 KB) come through wave 0; the other waves' copies of the
+    // instruction read nothing and write their zeros to the pad
+    const bool mine = w == 0;
+    const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(chunk_rec(c, ch) + REC_F), 0, on && mine ? 4 * CK * 4 : 0,
+        kBufferFlags);
+    dma16_buf(fr, 16 * lane, mine ? B.F : B.Fpad);
   }
 }
 
@@ -1009,7 +1020,26 @@ __device__ __forceinline__ void pack_split(const f32x4& t0, const f32x4& t1,
   using x8 = typename MT<TIN>::x8;
   const f32x8 x = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
   hi = __builtin_convertvector(x, x8);
-  lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), x8);
+  if constexpr (TIN == kF16) {
+    // x - hi as one mixed-precision FMA per element, the f16 half of the
+    // packed pair widened inside the instruction (v_fma_mix_f32): exact, as
+    // the subtraction is, and one instruction instead of a convert and a
+    // subtraction (the compiler turns a plain fma with -1 back into those)
+    const u32x4 hw = __builtin_bit_cast(u32x4, hi);
+    f32x8 d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float d0, d1;
+      asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d0) : "v"(hw[i]), "v"(x[2 * i]));
+      asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+          : "=v"(d1) : "v"(hw[i]), "v"(x[2 * i + 1]));
+      d[2 * i] = d0;
+      d[2 * i + 1] = d1;
+    }
+    lo = __builtin_convertvector(d, x8);
+  } else {
+    lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x8), x8);
+  }
 }
 
 // What a walk workgroup does (see the segment notes at the metadata):
@@ -1395,38 +1425,51 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     read_kq(kf[0], qf[0], 0);
     // Operands that do not depend on this step's products are read from LDS
     // well ahead of their use, so their latency hides under the MFMAs before
-    // them: here (after the first K and Q fragments) the V values and fz
+    // them: in the last k-step (which reads no K or Q) the V values and fz
     // factors of Z, and e^{G_C}.
     uint16_t vraw[NB][4][4];
     float4 fz4[4];
+    float gc;
+    auto read_vz = [&]() {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int rb = 32 * (b >> 1) + 4 * (b & 1);
-      fz4[b] = *reinterpret_cast<const float4*>(sm.F + fb + rb);
+      for (int b = 0; b < 4; ++b) {
+        const int rb = 32 * (b >> 1) + 4 * (b & 1);
+        fz4[b] = *reinterpret_cast<const float4*>(sm.F + fb + rb);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vraw[nb][b][r] = sm.V[vb[nb] + (rb + r) * VC];
-    }
-    const float gc = sm.F[3 * CK];
+          for (int r = 0; r < 4; ++r) vraw[nb][b][r] = sm.V[vb[nb] + (rb + r) * VC];
+      }
+      gc = sm.F[3 * CK];
+    };
+    // St's high/low split of k-step jj + 1 is formed while k-step jj multiplies
+    x8 sh[2][NB], sl[2][NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) pack_split<TIN>(St[nb][0], St[nb][1], sh[0][nb], sl[0][nb]);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       if (jj < 3) read_kq(kf[(jj + 1) & 1], qf[(jj + 1) & 1], jj + 1);
-      if (more && jj == 1) {
-        stage_dma_part<NW, NB, 0, OUTS>(*nxt, c, ch + 1, w, lane, so);
-        stage_dma_part<NW, NB, 1, OUTS>(*nxt, c, ch + 1, w, lane, so);
+      else read_vz();
+      if (jj == 1) {
+        stage_dma_part<NW, NB, 0, OUTS>(*nxt, c, ch + 1, w, lane, so, more);
+        stage_dma_part<NW, NB, 1, OUTS>(*nxt, c, ch + 1, w, lane, so, more);
       }
+      // the reads above stay a whole k-step ahead of their use: the scheduler
+      // would otherwise pull them down next to their MFMAs and wait on each
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        x8 sh, sl;
-        pack_split<TIN>(St[nb][2 * jj], St[nb][2 * jj + 1], sh, sl);
+        const x8 h = sh[jj & 1][nb], l = sl[jj & 1][nb];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          X[nb][b] = M::mma(kf[jj & 1][b], sh, X[nb][b]);
-          if constexpr (OUTS) QS[nb][b] = M::mma(qf[jj & 1][b], sh, QS[nb][b]);
-          X[nb][b] = M::mma(kf[jj & 1][b], sl, X[nb][b]);
-          if constexpr (OUTS) QS[nb][b] = M::mma(qf[jj & 1][b], sl, QS[nb][b]);
+          X[nb][b] = M::mma(kf[jj & 1][b], h, X[nb][b]);
+          if constexpr (OUTS) QS[nb][b] = M::mma(qf[jj & 1][b], h, QS[nb][b]);
+          X[nb][b] = M::mma(kf[jj & 1][b], l, X[nb][b]);
+          if constexpr (OUTS) QS[nb][b] = M::mma(qf[jj & 1][b], l, QS[nb][b]);
         }
+        if (jj < 3)
+          pack_split<TIN>(St[nb][2 * jj + 2], St[nb][2 * jj + 3], sh[(jj + 1) & 1][nb],
+                          sl[(jj + 1) & 1][nb]);
       }
     }
 
@@ -1463,7 +1506,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
-    if (more) stage_dma_part<NW, NB, 2, OUTS>(*nxt, c, ch + 1, w, lane, so);
+    stage_dma_part<NW, NB, 2, OUTS>(*nxt, c, ch + 1, w, lane, so, more);
     // ---- U = T_b Z (lower triangular in token blocks) ----
     f32x4 U[NB][4];
 #pragma unroll
@@ -1511,7 +1554,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
-    if (more) stage_dma_part<NW, NB, 3, OUTS>(*nxt, c, ch + 1, w, lane, so);
+    stage_dma_part<NW, NB, 3, OUTS>(*nxt, c, ch + 1, w, lane, so, more);
     // ---- O = diag(fo) QS + P U, stored ----
 #pragma unroll
     for (int b = 0; b < (OUTS ? 4 : 0); ++b) {
