@@ -458,12 +458,17 @@ def _prefill_common(q, k, v, state_pool, cu_seqlens, scale, state_idx, has_initi
 
 
 def _workspace(lib, ws_key, workspace, device, stream):
+    """The call's workspace (the caller's when large enough, else a new one),
+    its address and size.  The caller keeps the returned tensor referenced
+    until the launch has been enqueued: freed earlier, the caching allocator
+    would mark it free on `stream` before the kernels that use it, and could
+    hand it to other work while they run."""
     ws_need = lib.gdn_prefill_varlen_workspace_size(*ws_key)
     if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
         workspace = _new((ws_need,), torch.uint8, device, stream)
     ws_ptr = _dev(workspace, "workspace") if ws_need else None
     ws_bytes = workspace.numel() * workspace.element_size() if ws_need else 0
-    return ws_ptr, ws_bytes
+    return workspace, ws_ptr, ws_bytes
 
 
 def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
@@ -487,7 +492,7 @@ def prefill_varlen(q, k, v, g, beta, state_pool, cu_seqlens, *, scale: float,
     hv = state_pool.shape[1]
     gate = [_dev(g, "g", torch.float32), _rows2(g, "g", hv), _dev(beta, "beta", torch.float32),
             _rows2(beta, "beta", hv)]
-    ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
+    workspace, ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
     if aux_stream is not None:
         _check(lib.gdn_prefill_varlen_aux(*head, *gate, *tail, ws_ptr, ws_bytes, _stream(stream),
                                           aux_stream.cuda_stream))
@@ -512,7 +517,7 @@ def prefill_varlen_gated(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, cu_se
     gate = [_dev(alpha, "alpha"), _dt(alpha), _rows2(alpha, "alpha", hv),
             _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
             _dev(beta, "beta", torch.float32), _rows2(beta, "beta", hv)]
-    ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
+    workspace, ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
     _check(lib.gdn_prefill_varlen_gated(*head, *gate, *tail, ws_ptr, ws_bytes, _stream(stream),
                                         aux_stream.cuda_stream if aux_stream is not None
                                         else None))
@@ -539,7 +544,7 @@ def prefill_varlen_packed(q, k, v, a, b, dt_bias, ssm_a, state_pool, cu_seqlens,
         raise GdnError(-3, f"b: {b.shape[0]} rows, a has {a.shape[0]}")
     gate = [_dev(a, "a"), _dev(b, "b", a.dtype), _dt(a), _rows2(a, "a", hv), _rows2(b, "b", hv),
             _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32)]
-    ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
+    workspace, ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
     _check(lib.gdn_prefill_varlen_packed(*head, *gate, *tail, ws_ptr, ws_bytes, _stream(stream),
                                          aux_stream.cuda_stream if aux_stream is not None
                                          else None))
