@@ -58,9 +58,9 @@ constexpr int DKC = 128;      // key head size served here
 #define GDN_WALK_NB 1
 #endif
 #ifndef GDN_WALK_MINB
-#define GDN_WALK_MINB 2
+#define GDN_WALK_MINB 1
 #endif
-constexpr int WALK_NW = GDN_WALK_NW;      // waves per state-walk workgroup
+constexpr int WALK_NW = GDN_WALK_NW;      // compute waves per state-walk workgroup (plus one load wave)
 constexpr int WALK_NB = GDN_WALK_NB;      // 16-row state blocks per wave
 constexpr int WALK_MINB = GDN_WALK_MINB;  // register budget: as for this many workgroups per CU
 constexpr int WALK_BV = 16 * WALK_NW * WALK_NB;  // state rows per workgroup
@@ -99,9 +99,9 @@ struct MT<kF16> {
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 // Workgroup barrier ordering LDS only.  __syncthreads() also waits for every
-// outstanding global access, which would force the next chunk's prefetched
-// loads to land at the first barrier; all communication between the waves
-// here goes through LDS, so the global loads may stay in flight.
+// outstanding global access (the output stores, say); all communication
+// between the waves here goes through LDS, so global accesses may stay in
+// flight, and a wave whose loads must have landed waits for them itself.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -786,7 +786,11 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, MetaP
 // tiles.  Every product of a chunk step takes its state operand straight from
 // those registers and every result's accumulator layout is the B-operand
 // layout of the product that consumes it, so the waves never exchange data:
-// they share only the chunk's inputs, staged once per workgroup in LDS.
+// they share only the chunk's inputs, staged once per workgroup in LDS.  A
+// further wave (the load wave) stages them: while the compute waves work on
+// chunk ch it brings chunk ch + 1 into the other of two LDS buffers, so no
+// compute wave issues a global load or waits behind a full load queue (under
+// a busy memory system that stall took about a tenth of a chunk step).
 //
 // MFMA 16x16x32 layouts (lane l, g = l / 16, c = l % 16):
 //   A: A[c][8g + e] (e < 8),  B: B[8g + e][c],  D: D[4g + r][c] (r < 4).
@@ -830,7 +834,6 @@ struct WalkBuf {
   uint16_t Th[CK * CK], Tl[CK * CK], P[CK * CK];
   uint16_t V[CK * VC];
   float F[4 * CK];
-  float Fpad[4 * CK];  // where the factor loads of waves other than 0 land (zero bytes)
 };
 
 struct WalkCtx {
@@ -905,20 +908,16 @@ __device__ __forceinline__ void stage_offsets(StageOffsets<NW, NB>& o, const Pre
 // Issues part PART of the loads of chunk `ch` into B: 0 = K, 1 = Q, 2 = T_b
 // high/low and P, 3 = the V columns and the factors.  The q/k/v rows go
 // through buffer resources that end at the chunk's last token, so rows past
-// the end of the sequence arrive as zeros.  The walk spreads the parts over
-// a chunk step so the CU's load path works while the wave computes.  A walk
-// without outputs (OUTS false) loads neither Q nor P.  With `on` false every
-// resource is empty: the same instructions run, touch no memory and fill B
-// with zeros, so a step has no branch around them (the step's instructions
-// stay one region for the scheduler).
+// the end of the sequence arrive as zeros.  Issued by the walk's load wave,
+// one call per compute wave's share.  A walk without outputs (OUTS false)
+// loads neither Q nor P.
 template <int NW, int NB, int PART, bool OUTS>
 __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx& c, int ch,
-                                               int w, int lane, const StageOffsets<NW, NB>& o,
-                                               bool on = true) {
+                                               int w, int lane, const StageOffsets<NW, NB>& o) {
   using SO = StageOffsets<NW, NB>;
   const PrefillArgs& a = *c.a;
   const int64_t tb = c.t_begin + (int64_t)ch * CK;
-  const int L = on ? chunk_len(c, ch) : 0;
+  const int L = chunk_len(c, ch);
   if constexpr (PART == 0) {
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(static_cast<const uint16_t*>(a.k) + tb * a.k_rs +
@@ -936,7 +935,7 @@ __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx
     for (int i = 0; i < SO::NKQ; ++i) dma16_buf(qr, o.q[i], B.Q + 512 * (NW * i + w));
   } else if constexpr (PART == 2) {
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(chunk_rec(c, ch)), 0, on ? REC_BYTES : 0, kBufferFlags);
+        const_cast<char*>(chunk_rec(c, ch)), 0, REC_BYTES, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < SO::NTP; ++i) {
       const int u = NW * i + w;
@@ -951,13 +950,7 @@ __device__ __forceinline__ void stage_dma_part(WalkBuf<NW, NB>& B, const WalkCtx
         0, c.v_on ? (int)(L * a.v_rs * 2) : 0, kBufferFlags);
 #pragma unroll
     for (int i = 0; i < SO::NVL; ++i) dma16_buf(vr, o.v[i], B.V + 512 * (NW * i + w));
-    // the factors (1 KB) come through wave 0; the other waves' copies of the
-    // instruction read nothing and write their zeros to the pad
-    const bool mine = w == 0;
-    const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(chunk_rec(c, ch) + REC_F), 0, on && mine ? 4 * CK * 4 : 0,
-        kBufferFlags);
-    dma16_buf(fr, 16 * lane, mine ? B.F : B.Fpad);
+    if (w == 0) dma16(chunk_rec(c, ch) + REC_F + 16 * lane, B.F);
   }
 }
 
@@ -969,14 +962,6 @@ __device__ __forceinline__ void stage_dma(WalkBuf<NW, NB>& B, const WalkCtx& c, 
   stage_dma_part<NW, NB, 1, OUTS>(B, c, ch, w, lane, o);
   stage_dma_part<NW, NB, 2, OUTS>(B, c, ch, w, lane, o);
   stage_dma_part<NW, NB, 3, OUTS>(B, c, ch, w, lane, o);
-}
-
-// Waits for this wave's outstanding global accesses (the chunk loads above)
-// and then for the whole workgroup: the loaded chunk is visible to every wave
-// and every wave is done with the buffer the next loads will overwrite.
-__device__ __forceinline__ void stage_sync() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lds_barrier();
 }
 
 // Output element encoding of the state walk.
@@ -1056,10 +1041,11 @@ enum WalkKind {
 // OUTS: the walk forms outputs (full walks); else it updates the state alone
 // (the first phase of split sequences) and never loads Q or P.
 template <int TIN, int TOUT, int NW, int NB, int MINB, bool OUTS>
-__global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
+__global__ __launch_bounds__(64 * (NW + 1), MINB) void chunk_state_kernel(
     PrefillArgs a, MetaPtrs m, const char* recs, float* segws, int seg_slots, int ntiles,
     int max_chunks, int part) {
-  constexpr int NTH = 64 * NW;
+  constexpr int NTH = 64 * (NW + 1);  // the compute waves and the load wave
+  constexpr int NTHC = 64 * NW;       // the compute waves
   constexpr int VC = WalkBuf<NW, NB>::VC;
   // the two chunk buffers are dynamic LDS: the static size would make the
   // compiler assume one workgroup per CU and spread the registers over the
@@ -1162,6 +1148,34 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
         if (col < a.dv) store1(a.out, a.out_dt, t * out_rs + (int64_t)h * a.dv + col,
                                __builtin_nanf(""));
       }
+    }
+    return;
+  }
+
+  // The load wave (the workgroup's last) issues every chunk's loads into LDS
+  // and waits for them, so no compute wave ever stalls behind a full load
+  // queue; it meets the compute waves at each of their barriers (two per
+  // folded segment, one after clearing the buffers, one per chunk).
+  if (w == NW) {
+    if (kind == kFullWalk)
+      for (int i = 1; i < seg; ++i) {
+        lds_barrier();
+        lds_barrier();
+      }
+    if (nch == 0) return;
+    StageOffsets<NW, NB> sos[NW];
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) stage_offsets<NW, NB, kFullOut>(sos[ww], a, c.dv0, ww, lane);
+    lds_barrier();  // both buffers cleared
+    for (int ch = 0; ch <= nch; ++ch) {
+      // chunk 0 before the first step, chunk ch + 1 during step ch; the
+      // buffer it fills was released at the barrier that ended step ch - 1
+      if (ch < nch) {
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) stage_dma<NW, NB, OUTS>(sb[ch & 1], c, ch, ww, lane, sos[ww]);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
     }
     return;
   }
@@ -1282,7 +1296,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     uint16_t* ml = mh + DKC * DKC;
     for (int i = 1; i < seg; ++i) {
       const float* mt = ws_state(2 * i + 1);
-      for (int u = tid; u < DKC * 16; u += NTH) {
+      for (int u = tid; u < DKC * 16; u += NTHC) {
         const int row = u >> 4, c8 = u & 15;
         const f32x4 x0 = *reinterpret_cast<const f32x4*>(mt + row * DKC + 8 * c8);
         const f32x4 x1 = *reinterpret_cast<const f32x4*>(mt + row * DKC + 8 * c8 + 4);
@@ -1330,18 +1344,15 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     return;
   }
 
-  StageOffsets<NW, NB> so;
-  stage_offsets<NW, NB, kFullOut>(so, a, c.dv0, w, lane);
   // rows past the end of a sequence arrive as zeros; clearing both buffers
   // first also keeps every row that the first chunk does not load finite
   {
     u32x4* z = reinterpret_cast<u32x4*>(walk_lds);
     constexpr int n16 = (int)(2 * sizeof(WalkBuf<NW, NB>) / 16);
-    for (int i = tid; i < n16; i += NTH) z[i] = (u32x4){0u, 0u, 0u, 0u};
+    for (int i = tid; i < n16; i += NTHC) z[i] = (u32x4){0u, 0u, 0u, 0u};
   }
   lds_barrier();
-  stage_dma<NW, NB, OUTS>(sb[0], c, 0, w, lane, so);
-  stage_sync();
+  lds_barrier();  // the load wave has chunk 0 in buffer 0
 
   {
     // transposing reads: this lane supplies row 32 j + 8 g + 4 h + e, chunk
@@ -1369,9 +1380,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) blk_off[nb] = dvw + 16 * nb < a.dv ? 0 : kDropOffset;
 
-  // 16-bit outputs of a chunk are staged as rows in that chunk's V space and
-  // leave during the next step (or after the last one), so the wait for the
-  // next chunk's loads at the end of a step does not also wait for the stores.
+  // 16-bit outputs of a chunk are staged as rows in the wave's own columns of
+  // that chunk's V space and leave at the end of the step, 16 bytes per lane.
   auto store_rows = [&](const WalkBuf<NW, NB>* __restrict__ buf, int chp) {
     if constexpr (OUTS && TOUT != kF32) {
       const int64_t tbp = c.t_begin + (int64_t)chp * CK;
@@ -1386,17 +1396,12 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     }
   };
 
-  // One chunk step: `cur` holds chunk ch, `nxt` receives chunk ch + 1.  The
-  // restrict-qualified buffers tell the compiler that this step's LDS reads
-  // never alias the loads into the other buffer, so it does not wait for
-  // those loads before reading the current chunk.
-  auto chunk_step = [&](WalkBuf<NW, NB>* __restrict__ cur, WalkBuf<NW, NB>* __restrict__ nxt,
-                        int ch) {
+  // One chunk step: `cur` holds chunk ch while the load wave fills the other
+  // buffer with chunk ch + 1.
+  auto chunk_step = [&](WalkBuf<NW, NB>* __restrict__ cur, int ch) {
     const int64_t tb = c.t_begin + (int64_t)ch * CK;
     const int L = chunk_len(c, ch);
-    const bool more = ch + 1 < nch;  // the next chunk's loads go out in three groups
     WalkBuf<NW, NB>& sm = *cur;
-    if (ch > 0) store_rows(nxt, ch - 1);  // before the V loads below overwrite them
     // rows [0, L) of this chunk
     const __amdgpu_buffer_rsrc_t orsrc =
         __builtin_amdgcn_make_buffer_rsrc(out + tb * out_rs, 0, L * out_row, kBufferFlags);
@@ -1450,10 +1455,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
     for (int jj = 0; jj < 4; ++jj) {
       if (jj < 3) read_kq(kf[(jj + 1) & 1], qf[(jj + 1) & 1], jj + 1);
       else read_vz();
-      if (jj == 1) {
-        stage_dma_part<NW, NB, 0, OUTS>(*nxt, c, ch + 1, w, lane, so, more);
-        stage_dma_part<NW, NB, 1, OUTS>(*nxt, c, ch + 1, w, lane, so, more);
-      }
       // the reads above stay a whole k-step ahead of their use: the scheduler
       // would otherwise pull them down next to their MFMAs and wait on each
       __builtin_amdgcn_sched_barrier(0);
@@ -1506,7 +1507,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
-    stage_dma_part<NW, NB, 2, OUTS>(*nxt, c, ch + 1, w, lane, so, more);
     // ---- U = T_b Z (lower triangular in token blocks) ----
     f32x4 U[NB][4];
 #pragma unroll
@@ -1554,7 +1554,6 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
-    stage_dma_part<NW, NB, 3, OUTS>(*nxt, c, ch + 1, w, lane, so, more);
     // ---- O = diag(fo) QS + P U, stored ----
 #pragma unroll
     for (int b = 0; b < (OUTS ? 4 : 0); ++b) {
@@ -1629,10 +1628,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void chunk_state_kernel(
       }
     }
 
-    stage_sync();
+    store_rows(cur, ch);
+    lds_barrier();  // the chunk's buffer is free for the load wave
   };
-  for (int ch = 0; ch < nch; ++ch) chunk_step(&sb[ch & 1], &sb[(ch + 1) & 1], ch);
-  store_rows(&sb[(nch - 1) & 1], nch - 1);
+  for (int ch = 0; ch < nch; ++ch) chunk_step(&sb[ch & 1], ch);
 
   store_state();
 }
@@ -1762,7 +1761,7 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream,
         if (e != hipSuccess) return e;
         raised.fetch_or(bit, std::memory_order_acq_rel);
       }
-      hipLaunchKernelGGL(kern, dim3((unsigned)walk_blocks(items)), dim3(64 * WALK_NW), lds, st,
+      hipLaunchKernelGGL(kern, dim3((unsigned)walk_blocks(items)), dim3(64 * (WALK_NW + 1)), lds, st,
                          a, m, (const char*)recs, segws, sb.slots(), ntiles, (int)mc, part);
       return hipSuccess;
     };
