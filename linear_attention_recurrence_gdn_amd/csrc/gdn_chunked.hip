@@ -532,7 +532,10 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
   }
 
   // the lower 16x16 blocks t = 0..9 of K K^T and Q K^T: wave w owns blocks
-  // w, w + 4, w + 8 (< 10); element r of a tile at (4 (l/16) + r, l % 16)
+  // w, w + 4, w + 8 (< 10), each formed transposed (the products taken as
+  // K_j . K_i and K_j . Q_i) so that a lane holds one row i = 16 ti + l % 16
+  // and four consecutive columns j = 16 tj + 4 (l/16) + r: the row's four
+  // values then leave in one store
   f32x4 accA[3], accP[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
@@ -544,9 +547,9 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
       const int tj = t - (ti * (ti + 1)) / 2;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const typename M::x8 kb = frag_qk<TIN>(Ks, 16 * tj, 32 * kk, lane);
-        accA[k] = M::mma(frag_qk<TIN>(Ks, 16 * ti, 32 * kk, lane), kb, accA[k]);
-        accP[k] = M::mma(frag_qk<TIN>(Qs, 16 * ti, 32 * kk, lane), kb, accP[k]);
+        const typename M::x8 kj = frag_qk<TIN>(Ks, 16 * tj, 32 * kk, lane);
+        accA[k] = M::mma(kj, frag_qk<TIN>(Ks, 16 * ti, 32 * kk, lane), accA[k]);
+        accP[k] = M::mma(kj, frag_qk<TIN>(Qs, 16 * ti, 32 * kk, lane), accP[k]);
       }
     }
   }
@@ -603,38 +606,43 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
 
     // A (strictly lower, scaled) into LDS and P (lower incl. diagonal,
     // scaled) straight to the record: element (i, j) = acc * row factor(i) *
-    // n_k,j * exp(G_i - G_j), the exponential shared by the two
+    // n_k,j * exp(G_i - G_j), the exponential shared by the two; a lane's
+    // four columns of row i go out as one 16-byte LDS store and one 8-byte
+    // record store
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int t = w + 4 * k;
       if (t < 10) {
         const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int tj = t - (ti * (ti + 1)) / 2;
-        const int i0 = 16 * ti + 4 * g;
-        const int j = 16 * tj + cl;
-        const double2 ga = *reinterpret_cast<const double2*>(&sh.Gd[hs][i0]);
-        const double2 gb = *reinterpret_cast<const double2*>(&sh.Gd[hs][i0 + 2]);
-        const double gi[4] = {ga.x, ga.y, gb.x, gb.y};
-        const double gj = sh.Gd[hs][j];
-        const float4 b4 = *reinterpret_cast<const float4*>(&sh.bt[hs][i0]);
-        const float4 k4 = *reinterpret_cast<const float4*>(&sh.nk[i0]);
-        const float4 q4 = *reinterpret_cast<const float4*>(&sh.nq[i0]);
-        const float rfa[4] = {b4.x * k4.x, b4.y * k4.y, b4.z * k4.z, b4.w * k4.w};
-        const float rfp[4] = {a.scale * q4.x, a.scale * q4.y, a.scale * q4.z, a.scale * q4.w};
-        const float cj = sh.nk[j];
-        float* At = Ab + t * BLK;
+        const int i = 16 * ti + cl;
+        const int j0 = 16 * tj + 4 * g;
+        const double gi = sh.Gd[hs][i];
+        const double2 ga = *reinterpret_cast<const double2*>(&sh.Gd[hs][j0]);
+        const double2 gb = *reinterpret_cast<const double2*>(&sh.Gd[hs][j0 + 2]);
+        const double gj[4] = {ga.x, ga.y, gb.x, gb.y};
+        const float rfa = sh.bt[hs][i] * sh.nk[i];
+        const float rfp = a.scale * sh.nq[i];
+        const float4 c4 = *reinterpret_cast<const float4*>(&sh.nk[j0]);
+        const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+        float xa[4];
+        uint16_t ph[4], pl[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = i0 + r;
-          const float e = expf((float)(gi[r] - gj));
-          const float xa = accA[k][r] * rfa[r] * cj * e;
-          const float xp = accP[k][r] * rfp[r] * cj * e;
-          At[(4 * g + r) * LDB + cl] = j < i ? xa : 0.0f;
-          const float pv = j <= i ? xp : 0.0f;
-          const uint16_t ph = M::enc(pv);
-          Pg[i * CK + j] = ph;
-          if (plo) *plo_dst(i, j) = M::enc(pv - M::dec(ph));
+          const int j = j0 + r;
+          const float e = expf((float)(gi - gj[r]));
+          xa[r] = j < i ? accA[k][r] * rfa * cj[r] * e : 0.0f;
+          const float pv = j <= i ? accP[k][r] * rfp * cj[r] * e : 0.0f;
+          ph[r] = M::enc(pv);
+          pl[r] = M::enc(pv - M::dec(ph[r]));
         }
+        *reinterpret_cast<float4*>(Ab + t * BLK + cl * LDB + 4 * g) =
+            make_float4(xa[0], xa[1], xa[2], xa[3]);
+        *reinterpret_cast<uint2*>(Pg + i * CK + j0) =
+            make_uint2(ph[0] | ((uint32_t)ph[1] << 16), ph[2] | ((uint32_t)ph[3] << 16));
+        if (plo)
+          *reinterpret_cast<uint2*>(plo_dst(i, j0)) =
+              make_uint2(pl[0] | ((uint32_t)pl[1] << 16), pl[2] | ((uint32_t)pl[3] << 16));
       }
     }
     // the strictly-upper 16x16 blocks of P that the walk reads, (0, 1) and
