@@ -525,6 +525,33 @@ def test_prefill_on_a_side_stream_then_reallocate(dev):
     H.check_prefill(case, res, want_out, want_state)
 
 
+def test_prefill_split_on_side_streams_then_reallocate(dev):
+    """The same with the split schedule: the call and its second stream are
+    both side streams, and the output and workspace are the binding's own;
+    memory allocated and filled on the current stream right after the call
+    must not land on them while either stream's kernels run."""
+    announce("prefill split on two side streams, then reallocate on the current stream")
+    case = W.make_prefill_case("side2", 6065, lengths=[2100, 900, 300, 17], hk=2, hv=6, dk=128,
+                               dv=128, in_dtype=W.F16, out_dtype=W.F16, slots=6)
+    _, q, k, v = H.upload_views(case, dev, case.total_tokens)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    g = gdn.gate(t(case.alpha), t(case.dt_bias), t(case.ssm_a))
+    beta, cu, idx = t(case.beta), t(case.cu_seqlens), t(case.idx)
+    pool = t(case.pool)
+    side, aux = torch.cuda.Stream(), torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    out = gdn.prefill_varlen(q, k, v, g, beta, pool, cu, scale=case.scale, state_idx=idx,
+                             stream=side, aux_stream=aux)
+    junk = [torch.full((1 << 22,), 9, dtype=torch.uint8, device=dev) for _ in range(32)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del junk
+    want_out, want_state = oracle.prefill_case(case)
+    res = H.PrefillResult(H.out_to_f64(out), pool, None, True)
+    H.check_prefill(case, res, want_out, want_state)
+
+
 def test_prefill_calls_on_two_streams_run_concurrently(dev):
     """Two prefill calls on two streams, each with its own second stream for
     the split schedule, enqueued back to back with no synchronisation between
