@@ -731,27 +731,33 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     // the diagonal are zero; the unread upper-right quadrant is skipped)
     uint16_t* Th = reinterpret_cast<uint16_t*>(rec + REC_TH);
     uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + REC_TL);
+    // eight consecutive columns of a row per thread: one 16-byte store each
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 2; ++k) {
       const int idx = tid_h + 256 * k;
-      const int i = idx >> 4, j4 = 4 * (idx & 15);
-      if (i < 32 && j4 >= 32) continue;
-      const int bi = i >> 4, bj = j4 >> 4;
-      const float4 t = bj <= bi ? *reinterpret_cast<const float4*>(
-                                      Tb + lower_blk(bi, bj) * BLK + (i & 15) * LDB + (j4 & 15))
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 b4 = *reinterpret_cast<const float4*>(&sh.bt[hs][j4]);
-      const float x[4] = {t.x * b4.x, t.y * b4.y, t.z * b4.z, t.w * b4.w};
-      uint16_t hh[4], ll[4];
+      const int i = idx >> 3, j8 = 8 * (idx & 7);
+      if (i < 32 && j8 >= 32) continue;
+      const int bi = i >> 4, bj = j8 >> 4;
+      float4 t0 = make_float4(0.f, 0.f, 0.f, 0.f), t1 = t0;
+      if (bj <= bi) {
+        const float* tr = Tb + lower_blk(bi, bj) * BLK + (i & 15) * LDB + (j8 & 15);
+        t0 = *reinterpret_cast<const float4*>(tr);
+        t1 = *reinterpret_cast<const float4*>(tr + 4);
+      }
+      const float4 b0 = *reinterpret_cast<const float4*>(&sh.bt[hs][j8]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&sh.bt[hs][j8 + 4]);
+      const float x[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
+                          t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
+      uint32_t hw[4], lw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hh[e] = M::enc(x[e]);
-        ll[e] = M::enc(x[e] - M::dec(hh[e]));
+        const uint16_t h0 = M::enc(x[2 * e]), h1 = M::enc(x[2 * e + 1]);
+        const uint16_t l0 = M::enc(x[2 * e] - M::dec(h0)), l1 = M::enc(x[2 * e + 1] - M::dec(h1));
+        hw[e] = h0 | ((uint32_t)h1 << 16);
+        lw[e] = l0 | ((uint32_t)l1 << 16);
       }
-      *reinterpret_cast<uint2*>(Th + i * CK + j4) =
-          make_uint2(hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16));
-      *reinterpret_cast<uint2*>(Tl + i * CK + j4) =
-          make_uint2(ll[0] | ((uint32_t)ll[1] << 16), ll[2] | ((uint32_t)ll[3] << 16));
+      *reinterpret_cast<uint4*>(Th + i * CK + j8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(Tl + i * CK + j8) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
     __syncthreads();  // the next head rewrites A and T (and, per group, Gd and bt)
   }
