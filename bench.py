@@ -90,6 +90,45 @@ def measured_traffic():
         return None
 
 
+PREFILL_SOURCES = ("linear_attention_recurrence_gdn_amd/csrc/gdn_chunked.hip",
+                   "linear_attention_recurrence_gdn_amd/csrc/gdn_prefill_gate.h",
+                   "linear_attention_recurrence_gdn_amd/csrc/gdn_launch.h",
+                   "linear_attention_recurrence_gdn_amd/csrc/gdn_device.h")
+WALK_COUNTERS_PROFILE = "profiles/prefill_varlen8_walk_sq_counters.md"
+
+
+def prefill_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in PREFILL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def walk_mfma_busy():
+    """MFMA busy fraction of the varlen walk on the SIMDs it occupies, from the
+    committed SQ counter summary, or None when it is missing or was taken on
+    different kernel sources."""
+    path = os.path.join(ROOT, WALK_COUNTERS_PROFILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":", 1)[0].strip() in (
+                    "source_sha256", "walk_mfma_busy_frac"):
+                k, v = line.split(":", 1)
+                v = v.split()
+                fields[k.strip()] = v[0].strip("`") if v else ""
+    if fields.get("source_sha256") != prefill_source_hash():
+        return None
+    try:
+        return float(fields["walk_mfma_busy_frac"])
+    except (KeyError, ValueError):
+        return None
+
+
 def prefill_bytes(T, N, hk, hv, dk, dv, in_bytes, out_bytes, n_init=None):
     """Algorithmic HBM bytes of the varlen prefill with the gate fused: q/k/v
     read once, out written once, alpha (f32) and beta read once per (token,
@@ -450,6 +489,10 @@ def main():
                 "hbm_frac": round(pbytes / (pavg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "chunked_flops_per_step": pflops,
                 "mfma_frac_algorithmic": round(pflops / (pavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "walk_mfma_busy": walk_mfma_busy(),
+                "walk_mfma_busy_source": WALK_COUNTERS_PROFILE + " (SQ_VALU_MFMA_BUSY_CYCLES "
+                                         "over the SIMDs the longest walk occupies; null when "
+                                         "taken on other kernel sources)",
                 "path": "chunked" if ws_n > 0 else "token-sequential",
             }
             if ws_n > 0:
