@@ -41,6 +41,7 @@
 // when a head's gate is thousands per chunk.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -423,6 +424,7 @@ constexpr int REC_BYTES = REC_F + 4 * CK * 4;
 // LDS: Q and K are needed only for the products; the lower 16x16 blocks of A
 // and T and the per-wave partial products then reuse their space.  About
 // 36 KB in all, so four workgroups share a CU.
+constexpr double kLog2e = 1.4426950408889634;  // log2(e)
 constexpr int LDB = 20;         // padded f32 row of a 16x16 block of A or T
 constexpr int kPrepHeads = 4;   // v-heads whose factors are formed at once (one per wave)
 
@@ -438,7 +440,7 @@ struct PrepLds {
     } at;
   } u;
   float nq[CK], nk[CK];
-  double Gd[kPrepHeads][CK];
+  double Gd[kPrepHeads][CK];  // gate prefix sums in base-2 units, G log2(e)
   float bt[kPrepHeads][CK];
 };
 
@@ -563,7 +565,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
       const int h = hk * ratio + jh;
       char* rec = recs + ((int64_t)c * a.hv + h) * REC_BYTES;
       const double gcum = wave_prefix64((double)gv);
-      sh.Gd[w][lane] = gcum;
+      sh.Gd[w][lane] = gcum * kLog2e;
       sh.bt[w][lane] = bv;
       const double gl = __shfl(gcum, L - 1, 64);
       const float eg = expf((float)gcum);
@@ -606,43 +608,58 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
 
     // A (strictly lower, scaled) into LDS and P (lower incl. diagonal,
     // scaled) straight to the record: element (i, j) = acc * row factor(i) *
-    // n_k,j * exp(G_i - G_j), the exponential shared by the two; a lane's
-    // four columns of row i go out as one 16-byte LDS store and one 8-byte
-    // record store
+    // n_k,j * exp(G_i - G_j), the exponential (on the hardware base-2
+    // exponential of the f64 difference of the base-2 prefixes) and its
+    // product with n_k,j shared by the two; a lane's four columns of row i go
+    // out as one 16-byte LDS store and one 8-byte record store.  Only the
+    // four diagonal tiles need the triangle masks.
+    auto ap_tile = [&](auto diag, int k, int t, int ti, int tj) {
+      const int i = 16 * ti + cl;
+      const int j0 = 16 * tj + 4 * g;
+      const double gi = sh.Gd[hs][i];
+      const double2 ga = *reinterpret_cast<const double2*>(&sh.Gd[hs][j0]);
+      const double2 gb = *reinterpret_cast<const double2*>(&sh.Gd[hs][j0 + 2]);
+      const double gj[4] = {ga.x, ga.y, gb.x, gb.y};
+      const float rfa = sh.bt[hs][i] * sh.nk[i];
+      const float rfp = a.scale * sh.nq[i];
+      const float4 c4 = *reinterpret_cast<const float4*>(&sh.nk[j0]);
+      const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+      float xa[4], pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ec = __builtin_amdgcn_exp2f((float)(gi - gj[r])) * cj[r];
+        xa[r] = accA[k][r] * rfa * ec;
+        pv[r] = accP[k][r] * rfp * ec;
+        if constexpr (decltype(diag)::value) {
+          xa[r] = j0 + r < i ? xa[r] : 0.0f;
+          pv[r] = j0 + r <= i ? pv[r] : 0.0f;
+        }
+      }
+      *reinterpret_cast<float4*>(Ab + t * BLK + cl * LDB + 4 * g) =
+          make_float4(xa[0], xa[1], xa[2], xa[3]);
+      uint16_t ph[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ph[r] = M::enc(pv[r]);
+      *reinterpret_cast<uint2*>(Pg + i * CK + j0) =
+          make_uint2(ph[0] | ((uint32_t)ph[1] << 16), ph[2] | ((uint32_t)ph[3] << 16));
+      if (plo) {
+        uint16_t pl[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pl[r] = M::enc(pv[r] - M::dec(ph[r]));
+        *reinterpret_cast<uint2*>(plo_dst(i, j0)) =
+            make_uint2(pl[0] | ((uint32_t)pl[1] << 16), pl[2] | ((uint32_t)pl[3] << 16));
+      }
+    };
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int t = w + 4 * k;
       if (t < 10) {
         const int ti = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
         const int tj = t - (ti * (ti + 1)) / 2;
-        const int i = 16 * ti + cl;
-        const int j0 = 16 * tj + 4 * g;
-        const double gi = sh.Gd[hs][i];
-        const double2 ga = *reinterpret_cast<const double2*>(&sh.Gd[hs][j0]);
-        const double2 gb = *reinterpret_cast<const double2*>(&sh.Gd[hs][j0 + 2]);
-        const double gj[4] = {ga.x, ga.y, gb.x, gb.y};
-        const float rfa = sh.bt[hs][i] * sh.nk[i];
-        const float rfp = a.scale * sh.nq[i];
-        const float4 c4 = *reinterpret_cast<const float4*>(&sh.nk[j0]);
-        const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
-        float xa[4];
-        uint16_t ph[4], pl[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + r;
-          const float e = expf((float)(gi - gj[r]));
-          xa[r] = j < i ? accA[k][r] * rfa * cj[r] * e : 0.0f;
-          const float pv = j <= i ? accP[k][r] * rfp * cj[r] * e : 0.0f;
-          ph[r] = M::enc(pv);
-          pl[r] = M::enc(pv - M::dec(ph[r]));
-        }
-        *reinterpret_cast<float4*>(Ab + t * BLK + cl * LDB + 4 * g) =
-            make_float4(xa[0], xa[1], xa[2], xa[3]);
-        *reinterpret_cast<uint2*>(Pg + i * CK + j0) =
-            make_uint2(ph[0] | ((uint32_t)ph[1] << 16), ph[2] | ((uint32_t)ph[3] << 16));
-        if (plo)
-          *reinterpret_cast<uint2*>(plo_dst(i, j0)) =
-              make_uint2(pl[0] | ((uint32_t)pl[1] << 16), pl[2] | ((uint32_t)pl[3] << 16));
+        if (ti == tj)
+          ap_tile(std::true_type{}, k, t, ti, tj);
+        else
+          ap_tile(std::false_type{}, k, t, ti, tj);
       }
     }
     // the strictly-upper 16x16 blocks of P that the walk reads, (0, 1) and
