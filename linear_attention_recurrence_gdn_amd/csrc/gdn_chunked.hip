@@ -175,19 +175,29 @@ __host__ __device__ inline MetaPtrs meta_ptrs(void* ws, int64_t n) {
   return {p, p + n + 1, p + 2 * n + 1, p + 3 * n + 2};  // info: kInfoWords words
 }
 
-// block-wide inclusive scan of one value per thread (256 threads)
+// A DPP move of an int32; lanes the move does not reach read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int32_t dpp_i32(int32_t x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, true);
+}
+
+// block-wide inclusive scan of one value per thread (256 threads): each
+// wave scans its 64 values with DPP row shifts and row broadcasts, then adds
+// the totals of the waves before it (one barrier; part[0..3] is free again
+// when it returns)
 __device__ __forceinline__ int32_t block_scan256(int32_t v, int32_t* part) {
-  part[threadIdx.x] = v;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v += dpp_i32<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_i32<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_i32<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_i32<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_i32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  if (lane == 63) part[w] = v;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int32_t add = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += add;
-    __syncthreads();
-  }
-  const int32_t r = part[threadIdx.x];
+  for (int i = 0; i < w; ++i) v += part[i];
   __syncthreads();
-  return r;
+  return v;
 }
 
 // The schedule of a call, from a cost model in units of one chunk step of one
@@ -325,27 +335,42 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
     __syncthreads();
   }
   __syncthreads();
-  // the plan: one candidate per thread, then the cheapest (ties: the lowest index)
-  __shared__ double cost[256];
+  // the plan: one candidate per thread, then the cheapest (ties: the lowest
+  // index), by shuffles within each wave and then over the four waves
   __shared__ Plan plans[256];
+  __shared__ double wcost[4];
+  __shared__ int widx[4];
   {
     Plan p = {0, 0, 1};
     double t = 1e300;
     if (small && threadIdx.x < kPlanCands)
       t = plan_cost(threadIdx.x, ocs, n, a.hv, (double)a.hv * ntiles, ncu, kmax, ksmax, smax, p);
-    cost[threadIdx.x] = t;
     plans[threadIdx.x] = p;
+    int bi = threadIdx.x;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const double to = __shfl_xor(t, off, 64);
+      const int io = __shfl_xor(bi, off, 64);
+      if (to < t || (to == t && io < bi)) {
+        t = to;
+        bi = io;
+      }
+    }
+    if ((threadIdx.x & 63) == 0) {
+      wcost[threadIdx.x >> 6] = t;
+      widx[threadIdx.x >> 6] = bi;
+    }
   }
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < (unsigned)off && cost[threadIdx.x + off] < cost[threadIdx.x]) {
-      cost[threadIdx.x] = cost[threadIdx.x + off];
-      plans[threadIdx.x] = plans[threadIdx.x + off];
-    }
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    const Plan p = cost[0] < 1e299 ? plans[0] : Plan{0, 0, 1};
+    double t = wcost[0];
+    int bi = widx[0];
+    for (int i = 1; i < 4; ++i)
+      if (wcost[i] < t) {
+        t = wcost[i];
+        bi = widx[i];
+      }
+    const Plan p = t < 1e299 ? plans[bi] : Plan{0, 0, 1};
     m.info[0] = p.k;
     m.info[1] = p.ks;
     m.info[2] = p.S;
