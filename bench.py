@@ -206,7 +206,7 @@ def main():
     ap.add_argument("--only", default="",
                     help="comma list of legs to time (profiling runs): decode, decode_bf16, "
                          "decode_norm, decode_b1024, conv_update, prefill, t4096, conv_fwd, "
-                         "post_conv, rmsnorm, cpu; default all")
+                         "post_conv, rmsnorm, prefill_norm, cpu; default all")
     args = ap.parse_args()
     only = {x for x in args.only.split(",") if x}
 
@@ -622,6 +622,31 @@ def main():
                 "hbm_frac": round(nbytes / (navg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             }
             log(f"prefill gated norm: kernel avg {navg * 1e3:.1f} us")
+
+        if want("prefill_norm") and not args.no_norm:
+            gn = W.norm_inputs(404, T, pre.hv, pre.dv, W.F16)
+            gz = to_dev(gn.z.buf).view(T, pre.hv, pre.dv)
+            gw = to_dev(gn.w)
+
+            def prefill_norm_step(i):
+                gdn.prefill_varlen_gated_norm(qp, kp, vp, pa, pdt, pssm, pbeta, ppool, pcu, gz,
+                                              gw, scale=pre.scale, norm_eps=gn.eps,
+                                              state_idx=pidx, has_initial_state=phi, out=pout,
+                                              workspace=ws, stream=stream, aux_stream=aux)
+
+            gwall, gk = timed(prefill_norm_step, 4, args.prefill_steps)
+            g_ms = gwall * 1e3 / args.prefill_steps
+            result.setdefault("prefill", {})["with_gated_norm"] = {
+                "workload": "the same varlen prefill followed by the gated RMSNorm (silu, fp16 "
+                            "gate and weight) over its output in place, one call "
+                            "(gdn_prefill_varlen_gated_norm: the walks, then the norm pass)",
+                "ms_per_step": round(g_ms, 4),
+                "tokens_per_s": round(T / (g_ms * 1e-3), 1),
+                "kernel_avg_ms": round(float(gk.mean()), 4),
+            }
+            log(f"prefill + gated norm: {g_ms:.3f} ms/step -> "
+                f"{T / (g_ms * 1e-3) / 1e6:.2f} M tokens/s")
+            del gz, gw
 
     # ---------------- CPU oracle baseline ----------------
     if want("cpu") and not args.no_cpu:

@@ -435,6 +435,42 @@ int gdn_prefill_varlen_gated(void* out, gdn_dtype out_dt, const void* q, const v
                              hipStream_t aux_stream);
 
 /*
+ * gdn_prefill_varlen_gated_norm -- gdn_prefill_varlen_gated followed, on the
+ * same stream, by the gated RMSNorm of gdn_rmsnorm_gated over the output in
+ * place (vllm.cpp test_ops_gdn.cpp, "rmsnorm_gated: norm-then-gate, silu and
+ * sigmoid activations" and "rank-3 padded-row strided gate matches
+ * contiguous"):
+ *   out[t][h][i] = o / sqrt(mean_i(o^2) + norm_eps) * norm_w[i] * act(z),
+ * act = silu, or sigmoid with GDN_NORM_SIGMOID, from the output as stored.
+ * The result is bit-identical to gdn_prefill_varlen_gated then
+ * gdn_rmsnorm_gated(out, out, ...).  The norm is a second pass over out, not
+ * part of the walk's store: a v-head's Dv output rows are split between two
+ * workgroups of the walk, and a row's mean of squares would need an exchange
+ * between them at every chunk.
+ *   norm_z     [total_tokens, hv, dv] in in_dt, row stride norm_z_row_stride
+ *              (>= hv*dv; a padded view of a wider row is fine).
+ *   norm_w     [dv] in in_dt.   norm_eps  finite, >= 0.
+ *   out_dt     must equal in_dt (norm_z and norm_w share it).
+ *   flags      as gdn_prefill_varlen, plus GDN_NORM_SIGMOID.
+ *   every other argument as for gdn_prefill_varlen_gated (aux_stream may be
+ *   NULL), the same workspace size.  The norm's arguments are checked before
+ *   anything is enqueued; a failure of either launch returns GDN_ERR_HIP.
+ */
+int gdn_prefill_varlen_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                                  const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                                  int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
+                                  gdn_dtype alpha_dt, int64_t alpha_row_stride,
+                                  const float* dt_bias, const float* ssm_a, const float* beta,
+                                  int64_t beta_row_stride, void* state_pool, int64_t num_slots,
+                                  const int32_t* state_idx, const int8_t* has_initial_state,
+                                  const int32_t* cu_seqlens, int64_t num_seqs,
+                                  int64_t total_tokens, int64_t hk, int64_t hv, int64_t dk,
+                                  int64_t dv, float scale, float l2_eps, const void* norm_z,
+                                  int64_t norm_z_row_stride, const void* norm_w, float norm_eps,
+                                  uint32_t flags, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, hipStream_t aux_stream);
+
+/*
  * gdn_prefill_varlen_packed -- the prefill fed by the front-end's raw
  * projections (vllm.cpp test_ops_gdn.cpp, "gdn_post_conv fused == composed"
  * and the packed in_proj_ba case): q, k, v may be views into the conv output

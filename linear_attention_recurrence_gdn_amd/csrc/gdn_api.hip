@@ -703,6 +703,57 @@ int gdn_prefill_varlen_gated(void* out, gdn_dtype out_dt, const void* q, const v
                       scale, l2_eps, flags, workspace, workspace_bytes, stream, aux_stream);
 }
 
+int gdn_prefill_varlen_gated_norm(void* out, gdn_dtype out_dt, const void* q, const void* k,
+                                  const void* v, gdn_dtype in_dt, int64_t q_row_stride,
+                                  int64_t k_row_stride, int64_t v_row_stride, const void* alpha,
+                                  gdn_dtype alpha_dt, int64_t alpha_row_stride,
+                                  const float* dt_bias, const float* ssm_a, const float* beta,
+                                  int64_t beta_row_stride, void* state_pool, int64_t num_slots,
+                                  const int32_t* state_idx, const int8_t* has_initial_state,
+                                  const int32_t* cu_seqlens, int64_t num_seqs,
+                                  int64_t total_tokens, int64_t hk, int64_t hv, int64_t dk,
+                                  int64_t dv, float scale, float l2_eps, const void* norm_z,
+                                  int64_t norm_z_row_stride, const void* norm_w, float norm_eps,
+                                  uint32_t flags, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, hipStream_t aux_stream) {
+  const char* op = "gdn_prefill_varlen_gated_norm";
+  // the norm's arguments are checked before the prefill enqueues anything
+  if (!valid_dt(in_dt) || !valid_dt(out_dt)) return fail(GDN_ERR_DTYPE, "%s: unknown dtype", op);
+  if (out_dt != in_dt)
+    return fail(GDN_ERR_DTYPE, "%s: out dtype must be the input dtype (norm_z and norm_w share it)",
+                op);
+  if (!(norm_eps >= 0.0f) || !isfinite(norm_eps))
+    return fail(GDN_ERR_ARG, "%s: norm_eps must be finite and >= 0", op);
+  const bool rows = num_seqs > 0 && total_tokens > 0;
+  if (rows) {
+    if (hv <= 0 || dv <= 0 || hv > (1 << 20) || dv > (1 << 20))
+      return fail(GDN_ERR_SHAPE, "%s: hv and dv in [1, 2^20] required", op);
+    if (norm_z_row_stride < hv * dv)
+      return fail(GDN_ERR_SHAPE, "%s: norm_z row stride below hv*dv", op);
+    if (!norm_z || !norm_w) return fail(GDN_ERR_ARG, "%s: null pointer", op);
+    const size_t eb = (size_t)elem_bytes(in_dt);
+    if (!aligned(norm_z, eb) || !aligned(norm_w, eb))
+      return fail(GDN_ERR_ARG, "%s: norm_z/norm_w must be aligned to their element size", op);
+    if (total_tokens * hv > ((int64_t)1 << 40))
+      return fail(GDN_ERR_SHAPE, "%s: total_tokens*hv too large", op);
+  }
+  const GateIn gt{nullptr, 0, alpha, alpha_dt, alpha_row_stride, dt_bias, ssm_a, beta,
+                  beta_row_stride, false};
+  const int rc = prefill_impl(op, out, out_dt, q, k, v, in_dt, q_row_stride, k_row_stride,
+                              v_row_stride, gt, state_pool, num_slots, state_idx,
+                              has_initial_state, cu_seqlens, num_seqs, total_tokens, hk, hv, dk,
+                              dv, scale, l2_eps, flags & ~(uint32_t)GDN_NORM_SIGMOID, workspace,
+                              workspace_bytes, stream, aux_stream);
+  if (rc != GDN_OK || !rows) return rc;
+  // the norm in place over out, behind every walk (the second stream has
+  // joined `stream` by now); each lane reads its elements before it writes them
+  gdn::NormArgs a{};
+  a.out = out; a.out_dt = out_dt; a.x = out; a.x_dt = out_dt; a.z = norm_z;
+  a.z_rs = norm_z_row_stride; a.w = norm_w; a.rows = total_tokens; a.hv = (int)hv;
+  a.dv = (int)dv; a.eps = norm_eps; a.sigmoid = (flags & GDN_NORM_SIGMOID) ? 1 : 0;
+  return hip_status(op, gdn::launch_rmsnorm_gated(a, stream));
+}
+
 int gdn_prefill_varlen_packed(void* out, gdn_dtype out_dt, const void* q, const void* k,
                               const void* v, gdn_dtype in_dt, int64_t q_row_stride,
                               int64_t k_row_stride, int64_t v_row_stride, const void* a_raw,

@@ -34,7 +34,8 @@ EXPORTS = ("gdn_conv1d_fwd", "gdn_conv1d_update", "gdn_gate", "gdn_gate_beta", "
            "gdn_decode", "gdn_decode_packed", "gdn_decode_gated_norm",
            "gdn_rmsnorm_gated",
            "gdn_prefill_varlen_workspace_size", "gdn_prefill_varlen", "gdn_prefill_varlen_aux",
-           "gdn_prefill_varlen_gated", "gdn_prefill_varlen_packed", "gdn_prefill_varlen_noalloc",
+           "gdn_prefill_varlen_gated", "gdn_prefill_varlen_gated_norm", "gdn_prefill_varlen_packed",
+           "gdn_prefill_varlen_noalloc",
            "gdn_last_error")
 
 
@@ -98,6 +99,9 @@ def load_library(path: str = LIB_PATH):
     post = [vp, i64, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, u32, vp, sz, vp, vp]
     lib.gdn_prefill_varlen_gated.restype = i32
     lib.gdn_prefill_varlen_gated.argtypes = pre + [vp, i32, i64, vp, vp, vp, i64] + post
+    lib.gdn_prefill_varlen_gated_norm.restype = i32
+    lib.gdn_prefill_varlen_gated_norm.argtypes = (pre + [vp, i32, i64, vp, vp, vp, i64] +
+                                                  post[:13] + [vp, i64, vp, f32] + post[13:])
     lib.gdn_prefill_varlen_packed.restype = i32
     lib.gdn_prefill_varlen_packed.argtypes = pre + [vp, vp, i32, i64, i64, vp, vp] + post
     lib.gdn_prefill_varlen_noalloc.restype = i32
@@ -521,6 +525,41 @@ def prefill_varlen_gated(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, cu_se
     _check(lib.gdn_prefill_varlen_gated(*head, *gate, *tail, ws_ptr, ws_bytes, _stream(stream),
                                         aux_stream.cuda_stream if aux_stream is not None
                                         else None))
+    return out
+
+
+def prefill_varlen_gated_norm(q, k, v, alpha, dt_bias, ssm_a, beta, state_pool, cu_seqlens,
+                              norm_z, norm_w, *, scale: float, norm_eps: float = 1e-6,
+                              sigmoid: bool = False, state_idx=None, has_initial_state=None,
+                              l2norm: bool = True, l2_eps: float = 1e-6, out=None,
+                              sequential: bool = False, workspace=None,
+                              check_slots: bool = False, stream=None,
+                              aux_stream=None) -> torch.Tensor:
+    """prefill_varlen_gated, then the gated RMSNorm over the output in place
+    (gdn_prefill_varlen_gated_norm): out = o / sqrt(mean(o^2) + norm_eps) *
+    norm_w * act(norm_z), act = silu or sigmoid.  norm_z: [T, Hv, Dv] (rows
+    may be padded views of a wider buffer) and norm_w: [Dv], both in q's
+    dtype, which is also the output's."""
+    lib = load_library()
+    out, head, tail, ws_key = _prefill_common(q, k, v, state_pool, cu_seqlens, scale, state_idx,
+                                              has_initial_state, l2norm, l2_eps, out, None,
+                                              sequential, check_slots, stream)
+    hv, dv = state_pool.shape[1], state_pool.shape[2]
+    gate = [_dev(alpha, "alpha"), _dt(alpha), _rows2(alpha, "alpha", hv),
+            _dev(dt_bias, "dt_bias", torch.float32), _dev(ssm_a, "ssm_a", torch.float32),
+            _dev(beta, "beta", torch.float32), _rows2(beta, "beta", hv)]
+    if norm_z.dtype != q.dtype or norm_w.dtype != q.dtype:
+        raise GdnError(-2, "norm_z and norm_w must have q's dtype")
+    if norm_w.dim() != 1 or norm_w.shape[0] != dv or not norm_w.is_contiguous():
+        raise GdnError(-3, "norm_w: need contiguous [Dv]")
+    norm = [_dev(norm_z, "norm_z"), _rows(norm_z, "norm_z", hv, dv), _dev(norm_w, "norm_w"),
+            float(norm_eps)]
+    flags = tail[-1] | (GDN_NORM_SIGMOID if sigmoid else 0)
+    workspace, ws_ptr, ws_bytes = _workspace(lib, ws_key, workspace, q.device, stream)
+    _check(lib.gdn_prefill_varlen_gated_norm(*head, *gate, *tail[:-1], *norm, flags, ws_ptr,
+                                             ws_bytes, _stream(stream),
+                                             aux_stream.cuda_stream if aux_stream is not None
+                                             else None))
     return out
 
 

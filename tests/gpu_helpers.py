@@ -298,22 +298,24 @@ def run_prefill(case: W.PrefillCase, dev, *, sequential: bool = False, keep_pool
 
 
 def check_prefill(case, res: PrefillResult, want_out, want_state, heads=None,
-                  out_tolerance=None, state_tolerance=None, verbose=False):
+                  out_tolerance=None, state_tolerance=None, verbose=False, check_out=True):
     """Compare a GPU prefill with the oracle (optionally on a subset of
     v-heads): pooled and per-(token, v-head) relative L1 and every element of
-    the outputs, pooled and per-(sequence, v-head) relative L1 and every
-    element of the final states, untouched slots and inputs byte-identical."""
+    the outputs (unless the caller checks them itself: check_out=False),
+    pooled and per-(sequence, v-head) relative L1 and every element of the
+    final states, untouched slots and inputs byte-identical."""
     hsel = np.arange(case.hv) if heads is None else np.asarray(heads)
     tol = out_tolerance or out_tol(case)
     st_tol = state_tolerance or STATE_TOL
     got = res.out[:, hsel]
     want = want_out[:, hsel]
-    assert np.isfinite(got).all(), f"{case.name}: non-finite output"
-    check_units(got, want, 2, tol, f"{case.name} output")
-    atol, rtol = close_tol(case.in_dtype, case.out_dtype)
-    if out_tolerance is not None:
-        atol, rtol = min(atol, out_tolerance), min(rtol, out_tolerance)
-    check_close(got, want, atol, rtol, f"{case.name} output")
+    if check_out:
+        assert np.isfinite(got).all(), f"{case.name}: non-finite output"
+        check_units(got, want, 2, tol, f"{case.name} output")
+        atol, rtol = close_tol(case.in_dtype, case.out_dtype)
+        if out_tolerance is not None:
+            atol, rtol = min(atol, out_tolerance), min(rtol, out_tolerance)
+        check_close(got, want, atol, rtol, f"{case.name} output")
     r_out = rel_l1(got, want)
     idx = torch.from_numpy(case.idx.astype(np.int64)).to(res.pool.device)
     got_state = res.pool[idx][:, torch.from_numpy(hsel).to(res.pool.device)]

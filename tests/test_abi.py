@@ -93,6 +93,34 @@ def test_prefill_argument_errors():
     assert _prefill(lib, n=0) == 0
 
 
+def _prefill_norm(lib, **kw):
+    a = dict(out=None, out_dt=1, q=None, k=None, v=None, in_dt=1, q_rs=1024, k_rs=1024,
+             v_rs=3072, alpha=None, alpha_dt=0, alpha_rs=24, dt_bias=None, ssm_a=None,
+             beta=None, beta_rs=24, pool=None, slots=64, idx=None, has_init=None, cu=None,
+             n=8, t=32768, hk=8, hv=24, dk=128, dv=128, scale=0.088, eps=1e-6, z=None,
+             z_rs=3072, w=None, neps=1e-6, flags=1, ws=None, ws_bytes=0, stream=None, aux=None)
+    a.update(kw)
+    return lib.gdn_prefill_varlen_gated_norm(*a.values())
+
+
+def test_prefill_gated_norm_argument_errors():
+    # the norm's arguments are rejected before the prefill's own checks run
+    lib = pkg.load_library()
+    assert _prefill_norm(lib, out_dt=0) == -2 and "input dtype" in _err(lib)
+    assert _prefill_norm(lib, neps=-1.0) == -1
+    assert _prefill_norm(lib, neps=float("inf")) == -1
+    assert _prefill_norm(lib, z_rs=3071) == -3 and "norm_z row stride" in _err(lib)
+    assert _prefill_norm(lib) == -1 and "null pointer" in _err(lib)
+    assert _err(lib).startswith("gdn_prefill_varlen_gated_norm:")
+    # the sigmoid flag is the norm's, the prefill's checks never see it; a
+    # prefill error is reported under this entry point's name
+    assert _prefill_norm(lib, hv=25, z_rs=25 * 128) == -1     # the norm's null pointers first
+    assert _prefill_norm(lib, t=0, hv=25) == -3 and "multiple of Hk" in _err(lib)
+    assert _prefill_norm(lib, t=0, flags=1 | (1 << 5)) == -1 and "null pointer" in _err(lib)
+    assert _prefill_norm(lib, t=0, flags=1 | (1 << 6)) == -1 and "unknown flags" in _err(lib)
+    assert _prefill_norm(lib, n=0, t=0) == 0
+
+
 def test_gate_argument_errors():
     lib = pkg.load_library()
     assert lib.gdn_gate(None, 32, None, 0, 32, None, None, 10, 0, None) == -3

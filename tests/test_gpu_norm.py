@@ -1,8 +1,8 @@
 """GPU parity of the gated RMSNorm (vllm.cpp tests/vt/test_ops_gdn.cpp,
 "rmsnorm_gated: norm-then-gate, silu and sigmoid activations", the
 CPU-vs-CUDA rmsnorm_gated cases and the rank-3 padded-row gate case): the
-standalone kernel over a stored [T, Hv, Dv] output, and the epilogue fused into
-decode.  Tolerances as for the recurrence (relative L1): 1e-5 for f32 data,
+standalone kernel over a stored [T, Hv, Dv] output, the epilogue fused into
+decode, and the prefill entry that runs the norm over its output in place.  Tolerances as for the recurrence (relative L1): 1e-5 for f32 data,
 2e-2 for 16-bit outputs.  Gate rows are padded with NaN that must never be
 read; padded decode rows are exact zeros."""
 import sys
@@ -231,3 +231,126 @@ def test_prefill_then_gated_norm(dev, sequential):
     want_y, _ = oracle.prefill_norm_case(case, norm)
     r = H.rel_l1(y, want_y)
     assert np.isfinite(y).all() and r <= H.OUT_TOL_HALF, f"rel-L1 {r:.3e}"
+
+
+# ---------------------------------------------------------------------------
+# the prefill entry with the gated norm (gdn_prefill_varlen_gated_norm): the
+# gated prefill, then the norm in place over its output on the same stream
+# ---------------------------------------------------------------------------
+def run_prefill_norm(case, norm, dev, *, sigmoid, sequential=False, aux=False):
+    dbufs, q, k, v = H.upload_views(case, dev, case.total_tokens)
+    snap = [t.clone() for t in dbufs.values()]
+    alpha, dt_bias, ssm_a, beta, cu, idx, has_init = (
+        torch.from_numpy(x).to(dev) for x in (case.alpha, case.dt_bias, case.ssm_a, case.beta,
+                                              case.cu_seqlens, case.idx, case.has_init))
+    pool = torch.from_numpy(case.pool).to(dev)
+    pool0 = pool.clone()
+    z = z_view(norm, case.total_tokens, case.hv, case.dv, dev)
+    w = H.to_dev(norm.w, norm.dtype, dev)
+    zw = [z.clone(), w.clone()]
+    y = gdn.prefill_varlen_gated_norm(q, k, v, alpha, dt_bias, ssm_a, beta, pool, cu, z, w,
+                                      scale=case.scale, norm_eps=norm.eps, sigmoid=sigmoid,
+                                      state_idx=idx, has_initial_state=has_init,
+                                      l2norm=case.l2norm, l2_eps=case.l2_eps,
+                                      sequential=sequential,
+                                      aux_stream=torch.cuda.Stream() if aux else None)
+    torch.cuda.synchronize()
+    same = (all(H.bytes_equal(a, b) for a, b in zip(snap, dbufs.values())) and
+            H.bytes_equal(zw[0], z) and H.bytes_equal(zw[1], w))
+    return H.PrefillResult(H.out_to_f64(y), pool, pool0, same), y
+
+
+# The elementwise bar of a normalised output.  y_i = o_i / rms(o) * w_i act(z_i)
+# divides o's error, which is bounded relative to the row's scale (the
+# per-unit bar of o), by the row's rms, so it reaches y as the same fraction
+# of |w_i act(z_i)|; y's own rounding adds a fraction of |y_i|, and a 16-bit
+# output has an absolute floor, the spacing of its subnormals (2^-24 for
+# fp16; none that matters for bf16 or f32).  Hence
+#   |y_got - y_want| <= c (|w_i act(z_i)| + |y_want|) + floor
+# with c the per-unit relative-L1 bar of the output tier (1e-5 for f32 data,
+# 2e-2 for a 16-bit output, whose o on rows of small rms sits about 1 % of
+# the row's scale from the oracle's f64 o where large terms cancel).  An
+# element that is wrong outright is off by about |y| or |w act(z)| and fails.
+SUBNORMAL_FLOOR = {W.F32: 0.0, W.BF16: 0.0, W.F16: 2.0 ** -24}
+
+
+def check_prefill_norm(case, res, want_y, want_state, norm, dev, sigmoid):
+    name = f"{case.name} normalised output"
+    assert np.isfinite(res.out).all(), f"{name}: non-finite"
+    H.check_units(res.out, want_y, 2, H.out_tol(case), name)
+    z = z_view(norm, case.total_tokens, case.hv, case.dv, dev).double().cpu().numpy()
+    w = H.to_dev(norm.w, norm.dtype, dev).double().cpu().numpy()
+    sg = 1.0 / (1.0 + np.exp(-z))
+    gate = np.abs(w * (sg if sigmoid else z * sg))
+    c = H.out_tol(case)
+    floor = SUBNORMAL_FLOOR[case.out_dtype]
+    ratio = (np.abs(res.out - want_y) - floor) / (gate + np.abs(want_y) + 1e-30)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    print(f"  {name}: worst (|d| - {floor:g}) / (|w act(z)| + |y|) = {worst:.3e} (bar {c:g})",
+          flush=True)
+    bad = ratio > c
+    assert not bad.any(), (f"{name}: {int(bad.sum())} elements outside {c:g} (|w act(z)| + |y|) "
+                           f"+ {floor:g}, worst {worst:.3e}; first at {tuple(np.argwhere(bad)[0])}")
+    # the states, the untouched slots and the inputs as for the plain prefill
+    H.check_prefill(case, res, want_y, want_state, check_out=False)
+
+
+PREFILL_NORM_CASES = [
+    # (lengths, hk, hv, dk, dv, dtype, gate row padding, sigmoid, sequential)
+    ([130, 1, 64, 77], 2, 4, 128, 128, W.BF16, 6, False, False),
+    ([130, 1, 64, 77], 2, 4, 128, 128, W.BF16, 6, False, True),
+    ([65, 200], 1, 3, 128, 64, W.F16, 0, True, False),
+    ([40, 9], 2, 2, 64, 48, W.F32, 3, False, False),       # token-sequential; row norm kernel
+    ([0, 33, 1], 1, 2, 32, 32, W.BF16, 0, True, False),    # an empty sequence
+]
+
+
+@pytest.mark.parametrize("spec", PREFILL_NORM_CASES,
+                         ids=lambda s: "L{}-hv{}-dk{}-dv{}-{}-{}-{}".format(
+                             "_".join(map(str, s[0])), s[2], s[3], s[4],
+                             W.DTYPE_NAMES[s[5]], "sigmoid" if s[7] else "silu",
+                             "sequential" if s[8] else "default"))
+def test_prefill_gated_norm_matrix(dev, spec):
+    lengths, hk, hv, dk, dv, dt, zpad, sig, seq = spec
+    announce(f"prefill + gated norm {spec}")
+    case = W.make_prefill_case("pgn", 5000 + sum(lengths) + dv, lengths=lengths, hk=hk, hv=hv,
+                               dk=dk, dv=dv, in_dtype=dt, out_dtype=dt,
+                               slots=len(lengths) + 2, has_init=[1, 0, 1, 1][:len(lengths)])
+    norm = W.norm_inputs(5000 + dv, case.total_tokens, hv, dv, dt, pad=zpad)
+    res, _ = run_prefill_norm(case, norm, dev, sigmoid=sig, sequential=seq)
+    want_y, want_state = oracle.prefill_norm_case(case, norm, sigmoid=sig)
+    check_prefill_norm(case, res, want_y, want_state, norm, dev, sig)
+
+
+def test_prefill_gated_norm_equals_prefill_then_norm(dev):
+    announce("prefill + gated norm vs gdn_prefill_varlen_gated then gdn_rmsnorm_gated, "
+             "byte for byte (split schedule on a second stream)")
+    case = W.make_prefill_case("pgn2", 77, lengths=[300, 129, 64, 5], hk=2, hv=4, dk=128,
+                               dv=128, in_dtype=W.BF16, out_dtype=W.BF16, slots=6,
+                               has_init=[1, 1, 0, 1])
+    norm = W.norm_inputs(77, case.total_tokens, case.hv, case.dv, W.BF16, pad=5)
+    _, y = run_prefill_norm(case, norm, dev, sigmoid=True, aux=True)
+    dbufs, q, k, v = H.upload_views(case, dev, case.total_tokens)
+    alpha, dt_bias, ssm_a, beta, cu, idx, has_init = (
+        torch.from_numpy(x).to(dev) for x in (case.alpha, case.dt_bias, case.ssm_a, case.beta,
+                                              case.cu_seqlens, case.idx, case.has_init))
+    pool = torch.from_numpy(case.pool).to(dev)
+    o = gdn.prefill_varlen_gated(q, k, v, alpha, dt_bias, ssm_a, beta, pool, cu,
+                                 scale=case.scale, state_idx=idx, has_initial_state=has_init,
+                                 l2norm=case.l2norm, l2_eps=case.l2_eps,
+                                 aux_stream=torch.cuda.Stream())
+    z = z_view(norm, case.total_tokens, case.hv, case.dv, dev)
+    w = H.to_dev(norm.w, W.BF16, dev)
+    y2 = gdn.rmsnorm_gated(o, z, w, eps=norm.eps, sigmoid=True)
+    torch.cuda.synchronize()
+    assert H.bytes_equal(y, y2)
+
+
+def test_prefill_gated_norm_varlen_gqa3_all_heads(dev):
+    announce("prefill + gated norm, varlen 8 seqs T=32768 Hk8 Hv24 GQA3 fp16: every head "
+             "vs the oracle")
+    case = W.prefill_varlen_gqa3()
+    norm = W.norm_inputs(404, case.total_tokens, case.hv, case.dv, W.F16, pad=8)
+    res, _ = run_prefill_norm(case, norm, dev, sigmoid=False, aux=True)
+    want_y, want_state = oracle.prefill_norm_case(case, norm, sigmoid=False)
+    check_prefill_norm(case, res, want_y, want_state, norm, dev, False)
