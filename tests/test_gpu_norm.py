@@ -354,3 +354,56 @@ def test_prefill_gated_norm_varlen_gqa3_all_heads(dev):
     res, _ = run_prefill_norm(case, norm, dev, sigmoid=False, aux=True)
     want_y, want_state = oracle.prefill_norm_case(case, norm, sigmoid=False)
     check_prefill_norm(case, res, want_y, want_state, norm, dev, False)
+
+
+def test_prefill_gated_norm_in_a_captured_graph(dev):
+    """The entry's two launches captured into a graph (the whole call stays on
+    the captured stream): every replay, from a restored pool, gives the eager
+    call's normalised outputs and final states, and those match the oracle."""
+    announce("prefill + gated norm captured into a graph: replays equal the eager call")
+    case = W.make_prefill_case("pgng", 4545, lengths=[700, 130, 1, 64], hk=2, hv=4, dk=128,
+                               dv=128, in_dtype=W.BF16, out_dtype=W.BF16, slots=6,
+                               has_init=[1, 0, 1, 1])
+    norm = W.norm_inputs(4545, case.total_tokens, case.hv, case.dv, W.BF16, pad=3)
+    T, N = case.total_tokens, case.num_seqs
+    _, q, k, v = H.upload_views(case, dev, T)
+    t = lambda a: torch.from_numpy(a).to(dev)
+    alpha, dt_bias, ssm_a, beta = t(case.alpha), t(case.dt_bias), t(case.ssm_a), t(case.beta)
+    cu, idx, hi = t(case.cu_seqlens), t(case.idx), t(case.has_init)
+    z = z_view(norm, T, case.hv, case.dv, dev)
+    w = H.to_dev(norm.w, W.BF16, dev)
+    pool0 = t(case.pool)
+    ws = torch.empty(gdn.prefill_workspace_size(T, N, case.hk, case.hv, case.dk, case.dv,
+                                                torch.bfloat16), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, case.hv, case.dv), dtype=torch.bfloat16, device=dev)
+    pool = pool0.clone()
+
+    def call():
+        gdn.prefill_varlen_gated_norm(q, k, v, alpha, dt_bias, ssm_a, beta, pool, cu, z, w,
+                                      scale=case.scale, norm_eps=norm.eps, sigmoid=True,
+                                      state_idx=idx, has_initial_state=hi, out=out,
+                                      workspace=ws, stream=torch.cuda.current_stream())
+
+    call()
+    torch.cuda.synchronize()
+    want_out, want_pool = out.clone(), pool.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        pool.copy_(pool0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        pool.copy_(pool0)
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want_out), f"replay {rep}: outputs differ"
+        assert H.bytes_equal(pool, want_pool), f"replay {rep}: states differ"
+    want_y, want_s = oracle.prefill_norm_case(case, norm, sigmoid=True)
+    check_prefill_norm(case, H.PrefillResult(H.out_to_f64(want_out), want_pool, pool0, True),
+                       want_y, want_s, norm, dev, True)
