@@ -274,18 +274,27 @@ __device__ double plan_cost(int c, const int32_t* ocs, int n, int hv, double W, 
   return fmax(t1, t2) + 4.0;  // the second stream's launches and joins
 }
 
-__global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs m, int ntiles,
-                                                         int ncu, int kmax, int ksmax,
-                                                         int smax) {
-  __shared__ int32_t part[256];
+// The metadata kernel's LDS, also carved out of the prep kernel's when the
+// prep forms the metadata itself (one stream order).
+struct MetaLds {
+  int32_t part[256];
   // Up to kOrderMax sequences the three tables are built in LDS and copied
   // out once at the end (no global round trips between the steps).
-  __shared__ int32_t l_cs[kOrderMax + 1], l_order[kOrderMax], l_ocs[kOrderMax + 1];
+  int32_t l_cs[kOrderMax + 1], l_order[kOrderMax], l_ocs[kOrderMax + 1];
+  Plan plans[256];
+  double wcost[4];
+  int widx[4];
+};
+
+// Chunk offsets per sequence, the order of the sequences by length, the chunk
+// offsets in that order and the plan, by one workgroup of 256 threads.
+__device__ __forceinline__ void meta_body(const PrefillArgs& a, const MetaPtrs& m, int ntiles,
+                                          int ncu, int kmax, int ksmax, int smax, MetaLds& L) {
   const int n = (int)a.num_seqs;
   const bool small = n <= kOrderMax;
-  int32_t* const cs = small ? l_cs : m.cs;
-  int32_t* const order = small ? l_order : m.order;
-  int32_t* const ocs = small ? l_ocs : m.ocs;
+  int32_t* const cs = small ? L.l_cs : m.cs;
+  int32_t* const order = small ? L.l_order : m.order;
+  int32_t* const ocs = small ? L.l_ocs : m.ocs;
   int32_t carry = 0;
   if (threadIdx.x == 0) cs[0] = 0;
   for (int base = 0; base < n; base += 256) {
@@ -296,11 +305,11 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
       chunk_bounds(a, s, t0, t1);
       c = (int32_t)((t1 - t0 + CK - 1) / CK);
     }
-    const int32_t incl = block_scan256(c, part);
+    const int32_t incl = block_scan256(c, L.part);
     if (s < n) cs[s + 1] = carry + incl;
-    if (threadIdx.x == 255) part[0] = incl;
+    if (threadIdx.x == 255) L.part[0] = incl;
     __syncthreads();
-    carry += part[0];
+    carry += L.part[0];
     __syncthreads();
   }
   __syncthreads();
@@ -327,25 +336,22 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
       const int s = order[r];
       c = cs[s + 1] - cs[s];
     }
-    const int32_t incl = block_scan256(c, part);
+    const int32_t incl = block_scan256(c, L.part);
     if (r < n) ocs[r + 1] = carry + incl;
-    if (threadIdx.x == 255) part[0] = incl;
+    if (threadIdx.x == 255) L.part[0] = incl;
     __syncthreads();
-    carry += part[0];
+    carry += L.part[0];
     __syncthreads();
   }
   __syncthreads();
   // the plan: one candidate per thread, then the cheapest (ties: the lowest
   // index), by shuffles within each wave and then over the four waves
-  __shared__ Plan plans[256];
-  __shared__ double wcost[4];
-  __shared__ int widx[4];
   {
     Plan p = {0, 0, 1};
     double t = 1e300;
     if (small && threadIdx.x < kPlanCands)
       t = plan_cost(threadIdx.x, ocs, n, a.hv, (double)a.hv * ntiles, ncu, kmax, ksmax, smax, p);
-    plans[threadIdx.x] = p;
+    L.plans[threadIdx.x] = p;
     int bi = threadIdx.x;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -357,20 +363,20 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
       }
     }
     if ((threadIdx.x & 63) == 0) {
-      wcost[threadIdx.x >> 6] = t;
-      widx[threadIdx.x >> 6] = bi;
+      L.wcost[threadIdx.x >> 6] = t;
+      L.widx[threadIdx.x >> 6] = bi;
     }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    double t = wcost[0];
-    int bi = widx[0];
+    double t = L.wcost[0];
+    int bi = L.widx[0];
     for (int i = 1; i < 4; ++i)
-      if (wcost[i] < t) {
-        t = wcost[i];
-        bi = widx[i];
+      if (L.wcost[i] < t) {
+        t = L.wcost[i];
+        bi = L.widx[i];
       }
-    const Plan p = t < 1e299 ? plans[bi] : Plan{0, 0, 1};
+    const Plan p = t < 1e299 ? L.plans[bi] : Plan{0, 0, 1};
     m.info[0] = p.k;
     m.info[1] = p.ks;
     m.info[2] = p.S;
@@ -379,11 +385,18 @@ __global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs
   }
   if (small) {
     for (int i = threadIdx.x; i <= n; i += 256) {
-      m.cs[i] = l_cs[i];
-      m.ocs[i] = l_ocs[i];
-      if (i < n) m.order[i] = l_order[i];
+      m.cs[i] = L.l_cs[i];
+      m.ocs[i] = L.l_ocs[i];
+      if (i < n) m.order[i] = L.l_order[i];
     }
   }
+}
+
+__global__ __launch_bounds__(256) void chunk_meta_kernel(PrefillArgs a, MetaPtrs m, int ntiles,
+                                                         int ncu, int kmax, int ksmax,
+                                                         int smax) {
+  __shared__ MetaLds L;
+  meta_body(a, m, ntiles, ncu, kmax, ksmax, smax, L);
 }
 
 // The range of rank-order chunks [c0, c1) of a launch part: 0 = the ranks
@@ -805,32 +818,80 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
   }
 }
 
+// Launch part of the prep that also forms the metadata (one stream order, at
+// most 256 sequences): workgroup 0 runs the metadata kernel's work in the
+// prep's LDS, and every other workgroup finds its (sequence, chunk), in
+// sequence order, from cu_seqlens itself -- so no launch waits for the
+// metadata before the walks.
+constexpr int kPartSelf = 3;
+constexpr int kSelfMaxSeqs = 256;
+
+struct MetaIn {
+  int ntiles, ncu, ksmax, smax;
+};
+
 // One workgroup per (chunk, q/k head) unit of one launch part, the chunks
-// taken in rank order (longest sequences first); the grid covers every chunk
-// the call can have, and workgroups past the part's units leave at once.
-template <int TIN>
+// taken in rank order (longest sequences first; in sequence order for
+// kPartSelf); the grid covers every chunk the call can have, and workgroups
+// past the part's units leave at once.
+template <int TIN, bool SELF>
 __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, MetaPtrs m,
-                                                            char* recs, int part) {
+                                                            char* recs, int part, MetaIn mi) {
   __shared__ __align__(16) PrepLds sh;
   const int n = (int)a.num_seqs;
-  int c0, c1;
-  part_chunks(m, n, part, c0, c1);
-  const int64_t u = blockIdx.x;
-  if (u >= (int64_t)(c1 - c0) * a.hk) return;
-  const int cr = c0 + (int)(u / a.hk);
-  const int hk = (int)(u % a.hk);
-  int lo = 0, hi = n - 1;  // largest rank r with ocs[r] <= cr
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (m.ocs[mid] <= cr) lo = mid; else hi = mid - 1;
+  if constexpr (SELF) {  // part == kPartSelf
+    static_assert(sizeof(MetaLds) <= sizeof(PrepLds), "the metadata's LDS inside the prep's");
+    if (blockIdx.x == 0) {
+      meta_body(a, m, mi.ntiles, mi.ncu, 0, mi.ksmax, mi.smax, *reinterpret_cast<MetaLds*>(&sh));
+      return;
+    }
+    __shared__ int32_t scan_part[4];
+    __shared__ int32_t found[2];
+    const int64_t u = blockIdx.x - 1;
+    const int cr = (int)(u / a.hk);  // chunk index in sequence order: the record's
+    const int hk = (int)(u % a.hk);
+    const int t = threadIdx.x;
+    int32_t c = 0;
+    if (t < n) {
+      int64_t t0, t1;
+      chunk_bounds(a, t, t0, t1);
+      c = (int32_t)((t1 - t0 + CK - 1) / CK);
+    }
+    if (t == 0) found[0] = -1;
+    const int32_t incl = block_scan256(c, scan_part);  // its barriers order the line above
+    if (t < n && cr >= incl - c && cr < incl) {
+      found[0] = t;
+      found[1] = cr - (incl - c);
+    }
+    __syncthreads();
+    const int s = found[0];
+    if (s < 0) return;  // past the call's last chunk (the same for the whole workgroup)
+    const int j = found[1];
+    int64_t t0, t1;
+    chunk_bounds(a, s, t0, t1);
+    const int64_t tb = t0 + (int64_t)j * CK;
+    prep_unit<TIN>(a, recs, sh, cr, hk, tb, (int)min((int64_t)CK, t1 - tb));
+  } else {
+    (void)mi;
+    int c0, c1;
+    part_chunks(m, n, part, c0, c1);
+    const int64_t u = blockIdx.x;
+    if (u >= (int64_t)(c1 - c0) * a.hk) return;
+    const int cr = c0 + (int)(u / a.hk);
+    const int hk = (int)(u % a.hk);
+    int lo = 0, hi = n - 1;  // largest rank r with ocs[r] <= cr
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (m.ocs[mid] <= cr) lo = mid; else hi = mid - 1;
+    }
+    const int s = m.order[lo];
+    const int j = cr - m.ocs[lo];
+    int64_t t0, t1;
+    chunk_bounds(a, s, t0, t1);
+    const int64_t tb = t0 + (int64_t)j * CK;
+    const int L = (int)min((int64_t)CK, t1 - tb);
+    prep_unit<TIN>(a, recs, sh, m.cs[s] + j, hk, tb, L);
   }
-  const int s = m.order[lo];
-  const int j = cr - m.ocs[lo];
-  int64_t t0, t1;
-  chunk_bounds(a, s, t0, t1);
-  const int64_t tb = t0 + (int64_t)j * CK;
-  const int L = (int)min((int64_t)CK, t1 - tb);
-  prep_unit<TIN>(a, recs, sh, m.cs[s] + j, hk, tb, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1784,15 +1845,23 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream,
     kmax = (int)std::min<int64_t>({(int64_t)kSplitMax, a.num_seqs - 1,
                                    (int64_t)(ncu / 2 / per_seq_wgs)});
 
-  hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, m, ntiles, ncu, kmax,
-                     ksmax, smax);
+  // In one stream order with few sequences the prep launch forms the
+  // metadata itself (its workgroup 0); otherwise a launch of its own does.
+  const bool self_meta = kmax == 0 && a.num_seqs <= kSelfMaxSeqs;
+  const MetaIn mi{ntiles, ncu, ksmax, smax};
+  if (!self_meta)
+    hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(256), 0, stream, a, m, ntiles, ncu, kmax,
+                       ksmax, smax);
 
   const int64_t prep_units = mc * a.hk;
-  if (prep_units >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  const unsigned prep_grid = (unsigned)prep_units;
+  if (prep_units + 1 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   auto prep = [&](int part, hipStream_t st) {
-    hipLaunchKernelGGL((chunk_prep_kernel<TIN>), dim3(prep_grid), dim3(256), 0, st, a, m, recs,
-                       part);
+    if (part == kPartSelf)
+      hipLaunchKernelGGL((chunk_prep_kernel<TIN, true>), dim3((unsigned)(prep_units + 1)),
+                         dim3(256), 0, st, a, m, recs, part, mi);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<TIN, false>), dim3((unsigned)prep_units), dim3(256),
+                         0, st, a, m, recs, part, mi);
   };
   const int ratio = a.hv / a.hk;
   const size_t lds = 2 * sizeof(WalkBuf<WALK_NW, WALK_NB>);
@@ -1832,7 +1901,7 @@ hipError_t launch_chunked_t(const PrefillArgs& a, void* ws, hipStream_t stream,
   if (kmax == 0) {
     // one stream: all records, the first phase of the split ranks (if the
     // device chose any), then every walk with outputs
-    prep(2, stream);
+    prep(self_meta ? kPartSelf : 2, stream);
     if (a_items > 0 && (e = walk(0, a_items, stream, false)) != hipSuccess) return e;
     if ((e = walk(2, a.num_seqs + seg_items, stream, true)) != hipSuccess) return e;
     return hipGetLastError();
