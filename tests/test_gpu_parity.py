@@ -413,11 +413,14 @@ def test_prefill_skewed_batch_in_a_captured_graph(dev):
                     want_o, want_s)
 
 
-@pytest.mark.parametrize("nseq", [300, 1100], ids=["n300", "n1100"])
+@pytest.mark.parametrize("nseq", [256, 257, 300, 1100], ids=["n256", "n257", "n300", "n1100"])
 def test_prefill_many_short_sequences(dev, nseq):
-    """Hundreds of short sequences (zero-length ones among them): the chunked
-    path's per-call metadata spans several 256-wide scans, and beyond 1024
-    sequences the walk keeps index order instead of ranking by length."""
+    """Hundreds of short sequences (zero-length ones among them), in one
+    stream order: up to 256 sequences the prep launch forms the metadata in
+    its workgroup 0 and its other workgroups index themselves from
+    cu_seqlens, above that the metadata has a launch of its own and spans
+    several 256-wide scans, and beyond 1024 sequences the walk keeps index
+    order instead of ranking by length."""
     announce(f"prefill {nseq} short sequences (0..20 tokens), GQA 2, bf16")
     rng = np.random.default_rng(nseq)
     lengths = [int(x) for x in rng.integers(0, 21, size=nseq)]
