@@ -274,7 +274,7 @@ class PrefillResult:
 
 
 def run_prefill(case: W.PrefillCase, dev, *, sequential: bool = False, keep_pool0=True,
-                pool=None) -> PrefillResult:
+                pool=None, aux: bool = False) -> PrefillResult:
     dbufs, q, k, v = upload_views(case, dev, case.total_tokens)
     snap = [t.clone() for t in dbufs.values()]
     alpha = torch.from_numpy(case.alpha).to(dev)
@@ -291,7 +291,8 @@ def run_prefill(case: W.PrefillCase, dev, *, sequential: bool = False, keep_pool
     out = gdn.prefill_varlen(q, k, v, g, beta, pool, cu, scale=case.scale, state_idx=idx,
                              has_initial_state=has_init, l2norm=case.l2norm,
                              l2_eps=case.l2_eps, out_dtype=TORCH_OF[case.out_dtype],
-                             sequential=sequential)
+                             sequential=sequential,
+                             aux_stream=torch.cuda.Stream() if aux else None)
     torch.cuda.synchronize()
     same = all(bytes_equal(a, b) for a, b in zip(snap, dbufs.values()))
     return PrefillResult(out_to_f64(out), pool, pool0, same)

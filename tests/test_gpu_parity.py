@@ -113,6 +113,8 @@ DECODE_CASES = [
     (5, 3, 9, 128, 130, W.BF16, W.F32, 7, 256, ()),
     (3, 1, 2, 256, 128, W.BF16, W.BF16, 4, None, ()),
     (9, 4, 8, 128, 128, W.F32, W.F32, 12, 32, (0,)),
+    # GQA 8 with 256 state rows per head
+    (4, 1, 8, 128, 256, W.BF16, W.BF16, 6, None, (1,)),
 ]
 
 
@@ -428,6 +430,35 @@ def test_prefill_many_short_sequences(dev, nseq):
                                in_dtype=W.BF16, out_dtype=W.BF16, slots=nseq + 3,
                                has_init=[int(x) for x in rng.integers(0, 2, size=nseq)])
     res = H.run_prefill(case, dev)
+    want_out, want_state = oracle.prefill_case(case)
+    H.check_prefill(case, res, want_out, want_state)
+
+
+# GQA groups wider than the prep's four v-heads at once (ratios 5, 8 and 9:
+# the gate factors of a second and third group are formed mid-unit), exactly
+# one group (4), and the narrowest and widest state rows the chunked walk
+# takes (Dv = 16: three of its four waves past Dv; Dv = 256: four 64-row
+# workgroups per v-head)
+WIDE_CASES = [
+    # (lengths, hk, hv, dv, in, out, has_init)
+    ([130, 64, 1, 300], 1, 5, 128, W.BF16, W.BF16, [1, 0, 1, 1]),
+    ([200, 0, 65], 1, 8, 64, W.F16, W.F16, [1, 1, 0]),
+    ([129, 40], 2, 18, 32, W.BF16, W.F32, [0, 1]),
+    ([257, 3], 1, 4, 256, W.F16, W.F16, [1, 1]),
+    ([190, 64, 7], 2, 2, 16, W.BF16, W.BF16, [1, 0, 1]),
+]
+
+
+@pytest.mark.parametrize("aux", [False, True], ids=["one_stream", "split"])
+@pytest.mark.parametrize("spec", WIDE_CASES, ids=lambda s: "L{}-hk{}-hv{}-dv{}".format(
+    "_".join(map(str, s[0])), s[1], s[2], s[3]))
+def test_prefill_wide_gqa_and_state_rows(dev, spec, aux):
+    lengths, hk, hv, dv, ind, outd, hi = spec
+    announce(f"prefill wide GQA / state rows {spec} aux={aux}")
+    case = W.make_prefill_case("wide", 7100 + hv * 31 + dv, lengths=lengths, hk=hk, hv=hv,
+                               dk=128, dv=dv, in_dtype=ind, out_dtype=outd,
+                               slots=len(lengths) + 2, has_init=hi)
+    res = H.run_prefill(case, dev, aux=aux)
     want_out, want_state = oracle.prefill_case(case)
     H.check_prefill(case, res, want_out, want_state)
 
