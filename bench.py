@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
 METRIC = "GDN decode state GB/s (% HBM peak) @B=256; varlen prefill tokens/s"
+PREFILL_WARM_S = 0.3           # least warm-up of the prefill legs, in seconds of calls
 
 
 def log(*a):
@@ -251,25 +252,35 @@ def main():
     torch.cuda.synchronize()
     log(f"decode setup {time.time() - t_setup:.1f}s")
 
-    def timed(step, warmup, steps):
+    def timed(step, warmup, steps, warm_s=0.0):
         """Wall seconds over `steps` launches after `warmup` (the timed region:
         nothing but the launches between two synchronisations), then each
         launch's duration (ms) from HIP events recorded on the launch stream
         around `steps` further launches.  The events are kept out of the wall
-        region because their markers add a gap between launches."""
-        for i in range(warmup):
-            step(i)
+        region because their markers add a gap between launches.  warm_s
+        extends the warm-up to at least that many seconds of launches: after
+        the host has prepared a leg's inputs the GPU's clocks take a few tens
+        of calls of the compute-bound prefill to come back up (the first 20
+        calls after an idle second run about 10 % slower), while the
+        memory-bound decode shows no such ramp."""
+        n = 0
+        t_w = time.perf_counter()
+        while n < warmup or time.perf_counter() - t_w < warm_s:
+            step(n)
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            step(warmup + i)
+            step(n + i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         for i in range(steps):
             ev[i][0].record(stream)
-            step(warmup + steps + i)
+            step(n + steps + i)
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         return wall, np.array([a.elapsed_time(b) for a, b in ev])
@@ -470,7 +481,7 @@ def main():
                                      out=pout, workspace=ws, stream=stream, aux_stream=aux)
 
         if want("prefill"):
-            pwall, pms = timed(lambda i: prefill_step(), 8, args.prefill_steps)
+            pwall, pms = timed(lambda i: prefill_step(), 8, args.prefill_steps, PREFILL_WARM_S)
             p_ms_step = pwall * 1e3 / args.prefill_steps
             pbytes = prefill_bytes(T, N, pre.hk, pre.hv, pre.dk, pre.dv, 2, 2,
                                    int(pre.has_init.sum()))
@@ -521,7 +532,7 @@ def main():
                                          out=out3, workspace=ws3, stream=stream,
                                          aux_stream=aux)
 
-            w3, k3ms = timed(t4096_step, 8, args.prefill_steps)
+            w3, k3ms = timed(t4096_step, 8, args.prefill_steps, PREFILL_WARM_S)
             ms3 = w3 * 1e3 / args.prefill_steps
             avg3 = float(k3ms.mean())
             bytes3 = prefill_bytes(T3, 1, p3.hk, p3.hv, p3.dk, p3.dv, 2, 2, 0)
@@ -634,7 +645,7 @@ def main():
                                               state_idx=pidx, has_initial_state=phi, out=pout,
                                               workspace=ws, stream=stream, aux_stream=aux)
 
-            gwall, gk = timed(prefill_norm_step, 4, args.prefill_steps)
+            gwall, gk = timed(prefill_norm_step, 4, args.prefill_steps, PREFILL_WARM_S)
             g_ms = gwall * 1e3 / args.prefill_steps
             result.setdefault("prefill", {})["with_gated_norm"] = {
                 "workload": "the same varlen prefill followed by the gated RMSNorm (silu, fp16 "
