@@ -438,19 +438,31 @@ __device__ __forceinline__ double wave_prefix64(double x) {
 //         16-bit (high part only; it multiplies U in the output term only)
 //   F   = f32 [4][64]: fz_i = e^{G_i} n_k,i,  fo_i = e^{G_i} scale n_q,i,
 //         fw_i = e^{G_last - G_i} n_k,i,  and F[3][0] = e^{G_last}
-// The walk multiplies T_b and P only in 32-token block pairs on or below the
-// diagonal, so their upper-right 32 x 32 quadrants (rows 0-31, columns 32-63)
-// are free.  A 16-bit output needs only P's high part; for an f32 output the
-// low part of P (P - high, rounded to 16 bits) is kept there: its quadrant
-// (0, 0) in T_b-high's free quadrant, (1, 0) in T_b-low's and (1, 1) in P's,
-// element (i, j) at row i % 32, column 32 + j % 32.  For 16-bit outputs the
-// free quadrants are never written or read.
+// Each [64][64] part is stored as its 4 x 4 grid of 16 x 16 blocks, 512 bytes
+// each (rows of 32 bytes inside), so every block that is written or read is
+// four whole 128-byte lines.  T_b and P are lower triangular: their blocks
+// (0, 1) and (2, 3), above the diagonal inside the diagonal 32 x 32
+// quadrants, are zero and neither written nor read (the walk's loads of them
+// fall outside the record's buffer range and arrive as zeros).  The walk
+// multiplies T_b and P only in 32-token block pairs on or below the
+// diagonal, so their upper-right 32 x 32 quadrants (blocks (0, 2), (0, 3),
+// (1, 2), (1, 3)) are free.  A 16-bit output needs only P's high part; for an
+// f32 output the low part of P (P - high, rounded to 16 bits) is kept there:
+// its quadrant (0, 0) in T_b-high's free quadrant, (1, 0) in T_b-low's and
+// (1, 1) in P's, element (i, j) at row i % 32, column 32 + j % 32.  For 16-bit
+// outputs the free quadrants are never written or read.
 // ---------------------------------------------------------------------------
 constexpr int REC_TH = 0;
 constexpr int REC_TL = CK * CK * 2;
 constexpr int REC_P = 2 * CK * CK * 2;
 constexpr int REC_F = 3 * CK * CK * 2;
 constexpr int REC_BYTES = REC_F + 4 * CK * 4;
+
+// 16-bit element index of (i, j) in a record part: block (i / 16, j / 16) of
+// the part's 4 x 4 grid of 256-element blocks, row-major inside the block.
+__device__ __forceinline__ int rec_elem(int i, int j) {
+  return (((i >> 4) << 2) + (j >> 4)) * 256 + (i & 15) * 16 + (j & 15);
+}
 
 // One workgroup per (chunk, q/k head): the raw products K K^T and Q K^T of the
 // chunk are shared by the v-heads of the GQA group, so they are formed once
@@ -641,7 +653,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     auto plo_dst = [&](int i, int j) {
       const int part = (i >> 5) + (j >> 5);
       return reinterpret_cast<uint16_t*>(rec + (part == 0 ? REC_TH : part == 1 ? REC_TL : REC_P)) +
-             (i & 31) * CK + 32 + (j & 31);
+             rec_elem(i & 31, 32 + (j & 31));
     };
 
     // A (strictly lower, scaled) into LDS and P (lower incl. diagonal,
@@ -678,7 +690,7 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
       uint16_t ph[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ph[r] = M::enc(pv[r]);
-      *reinterpret_cast<uint2*>(Pg + i * CK + j0) =
+      *reinterpret_cast<uint2*>(Pg + rec_elem(i, j0)) =
           make_uint2(ph[0] | ((uint32_t)ph[1] << 16), ph[2] | ((uint32_t)ph[3] << 16));
       if (plo) {
         uint16_t pl[4];
@@ -700,13 +712,13 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
           ap_tile(std::false_type{}, k, t, ti, tj);
       }
     }
-    // the strictly-upper 16x16 blocks of P that the walk reads, (0, 1) and
-    // (2, 3), are zero
-    if (tid_h < 64) {
+    // P's strictly-upper blocks (0, 1) and (2, 3) reach the walk as zeros
+    // without being stored; the low part's, in the free quadrants the walk
+    // fetches for an f32 output, are stored as zeros
+    if (plo && tid_h < 64) {
       const int blk = tid_h >> 5, e = tid_h & 31;
       const int i = 32 * blk + (e >> 1), j8 = 32 * blk + 16 + 8 * (e & 1);
-      *reinterpret_cast<uint4*>(Pg + i * CK + j8) = make_uint4(0u, 0u, 0u, 0u);
-      if (plo) *reinterpret_cast<uint4*>(plo_dst(i, j8)) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(plo_dst(i, j8)) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
@@ -782,8 +794,9 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     }
     __syncthreads();
 
-    // T_b = T diag(beta), split into high and low 16-bit parts (blocks above
-    // the diagonal are zero; the unread upper-right quadrant is skipped)
+    // T_b = T diag(beta), split into high and low 16-bit parts; only the ten
+    // lower blocks are stored (those above the diagonal are zero or the free
+    // quadrant)
     uint16_t* Th = reinterpret_cast<uint16_t*>(rec + REC_TH);
     uint16_t* Tl = reinterpret_cast<uint16_t*>(rec + REC_TL);
     // eight consecutive columns of a row per thread: one 16-byte store each
@@ -791,14 +804,11 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
     for (int k = 0; k < 2; ++k) {
       const int idx = tid_h + 256 * k;
       const int i = idx >> 3, j8 = 8 * (idx & 7);
-      if (i < 32 && j8 >= 32) continue;
       const int bi = i >> 4, bj = j8 >> 4;
-      float4 t0 = make_float4(0.f, 0.f, 0.f, 0.f), t1 = t0;
-      if (bj <= bi) {
-        const float* tr = Tb + lower_blk(bi, bj) * BLK + (i & 15) * LDB + (j8 & 15);
-        t0 = *reinterpret_cast<const float4*>(tr);
-        t1 = *reinterpret_cast<const float4*>(tr + 4);
-      }
+      if (bj > bi) continue;  // zero blocks and the free quadrant
+      const float* tr = Tb + lower_blk(bi, bj) * BLK + (i & 15) * LDB + (j8 & 15);
+      const float4 t0 = *reinterpret_cast<const float4*>(tr);
+      const float4 t1 = *reinterpret_cast<const float4*>(tr + 4);
       const float4 b0 = *reinterpret_cast<const float4*>(&sh.bt[hs][j8]);
       const float4 b1 = *reinterpret_cast<const float4*>(&sh.bt[hs][j8 + 4]);
       const float x[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
@@ -811,8 +821,8 @@ __device__ __forceinline__ void prep_unit(const PrefillArgs& a, char* recs, Prep
         hw[e] = h0 | ((uint32_t)h1 << 16);
         lw[e] = l0 | ((uint32_t)l1 << 16);
       }
-      *reinterpret_cast<uint4*>(Th + i * CK + j8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4*>(Tl + i * CK + j8) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      *reinterpret_cast<uint4*>(Th + rec_elem(i, j8)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4*>(Tl + rec_elem(i, j8)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
     __syncthreads();  // the next head rewrites A and T (and, per group, Gd and bt)
   }
@@ -1009,8 +1019,11 @@ __device__ __forceinline__ void stage_offsets(StageOffsets<NW, NB>& o, const Pre
   for (int i = 0; i < SO::NTP; ++i) {
     const int p = 64 * (NW * i + w) + lane, row = p >> 3, chunk = (p & 7) ^ tp_swz(row);
     // the free upper-right quadrants hold P's low part for an f32 output and
-    // are otherwise not fetched (their offset then lies past the record)
-    o.tp[i] = !FULL && row < 32 && chunk >= 4 ? kDropOffset : 2 * (row * CK + 8 * chunk);
+    // are otherwise not fetched, nor are the zero blocks (0, 1) and (2, 3):
+    // their offset then lies past the record and they arrive as zeros
+    const bool free_q = row < 32 && chunk >= 4;
+    const bool zero_blk = (chunk >> 1) > (row >> 4) && !free_q;
+    o.tp[i] = (!FULL && free_q) || zero_blk ? kDropOffset : 2 * rec_elem(row, 8 * chunk);
   }
   constexpr int VCH = 2 * NW * NB;  // 16-byte chunks per V row
 #pragma unroll
