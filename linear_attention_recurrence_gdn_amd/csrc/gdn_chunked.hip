@@ -849,6 +849,10 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, MetaP
                                                             char* recs, int part, MetaIn mi) {
   __shared__ __align__(16) PrepLds sh;
   const int n = (int)a.num_seqs;
+  // records the workspace holds: a well-formed cu_seqlens never needs more,
+  // but overlapping ranges (clamped, not rejected) can, and their surplus
+  // records are not formed (the walk does not read past this count either)
+  const int64_t rec_cap = (a.total_tokens + CK - 1) / CK + a.num_seqs;
   if constexpr (SELF) {  // part == kPartSelf
     static_assert(sizeof(MetaLds) <= sizeof(PrepLds), "the metadata's LDS inside the prep's");
     if (blockIdx.x == 0) {
@@ -875,7 +879,9 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, MetaP
     }
     __syncthreads();
     const int s = found[0];
-    if (s < 0) return;  // past the call's last chunk (the same for the whole workgroup)
+    // past the call's last chunk, or past the records the workspace holds
+    // (the same for the whole workgroup)
+    if (s < 0 || cr >= rec_cap) return;
     const int j = found[1];
     int64_t t0, t1;
     chunk_bounds(a, s, t0, t1);
@@ -896,6 +902,7 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(PrefillArgs a, MetaP
     }
     const int s = m.order[lo];
     const int j = cr - m.ocs[lo];
+    if (m.cs[s] + j >= rec_cap) return;  // only with overlapping ranges
     int64_t t0, t1;
     chunk_bounds(a, s, t0, t1);
     const int64_t tb = t0 + (int64_t)j * CK;

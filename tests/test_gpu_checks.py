@@ -168,3 +168,40 @@ def test_prefill_check_slots_accepts_a_valid_table(dev, sequential):
     res = H.PrefillResult(H.out_to_f64(out), pool, pool0, True)
     want_out, want_state = oracle.prefill_case(case)
     H.check_prefill(case, res, want_out, want_state)
+
+
+@pytest.mark.parametrize("aux", [False, True], ids=["one_stream", "split"])
+def test_prefill_overlapping_cu_seqlens_stay_inside_the_workspace(dev, aux):
+    """Without the check an overlapping cu_seqlens is clamped, not rejected.
+    Here sequences 0 and 4 both cover all 6400 tokens: with the longest
+    sequences ranked first, sequence 4's chunks are formed at record indices
+    past the ceil(T / 64) + num_seqs records the workspace holds.  Nothing
+    may be written past the workspace (a guard of 0xA5 bytes right behind it
+    keeps its bytes), slots no sequence names keep theirs, empty sequences
+    hand their states through, and sequence 0, whose records all fit, still
+    ends in the oracle's state."""
+    announce(f"prefill with overlapping cu_seqlens, unchecked, aux={aux}")
+    case = W.make_prefill_case("ovl", 8800, lengths=[6400, 0, 0, 0, 0, 0], hk=2, hv=4,
+                               dk=128, dv=128, in_dtype=W.BF16, out_dtype=W.BF16, slots=9,
+                               has_init=[1] * 6)
+    cu = np.array([0, 6400, 0, 64, 0, 6400, 6400], dtype=np.int32)
+    q, k, v, g, beta, pool = prefill_inputs(case, dev)
+    T, N = case.total_tokens, case.num_seqs
+    ws_n = gdn.prefill_workspace_size(T, N, case.hk, case.hv, case.dk, case.dv, torch.bfloat16)
+    guard = 1 << 18
+    buf = torch.full((ws_n + guard,), 0xA5, dtype=torch.uint8, device=dev)
+    pool0 = pool.clone()
+    gdn.prefill_varlen(q, k, v, g, beta, pool, torch.from_numpy(cu).to(dev), scale=case.scale,
+                       state_idx=torch.from_numpy(case.idx).to(dev),
+                       has_initial_state=torch.from_numpy(case.has_init).to(dev),
+                       out_dtype=torch.bfloat16, workspace=buf[:ws_n],
+                       aux_stream=torch.cuda.Stream() if aux else None)
+    torch.cuda.synchronize()
+    assert torch.all(buf[ws_n:] == 0xA5), "bytes written past the workspace"
+    idx = [int(x) for x in case.idx]
+    for sl in range(case.num_slots):
+        if sl not in idx or sl in (idx[1], idx[3], idx[5]):
+            assert H.bytes_equal(pool[sl], pool0[sl]), f"slot {sl} changed"
+    _, want_state = oracle.prefill_case(case)
+    got = pool[idx[0]].float().cpu().numpy()[None]
+    H.check_units(got, want_state[0:1], 2, H.STATE_TOL, "sequence 0 state")
