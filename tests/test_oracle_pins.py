@@ -349,6 +349,40 @@ def test_linear_in_state_and_values():
     np.testing.assert_allclose(sab, sa + sb, rtol=1e-6, atol=1e-6)
 
 
+def test_a_run_of_tokens_maps_the_state_affinely():
+    """The map that splitting a sequence into segments rests on: over a run of
+    tokens the final state is S_in M + S_loc, with M = prod_t decay_t (I -
+    beta_t k_t k_t^T) the run's walk of the identity with v = 0 (a dk x dk
+    "state") and S_loc its walk from zero.  Both are formed here by the oracle
+    itself and checked against its walk from random entry states, with a
+    gate that underflows exp inside the run."""
+    rng = np.random.default_rng(29)
+    T, dk, dv = 23, 8, 5
+    q = r32(rng.normal(size=(T, 1, dk)))
+    k = r32(rng.normal(size=(T, 1, dk)))
+    v = r32(rng.normal(size=(T, 1, dv)))
+    g = -np.abs(rng.normal(size=(T, 1)))
+    g[7, 0] = -900.0
+    beta = rng.uniform(0.05, 0.95, size=(T, 1)).astype(np.float32)
+    eye = np.eye(dk, dtype=np.float32)[None, None]
+    _, M = run_prefill(q, k, np.zeros((T, 1, dk)), g, beta, eye, 0.3, [0, T], l2norm=True)
+    _, S_loc = run_prefill(q, k, v, g, beta, np.zeros((1, 1, dv, dk), np.float32), 0.3, [0, T],
+                           l2norm=True)
+    M, S_loc = M[0, 0], S_loc[0, 0]
+    # M is the product of the per-token maps, taken in token order
+    kn = k[:, 0].astype(np.float64)
+    kn = kn / np.sqrt((kn ** 2).sum(-1, keepdims=True) + 1e-6)
+    P = np.eye(dk)
+    for t in range(T):
+        P = P @ (math.exp(g[t, 0]) * (np.eye(dk) - float(beta[t, 0]) * np.outer(kn[t], kn[t])))
+    np.testing.assert_allclose(M, P, rtol=1e-10, atol=1e-12)
+    for trial in range(3):
+        S_in = rng.normal(0, 0.5, size=(1, 1, dv, dk)).astype(np.float32)
+        _, S_out = run_prefill(q, k, v, g, beta, S_in, 0.3, [0, T], l2norm=True)
+        want = S_in[0, 0].astype(np.float64) @ M + S_loc
+        np.testing.assert_allclose(S_out[0, 0], want, rtol=1e-10, atol=1e-12)
+
+
 def test_gqa_ratio3_equals_independent_heads():
     d = gold("gqa_varlen_indexed.json")["gqa"]
     hk, hv, dk, dv = d["hk"], d["hv"], d["dk"], d["dv"]
